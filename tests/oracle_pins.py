@@ -1,0 +1,233 @@
+"""Pins of the CPU reference to facts outside itself.
+
+Each pin takes `run`, a callable with the signature of oracle.oracle_sgemm,
+and raises AssertionError when the reference disagrees with what mathematics
+or the pages fix.  The same pins run against the real reference (which must
+pass them all) and against deliberately broken builds of it (each of which
+must fail at least one), so a dropped term, a wrong sign, a wrong index or a
+transposed operand in the reference cannot go unnoticed.
+
+What pins what:
+  exact_fraction     brute force in exact rational arithmetic (every float32
+                     is a dyadic rational) on tiny odd shapes, incl. K = 4097
+  identity           A = I gives B, B = I gives A, bit for bit, non-square
+  permutation        permutation matrices permute rows / columns exactly
+  alpha_zero         alpha = 0 gives beta*C exactly and never reads A, B
+  beta_only          A = 0 gives beta*C exactly
+  beta_zero_nan_c    beta = 0 never reads C (NaN-filled C)
+  integer_exact      small-integer matrices against int64 matrix product
+  all_ones           A = B = 1 gives alpha*K + beta*c exactly
+  numpy_float64      random data against numpy's float64 matmul
+  sumabs             the error scale equals |A| @ |B|
+  ld_views           padded buffers (NaN padding) give the dense result
+  pages_row_major    the row-major buffer example of the lecture notes
+  pages_sub_block    the pointer-offset + ld sub-block example
+"""
+
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from dense_fp32_matrix_row_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "pages_examples.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _exact(A, B, C, alpha, beta):
+    M, K = A.shape
+    N = B.shape[1]
+    a = [[Fraction(float(x)) for x in row] for row in A]
+    b = [[Fraction(float(x)) for x in row] for row in B]
+    ref = np.empty((M, N), dtype=object)
+    sab = np.empty((M, N), dtype=object)
+    fa, fb = Fraction(float(np.float32(alpha))), Fraction(float(np.float32(beta)))
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            t = Fraction(0)
+            for k in range(K):
+                p = a[i][k] * b[k][j]
+                s += p
+                t += abs(p)
+            ref[i, j] = fa * s + fb * Fraction(float(C[i, j]))
+            sab[i, j] = t
+    return ref, sab
+
+
+def pin_exact_fraction(run):
+    rng = np.random.default_rng(7)
+    shapes = [(1, 1, 1), (2, 3, 5), (7, 5, 3), (3, 13, 2), (13, 7, 13), (5, 1, 7), (1, 1, 4097)]
+    for idx, (M, N, K) in enumerate(shapes):
+        A = inputs.uniform_f32(rng, (M, K))
+        B = inputs.uniform_f32(rng, (K, N))
+        C = inputs.uniform_f32(rng, (M, N))
+        alpha, beta = [(1.0, 0.0), (0.5, 3.0), (-1.25, 1.0), (1.0, -1.0)][idx % 4]
+        res = run(A, B, C, alpha, beta)
+        ref_x, sab_x = _exact(A, B, C, alpha, beta)
+        for i in range(M):
+            for j in range(N):
+                scale = float(abs(Fraction(alpha)) * sab_x[i, j] + abs(Fraction(beta) * Fraction(float(C[i, j]))))
+                tol = 4.0 * (K + 2) * 2.0 ** -53 * scale
+                assert abs(Fraction(res.ref[i, j]) - ref_x[i, j]) <= Fraction(tol), (M, N, K, i, j)
+                assert abs(Fraction(res.sumabs[i, j]) - sab_x[i, j]) <= Fraction(4.0 * (K + 2) * 2.0 ** -53 * float(sab_x[i, j])), (M, N, K, i, j)
+
+
+def pin_identity(run):
+    rng = np.random.default_rng(11)
+    for (M, N) in [(5, 9), (17, 3), (1, 8)]:
+        B = inputs.uniform_f32(rng, (M, N))
+        res = run(np.eye(M, dtype=np.float32), B, None, 1.0, 0.0)
+        assert np.array_equal(res.ref, B.astype(np.float64)), ("A=I", M, N)
+        A = inputs.uniform_f32(rng, (N, M))
+        res = run(A, np.eye(M, dtype=np.float32), None, 1.0, 0.0)
+        assert np.array_equal(res.ref, A.astype(np.float64)), ("B=I", M, N)
+
+
+def pin_permutation(run):
+    rng = np.random.default_rng(13)
+    n = 19
+    P = inputs.permutation(n, seed=5)
+    perm = np.argmax(P, axis=1)             # (P @ X)[i] = X[perm[i]]
+    X = inputs.uniform_f32(rng, (n, 6))
+    res = run(P, X, None, 1.0, 0.0)
+    assert np.array_equal(res.ref, X[perm].astype(np.float64)), "row permutation"
+    Y = inputs.uniform_f32(rng, (4, n))
+    res = run(Y, P, None, 1.0, 0.0)         # (Y @ P)[:, perm[i]] = Y[:, i]
+    expect = np.empty_like(Y)
+    expect[:, perm] = Y
+    assert np.array_equal(res.ref, expect.astype(np.float64)), "column permutation"
+
+
+def pin_alpha_zero(run):
+    rng = np.random.default_rng(17)
+    M, N, K = 6, 7, 5
+    A = np.full((M, K), np.nan, dtype=np.float32)
+    B = np.full((K, N), np.nan, dtype=np.float32)
+    C = inputs.uniform_f32(rng, (M, N))
+    res = run(A, B, C, 0.0, 3.0)
+    assert np.array_equal(res.ref, 3.0 * C.astype(np.float64)), "alpha = 0 gives beta*C"
+    assert np.all(res.sumabs == 0.0)
+    res = run(A, B, C, 0.0, 0.0)
+    assert np.all(res.ref == 0.0), "alpha = beta = 0 gives 0"
+    # K = 0 is the same quick return
+    res = run(np.zeros((M, 0), np.float32), np.zeros((0, N), np.float32), C, 1.0, -1.0,
+              M=M, N=N, K=0, lda=1, ldb=N, ldc=N)
+    assert np.array_equal(res.ref, -1.0 * C.astype(np.float64)), "K = 0 gives beta*C"
+
+
+def pin_beta_only(run):
+    rng = np.random.default_rng(19)
+    M, N, K = 5, 11, 9
+    B = inputs.uniform_f32(rng, (K, N))
+    C = inputs.uniform_f32(rng, (M, N))
+    for beta in (0.5, 3.0, -1.0):
+        res = run(np.zeros((M, K), np.float32), B, C, 1.0, beta)
+        assert np.array_equal(res.ref, beta * C.astype(np.float64)), beta
+
+
+def pin_beta_zero_nan_c(run):
+    rng = np.random.default_rng(23)
+    M, N, K = 7, 5, 6
+    A, B, _ = inputs.make_abc(M, N, K, 3)
+    C = np.full((M, N), np.nan, dtype=np.float32)
+    res = run(A, B, C, 1.0, 0.0)
+    assert np.all(np.isfinite(res.ref)), "beta = 0 must not read C"
+    ref2 = run(A, B, np.zeros((M, N), np.float32), 1.0, 0.0).ref
+    assert np.array_equal(res.ref, ref2)
+
+
+def pin_integer_exact(run):
+    for idx, (M, N, K) in enumerate([(9, 13, 17), (33, 31, 65), (1, 129, 3), (40, 1, 257)]):
+        A, B, C = inputs.integer_abc(M, N, K, seed=100 + idx)
+        alpha, beta = [(1.0, 0.0), (2.0, 1.0), (0.5, -1.0), (1.0, 3.0)][idx]
+        res = run(A, B, C, alpha, beta)
+        prod = A.astype(np.int64) @ B.astype(np.int64)
+        expect = alpha * prod.astype(np.float64) + (beta * C.astype(np.float64) if beta else 0.0)
+        assert np.array_equal(res.ref, expect), (M, N, K)
+        assert np.array_equal(res.sumabs, (np.abs(A.astype(np.int64)) @ np.abs(B.astype(np.int64))).astype(np.float64))
+
+
+def pin_all_ones(run):
+    rng = np.random.default_rng(29)
+    for (M, N, K) in [(3, 4, 1), (8, 3, 37), (2, 2, 4097)]:
+        C = inputs.uniform_f32(rng, (M, N))
+        res = run(np.ones((M, K), np.float32), np.ones((K, N), np.float32), C, 0.5, 3.0)
+        assert np.array_equal(res.ref, 0.5 * K + 3.0 * C.astype(np.float64)), (M, N, K)
+
+
+def pin_numpy_float64(run):
+    M, N, K = 64, 80, 96
+    A, B, C = inputs.make_abc(M, N, K, 31)
+    for alpha, beta in [(1.0, 0.0), (0.5, 3.0), (-2.0, 1.0)]:
+        res = run(A, B, C, alpha, beta)
+        A64, B64, C64 = (x.astype(np.float64) for x in (A, B, C))
+        expect = alpha * (A64 @ B64) + beta * C64
+        scale = abs(alpha) * (np.abs(A64) @ np.abs(B64)) + np.abs(beta * C64)
+        assert np.all(np.abs(res.ref - expect) <= 1e-12 * scale), (alpha, beta)
+
+
+def pin_sumabs(run):
+    M, N, K = 23, 29, 31
+    A, B, C = inputs.make_abc(M, N, K, 37)
+    res = run(A, B, C, -0.75, 2.0)
+    expect = np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64))
+    assert np.all(np.abs(res.sumabs - expect) <= 1e-13 * expect)
+
+
+def pin_ld_views(run):
+    M, N, K = 13, 21, 17
+    A, B, C = inputs.make_abc(M, N, K, 41)
+    lda, ldb, ldc = K + 3, N + 5, N + 7
+    Ap = inputs.padded(A, lda, np.nan)
+    Bp = inputs.padded(B, ldb, np.nan)
+    Cp = inputs.padded(C, ldc, np.nan)
+    res = run(Ap, Bp, Cp, 0.5, 3.0, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
+    dense = run(A, B, C, 0.5, 3.0)
+    assert np.array_equal(res.ref, dense.ref)
+    assert np.array_equal(res.sumabs, dense.sumabs)
+
+
+def pin_pages_row_major(run):
+    g = golden()["row_major_buffer"]
+    buf = np.array(g["buffer"], dtype=np.float32)
+    # the buffer as a 2 x 3 row-major A times I3 reproduces the row-major reading
+    res = run(buf.copy(), np.eye(3, dtype=np.float32), None, 1.0, 0.0, M=2, N=3, K=3, lda=3)
+    assert np.array_equal(res.ref, np.array(g["row_major_2x3"], dtype=np.float64))
+    # the same memory read column-major is the transpose (the operand-swap
+    # trick of section 5.4 rests on this)
+    assert np.array_equal(res.ref.T, np.array(g["col_major_3x2"], dtype=np.float64))
+    # and as the right operand: I2 @ (buffer as 2 x 3) is the same matrix
+    res = run(np.eye(2, dtype=np.float32), buf.copy(), None, 1.0, 0.0, M=2, N=3, K=2, ldb=3)
+    assert np.array_equal(res.ref, np.array(g["row_major_2x3"], dtype=np.float64))
+
+
+def pin_pages_sub_block(run):
+    g = golden()["sub_block_view"]
+    R, Cc = g["parent_rows"], g["parent_cols"]
+    parent_cm = np.arange(1, R * Cc + 1, dtype=np.float32)       # column-major 5 x 4 buffer
+    X = parent_cm.reshape(Cc, R).T                               # X[r][c] = buf[r + c*R]
+    r0, c0 = g["start"]
+    h, w = g["shape"]
+    sub = X[r0:r0 + h, c0:c0 + w]                                # the 3 x 2 column-major sub-block
+    # the same buffer read row-major is X^T (4 x 5, ld 5); the sub-block's
+    # transpose starts at the page's offset with the page's ld
+    off, ld = g["offset"], g["ld"]
+    view = parent_cm[off:].copy()
+    res = run(view, np.eye(h, dtype=np.float32), None, 1.0, 0.0, M=w, N=h, K=h, lda=ld)
+    assert np.array_equal(res.ref, sub.T.astype(np.float64))
+
+
+ALL_PINS = [
+    pin_exact_fraction, pin_identity, pin_permutation, pin_alpha_zero, pin_beta_only,
+    pin_beta_zero_nan_c, pin_integer_exact, pin_all_ones, pin_numpy_float64, pin_sumabs,
+    pin_ld_views, pin_pages_row_major, pin_pages_sub_block,
+]
