@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of libsgemm on one MI355X.
+
+Default: the 4096^3 workload (alpha = 0.5, beta = 3, i.i.d. uniform[-1, 1]
+inputs from seed 1003) through hip_sgemm (the library's own kernel choice),
+W untimed warm-up calls, then exactly K timed calls, each on its own freshly
+filled copy of C (so every step computes C <- 0.5*A@B + 3*C from the same
+pristine inputs, and no restore copy sits inside the timed region).  Inputs
+are resident in HBM before timing starts.
+
+Prints one JSON line: TFLOPS over the timed region (2*M*N*K per step), the
+dominant kernel's roofline (its mean duration from HIP events recorded around
+each launch on the launch stream, against the 157.3 TFLOP/s FP32 matrix
+peak), and the CPU reference timed on the host on a bounded sample of the
+same problem (its first rows), whose output also checks the GPU's rows.
+
+Options: --level L forces a ladder rung (hip_sgemm_level); --workload picks
+another of the five problem sizes; --ladder PATH times every level on every
+workload and writes one JSON line per pair to PATH (the headline line is
+still printed last); --no-cpu skips the CPU leg.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SGEMM TFLOPS at M=N=K=4096 (fraction of FP32 peak) on one MI355X"
+PEAK_FP32_TFLOPS = 157.3   # MI355X FP32 matrix (and packed vector) peak
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--level", type=int, default=None)
+    ap.add_argument("--workload", default="sgemm_4096")
+    ap.add_argument("--ladder", default=None, metavar="PATH")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the reference sample")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources, used to tell whether recorded hardware
+    counters still describe the kernels being timed."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_fp32_matrix_row_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, level_name: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    passes (profiles/pmc_traffic_<level>_<workload>.txt), or None when absent
+    or taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"pmc_traffic_{level_name}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Problem:
+    def __init__(self, w, copies: int):
+        import numpy as np
+        import torch
+
+        from dense_fp32_matrix_row_amd import inputs
+        self.w = w
+        A, B, C = inputs.make_workload(w)
+        self.host = (A, B, C)
+        self.dA = torch.from_numpy(A).cuda()
+        self.dB = torch.from_numpy(B).cuda()
+        self.dC0 = torch.from_numpy(C).cuda()
+        self.copies = [torch.empty_like(self.dC0) for _ in range(copies)]
+        del np
+
+    def refill(self):
+        for c in self.copies:
+            c.copy_(self.dC0)
+
+
+def run_timed(prob: Problem, level, steps: int, warmup: int):
+    """Warm-up and timed calls on the current stream.  Returns (ms_per_step
+    from the host clock over the whole timed region, mean kernel ms from the
+    per-launch HIP events)."""
+    import torch
+
+    from dense_fp32_matrix_row_amd import sgemm
+    w = prob.w
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+
+    def call(c):
+        args = (w.M, w.N, w.K, w.alpha, prob.dA, w.K, prob.dB, w.N, w.beta, c, w.N, handle)
+        st = sgemm.hip_sgemm(*args) if level is None else sgemm.hip_sgemm_level(level, *args)
+        if st != 0:
+            raise RuntimeError(sgemm.hip_sgemm_status_string(st))
+
+    prob.refill()
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        call(prob.copies[i % len(prob.copies)])
+    prob.refill()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call(prob.copies[i])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+    return (t1 - t0) * 1e3 / steps, kernel_ms
+
+
+def cpu_baseline(prob: Problem, gpu_out_rows, target_s: float):
+    """The CPU reference on the first R rows of the same problem, R sized for
+    about target_s seconds; returns the baseline record and the GPU's max
+    normalised error on those rows."""
+    import numpy as np
+
+    from oracle import oracle
+    A, B, C = prob.host
+    w = prob.w
+    probe = 32
+    t = time.perf_counter()
+    oracle.oracle_sgemm(np.ascontiguousarray(A[:probe]), B, np.ascontiguousarray(C[:probe]), w.alpha, w.beta)
+    rate = probe / max(time.perf_counter() - t, 1e-6)          # rows per second
+    rows = int(min(w.M, max(probe, (rate * target_s) // 32 * 32)))
+    t = time.perf_counter()
+    ref = oracle.oracle_sgemm(np.ascontiguousarray(A[:rows]), B, np.ascontiguousarray(C[:rows]),
+                              w.alpha, w.beta)
+    dt = time.perf_counter() - t
+    out = gpu_out_rows(rows)
+    err = oracle.normalised_error(out, ref, C[:rows], w.alpha, w.beta, strict=True)
+    rec = {"value": 2.0 * rows * w.N * w.K / dt / 1e12, "unit": "TFLOPS", "cores": ref.threads,
+           "kind": "oracle",
+           "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} problem ({rows}x{w.N}x{w.K}, "
+                     f"{dt:.1f} s, float64 accumulation)"}
+    return rec, err
+
+
+def device_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    clock_mhz = None
+    try:
+        import ctypes
+        # hipDeviceAttributeClockRate (kHz) through torch's HIP runtime
+        lib = ctypes.CDLL("libamdhip64.so.7")
+        val = ctypes.c_int()
+        if lib.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) == 0:   # hipDeviceAttributeClockRate
+            clock_mhz = val.value / 1000.0
+    except OSError:
+        pass
+    cus = p.multi_processor_count
+    info = {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", None), "cus": cus,
+            "clock_mhz": clock_mhz}
+    if clock_mhz:
+        info["derived_fp32_peak_tflops"] = round(cus * 256 * clock_mhz * 1e6 / 1e12, 1)
+    return info
+
+
+def bench_one(w, level, steps, warmup, prob=None):
+    from dense_fp32_matrix_row_amd import sgemm
+    prob = prob or Problem(w, max(steps, warmup, 1))
+    ms, kms = run_timed(prob, level, steps, warmup)
+    eff_level = level if level is not None else sgemm.hip_sgemm_auto_level(
+        w.M, w.N, w.K, prob.dA, w.K, prob.dB, w.N, prob.dC0, w.N)
+    name = sgemm.hip_sgemm_level_name(eff_level)
+    return prob, ms, kms, eff_level, name
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernel shards by C tiles across GPUs, but no multi-GPU path is built)",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    from dense_fp32_matrix_row_amd import inputs, sgemm
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    sgemm.load()
+    w = inputs.WORKLOADS_BY_NAME[args.workload]
+    steps, warmup = max(1, args.steps), max(0, args.warmup)
+
+    if args.ladder:
+        with open(args.ladder, "w") as f:
+            for wl in inputs.WORKLOADS:
+                prob = Problem(wl, max(steps, warmup, 1))
+                for lv in range(sgemm.hip_sgemm_num_levels()):
+                    st = min(steps, 3) if lv <= 1 and wl.M >= 2048 else steps
+                    _, ms, kms, _, name = bench_one(wl, lv, st, min(warmup, 2), prob)
+                    rec = {"workload": wl.name, "level": lv, "level_name": name, "steps": st,
+                           "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+                           "tflops": round(wl.flops / (kms * 1e-3) / 1e12, 3),
+                           "frac_fp32_peak": round(wl.flops / (kms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+                    f.write(json.dumps(rec) + "\n")
+                    f.flush()
+                    print(f"[ladder] {wl.name} L{lv} {name}: {kms:.4f} ms, {rec['tflops']} TFLOPS",
+                          flush=True)
+                del prob
+                torch.cuda.empty_cache()
+
+    prob, ms, kms, lv, name = bench_one(w, args.level, steps, warmup)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    achieved = w.flops / (kms * 1e-3) / 1e12
+    roofline = {"bound": "mfma" if lv == 9 else "alu", "achieved": round(achieved, 3),
+                "peak": PEAK_FP32_TFLOPS if lv == 9 else PEAK_FP32_TFLOPS / 2,
+                "unit": "TFLOP/s", "frac": None, "traffic": recorded_traffic(w.name, name)}
+    roofline["frac"] = round(achieved / roofline["peak"], 4)
+    line = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (i.i.d. uniform[-1,1], seeded)",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha,
+                   "beta": w.beta, "level": lv, "level_name": name, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
+        "kernel_ms": round(kms, 4),
+        "device": device_info(),
+    }
+    if not args.no_cpu:
+        def rows_out(r):
+            # one more call on a fresh C, outside any timed region
+            c = prob.copies[0]
+            c.copy_(prob.dC0)
+            st = (sgemm.hip_sgemm if args.level is None else
+                  (lambda *a: sgemm.hip_sgemm_level(args.level, *a)))(
+                w.M, w.N, w.K, w.alpha, prob.dA, w.K, prob.dB, w.N, w.beta, c, w.N, None)
+            if st != 0:
+                raise RuntimeError(sgemm.hip_sgemm_status_string(st))
+            torch.cuda.synchronize()
+            return c[:r].cpu().numpy()
+        rec, err = cpu_baseline(prob, rows_out, args.cpu_seconds)
+        line["cpu_baseline"] = rec
+        line["parity_max_normalised_error_on_sample"] = err
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

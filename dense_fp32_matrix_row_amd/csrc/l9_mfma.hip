@@ -1,0 +1,241 @@
+// l9_mfma.hip -- level 9: the level-8 pipeline with the FMA core moved onto
+// the FP32 matrix cores (v_mfma_f32_32x32x2_f32: a 32 x 32 x 2 product, full
+// float32 inputs and accumulators, 2048 FMAs per instruction per wavefront).
+//
+// None of the pages programs matrix instructions for FP32 ([L04] section 5.5
+// only names them as what libraries add on top of tiling); GEMM is a dense
+// contraction, so on gfx950 the FMA core belongs on the matrix cores.  The
+// pages' xf32 reduced-precision modes are not used (gfx950 has none for FP32,
+// and ~10-bit inputs would miss the 1e-5 normalised error bound).
+//
+// Block tile BM x BN (128 x 128, or 64 x 64 for problems too small to fill
+// 256 CUs with 128 x 128 tiles), BK = 16, 256 threads = 2 x 2 wavefronts, each
+// owning a WTM x WTN wave tile made of BLK_M x BLK_N 32 x 32 MFMA blocks.
+//
+// Operand layout of the 32x32x2 instruction (one block): lane l supplies
+// A[l % 32][l / 32] and B[l / 32][l % 32]; accumulator register r of lane l
+// holds C[8*(r/4) + 4*(l/32) + r%4][l % 32].  Rows and columns of the wave tile
+// are interleaved over the blocks: MFMA row i of block bi is wave-tile row
+// BLK_M*i + bi (columns likewise), so the BLK_M A values a lane needs for one
+// k are adjacent in the transposed LDS tile (one 64-bit read for BLK_M = 2),
+// and a lane's BLK_N outputs of one row are adjacent in C (one 64-bit store).
+// MFMA step s of a K-phase consumes k = 2s + l/32.
+//
+// The staging (A transposed into LDS, 128-bit global loads when aligned,
+// element-wise edge-safe loads otherwise, zero-fill beyond M/N/K), the
+// double-buffered one-barrier pipeline and the XCD-aware grouped block order
+// are those of level 8.  The summation order inside an instruction is the
+// hardware's, so results differ from levels 0-8 in the last bits (all within
+// the float32 rounding bound); integer-valued inputs still give exact results.
+#include "sgemm_internal.h"
+
+namespace sgemm {
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kWavesM = 2, kWavesN = 2;
+constexpr int kBK = 16;
+constexpr int kPad = 4;      // LDS row padding (words)
+constexpr int kGroupM = 8;   // tile-rows per group of the block order
+
+template <int N>
+struct VecT;
+template <>
+struct VecT<1> { typedef float type; };
+template <>
+struct VecT<2> { typedef float2 type; };
+template <>
+struct VecT<4> { typedef float4 type; };
+
+template <int N>
+__device__ __forceinline__ float vget(const typename VecT<N>::type& v, int i);
+template <>
+__device__ __forceinline__ float vget<1>(const float& v, int) { return v; }
+template <>
+__device__ __forceinline__ float vget<2>(const float2& v, int i) {
+  return i == 0 ? v.x : v.y;
+}
+template <>
+__device__ __forceinline__ float vget<4>(const float4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t bid, int64_t nblocks) {
+  const int64_t q = nblocks / 8, r = nblocks % 8;
+  const int64_t x = bid % 8, local = bid / 8;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
+template <int BM, int BN, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_level9(Problem p, int64_t tiles_m,
+                                                     int64_t tiles_n,
+                                                     int64_t ntiles) {
+  constexpr int WTM = BM / kWavesM, WTN = BN / kWavesN;
+  constexpr int BLK_M = WTM / 32, BLK_N = WTN / 32;
+  constexpr int LDA = BM + kPad, LDB = BN + kPad;
+  constexpr int A_ITERS = (BM * kBK / 4) / kThreads;  // float4 of A per thread
+  constexpr int B_ITERS = (BN * kBK / 4) / kThreads;
+  static_assert(A_ITERS >= 1 && B_ITERS >= 1, "tile too small for 256 threads");
+  static_assert(BLK_M >= 1 && BLK_N >= 1, "wave tile below one MFMA block");
+  typedef typename VecT<BLK_M>::type AFrag;
+  typedef typename VecT<BLK_N>::type BFrag;
+
+  __shared__ __align__(16) float As[2][kBK][LDA];
+  __shared__ __align__(16) float Bs[2][kBK][LDB];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int lrow = lane % 32, khalf = lane / 32;
+  // LDS offsets (words) of this lane's fragments inside one k-row
+  const int a_off = wm * WTM + BLK_M * lrow;
+  const int b_off = wn * WTN + BLK_N * lrow;
+
+  const int64_t nk = ceil_div(p.K, kBK);
+  const int64_t first = xcd_contiguous(blockIdx.x, gridDim.x);
+  for (int64_t t = first; t < ntiles; t += gridDim.x) {
+    const int64_t group = kGroupM * tiles_n;
+    const int64_t first_m = (t / group) * kGroupM;
+    const int64_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+    const int64_t in = t % group;
+    const int64_t row0 = (first_m + in % gm) * BM;
+    const int64_t col0 = (in / gm) * BN;
+
+    floatx16 acc[BLK_M][BLK_N];
+#pragma unroll
+    for (int bi = 0; bi < BLK_M; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < BLK_N; ++bj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
+
+    float4 ra[A_ITERS], rb[B_ITERS];
+    auto load = [&](int64_t k0) {
+#pragma unroll
+      for (int s = 0; s < A_ITERS; ++s) {
+        const int idx = tid + s * kThreads;
+        const int r = idx / (kBK / 4), kq = idx % (kBK / 4);
+        ra[s] = load4<VEC>(p.A + (row0 + r) * p.lda, k0 + 4 * kq, p.K,
+                           row0 + r < p.M);
+      }
+#pragma unroll
+      for (int s = 0; s < B_ITERS; ++s) {
+        const int idx = tid + s * kThreads;
+        const int r = idx / (BN / 4), nq = idx % (BN / 4);
+        rb[s] = load4<VEC>(p.B + (k0 + r) * p.ldb, col0 + 4 * nq, p.N,
+                           k0 + r < p.K);
+      }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+      for (int s = 0; s < A_ITERS; ++s) {
+        const int idx = tid + s * kThreads;
+        const int r = idx / (kBK / 4), kq = idx % (kBK / 4);
+        As[buf][4 * kq + 0][r] = ra[s].x;
+        As[buf][4 * kq + 1][r] = ra[s].y;
+        As[buf][4 * kq + 2][r] = ra[s].z;
+        As[buf][4 * kq + 3][r] = ra[s].w;
+      }
+#pragma unroll
+      for (int s = 0; s < B_ITERS; ++s) {
+        const int idx = tid + s * kThreads;
+        const int r = idx / (BN / 4), nq = idx % (BN / 4);
+        *reinterpret_cast<float4*>(&Bs[buf][r][4 * nq]) = rb[s];
+      }
+    };
+
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      const int cur = static_cast<int>(kt & 1);
+      const bool more = kt + 1 < nk;
+      if (more) load((kt + 1) * kBK);
+#pragma unroll
+      for (int s = 0; s < kBK / 2; ++s) {
+        const int kk = 2 * s + khalf;
+        const AFrag af = *reinterpret_cast<const AFrag*>(&As[cur][kk][a_off]);
+        const BFrag bf = *reinterpret_cast<const BFrag*>(&Bs[cur][kk][b_off]);
+#pragma unroll
+        for (int bi = 0; bi < BLK_M; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < BLK_N; ++bj)
+            acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                vget<BLK_M>(af, bi), vget<BLK_N>(bf, bj), acc[bi][bj], 0, 0, 0);
+      }
+      if (more) store(cur ^ 1);
+      __syncthreads();
+    }
+
+    // Epilogue: register r of block (bi, bj) is C[row(bi, r)][col(bj)].
+#pragma unroll
+    for (int bi = 0; bi < BLK_M; ++bi) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r / 4) + 4 * khalf + (r % 4);
+        const int64_t row = row0 + wm * WTM + BLK_M * i + bi;
+        if (row >= p.M) continue;
+        const int64_t col = col0 + b_off;
+        float* c = p.C + row * p.ldc + col;
+        if (BLK_N == 2 && VEC && col + 1 < p.N) {
+          float2 o = make_float2(p.alpha * acc[bi][0][r],
+                                 p.alpha * acc[bi][BLK_N - 1][r]);
+          if (p.beta != 0.0f) {
+            const float2 old = *reinterpret_cast<const float2*>(c);
+            o.x = fmaf(p.beta, old.x, o.x);
+            o.y = fmaf(p.beta, old.y, o.y);
+          }
+          *reinterpret_cast<float2*>(c) = o;
+        } else {
+#pragma unroll
+          for (int bj = 0; bj < BLK_N; ++bj)
+            if (col + bj < p.N)
+              c[bj] = epilogue(acc[bi][bj][r], p.alpha, p.beta, c + bj);
+        }
+      }
+    }
+  }
+}
+
+// 128 x 128 tiles once they give every CU at least two blocks; 64 x 64 below.
+constexpr int kCUs = 256;
+bool use_big_tiles(int M, int N) {
+  return ceil_div(M, 128) * ceil_div(N, 128) >= 2 * kCUs;
+}
+
+Geometry geometry9(int M, int N, int K) {
+  const int t = use_big_tiles(M, N) ? 128 : 64;
+  return make_geometry(M, N, K, t, t, kBK, kThreads);
+}
+
+template <int BM, int BN>
+void launch_tiles(const Problem& p, hipStream_t s, const Geometry& g) {
+  const dim3 grid(static_cast<unsigned>(g.workgroups)), block(kThreads);
+  const int64_t tm = ceil_div(p.M, BM), tn = ceil_div(p.N, BN);
+  if (vec4_ok(p))
+    hipLaunchKernelGGL((k_level9<BM, BN, true>), grid, block, 0, s, p, tm, tn,
+                       g.tiles);
+  else
+    hipLaunchKernelGGL((k_level9<BM, BN, false>), grid, block, 0, s, p, tm, tn,
+                       g.tiles);
+}
+
+hipError_t launch9(const Problem& p, hipStream_t s) {
+  const Geometry g = geometry9(p.M, p.N, p.K);
+  if (g.tile_m == 128)
+    launch_tiles<128, 128>(p, s, g);
+  else
+    launch_tiles<64, 64>(p, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+const LevelDesc* level9() {
+  static const LevelDesc d = {"L9_mfma_f32_32x32x2", geometry9, launch9};
+  return &d;
+}
+
+}  // namespace sgemm

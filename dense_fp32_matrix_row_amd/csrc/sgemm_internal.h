@@ -1,0 +1,147 @@
+// sgemm_internal.h -- types and device helpers shared by the kernels of
+// libsgemm (not installed; the public interface is include/sgemm.h).
+//
+// Citation keys ([SIX], [CP04], [L04], [GEMM2]) are defined in sgemm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm {
+
+// One call's arguments, with the leading dimensions widened to 64 bits so
+// that row*ld never overflows (the page kernels index with int products,
+// which wrap past 46340^2 elements).
+struct Problem {
+  int M, N, K;
+  float alpha, beta;
+  const float* A;
+  int64_t lda;
+  const float* B;
+  int64_t ldb;
+  float* C;
+  int64_t ldc;
+};
+
+// Launch geometry of one level for one shape.
+struct Geometry {
+  int64_t workgroups;  // blocks launched (tiles are walked grid-stride when
+                       // there are more tiles than blocks)
+  int threads;         // threads per block
+  int64_t k_steps;     // K phases per tile: ceil(K / BK)
+  int tile_m, tile_n;  // C tile per block
+  int64_t tiles;       // tiles of C
+};
+
+using GeometryFn = Geometry (*)(int M, int N, int K);
+using LaunchFn = hipError_t (*)(const Problem&, hipStream_t);
+
+struct LevelDesc {
+  const char* name;
+  GeometryFn geometry;
+  LaunchFn launch;
+};
+
+// Blocks per launch are capped so that blocks * threads stays below 2^31
+// work-items (the dispatch packet's grid size is 32-bit); tiles beyond the
+// cap are walked grid-stride by the same blocks.
+constexpr int64_t kMaxWorkItems = int64_t(1) << 31;
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) {
+  return (a + b - 1) / b;
+}
+
+inline Geometry make_geometry(int M, int N, int K, int tile_m, int tile_n,
+                              int bk, int threads) {
+  Geometry g;
+  g.tile_m = tile_m;
+  g.tile_n = tile_n;
+  g.threads = threads;
+  g.tiles = ceil_div(M, tile_m) * ceil_div(N, tile_n);
+  const int64_t cap = kMaxWorkItems / threads;
+  g.workgroups = g.tiles < cap ? g.tiles : cap;
+  g.k_steps = ceil_div(K, bk);
+  return g;
+}
+
+// Vector (128-bit) paths need 16-byte aligned bases and row strides that
+// keep every row start 16-byte aligned.
+inline bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+inline bool vec4_ok(const Problem& p) {
+  return aligned16(p.A) && aligned16(p.B) && aligned16(p.C) &&
+         (p.lda % 4) == 0 && (p.ldb % 4) == 0 && (p.ldc % 4) == 0;
+}
+
+// The epilogue of every level: alpha*acc + beta*c, with C read only when
+// beta != 0 (BLAS convention; the page kernels read C unconditionally).
+__device__ __forceinline__ float epilogue(float acc, float alpha, float beta,
+                                          const float* c) {
+  const float r = alpha * acc;
+  return beta == 0.0f ? r : fmaf(beta, *c, r);
+}
+
+// Four consecutive elements [col, col+4) of one row, zero outside
+// [0, ncols) or when the row is out of range (the zero-fill boundary rule of
+// [L04] section 2.5).  VEC: the row start is 16-byte aligned and col is a
+// multiple of 4, so a full group is one 128-bit load; a partial group at the
+// edge falls back to element loads (never the whole-group drop of [SIX] K6).
+template <bool VEC>
+__device__ __forceinline__ float4 load4(const float* __restrict__ row_ptr,
+                                        int64_t col, int64_t ncols,
+                                        bool row_ok) {
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (!row_ok) return v;
+  if (VEC && col + 3 < ncols) {
+    v = *reinterpret_cast<const float4*>(row_ptr + col);
+  } else {
+    if (col + 0 < ncols) v.x = row_ptr[col + 0];
+    if (col + 1 < ncols) v.y = row_ptr[col + 1];
+    if (col + 2 < ncols) v.z = row_ptr[col + 2];
+    if (col + 3 < ncols) v.w = row_ptr[col + 3];
+  }
+  return v;
+}
+
+// Epilogue for four consecutive outputs C[row][col .. col+3] (only those
+// below N are written; c points at C[row][col]).
+template <bool VEC>
+__device__ __forceinline__ void store4(float* __restrict__ c, int64_t col,
+                                       int64_t N, float4 acc, float alpha,
+                                       float beta) {
+  if (VEC && col + 3 < N) {
+    float4 r = make_float4(alpha * acc.x, alpha * acc.y, alpha * acc.z,
+                           alpha * acc.w);
+    if (beta != 0.0f) {
+      const float4 old = *reinterpret_cast<const float4*>(c);
+      r.x = fmaf(beta, old.x, r.x);
+      r.y = fmaf(beta, old.y, r.y);
+      r.z = fmaf(beta, old.z, r.z);
+      r.w = fmaf(beta, old.w, r.w);
+    }
+    *reinterpret_cast<float4*>(c) = r;
+  } else {
+    if (col + 0 < N) c[0] = epilogue(acc.x, alpha, beta, c + 0);
+    if (col + 1 < N) c[1] = epilogue(acc.y, alpha, beta, c + 1);
+    if (col + 2 < N) c[2] = epilogue(acc.z, alpha, beta, c + 2);
+    if (col + 3 < N) c[3] = epilogue(acc.w, alpha, beta, c + 3);
+  }
+}
+
+// C <- beta*C over the M x N window (the K == 0 / alpha == 0 quick return).
+hipError_t launch_scale(const Problem& p, hipStream_t stream);
+
+// The ten rungs (host-side descriptors).
+const LevelDesc* level0();
+const LevelDesc* level1();
+const LevelDesc* level2();
+const LevelDesc* level3();
+const LevelDesc* level4();
+const LevelDesc* level5();
+const LevelDesc* level6();
+const LevelDesc* level7();
+const LevelDesc* level8();
+const LevelDesc* level9();
+
+}  // namespace sgemm

@@ -1,0 +1,174 @@
+"""Python binding of libsgemm (ctypes).  Argument marshalling only: every
+operation runs in the library's HIP kernels; there is no fallback.
+
+The functions carry the C ABI's names and argument order (include/sgemm.h).
+Matrix arguments accept a torch device tensor (its data_ptr() is passed), an
+integer device address, or None (NULL).  `stream` accepts None (torch's
+current stream on the current device), a torch.cuda.Stream, or an integer
+hipStream_t handle (0 = the null stream).
+
+torch is imported before the library is loaded: torch ships its own HIP
+runtime (libamdhip64.so.7) and the library must bind to that same runtime,
+so that device pointers and stream handles from torch are valid for it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libsgemm.so")
+
+STATUS_UNKNOWN_LEVEL = -100
+STATUS_TOO_LARGE = -101
+
+# Every exported symbol of include/sgemm.h.
+EXPORTS = (
+    "hip_sgemm", "hip_sgemm_level", "hip_sgemm_num_levels", "hip_sgemm_level_name",
+    "hip_sgemm_status_string", "hip_sgemm_auto_level", "hip_sgemm_launch_shape",
+)
+
+_lib = None
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libsgemm status {status}: {message}")
+        self.status = status
+
+
+def load(path: Optional[str] = None):
+    """Load libsgemm.so (built by dense_fp32_matrix_row_amd.build).  Raises
+    if it is missing: there is no other implementation to fall back on."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    import torch  # noqa: F401  (binds the library to torch's HIP runtime)
+    path = LIBRARY if path is None else path
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m dense_fp32_matrix_row_amd.build` "
+                           "or __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    fptr, vp, i32, f32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    gemm_args = [i32, i32, i32, f32, vp, i32, vp, i32, f32, vp, i32, vp]
+    lib.hip_sgemm.restype = i32
+    lib.hip_sgemm.argtypes = gemm_args
+    lib.hip_sgemm_level.restype = i32
+    lib.hip_sgemm_level.argtypes = [i32] + gemm_args
+    lib.hip_sgemm_num_levels.restype = i32
+    lib.hip_sgemm_num_levels.argtypes = []
+    lib.hip_sgemm_level_name.restype = ctypes.c_char_p
+    lib.hip_sgemm_level_name.argtypes = [i32]
+    lib.hip_sgemm_status_string.restype = ctypes.c_char_p
+    lib.hip_sgemm_status_string.argtypes = [i32]
+    lib.hip_sgemm_auto_level.restype = i32
+    lib.hip_sgemm_auto_level.argtypes = [i32, i32, i32, vp, i32, vp, i32, vp, i32]
+    lib.hip_sgemm_launch_shape.restype = i32
+    lib.hip_sgemm_launch_shape.argtypes = [i32, i32, i32, i32,
+                                           ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(i32),
+                                           ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(i32),
+                                           ctypes.POINTER(i32)]
+    del fptr
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def _addr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    dp = getattr(x, "data_ptr", None)
+    if dp is None:
+        raise TypeError(f"expected a tensor, an int address or None, got {type(x).__name__}")
+    if getattr(x, "is_cuda", True) is False:
+        raise TypeError("matrix tensors must live on the GPU")
+    return int(dp())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        if not torch.cuda.is_available():
+            return None
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    handle = getattr(stream, "cuda_stream", None)
+    if handle is None:
+        raise TypeError("stream must be None, an int handle or a torch.cuda.Stream")
+    return int(handle)
+
+
+def hip_sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    """C <- alpha*A@B + beta*C with the library's choice of kernel; returns the
+    status code (0 = enqueued)."""
+    return int(load().hip_sgemm(int(M), int(N), int(K), float(alpha), _addr(A), int(lda),
+                                _addr(B), int(ldb), float(beta), _addr(C), int(ldc),
+                                _stream(stream)))
+
+
+def hip_sgemm_level(level, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    """Same as hip_sgemm with the ladder rung `level` forced."""
+    return int(load().hip_sgemm_level(int(level), int(M), int(N), int(K), float(alpha), _addr(A),
+                                      int(lda), _addr(B), int(ldb), float(beta), _addr(C),
+                                      int(ldc), _stream(stream)))
+
+
+def hip_sgemm_num_levels() -> int:
+    return int(load().hip_sgemm_num_levels())
+
+
+def hip_sgemm_level_name(level) -> Optional[str]:
+    s = load().hip_sgemm_level_name(int(level))
+    return None if s is None else s.decode()
+
+
+def hip_sgemm_status_string(status) -> str:
+    return load().hip_sgemm_status_string(int(status)).decode()
+
+
+def hip_sgemm_auto_level(M, N, K, A, lda, B, ldb, C, ldc) -> int:
+    return int(load().hip_sgemm_auto_level(int(M), int(N), int(K), _addr(A), int(lda), _addr(B),
+                                           int(ldb), _addr(C), int(ldc)))
+
+
+def hip_sgemm_launch_shape(level, M, N, K) -> dict:
+    """Launch geometry of a level for a shape (nothing is launched)."""
+    wg, kst = ctypes.c_longlong(), ctypes.c_longlong()
+    thr, tm, tn = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rc = load().hip_sgemm_launch_shape(int(level), int(M), int(N), int(K), ctypes.byref(wg),
+                                       ctypes.byref(thr), ctypes.byref(kst), ctypes.byref(tm),
+                                       ctypes.byref(tn))
+    if rc != 0:
+        raise SgemmError(rc, hip_sgemm_status_string(rc))
+    return {"workgroups": wg.value, "threads": thr.value, "k_steps": kst.value,
+            "tile_m": tm.value, "tile_n": tn.value}
+
+
+def check(status: int) -> None:
+    """Raise SgemmError for a non-zero status."""
+    if status != 0:
+        raise SgemmError(status, hip_sgemm_status_string(status))
+
+
+def sgemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, level: Optional[int] = None,
+          stream=None) -> None:
+    """Convenience form on 2-D row-major torch float32 device tensors whose
+    rows may be strided (column stride 1): C <- alpha*A@B + beta*C."""
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError(f"{name} must be a 2-D row-major view with unit column stride")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    lda, ldb, ldc = (max(t.stride(0), t.shape[1], 1) for t in (A, B, C))
+    if level is None:
+        rc = hip_sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    else:
+        rc = hip_sgemm_level(level, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    check(rc)

@@ -1,0 +1,152 @@
+/*
+ * sgemm.h -- libsgemm, single-precision GEMM on row-major matrices for the
+ * AMD Instinct MI355X (gfx950).
+ *
+ *     C <- alpha * A * B + beta * C
+ *
+ * Sources this interface follows (web pages; cited by short key in the
+ * library's sources):
+ *   [SIX]   daleiyang.github.io, "SGEMM 六级优化：核心代码的演化"
+ *           (SGEMM in six levels: how the core code evolves)
+ *   [CP04]  smarter.xin, "CUDA-Practice：04 从 Shared Memory Tiling 到寄存器外积"
+ *   [L04]   semidirectx.com, CMU 11-868 lecture 4 notes,
+ *           "GPU 加速：分块、内存并行、稀疏矩阵与 cuBLAS"
+ *   [GEMM2] pinghaoyang.com.cn, "GPU GEMM 优化完全拆解（二）：
+ *           寄存器分块、向量化访存与 Warp Tiling"
+ *
+ * The operation is the one every kernel of [SIX] computes (the store line of
+ * its K1 kernel: alpha*acc + beta*C over row-major A (M x K), B (K x N),
+ * C (M x N)), with the BLAS sgemm contract of [L04] section 5.2
+ * (C = alpha*op(A)*op(B) + beta*C, op = identity here) and the leading
+ * dimension of [L04] section 5.3, mirrored for row-major storage: ld is the
+ * number of elements between the starts of consecutive ROWS.
+ *
+ * Element (i, j) of A is A[i*lda + j]; of B, B[i*ldb + j]; of C, C[i*ldc + j].
+ *
+ * Ownership and concurrency
+ *   The caller owns every buffer; A, B and C are device pointers (HBM of the
+ *   current HIP device).  The library allocates nothing, keeps no state and
+ *   needs no handle; calls on different streams may run concurrently.  C must
+ *   not overlap A or B (undefined, unchecked, as in BLAS).
+ *
+ * Asynchrony
+ *   Every call enqueues its kernel on `stream` (0 = the null stream) and
+ *   returns without synchronising.  Argument errors are detected on the host
+ *   before anything is enqueued.
+ *
+ * Conventions where the pages are silent (BLAS conventions)
+ *   - M == 0 or N == 0: nothing is launched, returns 0.
+ *   - K == 0 or alpha == 0: C <- beta*C; A and B are never read.
+ *   - beta == 0: C is write-only (never read; NaN in C does not propagate).
+ *   - Only the M x N window of C is written; elements of the rows' padding
+ *     (columns N .. ldc-1) are never touched.
+ *   - Only 4-byte alignment is required.  Kernels take 128-bit vector paths
+ *     when the base pointers are 16-byte aligned and lda, ldb, ldc are
+ *     multiples of 4, and element-wise edge-safe paths otherwise; both are
+ *     correct for every shape (the page kernels of [SIX] K6 that drop the last
+ *     partial float4 group are not followed).
+ *   - Accumulation is float32 (round to nearest even, fused multiply-add);
+ *     the summation order differs between levels.
+ *
+ * Status codes (return value of every compute entry point)
+ *   0             success (the work is enqueued)
+ *   -i (1..12)    the i-th argument of hip_sgemm is invalid, BLAS style
+ *                 ("which parameter is illegal", [L04] section 5.3):
+ *                 -1 M < 0, -2 N < 0, -3 K < 0, -5 A is NULL although it is
+ *                 read, -6 lda < max(1, K), -7 B is NULL although it is read,
+ *                 -8 ldb < max(1, N), -10 C is NULL with M, N > 0,
+ *                 -11 ldc < max(1, N).  hip_sgemm_level numbers its
+ *                 arguments the same way (level is not counted).
+ *   -100          unknown level
+ *   -101          the problem is too large for this level's grid
+ *   > 0           the hipError_t the launch reported
+ */
+#ifndef LIBSGEMM_SGEMM_H
+#define LIBSGEMM_SGEMM_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGEMM_STATUS_UNKNOWN_LEVEL (-100)
+#define SGEMM_STATUS_TOO_LARGE (-101)
+
+/*
+ * Best kernel for the shape: C <- alpha*A*B + beta*C.
+ * A: M x K device matrix, row stride lda >= max(1, K).
+ * B: K x N device matrix, row stride ldb >= max(1, N).
+ * C: M x N device matrix, row stride ldc >= max(1, N), read only if beta != 0.
+ */
+int hip_sgemm(int M, int N, int K, float alpha,
+              const float *A, int lda,
+              const float *B, int ldb,
+              float beta, float *C, int ldc,
+              hipStream_t stream);
+
+/*
+ * Same operation with the rung of the optimisation ladder forced.  Every
+ * level is correct for every shape and alignment.  Levels (the page kernels
+ * each one re-designs for gfx950):
+ *   0 naive, consecutive lanes walk consecutive ROWS ([SIX] K1)
+ *   1 naive, consecutive lanes walk consecutive COLUMNS ([SIX] K2;
+ *     [L04] section 1.1)
+ *   2 LDS tiles 32 x 32, one output per thread, two barriers per phase,
+ *     padded rows ([SIX] K3; [CP04] tiled_gemm; [L04] sections 2.2-2.5)
+ *   3 thread coarsening, 4 column tiles per block ([SIX] K3c; [CP04]
+ *     coarse_gemm; [L04] section 2.7)
+ *   4 1-D register tile, 8 rows per thread ([SIX] K4; [GEMM2] kernel 4)
+ *   5 2-D register tile, 128 x 128 block, 8 x 8 outer product per thread
+ *     ([SIX] K5; [CP04] register_tiling_gemm; [GEMM2] kernel 5)
+ *   6 128-bit loads, A transposed in LDS, 128-bit LDS reads ([SIX] K6;
+ *     [GEMM2] kernel 6)
+ *   7 double-buffered LDS, one barrier per K step ([CP04]
+ *     double_buffer_gemm)
+ *   8 wave tiling (block -> wave -> lane) with an XCD-aware, grouped
+ *     block-to-tile order ([GEMM2] warp tiling and thread swizzling sections)
+ *   9 FP32 matrix cores (v_mfma_f32_32x32x2_f32) on the level-8 pipeline
+ */
+int hip_sgemm_level(int level, int M, int N, int K, float alpha,
+                    const float *A, int lda,
+                    const float *B, int ldb,
+                    float beta, float *C, int ldc,
+                    hipStream_t stream);
+
+/* Number of levels (valid levels are 0 .. hip_sgemm_num_levels()-1). */
+int hip_sgemm_num_levels(void);
+
+/* Short name of a level ("L9_mfma_f32_32x32x2", ...); NULL if unknown.  The
+ * string is static and owned by the library. */
+const char *hip_sgemm_level_name(int level);
+
+/* Human-readable text for a status code; static, owned by the library. */
+const char *hip_sgemm_status_string(int status);
+
+/*
+ * The level hip_sgemm picks for a shape and alignment (the same rule it
+ * applies), without launching anything.  Returns the level, or a negative
+ * status for invalid sizes.
+ */
+int hip_sgemm_auto_level(int M, int N, int K,
+                         const float *A, int lda,
+                         const float *B, int ldb,
+                         const float *C, int ldc);
+
+/*
+ * Launch geometry a level would use for a shape, without launching: the
+ * number of workgroups, threads per workgroup, K steps each workgroup walks
+ * (ceil(K / BK): the boundary rule of [L04] section 2.5 rounds the phase
+ * count up and zero-fills the tail), and the output tile (tile_m x tile_n)
+ * each workgroup owns.  Any output pointer may be NULL.  Returns 0, or a
+ * negative status.
+ */
+int hip_sgemm_launch_shape(int level, int M, int N, int K,
+                           long long *workgroups, int *threads_per_group,
+                           long long *k_steps, int *tile_m, int *tile_n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSGEMM_SGEMM_H */

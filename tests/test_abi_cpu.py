@@ -1,0 +1,121 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol its header
+declares, and rejects bad arguments on the host before any HIP call."""
+
+import os
+import re
+
+import pytest
+
+from dense_fp32_matrix_row_amd import sgemm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hip_sgemm\w*)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(sgemm.EXPORTS)
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_symbol_exported(name):
+    lib = sgemm.load()
+    assert hasattr(lib, name), name
+
+
+def test_levels_and_names():
+    n = sgemm.hip_sgemm_num_levels()
+    assert n == 10
+    names = [sgemm.hip_sgemm_level_name(i) for i in range(n)]
+    assert all(names) and len(set(names)) == n
+    assert names[0].startswith("L0_") and names[9].startswith("L9_mfma")
+    assert sgemm.hip_sgemm_level_name(-1) is None
+    assert sgemm.hip_sgemm_level_name(n) is None
+
+
+FAKE = 0x1000  # a non-NULL address that is never dereferenced (errors return first)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4), -1),
+    ((4, -1, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4), -2),
+    ((4, 4, -1, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4), -3),
+    ((4, 4, 4, 1.0, None, 4, FAKE, 4, 0.0, FAKE, 4), -5),
+    ((4, 4, 8, 1.0, FAKE, 7, FAKE, 4, 0.0, FAKE, 4), -6),
+    ((4, 4, 0, 1.0, FAKE, 0, FAKE, 4, 0.0, FAKE, 4), -6),    # lda >= max(1, K)
+    ((4, 4, 4, 1.0, FAKE, 4, None, 4, 0.0, FAKE, 4), -7),
+    ((4, 9, 4, 1.0, FAKE, 4, FAKE, 8, 0.0, FAKE, 9), -8),
+    ((4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, None, 4), -10),
+    ((4, 9, 4, 1.0, FAKE, 4, FAKE, 9, 0.0, FAKE, 8), -11),
+    ((-1, -1, -1, 1.0, None, 0, None, 0, 0.0, None, 0), -1),  # first bad argument wins
+])
+def test_argument_errors(args, status):
+    assert sgemm.hip_sgemm(*args, stream=0) == status
+    for level in range(sgemm.hip_sgemm_num_levels()):
+        assert sgemm.hip_sgemm_level(level, *args, stream=0) == status
+    assert sgemm.hip_sgemm_status_string(status).startswith(f"argument {-status} ")
+
+
+def test_null_operands_allowed_when_not_read():
+    # M == 0 or N == 0: nothing is read or written, no launch -> success on CPU
+    assert sgemm.hip_sgemm(0, 5, 5, 1.0, None, 5, None, 5, 0.0, None, 5, stream=0) == 0
+    assert sgemm.hip_sgemm(5, 0, 5, 1.0, None, 5, None, 1, 0.0, None, 1, stream=0) == 0
+    # alpha == 0: A and B may be NULL (validation passes; the check stops
+    # before the launch by using M == 0)
+    assert sgemm.hip_sgemm(0, 4, 4, 0.0, None, 4, None, 4, 1.0, None, 4, stream=0) == 0
+
+
+def test_unknown_level():
+    args = (4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4)
+    assert sgemm.hip_sgemm_level(10, *args, stream=0) == sgemm.STATUS_UNKNOWN_LEVEL
+    assert sgemm.hip_sgemm_level(-1, *args, stream=0) == sgemm.STATUS_UNKNOWN_LEVEL
+    assert "unknown level" in sgemm.hip_sgemm_status_string(sgemm.STATUS_UNKNOWN_LEVEL)
+
+
+def test_auto_level_is_the_matrix_core_rung():
+    for M, N, K in [(256, 256, 256), (4096, 4096, 4096), (4097, 4097, 4097), (1, 1, 1)]:
+        assert sgemm.hip_sgemm_auto_level(M, N, K, FAKE, K, FAKE, N, FAKE, N) == 9
+    assert sgemm.hip_sgemm_auto_level(-1, 2, 2, FAKE, 2, FAKE, 2, FAKE, 2) == -1
+
+
+def test_launch_shapes():
+    shape = sgemm.hip_sgemm_launch_shape(9, 4096, 4096, 4096)
+    assert shape == {"workgroups": 1024, "threads": 256, "k_steps": 256, "tile_m": 128, "tile_n": 128}
+    shape = sgemm.hip_sgemm_launch_shape(9, 4097, 4097, 4097)
+    assert (shape["workgroups"], shape["k_steps"]) == (33 * 33, 257)
+    assert sgemm.hip_sgemm_launch_shape(2, 4096, 4096, 4096)["threads"] == 1024
+    assert sgemm.hip_sgemm_launch_shape(0, 4096, 4096, 4096)["k_steps"] == 4096
+    with pytest.raises(sgemm.SgemmError):
+        sgemm.hip_sgemm_launch_shape(99, 1, 1, 1)
+
+
+def test_phase_count_rounds_up_like_the_lecture_example():
+    """Lecture 4 notes, section 8 exercise 6: K = 100 with 16-wide phases needs
+    ceil(100/16) = 7 phases (the floor form would drop 4 terms).  Levels 7-9
+    stage BK = 16 and must walk exactly that many K steps."""
+    from tests.oracle_pins import golden
+    g = golden()["phase_count"]
+    for level in (7, 8, 9):
+        shape = sgemm.hip_sgemm_launch_shape(level, 64, 64, g["K"])
+        assert shape["k_steps"] == g["phases"]
+    assert sgemm.hip_sgemm_launch_shape(2, 64, 64, g["K"])["k_steps"] == -(-g["K"] // 32)
+
+
+def test_tile32_geometry_matches_the_six_level_example():
+    """SGEMM 六级优化, K3 section: with TILE = 32 the block at (x=2, y=3) owns
+    C rows 96-127 x cols 64-95.  Level 2 uses the same 32 x 32 tile and 1024
+    threads, so that block is tile (row 3, col 2) of its grid."""
+    from tests.oracle_pins import golden
+    g = golden()["tile32_block_thread"]
+    shape = sgemm.hip_sgemm_launch_shape(2, 4096, 4096, 4096)
+    assert shape["tile_m"] == shape["tile_n"] == g["tile"]
+    assert shape["threads"] == g["tile"] * g["tile"]
+    assert g["block_y"] * g["tile"] == g["block_rows"][0] and g["block_x"] * g["tile"] == g["block_cols"][0]
+    assert (g["block_y"] * g["tile"] + g["ty"], g["block_x"] * g["tile"] + g["tx"]) == (g["c_row"], g["c_col"])
+    coarse = golden()["coarse4_block"]
+    assert sgemm.hip_sgemm_launch_shape(3, 4096, 4096, 4096)["tile_n"] == coarse["tile"] * coarse["coarse"]
