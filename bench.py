@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the reference sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 10 device-to-device copies of MIB MiB (a kernel of "
+                         "known traffic, to scale hardware byte counters) and exit")
     return ap.parse_args()
 
 
@@ -214,6 +217,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.rand(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                          "copies": 10}), flush=True)
+        return 0
     sgemm.load()
     w = inputs.WORKLOADS_BY_NAME[args.workload]
     steps, warmup = max(1, args.steps), max(0, args.warmup)

@@ -144,7 +144,10 @@ __device__ __forceinline__ void pipeline_tiles(const Problem& p,
       const int cur = static_cast<int>(kt & 1);
       const bool more = kt + 1 < nk;
       if (more) load_stage<VEC>(st, p, row0, col0, (kt + 1) * kBK, tid);
-#pragma unroll
+      // Unrolled by 4, not 16: fully unrolled, the compiler hoists all 16 k-steps
+      // of fragment reads (~256 registers, one wavefront per SIMD, nothing to
+      // hide the barrier); by 4 it needs ~140 (three wavefronts per SIMD).
+#pragma unroll 4
       for (int k = 0; k < kBK; ++k) {
         const float4 m0 = *reinterpret_cast<const float4*>(&As[cur][k][map.m_off(0)]);
         const float4 m1 = *reinterpret_cast<const float4*>(&As[cur][k][map.m_off(1)]);

@@ -34,11 +34,17 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
-constexpr int kWavesM = 2, kWavesN = 2;
-constexpr int kBK = 16;
 constexpr int kPad = 4;      // LDS row padding (words)
 constexpr int kGroupM = 8;   // tile-rows per group of the block order
+
+// A tile configuration: BM x BN block tile, BK-deep K steps, WAVES_M x
+// WAVES_N wavefronts (each owning a (BM/WAVES_M) x (BN/WAVES_N) wave tile).
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+struct MfmaTile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+};
 
 template <int N>
 struct VecT;
@@ -68,32 +74,36 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t bid, int64_t nblocks) 
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
 }
 
-template <int BM, int BN, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_level9(Problem p, int64_t tiles_m,
-                                                     int64_t tiles_n,
-                                                     int64_t ntiles) {
-  constexpr int WTM = BM / kWavesM, WTN = BN / kWavesN;
+template <class T, bool VEC>
+__global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_m,
+                                                       int64_t tiles_n,
+                                                       int64_t ntiles) {
+  constexpr int BM = T::BM, BN = T::BN, BK = T::BK, THREADS = T::THREADS;
+  constexpr int WTM = BM / T::WAVES_M, WTN = BN / T::WAVES_N;
   constexpr int BLK_M = WTM / 32, BLK_N = WTN / 32;
   constexpr int LDA = BM + kPad, LDB = BN + kPad;
-  constexpr int A_ITERS = (BM * kBK / 4) / kThreads;  // float4 of A per thread
-  constexpr int B_ITERS = (BN * kBK / 4) / kThreads;
-  static_assert(A_ITERS >= 1 && B_ITERS >= 1, "tile too small for 256 threads");
-  static_assert(BLK_M >= 1 && BLK_N >= 1, "wave tile below one MFMA block");
+  constexpr int A_ITERS = (BM * BK / 4) / THREADS;  // float4 of A per thread
+  constexpr int B_ITERS = (BN * BK / 4) / THREADS;
+  static_assert(A_ITERS >= 1 && B_ITERS >= 1, "tile too small for the threads");
+  static_assert(A_ITERS * THREADS * 4 == BM * BK && B_ITERS * THREADS * 4 == BN * BK,
+                "tile not evenly staged");
+  static_assert(BLK_M * 32 == WTM && BLK_N * 32 == WTN, "wave tile not whole blocks");
+  static_assert(BK % 2 == 0, "MFMA steps consume k in pairs");
   typedef typename VecT<BLK_M>::type AFrag;
   typedef typename VecT<BLK_N>::type BFrag;
 
-  __shared__ __align__(16) float As[2][kBK][LDA];
-  __shared__ __align__(16) float Bs[2][kBK][LDB];
+  __shared__ __align__(16) float As[2][BK][LDA];
+  __shared__ __align__(16) float Bs[2][BK][LDB];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
-  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
   const int lrow = lane % 32, khalf = lane / 32;
   // LDS offsets (words) of this lane's fragments inside one k-row
   const int a_off = wm * WTM + BLK_M * lrow;
   const int b_off = wn * WTN + BLK_N * lrow;
 
-  const int64_t nk = ceil_div(p.K, kBK);
+  const int64_t nk = ceil_div(p.K, BK);
   const int64_t first = xcd_contiguous(blockIdx.x, gridDim.x);
   for (int64_t t = first; t < ntiles; t += gridDim.x) {
     const int64_t group = kGroupM * tiles_n;
@@ -115,14 +125,14 @@ __global__ __launch_bounds__(kThreads) void k_level9(Problem p, int64_t tiles_m,
     auto load = [&](int64_t k0) {
 #pragma unroll
       for (int s = 0; s < A_ITERS; ++s) {
-        const int idx = tid + s * kThreads;
-        const int r = idx / (kBK / 4), kq = idx % (kBK / 4);
+        const int idx = tid + s * THREADS;
+        const int r = idx / (BK / 4), kq = idx % (BK / 4);
         ra[s] = load4<VEC>(p.A + (row0 + r) * p.lda, k0 + 4 * kq, p.K,
                            row0 + r < p.M);
       }
 #pragma unroll
       for (int s = 0; s < B_ITERS; ++s) {
-        const int idx = tid + s * kThreads;
+        const int idx = tid + s * THREADS;
         const int r = idx / (BN / 4), nq = idx % (BN / 4);
         rb[s] = load4<VEC>(p.B + (k0 + r) * p.ldb, col0 + 4 * nq, p.N,
                            k0 + r < p.K);
@@ -131,8 +141,8 @@ __global__ __launch_bounds__(kThreads) void k_level9(Problem p, int64_t tiles_m,
     auto store = [&](int buf) {
 #pragma unroll
       for (int s = 0; s < A_ITERS; ++s) {
-        const int idx = tid + s * kThreads;
-        const int r = idx / (kBK / 4), kq = idx % (kBK / 4);
+        const int idx = tid + s * THREADS;
+        const int r = idx / (BK / 4), kq = idx % (BK / 4);
         As[buf][4 * kq + 0][r] = ra[s].x;
         As[buf][4 * kq + 1][r] = ra[s].y;
         As[buf][4 * kq + 2][r] = ra[s].z;
@@ -140,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_level9(Problem p, int64_t tiles_m,
       }
 #pragma unroll
       for (int s = 0; s < B_ITERS; ++s) {
-        const int idx = tid + s * kThreads;
+        const int idx = tid + s * THREADS;
         const int r = idx / (BN / 4), nq = idx % (BN / 4);
         *reinterpret_cast<float4*>(&Bs[buf][r][4 * nq]) = rb[s];
       }
@@ -152,9 +162,9 @@ __global__ __launch_bounds__(kThreads) void k_level9(Problem p, int64_t tiles_m,
     for (int64_t kt = 0; kt < nk; ++kt) {
       const int cur = static_cast<int>(kt & 1);
       const bool more = kt + 1 < nk;
-      if (more) load((kt + 1) * kBK);
+      if (more) load((kt + 1) * BK);
 #pragma unroll
-      for (int s = 0; s < kBK / 2; ++s) {
+      for (int s = 0; s < BK / 2; ++s) {
         const int kk = 2 * s + khalf;
         const AFrag af = *reinterpret_cast<const AFrag*>(&As[cur][kk][a_off]);
         const BFrag bf = *reinterpret_cast<const BFrag*>(&Bs[cur][kk][b_off]);
@@ -169,7 +179,10 @@ __global__ __launch_bounds__(kThreads) void k_level9(Problem p, int64_t tiles_m,
       __syncthreads();
     }
 
-    // Epilogue: register r of block (bi, bj) is C[row(bi, r)][col(bj)].
+    // Epilogue: register r of block (bi, bj) is C[row(bi, r)][col(bj)]; a
+    // lane's BLK_N outputs of one row are adjacent.
+    const int64_t col = col0 + b_off;
+    const bool vec_ok = VEC && BLK_N > 1 && col + BLK_N - 1 < p.N;
 #pragma unroll
     for (int bi = 0; bi < BLK_M; ++bi) {
 #pragma unroll
@@ -177,17 +190,19 @@ __global__ __launch_bounds__(kThreads) void k_level9(Problem p, int64_t tiles_m,
         const int i = 8 * (r / 4) + 4 * khalf + (r % 4);
         const int64_t row = row0 + wm * WTM + BLK_M * i + bi;
         if (row >= p.M) continue;
-        const int64_t col = col0 + b_off;
         float* c = p.C + row * p.ldc + col;
-        if (BLK_N == 2 && VEC && col + 1 < p.N) {
-          float2 o = make_float2(p.alpha * acc[bi][0][r],
-                                 p.alpha * acc[bi][BLK_N - 1][r]);
+        if (vec_ok) {
+          typedef typename VecT<BLK_N>::type CVec;
+          float o[BLK_N];
+#pragma unroll
+          for (int bj = 0; bj < BLK_N; ++bj) o[bj] = p.alpha * acc[bi][bj][r];
           if (p.beta != 0.0f) {
-            const float2 old = *reinterpret_cast<const float2*>(c);
-            o.x = fmaf(p.beta, old.x, o.x);
-            o.y = fmaf(p.beta, old.y, o.y);
+            const CVec old = *reinterpret_cast<const CVec*>(c);
+#pragma unroll
+            for (int bj = 0; bj < BLK_N; ++bj)
+              o[bj] = fmaf(p.beta, vget<BLK_N>(old, bj), o[bj]);
           }
-          *reinterpret_cast<float2*>(c) = o;
+          *reinterpret_cast<CVec*>(c) = *reinterpret_cast<const CVec*>(o);
         } else {
 #pragma unroll
           for (int bj = 0; bj < BLK_N; ++bj)
@@ -199,36 +214,40 @@ __global__ __launch_bounds__(kThreads) void k_level9(Problem p, int64_t tiles_m,
   }
 }
 
-// 128 x 128 tiles once they give every CU at least two blocks; 64 x 64 below.
+template <class T>
+Geometry tile_geometry(int M, int N, int K) {
+  return make_geometry(M, N, K, T::BM, T::BN, T::BK, T::THREADS);
+}
+
+template <class T>
+hipError_t launch_tiles(const Problem& p, hipStream_t s) {
+  const Geometry g = tile_geometry<T>(p.M, p.N, p.K);
+  const dim3 grid(static_cast<unsigned>(g.workgroups)), block(T::THREADS);
+  const int64_t tm = ceil_div(p.M, T::BM), tn = ceil_div(p.N, T::BN);
+  if (vec4_ok(p))
+    hipLaunchKernelGGL((k_level9<T, true>), grid, block, 0, s, p, tm, tn, g.tiles);
+  else
+    hipLaunchKernelGGL((k_level9<T, false>), grid, block, 0, s, p, tm, tn, g.tiles);
+  return hipGetLastError();
+}
+
+// The configurations hip_sgemm uses: 128 x 128 tiles once they give every CU
+// at least two blocks, 64 x 64 below.
+typedef MfmaTile<128, 128, 16, 2, 2> TileLarge;
+typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;
 constexpr int kCUs = 256;
-bool use_big_tiles(int M, int N) {
-  return ceil_div(M, 128) * ceil_div(N, 128) >= 2 * kCUs;
+bool use_large_tiles(int M, int N) {
+  return ceil_div(M, TileLarge::BM) * ceil_div(N, TileLarge::BN) >= 2 * kCUs;
 }
 
 Geometry geometry9(int M, int N, int K) {
-  const int t = use_big_tiles(M, N) ? 128 : 64;
-  return make_geometry(M, N, K, t, t, kBK, kThreads);
-}
-
-template <int BM, int BN>
-void launch_tiles(const Problem& p, hipStream_t s, const Geometry& g) {
-  const dim3 grid(static_cast<unsigned>(g.workgroups)), block(kThreads);
-  const int64_t tm = ceil_div(p.M, BM), tn = ceil_div(p.N, BN);
-  if (vec4_ok(p))
-    hipLaunchKernelGGL((k_level9<BM, BN, true>), grid, block, 0, s, p, tm, tn,
-                       g.tiles);
-  else
-    hipLaunchKernelGGL((k_level9<BM, BN, false>), grid, block, 0, s, p, tm, tn,
-                       g.tiles);
+  return use_large_tiles(M, N) ? tile_geometry<TileLarge>(M, N, K)
+                               : tile_geometry<TileSmall>(M, N, K);
 }
 
 hipError_t launch9(const Problem& p, hipStream_t s) {
-  const Geometry g = geometry9(p.M, p.N, p.K);
-  if (g.tile_m == 128)
-    launch_tiles<128, 128>(p, s, g);
-  else
-    launch_tiles<64, 64>(p, s, g);
-  return hipGetLastError();
+  return use_large_tiles(p.M, p.N) ? launch_tiles<TileLarge>(p, s)
+                                   : launch_tiles<TileSmall>(p, s);
 }
 
 }  // namespace
