@@ -12,10 +12,10 @@
 // Level 6 adds the two changes of [SIX] K6 and [GEMM2] kernel 6: A is stored
 // TRANSPOSED in LDS (As[k][m]) so a thread's 8 M-direction values are
 // contiguous and come in as two 128-bit LDS reads (B's already are), and the
-// global loads and the C epilogue move 128 bits per lane.  The vector path
-// runs when pointers and row strides allow it; otherwise the same kernel
-// stages element-wise (edge-safe path), and partial groups at the K and N
-// edges are always element-wise, never dropped.  The transposed rows are
+// global loads and the C epilogue move 128 bits per lane.  On gfx950 a
+// 128-bit global access needs only 4-byte alignment, so the vector path runs
+// for any row stride; partial groups at the K and N edges are element-wise,
+// never dropped.  The transposed rows are
 // padded to 136 words, which spreads the four-word transposing stores of the
 // two k-groups a wavefront writes over distinct banks.
 //
@@ -95,7 +95,6 @@ __global__ __launch_bounds__(kThreads) void k_level5(Problem p, int64_t tiles_n,
 
 constexpr int kLdaT = kBM + 8;  // transposed-A row stride in LDS (words)
 
-template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_level6(Problem p, int64_t tiles_n,
                                                      int64_t ntiles) {
   __shared__ __align__(16) float As[kBK][kLdaT];
@@ -116,12 +115,12 @@ __global__ __launch_bounds__(kThreads) void k_level6(Problem p, int64_t tiles_n,
     const float* a_row = p.A + (row0 + a_r) * p.lda;
     const bool a_ok = row0 + a_r < p.M;
     for (int64_t k0 = 0; k0 < p.K; k0 += kBK) {
-      const float4 va = load4<VEC>(a_row, k0 + 4 * a_kq, p.K, a_ok);
+      const float4 va = load4(a_row, k0 + 4 * a_kq, p.K, a_ok);
       As[4 * a_kq + 0][a_r] = va.x;
       As[4 * a_kq + 1][a_r] = va.y;
       As[4 * a_kq + 2][a_r] = va.z;
       As[4 * a_kq + 3][a_r] = va.w;
-      const float4 vb = load4<VEC>(p.B + (k0 + b_r) * p.ldb, col0 + 4 * b_nq,
+      const float4 vb = load4(p.B + (k0 + b_r) * p.ldb, col0 + 4 * b_nq,
                                    p.N, k0 + b_r < p.K);
       *reinterpret_cast<float4*>(&Bs[b_r][4 * b_nq]) = vb;
       __syncthreads();
@@ -147,10 +146,10 @@ __global__ __launch_bounds__(kThreads) void k_level6(Problem p, int64_t tiles_n,
       const int64_t row = row0 + tr * kTM + i;
       if (row >= p.M) continue;
       float* c = p.C + row * p.ldc + col;
-      store4<VEC>(c, col, p.N,
+      store4(c, col, p.N,
                   make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]),
                   p.alpha, p.beta);
-      store4<VEC>(c + 4, col + 4, p.N,
+      store4(c + 4, col + 4, p.N,
                   make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]),
                   p.alpha, p.beta);
     }
@@ -170,12 +169,8 @@ hipError_t launch5(const Problem& p, hipStream_t s) {
 
 hipError_t launch6(const Problem& p, hipStream_t s) {
   const Geometry g = geometry56(p.M, p.N, p.K);
-  const dim3 grid(static_cast<unsigned>(g.workgroups)), block(kThreads);
-  const int64_t tiles_n = ceil_div(p.N, kBN);
-  if (vec4_ok(p))
-    hipLaunchKernelGGL(k_level6<true>, grid, block, 0, s, p, tiles_n, g.tiles);
-  else
-    hipLaunchKernelGGL(k_level6<false>, grid, block, 0, s, p, tiles_n, g.tiles);
+  hipLaunchKernelGGL(k_level6, dim3(static_cast<unsigned>(g.workgroups)),
+                     dim3(kThreads), 0, s, p, ceil_div(p.N, kBN), g.tiles);
   return hipGetLastError();
 }
 

@@ -42,7 +42,6 @@ struct Staged {
   float4 b[kStageIters];
 };
 
-template <bool VEC>
 __device__ __forceinline__ void load_stage(Staged& r, const Problem& p,
                                            int64_t row0, int64_t col0,
                                            int64_t k0, int tid) {
@@ -50,10 +49,10 @@ __device__ __forceinline__ void load_stage(Staged& r, const Problem& p,
   for (int s = 0; s < kStageIters; ++s) {
     const int idx = tid + s * kThreads;
     const int a_r = idx / (kBK / 4), a_kq = idx % (kBK / 4);
-    r.a[s] = load4<VEC>(p.A + (row0 + a_r) * p.lda, k0 + 4 * a_kq, p.K,
+    r.a[s] = load4(p.A + (row0 + a_r) * p.lda, k0 + 4 * a_kq, p.K,
                         row0 + a_r < p.M);
     const int b_r = idx / (kBN / 4), b_nq = idx % (kBN / 4);
-    r.b[s] = load4<VEC>(p.B + (k0 + b_r) * p.ldb, col0 + 4 * b_nq, p.N,
+    r.b[s] = load4(p.B + (k0 + b_r) * p.ldb, col0 + 4 * b_nq, p.N,
                         k0 + b_r < p.K);
   }
 }
@@ -103,7 +102,7 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t bid, int64_t nblocks) 
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
 }
 
-template <bool VEC, bool SWIZZLE, class Map>
+template <bool SWIZZLE, class Map>
 __device__ __forceinline__ void pipeline_tiles(const Problem& p,
                                                int64_t tiles_m,
                                                int64_t tiles_n,
@@ -137,13 +136,13 @@ __device__ __forceinline__ void pipeline_tiles(const Problem& p,
       for (int j = 0; j < kTN; ++j) acc[i][j] = 0.0f;
 
     Staged st;
-    load_stage<VEC>(st, p, row0, col0, 0, tid);
+    load_stage(st, p, row0, col0, 0, tid);
     store_stage(st, As[0], Bs[0], tid);
     __syncthreads();
     for (int64_t kt = 0; kt < nk; ++kt) {
       const int cur = static_cast<int>(kt & 1);
       const bool more = kt + 1 < nk;
-      if (more) load_stage<VEC>(st, p, row0, col0, (kt + 1) * kBK, tid);
+      if (more) load_stage(st, p, row0, col0, (kt + 1) * kBK, tid);
       // Unrolled by 4, not 16: fully unrolled, the compiler hoists all 16 k-steps
       // of fragment reads (~256 registers, one wavefront per SIMD, nothing to
       // hide the barrier); by 4 it needs ~140 (three wavefronts per SIMD).
@@ -172,7 +171,7 @@ __device__ __forceinline__ void pipeline_tiles(const Problem& p,
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int64_t col = col0 + map.n_off(h);
-        store4<VEC>(p.C + row * p.ldc + col, col, p.N,
+        store4(p.C + row * p.ldc + col, col, p.N,
                     make_float4(acc[i][4 * h + 0], acc[i][4 * h + 1],
                                 acc[i][4 * h + 2], acc[i][4 * h + 3]),
                     p.alpha, p.beta);
@@ -181,18 +180,16 @@ __device__ __forceinline__ void pipeline_tiles(const Problem& p,
   }
 }
 
-template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_level7(Problem p, int64_t tiles_m,
                                                      int64_t tiles_n,
                                                      int64_t ntiles) {
-  pipeline_tiles<VEC, false, MapContiguous>(p, tiles_m, tiles_n, ntiles);
+  pipeline_tiles<false, MapContiguous>(p, tiles_m, tiles_n, ntiles);
 }
 
-template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_level8(Problem p, int64_t tiles_m,
                                                      int64_t tiles_n,
                                                      int64_t ntiles) {
-  pipeline_tiles<VEC, true, MapWaveTiled>(p, tiles_m, tiles_n, ntiles);
+  pipeline_tiles<true, MapWaveTiled>(p, tiles_m, tiles_n, ntiles);
 }
 
 Geometry geometry78(int M, int N, int K) {
@@ -203,10 +200,7 @@ hipError_t launch7(const Problem& p, hipStream_t s) {
   const Geometry g = geometry78(p.M, p.N, p.K);
   const dim3 grid(static_cast<unsigned>(g.workgroups)), block(kThreads);
   const int64_t tm = ceil_div(p.M, kBM), tn = ceil_div(p.N, kBN);
-  if (vec4_ok(p))
-    hipLaunchKernelGGL(k_level7<true>, grid, block, 0, s, p, tm, tn, g.tiles);
-  else
-    hipLaunchKernelGGL(k_level7<false>, grid, block, 0, s, p, tm, tn, g.tiles);
+  hipLaunchKernelGGL(k_level7, grid, block, 0, s, p, tm, tn, g.tiles);
   return hipGetLastError();
 }
 
@@ -214,10 +208,7 @@ hipError_t launch8(const Problem& p, hipStream_t s) {
   const Geometry g = geometry78(p.M, p.N, p.K);
   const dim3 grid(static_cast<unsigned>(g.workgroups)), block(kThreads);
   const int64_t tm = ceil_div(p.M, kBM), tn = ceil_div(p.N, kBN);
-  if (vec4_ok(p))
-    hipLaunchKernelGGL(k_level8<true>, grid, block, 0, s, p, tm, tn, g.tiles);
-  else
-    hipLaunchKernelGGL(k_level8<false>, grid, block, 0, s, p, tm, tn, g.tiles);
+  hipLaunchKernelGGL(k_level8, grid, block, 0, s, p, tm, tn, g.tiles);
   return hipGetLastError();
 }
 

@@ -8,9 +8,9 @@
 // pages' xf32 reduced-precision modes are not used (gfx950 has none for FP32,
 // and ~10-bit inputs would miss the 1e-5 normalised error bound).
 //
-// Block tile BM x BN (128 x 128, or 64 x 64 for problems too small to fill
-// 256 CUs with 128 x 128 tiles), BK = 16, 256 threads = 2 x 2 wavefronts, each
-// owning a WTM x WTN wave tile made of BLK_M x BLK_N 32 x 32 MFMA blocks.
+// Block tile BM x BN with BK-deep K steps and WAVES_M x WAVES_N wavefronts,
+// each owning a WTM x WTN wave tile made of BLK_M x BLK_N 32 x 32 MFMA blocks
+// (the shapes used per problem size are listed at the end of this file).
 //
 // Operand layout of the 32x32x2 instruction (one block): lane l supplies
 // A[l % 32][l / 32] and B[l / 32][l % 32]; accumulator register r of lane l
@@ -21,10 +21,10 @@
 // and a lane's BLK_N outputs of one row are adjacent in C (one 64-bit store).
 // MFMA step s of a K-phase consumes k = 2s + l/32.
 //
-// The staging (A transposed into LDS, 128-bit global loads when aligned,
-// element-wise edge-safe loads otherwise, zero-fill beyond M/N/K), the
-// double-buffered one-barrier pipeline and the XCD-aware grouped block order
-// are those of level 8.  The summation order inside an instruction is the
+// The staging (A transposed into LDS, 128-bit global loads, element-wise
+// loads only for partial groups at the K/N edges, zero-fill beyond M/N/K),
+// the double-buffered one-barrier pipeline and the XCD-aware grouped block
+// order are those of level 8.  The summation order inside an instruction is the
 // hardware's, so results differ from levels 0-8 in the last bits (all within
 // the float32 rounding bound); integer-valued inputs still give exact results.
 #include "sgemm_internal.h"
@@ -38,12 +38,15 @@ constexpr int kPad = 4;      // LDS row padding (words)
 constexpr int kGroupM = 8;   // tile-rows per group of the block order
 
 // A tile configuration: BM x BN block tile, BK-deep K steps, WAVES_M x
-// WAVES_N wavefronts (each owning a (BM/WAVES_M) x (BN/WAVES_N) wave tile).
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+// WAVES_N wavefronts (each owning a (BM/WAVES_M) x (BN/WAVES_N) wave tile),
+// and how many of a K step's BK/2 MFMA steps are unrolled together (fewer
+// keeps the compiler from hoisting every fragment read into registers).
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int UNROLL_ = BK_ / 2>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  static constexpr int UNROLL = UNROLL_;
 };
 
 template <int N>
@@ -74,7 +77,10 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t bid, int64_t nblocks) 
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
 }
 
-template <class T, bool VEC>
+// EDGE = false: the host guarantees M % BM == N % BN == K % BK == 0, so every
+// tile and K step is whole and the kernel carries no bounds logic (fewer
+// registers and instructions); EDGE = true handles any shape.
+template <class T, bool EDGE>
 __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_m,
                                                        int64_t tiles_n,
                                                        int64_t ntiles) {
@@ -121,21 +127,45 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
 
+    // Source pointers of this thread's staged groups: float4 s of A is row r
+    // of the panel at k-group kq, float4 s of B is row r of the panel at
+    // column group nq (advanced by k0 columns of A / k0 rows of B).  Rows
+    // beyond M and the B rows beyond K are never dereferenced.
+    const bool interior = !EDGE || (row0 + BM <= p.M && col0 + BN <= p.N);
+    const float* pa[A_ITERS];
+    const float* pb[B_ITERS];
+#pragma unroll
+    for (int s = 0; s < A_ITERS; ++s) {
+      const int idx = tid + s * THREADS;
+      pa[s] = p.A + (row0 + idx / (BK / 4)) * p.lda + 4 * (idx % (BK / 4));
+    }
+#pragma unroll
+    for (int s = 0; s < B_ITERS; ++s) {
+      const int idx = tid + s * THREADS;
+      pb[s] = p.B + (idx / (BN / 4)) * p.ldb + col0 + 4 * (idx % (BN / 4));
+    }
     float4 ra[A_ITERS], rb[B_ITERS];
     auto load = [&](int64_t k0) {
+      if (!EDGE || (interior && k0 + BK <= p.K)) {
+        // whole K step inside the matrix: no bounds tests (uniform branch)
+#pragma unroll
+        for (int s = 0; s < A_ITERS; ++s) ra[s] = ld_global4(pa[s] + k0);
+#pragma unroll
+        for (int s = 0; s < B_ITERS; ++s) rb[s] = ld_global4(pb[s] + k0 * p.ldb);
+        return;
+      }
 #pragma unroll
       for (int s = 0; s < A_ITERS; ++s) {
         const int idx = tid + s * THREADS;
         const int r = idx / (BK / 4), kq = idx % (BK / 4);
-        ra[s] = load4<VEC>(p.A + (row0 + r) * p.lda, k0 + 4 * kq, p.K,
-                           row0 + r < p.M);
+        ra[s] = load4(pa[s] - 4 * kq, k0 + 4 * kq, p.K, row0 + r < p.M);
       }
 #pragma unroll
       for (int s = 0; s < B_ITERS; ++s) {
         const int idx = tid + s * THREADS;
         const int r = idx / (BN / 4), nq = idx % (BN / 4);
-        rb[s] = load4<VEC>(p.B + (k0 + r) * p.ldb, col0 + 4 * nq, p.N,
-                           k0 + r < p.K);
+        rb[s] = load4(pb[s] + k0 * p.ldb - (col0 + 4 * nq), col0 + 4 * nq, p.N,
+                      k0 + r < p.K);
       }
     };
     auto store = [&](int buf) {
@@ -163,7 +193,7 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
       const int cur = static_cast<int>(kt & 1);
       const bool more = kt + 1 < nk;
       if (more) load((kt + 1) * BK);
-#pragma unroll
+#pragma unroll T::UNROLL
       for (int s = 0; s < BK / 2; ++s) {
         const int kk = 2 * s + khalf;
         const AFrag af = *reinterpret_cast<const AFrag*>(&As[cur][kk][a_off]);
@@ -181,28 +211,31 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
 
     // Epilogue: register r of block (bi, bj) is C[row(bi, r)][col(bj)]; a
     // lane's BLK_N outputs of one row are adjacent.
+    // Each lane keeps one base pointer per block row; the offsets of its 16
+    // registers' rows are lane-independent multiples of ldc (scalar work).
     const int64_t col = col0 + b_off;
-    const bool vec_ok = VEC && BLK_N > 1 && col + BLK_N - 1 < p.N;
+    const bool vec_ok = !EDGE || (BLK_N > 1 && col + BLK_N - 1 < p.N);
 #pragma unroll
     for (int bi = 0; bi < BLK_M; ++bi) {
+      const int64_t row_base = row0 + wm * WTM + BLK_M * 4 * khalf + bi;
+      float* const c_base = p.C + row_base * p.ldc + col;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = 8 * (r / 4) + 4 * khalf + (r % 4);
-        const int64_t row = row0 + wm * WTM + BLK_M * i + bi;
-        if (row >= p.M) continue;
-        float* c = p.C + row * p.ldc + col;
-        if (vec_ok) {
-          typedef typename VecT<BLK_N>::type CVec;
+        const int dr = BLK_M * (8 * (r / 4) + (r % 4));
+        if (!interior && row_base + dr >= p.M) continue;
+        float* c = c_base + dr * p.ldc;
+        if (interior || vec_ok) {
+          // one 64- or 128-bit access per lane (4-byte alignment suffices)
           float o[BLK_N];
 #pragma unroll
           for (int bj = 0; bj < BLK_N; ++bj) o[bj] = p.alpha * acc[bi][bj][r];
           if (p.beta != 0.0f) {
-            const CVec old = *reinterpret_cast<const CVec*>(c);
+            float old[BLK_N];
+            __builtin_memcpy(old, c, sizeof(old));
 #pragma unroll
-            for (int bj = 0; bj < BLK_N; ++bj)
-              o[bj] = fmaf(p.beta, vget<BLK_N>(old, bj), o[bj]);
+            for (int bj = 0; bj < BLK_N; ++bj) o[bj] = fmaf(p.beta, old[bj], o[bj]);
           }
-          *reinterpret_cast<CVec*>(c) = *reinterpret_cast<const CVec*>(o);
+          __builtin_memcpy(c, o, sizeof(o));
         } else {
 #pragma unroll
           for (int bj = 0; bj < BLK_N; ++bj)
@@ -224,30 +257,56 @@ hipError_t launch_tiles(const Problem& p, hipStream_t s) {
   const Geometry g = tile_geometry<T>(p.M, p.N, p.K);
   const dim3 grid(static_cast<unsigned>(g.workgroups)), block(T::THREADS);
   const int64_t tm = ceil_div(p.M, T::BM), tn = ceil_div(p.N, T::BN);
-  if (vec4_ok(p))
-    hipLaunchKernelGGL((k_level9<T, true>), grid, block, 0, s, p, tm, tn, g.tiles);
-  else
+  const bool whole = p.M % T::BM == 0 && p.N % T::BN == 0 && p.K % T::BK == 0;
+  if (whole)
     hipLaunchKernelGGL((k_level9<T, false>), grid, block, 0, s, p, tm, tn, g.tiles);
+  else
+    hipLaunchKernelGGL((k_level9<T, true>), grid, block, 0, s, p, tm, tn, g.tiles);
   return hipGetLastError();
 }
 
-// The configurations hip_sgemm uses: 128 x 128 tiles once they give every CU
-// at least two blocks, 64 x 64 below.
-typedef MfmaTile<128, 128, 16, 2, 2> TileLarge;
+// The tile shapes the level uses, chosen per problem from measurements on
+// MI355X (256 CUs).  Whole-tile problems large enough to give every CU two
+// 256 x 128 tiles take the big tile (fewest L2->LDS bytes per FLOP, 8
+// wavefronts per block); mid-size whole-tile problems take 128 x 128 with
+// 32-deep K steps; large ragged problems (4097^3 leaves a one-row /
+// one-column fringe of tiles) take 128 x 64, whose many small blocks soak up
+// the fringe; small problems take 64 x 64 so that more CUs get work.
+typedef MfmaTile<256, 128, 16, 4, 2> TileHuge;
+typedef MfmaTile<128, 128, 32, 4, 1> TileLarge;
+typedef MfmaTile<128, 64, 16, 2, 2> TileMid;
 typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;
 constexpr int kCUs = 256;
-bool use_large_tiles(int M, int N) {
-  return ceil_div(M, TileLarge::BM) * ceil_div(N, TileLarge::BN) >= 2 * kCUs;
+
+enum class Shape { kHuge, kLarge, kMid, kSmall };
+
+Shape pick_shape(int M, int N) {
+  const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
+  if (M % TileHuge::BM == 0 && N % TileHuge::BN == 0 &&
+      (int64_t(M) / TileHuge::BM) * (N / TileHuge::BN) >= 2 * kCUs)
+    return Shape::kHuge;
+  if (M % TileLarge::BM == 0 && N % TileLarge::BN == 0 && tiles128 >= kCUs)
+    return Shape::kLarge;
+  if (int64_t(M) * N >= int64_t(2048) * 2048) return Shape::kMid;
+  return Shape::kSmall;
 }
 
 Geometry geometry9(int M, int N, int K) {
-  return use_large_tiles(M, N) ? tile_geometry<TileLarge>(M, N, K)
-                               : tile_geometry<TileSmall>(M, N, K);
+  switch (pick_shape(M, N)) {
+    case Shape::kHuge: return tile_geometry<TileHuge>(M, N, K);
+    case Shape::kLarge: return tile_geometry<TileLarge>(M, N, K);
+    case Shape::kMid: return tile_geometry<TileMid>(M, N, K);
+    default: return tile_geometry<TileSmall>(M, N, K);
+  }
 }
 
 hipError_t launch9(const Problem& p, hipStream_t s) {
-  return use_large_tiles(p.M, p.N) ? launch_tiles<TileLarge>(p, s)
-                                   : launch_tiles<TileSmall>(p, s);
+  switch (pick_shape(p.M, p.N)) {
+    case Shape::kHuge: return launch_tiles<TileHuge>(p, s);
+    case Shape::kLarge: return launch_tiles<TileLarge>(p, s);
+    case Shape::kMid: return launch_tiles<TileMid>(p, s);
+    default: return launch_tiles<TileSmall>(p, s);
+  }
 }
 
 }  // namespace

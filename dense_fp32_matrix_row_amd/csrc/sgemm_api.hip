@@ -128,7 +128,6 @@ const char* hip_sgemm_status_string(int status) {
     case -10: return "argument 10 (C) is NULL with M, N > 0";
     case -11: return "argument 11 (ldc) is smaller than max(1, N)";
     case SGEMM_STATUS_UNKNOWN_LEVEL: return "unknown level";
-    case SGEMM_STATUS_TOO_LARGE: return "problem too large for this level";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

@@ -64,16 +64,6 @@ inline Geometry make_geometry(int M, int N, int K, int tile_m, int tile_n,
   return g;
 }
 
-// Vector (128-bit) paths need 16-byte aligned bases and row strides that
-// keep every row start 16-byte aligned.
-inline bool aligned16(const void* p) {
-  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
-}
-inline bool vec4_ok(const Problem& p) {
-  return aligned16(p.A) && aligned16(p.B) && aligned16(p.C) &&
-         (p.lda % 4) == 0 && (p.ldb % 4) == 0 && (p.ldc % 4) == 0;
-}
-
 // The epilogue of every level: alpha*acc + beta*c, with C read only when
 // beta != 0 (BLAS convention; the page kernels read C unconditionally).
 __device__ __forceinline__ float epilogue(float acc, float alpha, float beta,
@@ -82,19 +72,32 @@ __device__ __forceinline__ float epilogue(float acc, float alpha, float beta,
   return beta == 0.0f ? r : fmaf(beta, *c, r);
 }
 
+// 128-bit global accesses need only 4-byte alignment on gfx950 (the compiler
+// itself emits global_load_dwordx4 / global_store_dwordx4 for 16-byte copies
+// of float data), so the vector paths below run for any row stride and any
+// float-aligned base; the "alignment promise" of a float4 cast that [GEMM2]
+// kernel 6 relies on is not needed for global memory here.
+__device__ __forceinline__ float4 ld_global4(const float* p) {
+  float4 v;
+  __builtin_memcpy(&v, p, sizeof(v));
+  return v;
+}
+__device__ __forceinline__ void st_global4(float* p, float4 v) {
+  __builtin_memcpy(p, &v, sizeof(v));
+}
+
 // Four consecutive elements [col, col+4) of one row, zero outside
 // [0, ncols) or when the row is out of range (the zero-fill boundary rule of
-// [L04] section 2.5).  VEC: the row start is 16-byte aligned and col is a
-// multiple of 4, so a full group is one 128-bit load; a partial group at the
-// edge falls back to element loads (never the whole-group drop of [SIX] K6).
-template <bool VEC>
+// [L04] section 2.5).  A full group is one 128-bit load; a partial group at
+// the edge falls back to element loads (never the whole-group drop of [SIX]
+// K6).
 __device__ __forceinline__ float4 load4(const float* __restrict__ row_ptr,
                                         int64_t col, int64_t ncols,
                                         bool row_ok) {
   float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (!row_ok) return v;
-  if (VEC && col + 3 < ncols) {
-    v = *reinterpret_cast<const float4*>(row_ptr + col);
+  if (col + 3 < ncols) {
+    v = ld_global4(row_ptr + col);
   } else {
     if (col + 0 < ncols) v.x = row_ptr[col + 0];
     if (col + 1 < ncols) v.y = row_ptr[col + 1];
@@ -106,21 +109,20 @@ __device__ __forceinline__ float4 load4(const float* __restrict__ row_ptr,
 
 // Epilogue for four consecutive outputs C[row][col .. col+3] (only those
 // below N are written; c points at C[row][col]).
-template <bool VEC>
 __device__ __forceinline__ void store4(float* __restrict__ c, int64_t col,
                                        int64_t N, float4 acc, float alpha,
                                        float beta) {
-  if (VEC && col + 3 < N) {
+  if (col + 3 < N) {
     float4 r = make_float4(alpha * acc.x, alpha * acc.y, alpha * acc.z,
                            alpha * acc.w);
     if (beta != 0.0f) {
-      const float4 old = *reinterpret_cast<const float4*>(c);
+      const float4 old = ld_global4(c);
       r.x = fmaf(beta, old.x, r.x);
       r.y = fmaf(beta, old.y, r.y);
       r.z = fmaf(beta, old.z, r.z);
       r.w = fmaf(beta, old.w, r.w);
     }
-    *reinterpret_cast<float4*>(c) = r;
+    st_global4(c, r);
   } else {
     if (col + 0 < N) c[0] = epilogue(acc.x, alpha, beta, c + 0);
     if (col + 1 < N) c[1] = epilogue(acc.y, alpha, beta, c + 1);

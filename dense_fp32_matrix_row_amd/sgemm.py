@@ -22,7 +22,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libsgemm.so")
 
 STATUS_UNKNOWN_LEVEL = -100
-STATUS_TOO_LARGE = -101
 
 # Every exported symbol of include/sgemm.h.
 EXPORTS = (

@@ -40,11 +40,11 @@
  *   - beta == 0: C is write-only (never read; NaN in C does not propagate).
  *   - Only the M x N window of C is written; elements of the rows' padding
  *     (columns N .. ldc-1) are never touched.
- *   - Only 4-byte alignment is required.  Kernels take 128-bit vector paths
- *     when the base pointers are 16-byte aligned and lda, ldb, ldc are
- *     multiples of 4, and element-wise edge-safe paths otherwise; both are
- *     correct for every shape (the page kernels of [SIX] K6 that drop the last
- *     partial float4 group are not followed).
+ *   - Only 4-byte (float) alignment is required, for any lda, ldb, ldc:
+ *     128-bit global accesses on gfx950 need no more, so the vector paths
+ *     serve every stride; partial 4-element groups at the K and N edges are
+ *     loaded and stored element-wise (the page kernels of [SIX] K6 that drop
+ *     the last partial float4 group are not followed).
  *   - Accumulation is float32 (round to nearest even, fused multiply-add);
  *     the summation order differs between levels.
  *
@@ -58,7 +58,6 @@
  *                 -11 ldc < max(1, N).  hip_sgemm_level numbers its
  *                 arguments the same way (level is not counted).
  *   -100          unknown level
- *   -101          the problem is too large for this level's grid
  *   > 0           the hipError_t the launch reported
  */
 #ifndef LIBSGEMM_SGEMM_H
@@ -71,7 +70,6 @@ extern "C" {
 #endif
 
 #define SGEMM_STATUS_UNKNOWN_LEVEL (-100)
-#define SGEMM_STATUS_TOO_LARGE (-101)
 
 /*
  * Best kernel for the shape: C <- alpha*A*B + beta*C.

@@ -84,10 +84,16 @@ def test_auto_level_is_the_matrix_core_rung():
 
 
 def test_launch_shapes():
+    # level 9 picks its tile per problem: 256 x 128 for whole-tile large
+    # problems, 128 x 128 (BK 32) mid-size, 128 x 64 large ragged, 64 x 64 small
     shape = sgemm.hip_sgemm_launch_shape(9, 4096, 4096, 4096)
-    assert shape == {"workgroups": 1024, "threads": 256, "k_steps": 256, "tile_m": 128, "tile_n": 128}
+    assert shape == {"workgroups": 512, "threads": 512, "k_steps": 256, "tile_m": 256, "tile_n": 128}
+    shape = sgemm.hip_sgemm_launch_shape(9, 2048, 2048, 2048)
+    assert shape == {"workgroups": 256, "threads": 256, "k_steps": 64, "tile_m": 128, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(9, 4097, 4097, 4097)
-    assert (shape["workgroups"], shape["k_steps"]) == (33 * 33, 257)
+    assert shape == {"workgroups": 33 * 65, "threads": 256, "k_steps": 257, "tile_m": 128, "tile_n": 64}
+    shape = sgemm.hip_sgemm_launch_shape(9, 1024, 1024, 1024)
+    assert shape == {"workgroups": 256, "threads": 256, "k_steps": 64, "tile_m": 64, "tile_n": 64}
     assert sgemm.hip_sgemm_launch_shape(2, 4096, 4096, 4096)["threads"] == 1024
     assert sgemm.hip_sgemm_launch_shape(0, 4096, 4096, 4096)["k_steps"] == 4096
     with pytest.raises(sgemm.SgemmError):
