@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--workload", default="sgemm_4096")
     ap.add_argument("--ladder", default=None, metavar="PATH")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time torch.addmm (the vendor BLAS) on the same workload, as context")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the reference sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -197,6 +199,30 @@ def device_info():
     return info
 
 
+def vendor_timed(prob: Problem, steps: int, warmup: int):
+    """The same call through torch.addmm on FP32 tensors (rocBLAS/hipBLASLt,
+    TF32 off): a context figure for the vendor library, never a dependency of
+    libsgemm.  Returns the mean kernel ms from HIP events, like run_timed."""
+    import torch
+    torch.backends.cuda.matmul.allow_tf32 = False
+    w = prob.w
+    stream = torch.cuda.current_stream()
+    prob.refill()
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        prob.copies[i % len(prob.copies)].addmm_(prob.dA, prob.dB, beta=w.beta, alpha=w.alpha)
+    prob.refill()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        prob.copies[i].addmm_(prob.dA, prob.dB, beta=w.beta, alpha=w.alpha)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
 def bench_one(w, level, steps, warmup, prob=None):
     from dense_fp32_matrix_row_amd import sgemm
     prob = prob or Problem(w, max(steps, warmup, 1))
@@ -254,6 +280,14 @@ def main():
                     f.flush()
                     print(f"[ladder] {wl.name} L{lv} {name}: {kms:.4f} ms, {rec['tflops']} TFLOPS",
                           flush=True)
+                vms = vendor_timed(prob, min(steps, 20), min(warmup, 10))
+                tf = wl.flops / (vms * 1e-3) / 1e12
+                f.write(json.dumps({"workload": wl.name, "level": "vendor",
+                                    "level_name": "torch.addmm (rocBLAS/hipBLASLt, FP32)",
+                                    "kernel_ms": round(vms, 4), "tflops": round(tf, 3),
+                                    "frac_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4),
+                                    "algorithmic_gbs": round(wl.algorithmic_bytes / (vms * 1e-3) / 1e9, 1)}) + "\n")
+                print(f"[ladder] {wl.name} vendor: {vms:.4f} ms, {tf:.3f} TFLOPS", flush=True)
                 del prob
                 torch.cuda.empty_cache()
 
@@ -277,6 +311,12 @@ def main():
         "algorithmic_gbs": round(w.algorithmic_bytes / (kms * 1e-3) / 1e9, 1),
         "device": device_info(),
     }
+    if args.vendor:
+        vms = vendor_timed(prob, steps, warmup)
+        line["vendor_blas"] = {"library": "torch.addmm (rocBLAS/hipBLASLt), FP32, TF32 off",
+                               "kernel_ms": round(vms, 4),
+                               "tflops": round(w.flops / (vms * 1e-3) / 1e12, 3),
+                               "note": "context only; not part of libsgemm"}
     if not args.no_cpu:
         def rows_out(r):
             # one more call on a fresh C, outside any timed region

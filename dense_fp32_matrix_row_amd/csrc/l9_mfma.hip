@@ -35,18 +35,22 @@ namespace {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPad = 4;      // LDS row padding (words)
-constexpr int kGroupM = 8;   // tile-rows per group of the block order
 
 // A tile configuration: BM x BN block tile, BK-deep K steps, WAVES_M x
 // WAVES_N wavefronts (each owning a (BM/WAVES_M) x (BN/WAVES_N) wave tile),
-// and how many of a K step's BK/2 MFMA steps are unrolled together (fewer
-// keeps the compiler from hoisting every fragment read into registers).
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int UNROLL_ = BK_ / 2>
+// how many of a K step's BK/2 MFMA steps are unrolled together (fewer keeps
+// the compiler from hoisting every fragment read into registers), how many
+// tile-rows one group of the block order spans, and whether wavefronts raise
+// their issue priority around the barrier (PRIO, below).
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int UNROLL_ = BK_ / 2,
+          int GROUP_M_ = 8, bool PRIO_ = false>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
   static constexpr int UNROLL = UNROLL_;
+  static constexpr int GROUP_M = GROUP_M_;
+  static constexpr bool PRIO = PRIO_;
 };
 
 template <int N>
@@ -112,9 +116,9 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
   const int64_t nk = ceil_div(p.K, BK);
   const int64_t first = xcd_contiguous(blockIdx.x, gridDim.x);
   for (int64_t t = first; t < ntiles; t += gridDim.x) {
-    const int64_t group = kGroupM * tiles_n;
-    const int64_t first_m = (t / group) * kGroupM;
-    const int64_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+    const int64_t group = T::GROUP_M * tiles_n;
+    const int64_t first_m = (t / group) * T::GROUP_M;
+    const int64_t gm = tiles_m - first_m < T::GROUP_M ? tiles_m - first_m : T::GROUP_M;
     const int64_t in = t % group;
     const int64_t row0 = (first_m + in % gm) * BM;
     const int64_t col0 = (in / gm) * BN;
@@ -193,6 +197,13 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
       const int cur = static_cast<int>(kt & 1);
       const bool more = kt + 1 < nk;
       if (more) load((kt + 1) * BK);
+      // PRIO: two blocks share each CU's matrix pipes and a block is only as
+      // fast as its slowest wavefront at the barrier, so a wavefront takes
+      // priority 1 while it issues MFMAs and 3 while it stores the next stage
+      // and waits at the barrier (the stragglers reach the barrier sooner),
+      // then drops to 0.  Measured on MI355X: +3 % at 4096^3 with 256 x 128
+      // tiles; it slows the small-tile shapes, which leave it off.
+      if (T::PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll T::UNROLL
       for (int s = 0; s < BK / 2; ++s) {
         const int kk = 2 * s + khalf;
@@ -205,8 +216,10 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
             acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                 vget<BLK_M>(af, bi), vget<BLK_N>(bf, bj), acc[bi][bj], 0, 0, 0);
       }
+      if (T::PRIO) __builtin_amdgcn_s_setprio(3);
       if (more) store(cur ^ 1);
       __syncthreads();
+      if (T::PRIO) __builtin_amdgcn_s_setprio(0);
     }
 
     // Epilogue: register r of block (bi, bj) is C[row(bi, r)][col(bj)]; a
@@ -272,8 +285,8 @@ hipError_t launch_tiles(const Problem& p, hipStream_t s) {
 // 32-deep K steps; large ragged problems (4097^3 leaves a one-row /
 // one-column fringe of tiles) take 128 x 64, whose many small blocks soak up
 // the fringe; small problems take 64 x 64 so that more CUs get work.
-typedef MfmaTile<256, 128, 16, 4, 2> TileHuge;
-typedef MfmaTile<128, 128, 32, 4, 1> TileLarge;
+typedef MfmaTile<256, 128, 16, 4, 2, 8, 8, true> TileHuge;
+typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true> TileLarge;
 typedef MfmaTile<128, 64, 16, 2, 2> TileMid;
 typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;
 constexpr int kCUs = 256;
