@@ -81,10 +81,15 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t bid, int64_t nblocks) 
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
 }
 
-// EDGE = false: the host guarantees M % BM == N % BN == K % BK == 0, so every
+// MODE kWhole: the host guarantees M % BM == N % BN == K % BK == 0, so every
 // tile and K step is whole and the kernel carries no bounds logic (fewer
-// registers and instructions); EDGE = true handles any shape.
-template <class T, bool EDGE>
+// registers and instructions).  kRaggedK: whole M and N tiles, K not a
+// multiple of BK; only the last K step masks (k beyond K reads as zero), and
+// the register budget stays that of kWhole, so two blocks of the 256 x 128
+// tile still share a CU.  kEdge handles any shape.
+constexpr int kWhole = 0, kRaggedK = 1, kEdge = 2;
+
+template <class T, int MODE>
 __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_m,
                                                        int64_t tiles_n,
                                                        int64_t ntiles) {
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
     // of the panel at k-group kq, float4 s of B is row r of the panel at
     // column group nq (advanced by k0 columns of A / k0 rows of B).  Rows
     // beyond M and the B rows beyond K are never dereferenced.
-    const bool interior = !EDGE || (row0 + BM <= p.M && col0 + BN <= p.N);
+    const bool interior = MODE != kEdge || (row0 + BM <= p.M && col0 + BN <= p.N);
     const float* pa[A_ITERS];
     const float* pb[B_ITERS];
 #pragma unroll
@@ -150,12 +155,30 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
     }
     float4 ra[A_ITERS], rb[B_ITERS];
     auto load = [&](int64_t k0) {
-      if (!EDGE || (interior && k0 + BK <= p.K)) {
+      if (MODE == kWhole || (interior && k0 + BK <= p.K)) {
         // whole K step inside the matrix: no bounds tests (uniform branch)
 #pragma unroll
         for (int s = 0; s < A_ITERS; ++s) ra[s] = ld_global4(pa[s] + k0);
 #pragma unroll
         for (int s = 0; s < B_ITERS; ++s) rb[s] = ld_global4(pb[s] + k0 * p.ldb);
+        return;
+      }
+      if (MODE == kRaggedK) {
+        // the last K step of a whole tile: k at or beyond K reads as zero
+#pragma unroll
+        for (int s = 0; s < A_ITERS; ++s) {
+          const int kq = (tid + s * THREADS) % (BK / 4);
+          const float* q = pa[s] + k0;
+          const int64_t k = k0 + 4 * kq;
+          ra[s] = make_float4(k < p.K ? q[0] : 0.0f, k + 1 < p.K ? q[1] : 0.0f,
+                              k + 2 < p.K ? q[2] : 0.0f, k + 3 < p.K ? q[3] : 0.0f);
+        }
+#pragma unroll
+        for (int s = 0; s < B_ITERS; ++s) {
+          const int r = (tid + s * THREADS) / (BN / 4);
+          rb[s] = k0 + r < p.K ? ld_global4(pb[s] + k0 * p.ldb)
+                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
         return;
       }
 #pragma unroll
@@ -227,7 +250,7 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
     // Each lane keeps one base pointer per block row; the offsets of its 16
     // registers' rows are lane-independent multiples of ldc (scalar work).
     const int64_t col = col0 + b_off;
-    const bool vec_ok = !EDGE || (BLK_N > 1 && col + BLK_N - 1 < p.N);
+    const bool vec_ok = MODE != kEdge || (BLK_N > 1 && col + BLK_N - 1 < p.N);
 #pragma unroll
     for (int bi = 0; bi < BLK_M; ++bi) {
       const int64_t row_base = row0 + wm * WTM + BLK_M * 4 * khalf + bi;
@@ -270,11 +293,13 @@ hipError_t launch_tiles(const Problem& p, hipStream_t s) {
   const Geometry g = tile_geometry<T>(p.M, p.N, p.K);
   const dim3 grid(static_cast<unsigned>(g.workgroups)), block(T::THREADS);
   const int64_t tm = ceil_div(p.M, T::BM), tn = ceil_div(p.N, T::BN);
-  const bool whole = p.M % T::BM == 0 && p.N % T::BN == 0 && p.K % T::BK == 0;
-  if (whole)
-    hipLaunchKernelGGL((k_level9<T, false>), grid, block, 0, s, p, tm, tn, g.tiles);
+  const bool whole_mn = p.M % T::BM == 0 && p.N % T::BN == 0;
+  if (whole_mn && p.K % T::BK == 0)
+    hipLaunchKernelGGL((k_level9<T, kWhole>), grid, block, 0, s, p, tm, tn, g.tiles);
+  else if (whole_mn)
+    hipLaunchKernelGGL((k_level9<T, kRaggedK>), grid, block, 0, s, p, tm, tn, g.tiles);
   else
-    hipLaunchKernelGGL((k_level9<T, true>), grid, block, 0, s, p, tm, tn, g.tiles);
+    hipLaunchKernelGGL((k_level9<T, kEdge>), grid, block, 0, s, p, tm, tn, g.tiles);
   return hipGetLastError();
 }
 
@@ -291,7 +316,7 @@ typedef MfmaTile<128, 64, 16, 2, 2> TileMid;
 typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;
 constexpr int kCUs = 256;
 
-enum class Shape { kHuge, kLarge, kMid, kSmall };
+}  // namespace
 
 Shape pick_shape(int M, int N) {
   const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
@@ -304,8 +329,17 @@ Shape pick_shape(int M, int N) {
   return Shape::kSmall;
 }
 
-Geometry geometry9(int M, int N, int K) {
-  switch (pick_shape(M, N)) {
+TileDims shape_dims(Shape shape) {
+  switch (shape) {
+    case Shape::kHuge: return {TileHuge::BM, TileHuge::BN, 2 * kCUs};
+    case Shape::kLarge: return {TileLarge::BM, TileLarge::BN, kCUs};
+    case Shape::kMid: return {TileMid::BM, TileMid::BN, 0};
+    default: return {TileSmall::BM, TileSmall::BN, 0};
+  }
+}
+
+Geometry mfma_geometry(Shape shape, int M, int N, int K) {
+  switch (shape) {
     case Shape::kHuge: return tile_geometry<TileHuge>(M, N, K);
     case Shape::kLarge: return tile_geometry<TileLarge>(M, N, K);
     case Shape::kMid: return tile_geometry<TileMid>(M, N, K);
@@ -313,14 +347,20 @@ Geometry geometry9(int M, int N, int K) {
   }
 }
 
-hipError_t launch9(const Problem& p, hipStream_t s) {
-  switch (pick_shape(p.M, p.N)) {
+hipError_t launch_mfma(Shape shape, const Problem& p, hipStream_t s) {
+  switch (shape) {
     case Shape::kHuge: return launch_tiles<TileHuge>(p, s);
     case Shape::kLarge: return launch_tiles<TileLarge>(p, s);
     case Shape::kMid: return launch_tiles<TileMid>(p, s);
     default: return launch_tiles<TileSmall>(p, s);
   }
 }
+
+namespace {
+
+Geometry geometry9(int M, int N, int K) { return mfma_geometry(pick_shape(M, N), M, N, K); }
+
+hipError_t launch9(const Problem& p, hipStream_t s) { return launch_mfma(pick_shape(p.M, p.N), p, s); }
 
 }  // namespace
 

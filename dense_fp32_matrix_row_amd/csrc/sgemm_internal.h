@@ -134,7 +134,28 @@ __device__ __forceinline__ void store4(float* __restrict__ c, int64_t col,
 // C <- beta*C over the M x N window (the K == 0 / alpha == 0 quick return).
 hipError_t launch_scale(const Problem& p, hipStream_t stream);
 
-// The ten rungs (host-side descriptors).
+// Level 9's matrix-core tile shapes, which the dispatching rung composes:
+// Huge 256 x 128, Large 128 x 128, Mid 128 x 64, Small 64 x 64 block tiles.
+enum class Shape { kHuge, kLarge, kMid, kSmall };
+struct TileDims {
+  int bm, bn;         // block tile
+  int64_t min_tiles;  // tiles a problem needs before level 9 picks the shape
+};
+Shape pick_shape(int M, int N);  // level 9's own choice for a problem
+TileDims shape_dims(Shape shape);
+Geometry mfma_geometry(Shape shape, int M, int N, int K);
+hipError_t launch_mfma(Shape shape, const Problem& p, hipStream_t s);
+
+// Thin problems (M or N at most kThin) on the vector ALUs: every output is a
+// K-long dot product split over lanes and wavefronts and summed in a fixed
+// order (deterministic, no atomics, no workspace).
+constexpr int kThin = 16;
+Geometry few_rows_geometry(int M, int N, int K);
+hipError_t launch_few_rows(const Problem& p, hipStream_t s);  // needs M <= kThin
+Geometry few_cols_geometry(int M, int N, int K);
+hipError_t launch_few_cols(const Problem& p, hipStream_t s);  // needs N <= kThin
+
+// The rungs (host-side descriptors).
 const LevelDesc* level0();
 const LevelDesc* level1();
 const LevelDesc* level2();
@@ -145,5 +166,6 @@ const LevelDesc* level6();
 const LevelDesc* level7();
 const LevelDesc* level8();
 const LevelDesc* level9();
+const LevelDesc* level10();
 
 }  // namespace sgemm

@@ -30,10 +30,11 @@ def test_symbol_exported(name):
 
 def test_levels_and_names():
     n = sgemm.hip_sgemm_num_levels()
-    assert n == 10
+    assert n == 11
     names = [sgemm.hip_sgemm_level_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert names[0].startswith("L0_") and names[9].startswith("L9_mfma")
+    assert names[10].startswith("L10_shape_dispatch")
     assert sgemm.hip_sgemm_level_name(-1) is None
     assert sgemm.hip_sgemm_level_name(n) is None
 
@@ -72,14 +73,14 @@ def test_null_operands_allowed_when_not_read():
 
 def test_unknown_level():
     args = (4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4)
-    assert sgemm.hip_sgemm_level(10, *args, stream=0) == sgemm.STATUS_UNKNOWN_LEVEL
+    assert sgemm.hip_sgemm_level(11, *args, stream=0) == sgemm.STATUS_UNKNOWN_LEVEL
     assert sgemm.hip_sgemm_level(-1, *args, stream=0) == sgemm.STATUS_UNKNOWN_LEVEL
     assert "unknown level" in sgemm.hip_sgemm_status_string(sgemm.STATUS_UNKNOWN_LEVEL)
 
 
-def test_auto_level_is_the_matrix_core_rung():
+def test_auto_level_is_the_dispatching_rung():
     for M, N, K in [(256, 256, 256), (4096, 4096, 4096), (4097, 4097, 4097), (1, 1, 1)]:
-        assert sgemm.hip_sgemm_auto_level(M, N, K, FAKE, K, FAKE, N, FAKE, N) == 9
+        assert sgemm.hip_sgemm_auto_level(M, N, K, FAKE, K, FAKE, N, FAKE, N) == 10
     assert sgemm.hip_sgemm_auto_level(-1, 2, 2, FAKE, 2, FAKE, 2, FAKE, 2) == -1
 
 
@@ -94,6 +95,28 @@ def test_launch_shapes():
     assert shape == {"workgroups": 33 * 65, "threads": 256, "k_steps": 257, "tile_m": 128, "tile_n": 64}
     shape = sgemm.hip_sgemm_launch_shape(9, 1024, 1024, 1024)
     assert shape == {"workgroups": 256, "threads": 256, "k_steps": 64, "tile_m": 64, "tile_n": 64}
+    # level 10 reports its largest launch: the whole-tile grid of a problem
+    # that misses the 256 x 128 tile by at most 16 rows / columns ...
+    shape = sgemm.hip_sgemm_launch_shape(10, 4097, 4097, 4097)
+    assert shape == {"workgroups": 512, "threads": 512, "k_steps": 257, "tile_m": 256, "tile_n": 128}
+    shape = sgemm.hip_sgemm_launch_shape(10, 4096 + 16, 4096 + 16, 100)
+    assert (shape["workgroups"], shape["tile_m"], shape["tile_n"]) == (512, 256, 128)
+    # ... or the 128 x 128 tile when there are too few 256 x 128 tiles ...
+    shape = sgemm.hip_sgemm_launch_shape(10, 2051, 2055, 300)
+    assert (shape["workgroups"], shape["tile_m"], shape["tile_n"]) == (256, 128, 128)
+    # ... level 9's choice when the fringe would be wider than 16 ...
+    assert sgemm.hip_sgemm_launch_shape(10, 4096 + 17, 4096, 64) == \
+        sgemm.hip_sgemm_launch_shape(9, 4096 + 17, 4096, 64)
+    assert sgemm.hip_sgemm_launch_shape(10, 1024, 1024, 1024) == \
+        sgemm.hip_sgemm_launch_shape(9, 1024, 1024, 1024)
+    # ... and the thin kernels for M <= 16 (one block per 16 columns) or
+    # N <= 16 (one block per 16 rows)
+    shape = sgemm.hip_sgemm_launch_shape(10, 1, 4097, 4097)
+    assert (shape["workgroups"], shape["threads"], shape["tile_n"]) == (257, 1024, 16)
+    shape = sgemm.hip_sgemm_launch_shape(10, 16, 4096, 64)
+    assert (shape["workgroups"], shape["threads"], shape["tile_m"]) == (256, 512, 16)
+    shape = sgemm.hip_sgemm_launch_shape(10, 4096, 3, 4097)
+    assert (shape["workgroups"], shape["threads"], shape["tile_m"], shape["tile_n"]) == (256, 1024, 16, 4)
     assert sgemm.hip_sgemm_launch_shape(2, 4096, 4096, 4096)["threads"] == 1024
     assert sgemm.hip_sgemm_launch_shape(0, 4096, 4096, 4096)["k_steps"] == 4096
     with pytest.raises(sgemm.SgemmError):

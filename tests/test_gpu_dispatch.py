@@ -1,0 +1,97 @@
+"""Level 10 (shape-aware dispatch) on the problem classes it splits: a
+whole-tile grid plus one- to sixteen-wide fringes (both tile shapes), a
+ragged K under whole M/N tiles, and thin problems (M <= 16 or N <= 16) on the
+vector-ALU kernels.  Every case is compared in full with the CPU reference
+through the C ABI, with guard regions around C (nothing outside the window
+may change); integer-valued data must match bit for bit, and repeated calls
+must be bit-identical (the thin kernels' cross-lane sums have a fixed order).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from dense_fp32_matrix_row_amd import inputs, sgemm
+from oracle import oracle
+from tests import gpu_harness as gh
+
+pytestmark = pytest.mark.gpu
+
+LEVEL = 10
+BOUND = 1e-5
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    sgemm.load()
+
+
+# (M, N, K, what it exercises); the plan each shape takes is pinned on the
+# CPU by the launch-shape test of the ABI suite.
+SHAPES = [
+    (2051, 2055, 300, "128x128 grid + 3-row / 7-column fringe"),
+    (4096 + 3, 4096 + 16, 40, "256x128 grid + 3-row / 16-column fringe"),
+    (4096, 4096, 36, "256x128 grid, K ragged (36 = 2*16 + 4)"),
+    (2048, 2048, 100, "128x128 grid, K ragged (100 = 3*32 + 4)"),
+    (1, 3001, 5003, "one row (matrix-vector)"),
+    (5, 3001, 5003, "five rows"),
+    (16, 1000, 777, "sixteen rows"),
+    (1500, 1, 5003, "one column"),
+    (1500, 7, 5003, "seven columns"),
+    (300, 16, 2049, "sixteen columns"),
+    (17, 17, 4097, "smallest non-thin shape (level 9 tiles)"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,what", SHAPES, ids=[s[3] for s in SHAPES])
+def test_dispatch_plans_match_reference(M, N, K, what):
+    print(f"[dispatch] {M}x{N}x{K}: {what}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 7000 + M + N + K)
+    for alpha, beta in [(0.5, 3.0), (1.0, 0.0)]:
+        out, st = gh.run(gh.Case(M, N, K, alpha, beta, A, B, C), LEVEL)
+        assert st == 0, sgemm.hip_sgemm_status_string(st)
+        ref = oracle.oracle_sgemm(A, B, C, alpha, beta)
+        err = oracle.normalised_error(out, ref, C, alpha, beta, strict=True)
+        assert err <= BOUND, (M, N, K, alpha, beta, err)
+
+
+@pytest.mark.parametrize("M,N,K", [(2051, 2055, 67), (3, 1025, 999), (1025, 5, 999)])
+def test_dispatch_padded_and_misaligned(M, N, K):
+    """Row strides that are not multiples of 4 and bases only 4-byte aligned
+    (lda = K + 3, ldb = N + 5, ldc = N + 7; offsets 1, 2, 3 elements)."""
+    print(f"[dispatch alignment] {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 8100 + M)
+    case = gh.Case(M, N, K, -2.0, -1.0, A, B, C, K + 3, N + 5, N + 7, 1, 2, 3)
+    out, st = gh.run(case, LEVEL)
+    assert st == 0
+    ref = oracle.oracle_sgemm(A, B, C, -2.0, -1.0)
+    assert oracle.normalised_error(out, ref, C, -2.0, -1.0, strict=True) <= BOUND
+
+
+@pytest.mark.parametrize("M,N,K", [(2051, 2055, 300), (7, 2000, 3001), (2000, 9, 3001),
+                                   (4096 + 1, 4096 + 1, 33)])
+def test_dispatch_integer_exact(M, N, K):
+    """Integer entries in [-8, 8]: every partial sum is an integer far below
+    2^24, so any summation order is exact and the result must equal the
+    reference bit for bit -- on the grid, the fringes and the thin kernels."""
+    print(f"[dispatch integer] {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.integer_abc(M, N, K, seed=M + 3 * N + K)
+    out, st = gh.run(gh.Case(M, N, K, 1.0, 3.0, A, B, C), LEVEL)
+    assert st == 0
+    ref = oracle.oracle_sgemm(A, B, C, 1.0, 3.0)
+    assert np.array_equal(out.astype(np.float64), ref.ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(4097, 4097, 97), (1, 4097, 4097), (4097, 2, 4097)])
+def test_dispatch_deterministic(M, N, K):
+    print(f"[dispatch determinism] {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 9100 + K)
+    a, st1 = gh.run(gh.Case(M, N, K, 1.0, 1.0, A, B, C), LEVEL)
+    b, st2 = gh.run(gh.Case(M, N, K, 1.0, 1.0, A, B, C), LEVEL)
+    assert st1 == st2 == 0
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -28,7 +28,7 @@ from tests import gpu_harness as gh
 
 pytestmark = pytest.mark.gpu
 
-LEVELS = list(range(10))
+LEVELS = list(range(11))
 BOUND = 1e-5
 SANITY = 1e-6          # typical float32 error is ~1e-7; above this is suspicious
 _errors = {}           # (level, workload) -> strict error, for the sanity check
@@ -86,14 +86,20 @@ def test_workload_parity(level, name):
 
 
 @pytest.mark.parametrize("name", WORKLOAD_NAMES)
-def test_auto_dispatch_matches_level9(name):
+def test_auto_dispatch_matches_level10(name):
+    """hip_sgemm runs the shape-aware rung; on whole-tile workloads that rung
+    launches exactly level 9's kernel, so those agree bit for bit too."""
     w, A, B, C, res, rows, ref = workload(name)
     print(f"[auto] {name}", flush=True)
     out_auto, st = res.call(None, w.alpha, w.beta, rows=rows)
     assert st == 0
-    out9, st = res.call(9, w.alpha, w.beta, rows=rows)
+    out10, st = res.call(10, w.alpha, w.beta, rows=rows)
     assert st == 0
-    assert np.array_equal(out_auto.view(np.uint32), out9.view(np.uint32))
+    assert np.array_equal(out_auto.view(np.uint32), out10.view(np.uint32))
+    if w.M % 128 == 0 and w.N % 128 == 0 and w.K % 32 == 0:
+        out9, st = res.call(9, w.alpha, w.beta, rows=rows)
+        assert st == 0
+        assert np.array_equal(out9.view(np.uint32), out10.view(np.uint32))
 
 
 @pytest.mark.parametrize("level", LEVELS)
