@@ -14,50 +14,114 @@
 //     ragged), plus the thin kernels on the fringe.  At 4097^3 this replaces
 //     level 9's 2145 edge-checked 128 x 64 tiles by the 512 whole 256 x 128
 //     tiles of 4096^3 (exactly two per CU) and two one-element-wide strips;
-//   - anything else: level 9's own tile choice.
-// Every output element is still computed by exactly one kernel; the regions
-// are disjoint, so the launches need no ordering beyond the stream's.
+//   - a deep K over a small tile grid: split K (l10_splitk.hip);
+//   - anything else: the tile shape whose grid fills the CUs best, with two
+//     K slices per stage where one block per CU would leave each SIMD a
+//     single wavefront.
+// Every output element is computed by exactly one tile or thin kernel (or,
+// split, by one reduction over its slices); the regions are disjoint, so
+// the launches need no ordering beyond the stream's.
 #include "sgemm_internal.h"
 
 namespace sgemm {
 namespace {
 
-enum class Plan { kFewRows, kFewCols, kTiles, kTilesWithFringe };
+enum class Plan { kFewRows, kFewCols, kTiles, kTilesWithFringe, kSplitK };
 
 struct Decomp {
   Plan plan;
-  Shape shape;  // matrix-core tile shape of the tile grid
-  int Mm, Nm;   // extent of the tile grid
+  Shape shape;      // matrix-core tile shape
+  int Mm, Nm;       // extent of the tile grid (kTilesWithFringe)
+  int64_t k_split;  // slice length (kSplitK)
 };
 
-Decomp decompose(int M, int N) {
-  if (M <= kThin) return {Plan::kFewRows, Shape::kSmall, 0, 0};
-  if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, 0, 0};
-  for (Shape s : {Shape::kHuge, Shape::kLarge}) {
-    const TileDims d = shape_dims(s);
-    const int mr = M % d.bm, nr = N % d.bn;
-    const int Mm = M - mr, Nm = N - nr;
-    if (mr <= kThin && nr <= kThin && int64_t(Mm / d.bm) * (Nm / d.bn) >= d.min_tiles)
-      return {mr == 0 && nr == 0 ? Plan::kTiles : Plan::kTilesWithFringe, s, Mm, Nm};
+constexpr int kCUs = 256;
+
+// Fraction of the last round of blocks that is busy: tiles over whole
+// rounds of one block per CU.
+double round_fill(int64_t tiles) {
+  const int64_t rounds = ceil_div(tiles, kCUs);
+  return double(tiles) / double(rounds * kCUs);
+}
+
+// The rules below were fitted to sweeps of every tile shape and slice count
+// on MI355X (dense_fp32_matrix_row_amd.autotune); the comments give the
+// measurements that decided them.
+Decomp decompose(int M, int N, int K) {
+  if (M <= kThin) return {Plan::kFewRows, Shape::kSmall, M, N, K};
+  if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, M, N, K};
+
+  // 1. At least two 256 x 128 tiles per CU (plus a fringe of <= 16): the
+  //    big tile (4096^3: 138 TFLOP/s; 4097^3 with the fringe: 127).
+  {
+    const int mr = M % 256, nr = N % 128;
+    const int64_t tiles = int64_t((M - mr) / 256) * ((N - nr) / 128);
+    if (mr <= kThin && nr <= kThin && tiles >= 2 * kCUs)
+      return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, Shape::kHuge, M - mr, N - nr, K};
   }
-  return {Plan::kTiles, pick_shape(M, N), M, N};
+
+  // 2. Deep K over a small tile grid: split K so that about two work items
+  //    per CU run (1024 x 1024 x 4096: 128 x 128 in 8 slices 94 TFLOP/s
+  //    against 80 unsplit; 2048 x 2048 x 8192: 256 x 128 in 4 slices 131
+  //    against 115; 512 x 512 x 8192: 74 against 19).  Slices stay >= 256
+  //    deep (512 for the big tile) and at most 16.
+  const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
+  if (K >= 2048 && K >= 2 * int64_t(M > N ? M : N) && tiles128 < 2 * kCUs) {
+    Shape shape = Shape::kSmall;
+    int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64), min_slice = 256;
+    if (M % 256 == 0 && N % 128 == 0 && int64_t(M / 256) * (N / 128) >= 64) {
+      shape = Shape::kHuge;
+      tiles = int64_t(M / 256) * (N / 128);
+      min_slice = 512;
+    } else if (tiles128 >= 16) {
+      shape = Shape::kLarge;
+      tiles = tiles128;
+    }
+    int64_t splits = ceil_div(2 * kCUs, tiles);
+    if (splits > 16) splits = 16;
+    if (splits > K / min_slice) splits = K / min_slice;
+    if (splits >= 2) {
+      const int64_t k_split = k_split_for(K, splits, shape_bk(shape));
+      if (k_split < K) return {Plan::kSplitK, shape, M, N, k_split};
+    }
+  }
+
+  // 3. 128 x 128 tiles (plus a fringe of <= 16) when they fill whole rounds
+  //    of CUs: with two K slices at about one round (2048^3: 115 against
+  //    110 unsliced), unsliced beyond (2048 x 4096: 124).
+  {
+    const int mr = M % 128, nr = N % 128;
+    const int64_t tiles = int64_t((M - mr) / 128) * ((N - nr) / 128);
+    if (mr <= kThin && nr <= kThin && tiles >= kCUs && round_fill(tiles) >= 0.9) {
+      const Shape shape = tiles <= kCUs + kCUs / 8 ? Shape::kLargeSliced : Shape::kLarge;
+      return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, shape, M - mr, N - nr, K};
+    }
+  }
+
+  // 4. Everything else: 64 x 64 tiles with two K slices, up to three blocks
+  //    per CU (1024^3: 66 against 56 unsliced; 3072^3: 115 against 73 for
+  //    128 x 128 tiles, whose 576 tiles leave the third round 1/4 full;
+  //    it beats the 128 x 64 tile at every size measured, 512^3 to 4096^3).
+  return {Plan::kTiles, Shape::kSmallSliced, M, N, K};
 }
 
 Geometry geometry10(int M, int N, int K) {
-  const Decomp d = decompose(M, N);
+  const Decomp d = decompose(M, N, K);
   switch (d.plan) {
     case Plan::kFewRows: return few_rows_geometry(M, N, K);
     case Plan::kFewCols: return few_cols_geometry(M, N, K);
+    case Plan::kSplitK: return mfma_split_geometry(d.shape, M, N, K, d.k_split);
     default: return mfma_geometry(d.shape, d.Mm, d.Nm, K);
   }
 }
 
 hipError_t launch10(const Problem& p, hipStream_t s) {
-  const Decomp d = decompose(p.M, p.N);
+  const Decomp d = decompose(p.M, p.N, p.K);
   switch (d.plan) {
     case Plan::kFewRows: return launch_few_rows(p, s);
     case Plan::kFewCols: return launch_few_cols(p, s);
     case Plan::kTiles: return launch_mfma(d.shape, p, s);
+    case Plan::kSplitK: return launch_splitk(d.shape, d.k_split, p, s);
     case Plan::kTilesWithFringe: break;
   }
   Problem grid = p;

@@ -1,0 +1,114 @@
+// l10_splitk.hip -- split K for problems too small in M x N to fill the
+// GPU: level 9's tiles, each with its K range cut into slices that run as
+// separate work items, then one reduction kernel.
+//
+// The technique is the one the pages describe behind the vendor library's
+// small-size advantage ([GEMM2], size-sweep section: at 256 the vendor calls
+// a tiled GEMM plus a reduce kernel; each block computes part of the K sum
+// for its C block, the partial sums need extra storage, a reduce kernel adds
+// them).  At 1024^3 the 128 x 128 tile grid has 64 tiles for 256 CUs; four
+// slices of K make 256 work items, eight make 512 (two per CU).
+//
+// Determinism: the number of slices depends only on the shape, every slice
+// stores its float32 sums into its own plane of the workspace (no atomics),
+// and the reduction adds the planes in slice order 0, 1, ..., S-1 before
+// the alpha/beta epilogue.  Results are bit-reproducible; they differ from
+// the unsplit tile in the last bits (one float32 chain per slice instead of
+// one for the whole K), within the same rounding bound.
+//
+// Workspace: S x M x N floats per call, taken from a stream-ordered memory
+// pool that the library creates per device on first use and keeps for the
+// life of the process (release threshold: never), allocated and freed on the
+// caller's stream around the two kernels.  Concurrent calls on other
+// streams therefore never share a workspace.
+#include <mutex>
+
+#include "sgemm_internal.h"
+
+namespace sgemm {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mutex;
+hipMemPool_t g_pools[kMaxDevices];
+
+hipError_t pool_for_current_device(hipMemPool_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_pool_mutex);
+  if (g_pools[dev] == nullptr) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;  // keep freed blocks cached for reuse
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return e;
+    }
+    g_pools[dev] = pool;
+  }
+  *out = g_pools[dev];
+  return hipSuccess;
+}
+
+// C[i][j] <- alpha * (((W_0 + W_1) + W_2) + ... + W_{S-1})[i][j] + beta * C[i][j],
+// four adjacent columns per thread (128-bit accesses where whole).
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws,
+                                                       int64_t splits, int M, int N,
+                                                       float alpha, float beta,
+                                                       float* __restrict__ C, int64_t ldc,
+                                                       int64_t groups_per_row,
+                                                       int64_t ngroups) {
+  const int64_t plane = int64_t(M) * N;
+  for (int64_t g = int64_t(blockIdx.x) * 256 + threadIdx.x; g < ngroups;
+       g += int64_t(gridDim.x) * 256) {
+    const int64_t row = g / groups_per_row, col = 4 * (g % groups_per_row);
+    const float* w = ws + row * N;
+    float4 sum = load4(w, col, N, true);
+    for (int64_t s = 1; s < splits; ++s) {
+      const float4 v = load4(w + s * plane, col, N, true);
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+    }
+    store4(C + row * ldc + col, col, N, sum, alpha, beta);
+  }
+}
+
+hipError_t launch_reduce(const float* ws, int64_t splits, const Problem& p, hipStream_t s) {
+  const int64_t groups_per_row = ceil_div(p.N, 4);
+  const int64_t ngroups = int64_t(p.M) * groups_per_row;
+  const int64_t want = ceil_div(ngroups, 256);
+  const int64_t blocks = want < 8192 ? want : 8192;  // grid-stride beyond
+  hipLaunchKernelGGL(k_splitk_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, ws,
+                     splits, p.M, p.N, p.alpha, p.beta, p.C, p.ldc, groups_per_row, ngroups);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStream_t s) {
+  const int64_t splits = ceil_div(p.K, k_split);
+  const size_t bytes = size_t(splits) * size_t(p.M) * size_t(p.N) * sizeof(float);
+  hipMemPool_t pool = nullptr;
+  hipError_t e = pool_for_current_device(&pool);
+  if (e != hipSuccess) return e;
+  void* ws = nullptr;
+  e = hipMallocFromPoolAsync(&ws, bytes, pool, s);
+  if (e != hipSuccess) return e;
+  e = launch_mfma_split(shape, p, k_split, static_cast<float*>(ws), s);
+  if (e == hipSuccess) e = launch_reduce(static_cast<const float*>(ws), splits, p, s);
+  const hipError_t f = hipFreeAsync(ws, s);
+  return e != hipSuccess ? e : f;
+}
+
+}  // namespace sgemm

@@ -40,14 +40,21 @@ constexpr int kPad = 4;      // LDS row padding (words)
 // WAVES_N wavefronts (each owning a (BM/WAVES_M) x (BN/WAVES_N) wave tile),
 // how many of a K step's BK/2 MFMA steps are unrolled together (fewer keeps
 // the compiler from hoisting every fragment read into registers), how many
-// tile-rows one group of the block order spans, and whether wavefronts raise
-// their issue priority around the barrier (PRIO, below).
+// tile-rows one group of the block order spans, whether wavefronts raise
+// their issue priority around the barrier (PRIO, below), and into how many
+// K slices each stage is cut (KSLICE: KSLICE x WAVES_M x WAVES_N wavefronts;
+// slice j takes MFMA steps [j, j+1) * BK/2/KSLICE of every stage, and the
+// slices' sums meet in LDS after the K loop, added in slice order).  More
+// slices put more wavefronts on each SIMD for the same tile, which hides the
+// dependent-MFMA and LDS latencies of a tile grid too small to fill the GPU
+// otherwise, without a second kernel or workspace.
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int UNROLL_ = BK_ / 2,
-          int GROUP_M_ = 8, bool PRIO_ = false>
+          int GROUP_M_ = 8, bool PRIO_ = false, int KSLICE_ = 1>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  static constexpr int KSLICE = KSLICE_;
+  static constexpr int THREADS = 64 * WAVES_M * WAVES_N * KSLICE;
   static constexpr int UNROLL = UNROLL_;
   static constexpr int GROUP_M = GROUP_M_;
   static constexpr bool PRIO = PRIO_;
@@ -88,11 +95,17 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t bid, int64_t nblocks) 
 // the register budget stays that of kWhole, so two blocks of the 256 x 128
 // tile still share a CU.  kEdge handles any shape.
 constexpr int kWhole = 0, kRaggedK = 1, kEdge = 2;
-
-template <class T, int MODE>
+//
+// SPLIT (split K): work item t is K slice t / ntiles, k in
+// [k_lo, k_lo + k_split), of tile t % ntiles; it stores its raw float32 sums
+// (no alpha, beta or C) into plane t / ntiles of ws, an M x N row-major array
+// per slice, and k_splitk_reduce adds the planes in slice order.  The slice
+// length is a multiple of BK, so every slice but the last is whole.
+template <class T, int MODE, bool SPLIT = false>
 __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_m,
-                                                       int64_t tiles_n,
-                                                       int64_t ntiles) {
+                                                       int64_t tiles_n, int64_t ntiles,
+                                                       int64_t k_split,
+                                                       float* __restrict__ ws) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK, THREADS = T::THREADS;
   constexpr int WTM = BM / T::WAVES_M, WTN = BN / T::WAVES_N;
   constexpr int BLK_M = WTM / 32, BLK_N = WTN / 32;
@@ -104,23 +117,34 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
                 "tile not evenly staged");
   static_assert(BLK_M * 32 == WTM && BLK_N * 32 == WTN, "wave tile not whole blocks");
   static_assert(BK % 2 == 0, "MFMA steps consume k in pairs");
+  static_assert((BK / 2) % T::KSLICE == 0, "K slices must split a stage's MFMA steps evenly");
+  constexpr int WAVE_TILES = T::WAVES_M * T::WAVES_N;
+  constexpr int STEPS = BK / 2 / T::KSLICE;           // MFMA steps per stage per wavefront
+  constexpr int PER_WAVE = BLK_M * BLK_N * 16 * 64;   // accumulator floats per wavefront
   typedef typename VecT<BLK_M>::type AFrag;
   typedef typename VecT<BLK_N>::type BFrag;
 
   __shared__ __align__(16) float As[2][BK][LDA];
   __shared__ __align__(16) float Bs[2][BK][LDB];
+  __shared__ __align__(16) float red[T::KSLICE > 1 ? (T::KSLICE - 1) * WAVE_TILES * PER_WAVE : 1];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
-  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const int kslice = wave / WAVE_TILES, wv = wave % WAVE_TILES;
+  const int wm = wv / T::WAVES_N, wn = wv % T::WAVES_N;
   const int lrow = lane % 32, khalf = lane / 32;
   // LDS offsets (words) of this lane's fragments inside one k-row
   const int a_off = wm * WTM + BLK_M * lrow;
   const int b_off = wn * WTN + BLK_N * lrow;
 
-  const int64_t nk = ceil_div(p.K, BK);
+  const int64_t items = SPLIT ? ntiles * ceil_div(p.K, k_split) : ntiles;
   const int64_t first = xcd_contiguous(blockIdx.x, gridDim.x);
-  for (int64_t t = first; t < ntiles; t += gridDim.x) {
+  for (int64_t item = first; item < items; item += gridDim.x) {
+    const int64_t t = SPLIT ? item % ntiles : item;
+    const int64_t split = SPLIT ? item / ntiles : 0;
+    const int64_t k_lo = split * k_split;
+    const int64_t K = SPLIT ? (p.K - k_lo < k_split ? p.K - k_lo : k_split) : p.K;
+    const int64_t nk = ceil_div(K, BK);
     const int64_t group = T::GROUP_M * tiles_n;
     const int64_t first_m = (t / group) * T::GROUP_M;
     const int64_t gm = tiles_m - first_m < T::GROUP_M ? tiles_m - first_m : T::GROUP_M;
@@ -146,16 +170,16 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
 #pragma unroll
     for (int s = 0; s < A_ITERS; ++s) {
       const int idx = tid + s * THREADS;
-      pa[s] = p.A + (row0 + idx / (BK / 4)) * p.lda + 4 * (idx % (BK / 4));
+      pa[s] = p.A + (row0 + idx / (BK / 4)) * p.lda + k_lo + 4 * (idx % (BK / 4));
     }
 #pragma unroll
     for (int s = 0; s < B_ITERS; ++s) {
       const int idx = tid + s * THREADS;
-      pb[s] = p.B + (idx / (BN / 4)) * p.ldb + col0 + 4 * (idx % (BN / 4));
+      pb[s] = p.B + (k_lo + idx / (BN / 4)) * p.ldb + col0 + 4 * (idx % (BN / 4));
     }
     float4 ra[A_ITERS], rb[B_ITERS];
     auto load = [&](int64_t k0) {
-      if (MODE == kWhole || (interior && k0 + BK <= p.K)) {
+      if (MODE == kWhole || (interior && k0 + BK <= K)) {
         // whole K step inside the matrix: no bounds tests (uniform branch)
 #pragma unroll
         for (int s = 0; s < A_ITERS; ++s) ra[s] = ld_global4(pa[s] + k0);
@@ -170,13 +194,13 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
           const int kq = (tid + s * THREADS) % (BK / 4);
           const float* q = pa[s] + k0;
           const int64_t k = k0 + 4 * kq;
-          ra[s] = make_float4(k < p.K ? q[0] : 0.0f, k + 1 < p.K ? q[1] : 0.0f,
-                              k + 2 < p.K ? q[2] : 0.0f, k + 3 < p.K ? q[3] : 0.0f);
+          ra[s] = make_float4(k < K ? q[0] : 0.0f, k + 1 < K ? q[1] : 0.0f,
+                              k + 2 < K ? q[2] : 0.0f, k + 3 < K ? q[3] : 0.0f);
         }
 #pragma unroll
         for (int s = 0; s < B_ITERS; ++s) {
           const int r = (tid + s * THREADS) / (BN / 4);
-          rb[s] = k0 + r < p.K ? ld_global4(pb[s] + k0 * p.ldb)
+          rb[s] = k0 + r < K ? ld_global4(pb[s] + k0 * p.ldb)
                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
         return;
@@ -185,14 +209,14 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
       for (int s = 0; s < A_ITERS; ++s) {
         const int idx = tid + s * THREADS;
         const int r = idx / (BK / 4), kq = idx % (BK / 4);
-        ra[s] = load4(pa[s] - 4 * kq, k0 + 4 * kq, p.K, row0 + r < p.M);
+        ra[s] = load4(pa[s] - 4 * kq, k0 + 4 * kq, K, row0 + r < p.M);
       }
 #pragma unroll
       for (int s = 0; s < B_ITERS; ++s) {
         const int idx = tid + s * THREADS;
         const int r = idx / (BN / 4), nq = idx % (BN / 4);
         rb[s] = load4(pb[s] + k0 * p.ldb - (col0 + 4 * nq), col0 + 4 * nq, p.N,
-                      k0 + r < p.K);
+                      k0 + r < K);
       }
     };
     auto store = [&](int buf) {
@@ -228,8 +252,8 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
       // tiles; it slows the small-tile shapes, which leave it off.
       if (T::PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll T::UNROLL
-      for (int s = 0; s < BK / 2; ++s) {
-        const int kk = 2 * s + khalf;
+      for (int s = 0; s < STEPS; ++s) {
+        const int kk = 2 * (kslice * STEPS + s) + khalf;
         const AFrag af = *reinterpret_cast<const AFrag*>(&As[cur][kk][a_off]);
         const BFrag bf = *reinterpret_cast<const BFrag*>(&Bs[cur][kk][b_off]);
 #pragma unroll
@@ -245,12 +269,66 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
       if (T::PRIO) __builtin_amdgcn_s_setprio(0);
     }
 
+    if (T::KSLICE > 1) {
+      // Slices 1.. hand their sums to slice 0 (lane-contiguous, conflict
+      // free); slice 0 adds them in slice order and runs the epilogue.  The
+      // next tile's reduction writes red only after that tile's K loop,
+      // whose barriers slice 0 reaches after finishing this epilogue.
+      if (kslice > 0) {
+        float* dst = red + ((kslice - 1) * WAVE_TILES + wv) * PER_WAVE + lane;
+#pragma unroll
+        for (int bi = 0; bi < BLK_M; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < BLK_N; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[((bi * BLK_N + bj) * 16 + r) * 64] = acc[bi][bj][r];
+      }
+      __syncthreads();
+      if (kslice > 0) continue;
+#pragma unroll
+      for (int ks = 1; ks < T::KSLICE; ++ks) {
+        const float* src = red + ((ks - 1) * WAVE_TILES + wv) * PER_WAVE + lane;
+#pragma unroll
+        for (int bi = 0; bi < BLK_M; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < BLK_N; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[bi][bj][r] += src[((bi * BLK_N + bj) * 16 + r) * 64];
+      }
+    }
+
     // Epilogue: register r of block (bi, bj) is C[row(bi, r)][col(bj)]; a
     // lane's BLK_N outputs of one row are adjacent.
     // Each lane keeps one base pointer per block row; the offsets of its 16
     // registers' rows are lane-independent multiples of ldc (scalar work).
     const int64_t col = col0 + b_off;
     const bool vec_ok = MODE != kEdge || (BLK_N > 1 && col + BLK_N - 1 < p.N);
+    if (SPLIT) {
+      // raw sums into this slice's plane (row stride N)
+      float* const plane = ws + split * int64_t(p.M) * p.N;
+#pragma unroll
+      for (int bi = 0; bi < BLK_M; ++bi) {
+        const int64_t row_base = row0 + wm * WTM + BLK_M * 4 * khalf + bi;
+        float* const w_base = plane + row_base * p.N + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dr = BLK_M * (8 * (r / 4) + (r % 4));
+          if (!interior && row_base + dr >= p.M) continue;
+          float* w = w_base + dr * p.N;
+          float o[BLK_N];
+#pragma unroll
+          for (int bj = 0; bj < BLK_N; ++bj) o[bj] = acc[bi][bj][r];
+          if (interior || vec_ok) {
+            __builtin_memcpy(w, o, sizeof(o));
+          } else {
+#pragma unroll
+            for (int bj = 0; bj < BLK_N; ++bj)
+              if (col + bj < p.N) w[bj] = o[bj];
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int bi = 0; bi < BLK_M; ++bi) {
       const int64_t row_base = row0 + wm * WTM + BLK_M * 4 * khalf + bi;
@@ -295,11 +373,44 @@ hipError_t launch_tiles(const Problem& p, hipStream_t s) {
   const int64_t tm = ceil_div(p.M, T::BM), tn = ceil_div(p.N, T::BN);
   const bool whole_mn = p.M % T::BM == 0 && p.N % T::BN == 0;
   if (whole_mn && p.K % T::BK == 0)
-    hipLaunchKernelGGL((k_level9<T, kWhole>), grid, block, 0, s, p, tm, tn, g.tiles);
+    hipLaunchKernelGGL((k_level9<T, kWhole>), grid, block, 0, s, p, tm, tn, g.tiles,
+                       int64_t(p.K), nullptr);
   else if (whole_mn)
-    hipLaunchKernelGGL((k_level9<T, kRaggedK>), grid, block, 0, s, p, tm, tn, g.tiles);
+    hipLaunchKernelGGL((k_level9<T, kRaggedK>), grid, block, 0, s, p, tm, tn, g.tiles,
+                       int64_t(p.K), nullptr);
   else
-    hipLaunchKernelGGL((k_level9<T, kEdge>), grid, block, 0, s, p, tm, tn, g.tiles);
+    hipLaunchKernelGGL((k_level9<T, kEdge>), grid, block, 0, s, p, tm, tn, g.tiles,
+                       int64_t(p.K), nullptr);
+  return hipGetLastError();
+}
+
+// Split K: ceil(K / k_split) slices per tile (k_split a multiple of BK),
+// raw sums into ws (slices x M x N floats).
+template <class T>
+Geometry split_geometry(int M, int N, int K, int64_t k_split) {
+  Geometry g = make_geometry(M, N, K, T::BM, T::BN, T::BK, T::THREADS);
+  g.tiles *= ceil_div(K, k_split);
+  const int64_t cap = kMaxWorkItems / T::THREADS;
+  g.workgroups = g.tiles < cap ? g.tiles : cap;
+  g.k_steps = ceil_div(k_split, T::BK);
+  return g;
+}
+
+template <class T>
+hipError_t launch_split(const Problem& p, int64_t k_split, float* ws, hipStream_t s) {
+  const Geometry g = split_geometry<T>(p.M, p.N, p.K, k_split);
+  const dim3 grid(static_cast<unsigned>(g.workgroups)), block(T::THREADS);
+  const int64_t tm = ceil_div(p.M, T::BM), tn = ceil_div(p.N, T::BN);
+  const bool whole_mn = p.M % T::BM == 0 && p.N % T::BN == 0;
+  if (whole_mn && p.K % T::BK == 0)
+    hipLaunchKernelGGL((k_level9<T, kWhole, true>), grid, block, 0, s, p, tm, tn, tm * tn,
+                       k_split, ws);
+  else if (whole_mn)
+    hipLaunchKernelGGL((k_level9<T, kRaggedK, true>), grid, block, 0, s, p, tm, tn, tm * tn,
+                       k_split, ws);
+  else
+    hipLaunchKernelGGL((k_level9<T, kEdge, true>), grid, block, 0, s, p, tm, tn, tm * tn,
+                       k_split, ws);
   return hipGetLastError();
 }
 
@@ -314,6 +425,12 @@ typedef MfmaTile<256, 128, 16, 4, 2, 8, 8, true> TileHuge;
 typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true> TileLarge;
 typedef MfmaTile<128, 64, 16, 2, 2> TileMid;
 typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;
+// Two K slices per stage (8 wavefronts): for tile grids of about one block
+// per CU, where a single wavefront per SIMD leaves MFMA and LDS latency
+// exposed.  Measured on MI355X: 64 x 64 at 1024^3 +18 %, at 3072^3 +10 %;
+// 128 x 128 (2 x 2 wave tiles of 64 x 64) at 2048^3 +5 %.
+typedef MfmaTile<128, 128, 32, 2, 2, 16, 8, false, 2> TileLargeSliced;
+typedef MfmaTile<64, 64, 32, 2, 2, 16, 8, false, 2> TileSmallSliced;
 constexpr int kCUs = 256;
 
 }  // namespace
@@ -334,6 +451,8 @@ TileDims shape_dims(Shape shape) {
     case Shape::kHuge: return {TileHuge::BM, TileHuge::BN, 2 * kCUs};
     case Shape::kLarge: return {TileLarge::BM, TileLarge::BN, kCUs};
     case Shape::kMid: return {TileMid::BM, TileMid::BN, 0};
+    case Shape::kLargeSliced: return {TileLargeSliced::BM, TileLargeSliced::BN, 0};
+    case Shape::kSmallSliced: return {TileSmallSliced::BM, TileSmallSliced::BN, 0};
     default: return {TileSmall::BM, TileSmall::BN, 0};
   }
 }
@@ -343,6 +462,8 @@ Geometry mfma_geometry(Shape shape, int M, int N, int K) {
     case Shape::kHuge: return tile_geometry<TileHuge>(M, N, K);
     case Shape::kLarge: return tile_geometry<TileLarge>(M, N, K);
     case Shape::kMid: return tile_geometry<TileMid>(M, N, K);
+    case Shape::kLargeSliced: return tile_geometry<TileLargeSliced>(M, N, K);
+    case Shape::kSmallSliced: return tile_geometry<TileSmallSliced>(M, N, K);
     default: return tile_geometry<TileSmall>(M, N, K);
   }
 }
@@ -352,7 +473,43 @@ hipError_t launch_mfma(Shape shape, const Problem& p, hipStream_t s) {
     case Shape::kHuge: return launch_tiles<TileHuge>(p, s);
     case Shape::kLarge: return launch_tiles<TileLarge>(p, s);
     case Shape::kMid: return launch_tiles<TileMid>(p, s);
+    case Shape::kLargeSliced: return launch_tiles<TileLargeSliced>(p, s);
+    case Shape::kSmallSliced: return launch_tiles<TileSmallSliced>(p, s);
     default: return launch_tiles<TileSmall>(p, s);
+  }
+}
+
+int shape_bk(Shape shape) {
+  switch (shape) {
+    case Shape::kHuge: return TileHuge::BK;
+    case Shape::kLarge: return TileLarge::BK;
+    case Shape::kMid: return TileMid::BK;
+    case Shape::kLargeSliced: return TileLargeSliced::BK;
+    case Shape::kSmallSliced: return TileSmallSliced::BK;
+    default: return TileSmall::BK;
+  }
+}
+
+Geometry mfma_split_geometry(Shape shape, int M, int N, int K, int64_t k_split) {
+  switch (shape) {
+    case Shape::kHuge: return split_geometry<TileHuge>(M, N, K, k_split);
+    case Shape::kLarge: return split_geometry<TileLarge>(M, N, K, k_split);
+    case Shape::kMid: return split_geometry<TileMid>(M, N, K, k_split);
+    case Shape::kLargeSliced: return split_geometry<TileLargeSliced>(M, N, K, k_split);
+    case Shape::kSmallSliced: return split_geometry<TileSmallSliced>(M, N, K, k_split);
+    default: return split_geometry<TileSmall>(M, N, K, k_split);
+  }
+}
+
+hipError_t launch_mfma_split(Shape shape, const Problem& p, int64_t k_split, float* ws,
+                             hipStream_t s) {
+  switch (shape) {
+    case Shape::kHuge: return launch_split<TileHuge>(p, k_split, ws, s);
+    case Shape::kLarge: return launch_split<TileLarge>(p, k_split, ws, s);
+    case Shape::kMid: return launch_split<TileMid>(p, k_split, ws, s);
+    case Shape::kLargeSliced: return launch_split<TileLargeSliced>(p, k_split, ws, s);
+    case Shape::kSmallSliced: return launch_split<TileSmallSliced>(p, k_split, ws, s);
+    default: return launch_split<TileSmall>(p, k_split, ws, s);
   }
 }
 

@@ -67,6 +67,14 @@ int run(const LevelDesc* lv, int M, int N, int K, float alpha, const float* A,
   return status_of(lv->launch(p, stream));
 }
 
+constexpr int kNumTiles = 6;
+
+Shape tile_shape(int tile) {
+  static const Shape shapes[kNumTiles] = {Shape::kHuge,  Shape::kLarge,       Shape::kMid,
+                                          Shape::kSmall, Shape::kLargeSliced, Shape::kSmallSliced};
+  return shapes[tile];
+}
+
 int choose_level(int M, int N, int K) {
   (void)M;
   (void)N;
@@ -108,6 +116,31 @@ int hip_sgemm_level(int level, int M, int N, int K, float alpha,
              stream);
 }
 
+int hip_sgemm_tile_split(int tile, int splits, int M, int N, int K, float alpha,
+                        const float* A, int lda, const float* B, int ldb, float beta,
+                        float* C, int ldc, hipStream_t stream) {
+  if (tile < 0 || tile >= kNumTiles || splits < 1) return SGEMM_STATUS_UNKNOWN_CONFIG;
+  const int bad = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+  if (bad) return bad;
+  if (M == 0 || N == 0) return 0;
+  Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+  if (K == 0 || alpha == 0.0f) return status_of(launch_scale(p, stream));
+  const Shape shape = tile_shape(tile);
+  const int64_t k_split = k_split_for(K, splits, shape_bk(shape));
+  if (k_split >= K) return status_of(launch_mfma(shape, p, stream));
+  return status_of(launch_splitk(shape, k_split, p, stream));
+}
+
+int hip_sgemm_num_tiles(void) { return kNumTiles; }
+
+const char* hip_sgemm_tile_name(int tile) {
+  if (tile < 0 || tile >= kNumTiles) return nullptr;
+  static const char* const names[kNumTiles] = {"256x128x16_8w", "128x128x32_4w", "128x64x16_4w",
+                                               "64x64x16_4w", "128x128x32_8w_2slices",
+                                               "64x64x32_8w_2slices"};
+  return names[tile];
+}
+
 int hip_sgemm_num_levels(void) { return kNumLevels; }
 
 const char* hip_sgemm_level_name(int level) {
@@ -128,6 +161,7 @@ const char* hip_sgemm_status_string(int status) {
     case -10: return "argument 10 (C) is NULL with M, N > 0";
     case -11: return "argument 11 (ldc) is smaller than max(1, N)";
     case SGEMM_STATUS_UNKNOWN_LEVEL: return "unknown level";
+    case SGEMM_STATUS_UNKNOWN_CONFIG: return "unknown tile shape or split count";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

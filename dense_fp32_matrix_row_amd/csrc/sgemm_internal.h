@@ -135,8 +135,10 @@ __device__ __forceinline__ void store4(float* __restrict__ c, int64_t col,
 hipError_t launch_scale(const Problem& p, hipStream_t stream);
 
 // Level 9's matrix-core tile shapes, which the dispatching rung composes:
-// Huge 256 x 128, Large 128 x 128, Mid 128 x 64, Small 64 x 64 block tiles.
-enum class Shape { kHuge, kLarge, kMid, kSmall };
+// Huge 256 x 128, Large 128 x 128, Mid 128 x 64, Small 64 x 64 block tiles,
+// and 128 x 128 / 64 x 64 tiles whose stages are cut into two K slices
+// (twice the wavefronts per tile; their sums meet in LDS).
+enum class Shape { kHuge, kLarge, kMid, kSmall, kLargeSliced, kSmallSliced };
 struct TileDims {
   int bm, bn;         // block tile
   int64_t min_tiles;  // tiles a problem needs before level 9 picks the shape
@@ -145,6 +147,21 @@ Shape pick_shape(int M, int N);  // level 9's own choice for a problem
 TileDims shape_dims(Shape shape);
 Geometry mfma_geometry(Shape shape, int M, int N, int K);
 hipError_t launch_mfma(Shape shape, const Problem& p, hipStream_t s);
+// Split K over the same tiles: the K range is cut into slices of k_split
+// (a multiple of the shape's BK) and each (tile, slice) is one work item
+// that stores raw float32 sums into its slice's M x N plane of ws.
+int shape_bk(Shape shape);
+Geometry mfma_split_geometry(Shape shape, int M, int N, int K, int64_t k_split);
+hipError_t launch_mfma_split(Shape shape, const Problem& p, int64_t k_split, float* ws,
+                             hipStream_t s);
+// The whole split-K call: workspace from the library's stream-ordered pool,
+// the split tile kernel, the in-order reduction with the alpha/beta epilogue.
+hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStream_t s);
+// k_split for a requested slice count: ceil(K / splits) rounded up to BK.
+inline int64_t k_split_for(int64_t K, int64_t splits, int bk) {
+  const int64_t per = (K + splits - 1) / splits;
+  return (per + bk - 1) / bk * bk;
+}
 
 // Thin problems (M or N at most kThin) on the vector ALUs: every output is a
 // K-long dot product split over lanes and wavefronts and summed in a fixed

@@ -22,11 +22,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libsgemm.so")
 
 STATUS_UNKNOWN_LEVEL = -100
+STATUS_UNKNOWN_CONFIG = -101
 
 # Every exported symbol of include/sgemm.h.
 EXPORTS = (
     "hip_sgemm", "hip_sgemm_level", "hip_sgemm_num_levels", "hip_sgemm_level_name",
     "hip_sgemm_status_string", "hip_sgemm_auto_level", "hip_sgemm_launch_shape",
+    "hip_sgemm_tile_split", "hip_sgemm_num_tiles", "hip_sgemm_tile_name",
 )
 
 _lib = None
@@ -56,6 +58,12 @@ def load(path: Optional[str] = None):
     lib.hip_sgemm.argtypes = gemm_args
     lib.hip_sgemm_level.restype = i32
     lib.hip_sgemm_level.argtypes = [i32] + gemm_args
+    lib.hip_sgemm_tile_split.restype = i32
+    lib.hip_sgemm_tile_split.argtypes = [i32, i32] + gemm_args
+    lib.hip_sgemm_num_tiles.restype = i32
+    lib.hip_sgemm_num_tiles.argtypes = []
+    lib.hip_sgemm_tile_name.restype = ctypes.c_char_p
+    lib.hip_sgemm_tile_name.argtypes = [i32]
     lib.hip_sgemm_num_levels.restype = i32
     lib.hip_sgemm_num_levels.argtypes = []
     lib.hip_sgemm_level_name.restype = ctypes.c_char_p
@@ -115,6 +123,23 @@ def hip_sgemm_level(level, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=
     return int(load().hip_sgemm_level(int(level), int(M), int(N), int(K), float(alpha), _addr(A),
                                       int(lda), _addr(B), int(ldb), float(beta), _addr(C),
                                       int(ldc), _stream(stream)))
+
+
+def hip_sgemm_tile_split(tile, splits, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         stream=None) -> int:
+    """Level 9's kernel with tile shape `tile` and K cut into `splits` slices."""
+    return int(load().hip_sgemm_tile_split(int(tile), int(splits), int(M), int(N), int(K),
+                                           float(alpha), _addr(A), int(lda), _addr(B), int(ldb),
+                                           float(beta), _addr(C), int(ldc), _stream(stream)))
+
+
+def hip_sgemm_num_tiles() -> int:
+    return int(load().hip_sgemm_num_tiles())
+
+
+def hip_sgemm_tile_name(tile) -> Optional[str]:
+    s = load().hip_sgemm_tile_name(int(tile))
+    return None if s is None else s.decode()
 
 
 def hip_sgemm_num_levels() -> int:

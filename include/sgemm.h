@@ -58,6 +58,7 @@
  *                 -11 ldc < max(1, N).  hip_sgemm_level numbers its
  *                 arguments the same way (level is not counted).
  *   -100          unknown level
+ *   -101          unknown tile shape or split count (hip_sgemm_tile_split)
  *   > 0           the hipError_t the launch reported
  */
 #ifndef LIBSGEMM_SGEMM_H
@@ -70,6 +71,7 @@ extern "C" {
 #endif
 
 #define SGEMM_STATUS_UNKNOWN_LEVEL (-100)
+#define SGEMM_STATUS_UNKNOWN_CONFIG (-101)
 
 /*
  * Best kernel for the shape: C <- alpha*A*B + beta*C.
@@ -104,12 +106,52 @@ int hip_sgemm(int M, int N, int K, float alpha,
  *   8 wave tiling (block -> wave -> lane) with an XCD-aware, grouped
  *     block-to-tile order ([GEMM2] warp tiling and thread swizzling sections)
  *   9 FP32 matrix cores (v_mfma_f32_32x32x2_f32) on the level-8 pipeline
+ *  10 shape-aware dispatch, the level hip_sgemm runs: level 9's tiles over
+ *     the largest whole-tile part of a problem whose M and N miss a tile
+ *     multiple by at most 16, with vector-ALU kernels on the thin fringe;
+ *     problems with M <= 16 or N <= 16 entirely on those kernels (their
+ *     cross-lane sums have a fixed order, so results are reproducible);
+ *     otherwise level 9's own choice.  A call may enqueue up to three
+ *     kernels on the stream, over disjoint parts of C ([GEMM2] size-sweep
+ *     section: a library is many kernels picked by shape)
  */
 int hip_sgemm_level(int level, int M, int N, int K, float alpha,
                     const float *A, int lda,
                     const float *B, int ldb,
                     float beta, float *C, int ldc,
                     hipStream_t stream);
+
+/*
+ * Level 9's matrix-core kernel with its configuration forced, for tuning
+ * sweeps (the per-shape choices of level 10 were measured with it):
+ *   tile    0 .. hip_sgemm_num_tiles()-1: 256 x 128 (BK 16, 8 wavefronts),
+ *           128 x 128 (BK 32, 4), 128 x 64 (BK 16, 4), 64 x 64 (BK 16, 4),
+ *           and with each stage cut into two K slices whose sums meet in LDS
+ *           (twice the wavefronts): 128 x 128 (BK 32, 8), 64 x 64 (BK 32, 8);
+ *   splits  >= 1: the K range is cut into about `splits` slices (each a
+ *           multiple of the tile's BK; ceil(K / slice) of them run) that
+ *           compute separately, and a second kernel adds the slices' float32
+ *           sums in slice order, then applies alpha and beta ([GEMM2]
+ *           size-sweep section: split-K, a tiled GEMM plus a reduce kernel).
+ *           splits = 1, or a slice covering all of K, is the unsplit kernel.
+ * Split K needs S x M x N floats of workspace: the library takes it from a
+ * stream-ordered memory pool of its own (one per device, created on first
+ * use, memory kept cached until the process ends), allocated and released on
+ * `stream` around the two kernels; concurrent calls never share it.  Results
+ * are bit-reproducible for a given (tile, splits, shape).  Other arguments,
+ * quick returns and status codes as hip_sgemm; -101 for a bad tile or
+ * splits < 1.
+ */
+int hip_sgemm_tile_split(int tile, int splits, int M, int N, int K, float alpha,
+                         const float *A, int lda,
+                         const float *B, int ldb,
+                         float beta, float *C, int ldc,
+                         hipStream_t stream);
+
+/* Number of tile shapes hip_sgemm_tile_split accepts, and their names
+ * ("256x128x16_8w", ...; NULL if unknown; static, owned by the library). */
+int hip_sgemm_num_tiles(void);
+const char *hip_sgemm_tile_name(int tile);
 
 /* Number of levels (valid levels are 0 .. hip_sgemm_num_levels()-1). */
 int hip_sgemm_num_levels(void);
@@ -136,8 +178,9 @@ int hip_sgemm_auto_level(int M, int N, int K,
  * number of workgroups, threads per workgroup, K steps each workgroup walks
  * (ceil(K / BK): the boundary rule of [L04] section 2.5 rounds the phase
  * count up and zero-fills the tail), and the output tile (tile_m x tile_n)
- * each workgroup owns.  Any output pointer may be NULL.  Returns 0, or a
- * negative status.
+ * each workgroup owns.  For level 10 this is its largest launch (the tile
+ * grid, or the thin kernel).  Any output pointer may be NULL.  Returns 0, or
+ * a negative status.
  */
 int hip_sgemm_launch_shape(int level, int M, int N, int K,
                            long long *workgroups, int *threads_per_group,

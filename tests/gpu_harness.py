@@ -47,9 +47,10 @@ def _flat(mat: np.ndarray, ld: int, off: int, guard: int, fill_pad, fill_guard) 
     return out
 
 
-def run(case: Case, level: Optional[int], stream=None, guard: int = 67):
+def run(case: Case, level, stream=None, guard: int = 67):
     """Run one call; returns (C_out M x N float32, status).  Raises if a value
-    outside the window of C changed."""
+    outside the window of C changed.  `level` is a level number, None
+    (hip_sgemm), or a callable taking hip_sgemm's twelve arguments."""
     M, N, K = case.M, case.N, case.K
     lda = max(1, K) if case.lda is None else case.lda
     ldb = max(1, N) if case.ldb is None else case.ldb
@@ -63,6 +64,8 @@ def run(case: Case, level: Optional[int], stream=None, guard: int = 67):
     pc = dC.data_ptr() + 4 * case.c_off
     if level is None:
         st = sgemm.hip_sgemm(M, N, K, case.alpha, pa, lda, pb, ldb, case.beta, pc, ldc, stream)
+    elif callable(level):
+        st = level(M, N, K, case.alpha, pa, lda, pb, ldb, case.beta, pc, ldc, stream)
     else:
         st = sgemm.hip_sgemm_level(level, M, N, K, case.alpha, pa, lda, pb, ldb, case.beta, pc, ldc,
                                    stream)

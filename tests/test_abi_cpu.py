@@ -101,14 +101,25 @@ def test_launch_shapes():
     assert shape == {"workgroups": 512, "threads": 512, "k_steps": 257, "tile_m": 256, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(10, 4096 + 16, 4096 + 16, 100)
     assert (shape["workgroups"], shape["tile_m"], shape["tile_n"]) == (512, 256, 128)
-    # ... or the 128 x 128 tile when there are too few 256 x 128 tiles ...
+    # ... or the 128 x 128 tile with two K slices (8 wavefronts) when there
+    # are about one round of them ...
     shape = sgemm.hip_sgemm_launch_shape(10, 2051, 2055, 300)
-    assert (shape["workgroups"], shape["tile_m"], shape["tile_n"]) == (256, 128, 128)
-    # ... level 9's choice when the fringe would be wider than 16 ...
-    assert sgemm.hip_sgemm_launch_shape(10, 4096 + 17, 4096, 64) == \
-        sgemm.hip_sgemm_launch_shape(9, 4096 + 17, 4096, 64)
-    assert sgemm.hip_sgemm_launch_shape(10, 1024, 1024, 1024) == \
-        sgemm.hip_sgemm_launch_shape(9, 1024, 1024, 1024)
+    assert shape == {"workgroups": 256, "threads": 512, "k_steps": 10, "tile_m": 128, "tile_n": 128}
+    shape = sgemm.hip_sgemm_launch_shape(10, 2048, 4096, 2048)
+    assert shape == {"workgroups": 512, "threads": 256, "k_steps": 64, "tile_m": 128, "tile_n": 128}
+    # ... split K for a deep K over a small grid: 8 slices of 512 over the
+    # 64 tiles of 128 x 128 at 1024 x 1024 x 4096, 4 slices of 2048 over the
+    # 128 tiles of 256 x 128 at 2048 x 2048 x 8192 ...
+    shape = sgemm.hip_sgemm_launch_shape(10, 1024, 1024, 4096)
+    assert shape == {"workgroups": 512, "threads": 256, "k_steps": 16, "tile_m": 128, "tile_n": 128}
+    shape = sgemm.hip_sgemm_launch_shape(10, 2048, 2048, 8192)
+    assert shape == {"workgroups": 512, "threads": 512, "k_steps": 128, "tile_m": 256, "tile_n": 128}
+    # ... and otherwise 64 x 64 tiles with two K slices (1024^3, 3072^3, and
+    # shapes whose fringe would be wider than 16)
+    for M, N, K in [(1024, 1024, 1024), (3072, 3072, 3072), (4096 + 17, 4096, 64)]:
+        shape = sgemm.hip_sgemm_launch_shape(10, M, N, K)
+        assert shape == {"workgroups": -(-M // 64) * -(-N // 64), "threads": 512,
+                         "k_steps": -(-K // 32), "tile_m": 64, "tile_n": 64}
     # ... and the thin kernels for M <= 16 (one block per 16 columns) or
     # N <= 16 (one block per 16 rows)
     shape = sgemm.hip_sgemm_launch_shape(10, 1, 4097, 4097)
@@ -148,3 +159,19 @@ def test_tile32_geometry_matches_the_six_level_example():
     assert (g["block_y"] * g["tile"] + g["ty"], g["block_x"] * g["tile"] + g["tx"]) == (g["c_row"], g["c_col"])
     coarse = golden()["coarse4_block"]
     assert sgemm.hip_sgemm_launch_shape(3, 4096, 4096, 4096)["tile_n"] == coarse["tile"] * coarse["coarse"]
+
+
+def test_tile_split_arguments():
+    assert sgemm.hip_sgemm_num_tiles() == 6
+    names = [sgemm.hip_sgemm_tile_name(t) for t in range(4)]
+    assert names[0].startswith("256x128") and names[3].startswith("64x64")
+    names = [sgemm.hip_sgemm_tile_name(t) for t in range(6)]
+    assert names[4].startswith("128x128") and names[5].startswith("64x64") and "2slices" in names[5]
+    assert sgemm.hip_sgemm_tile_name(6) is None and sgemm.hip_sgemm_tile_name(-1) is None
+    args = (4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4)
+    for tile, splits in [(-1, 1), (6, 1), (0, 0), (1, -3)]:
+        assert sgemm.hip_sgemm_tile_split(tile, splits, *args, stream=0) == sgemm.STATUS_UNKNOWN_CONFIG
+    assert "split" in sgemm.hip_sgemm_status_string(sgemm.STATUS_UNKNOWN_CONFIG)
+    # argument errors as hip_sgemm once the configuration is valid
+    assert sgemm.hip_sgemm_tile_split(0, 2, 4, 4, 8, 1.0, FAKE, 7, FAKE, 4, 0.0, FAKE, 4, stream=0) == -6
+    assert sgemm.hip_sgemm_tile_split(1, 2, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, stream=0) == 0

@@ -1,7 +1,9 @@
-"""Level 10 (shape-aware dispatch) on the problem classes it splits: a
-whole-tile grid plus one- to sixteen-wide fringes (both tile shapes), a
-ragged K under whole M/N tiles, and thin problems (M <= 16 or N <= 16) on the
-vector-ALU kernels.  Every case is compared in full with the CPU reference
+"""Level 10 (shape-aware dispatch) on every plan it has: a whole-tile grid
+plus one- to sixteen-wide fringes (both tile shapes), a ragged K under whole
+M/N tiles, the two-K-slice tiles, split K for a deep K over a small grid, and
+thin problems (M <= 16 or N <= 16) on the vector-ALU kernels.  The plan each
+shape takes is pinned on the CPU by the launch-shape test of the ABI suite.
+Every case is compared in full with the CPU reference
 through the C ABI, with guard regions around C (nothing outside the window
 may change); integer-valued data must match bit for bit, and repeated calls
 must be bit-identical (the thin kernels' cross-lane sums have a fixed order).
@@ -31,13 +33,15 @@ def _device():
     sgemm.load()
 
 
-# (M, N, K, what it exercises); the plan each shape takes is pinned on the
-# CPU by the launch-shape test of the ABI suite.
 SHAPES = [
-    (2051, 2055, 300, "128x128 grid + 3-row / 7-column fringe"),
+    (2051, 2055, 300, "128x128 two-slice grid + 3-row / 7-column fringe"),
     (4096 + 3, 4096 + 16, 40, "256x128 grid + 3-row / 16-column fringe"),
     (4096, 4096, 36, "256x128 grid, K ragged (36 = 2*16 + 4)"),
-    (2048, 2048, 100, "128x128 grid, K ragged (100 = 3*32 + 4)"),
+    (2048, 2048, 100, "128x128 two-slice grid, K ragged (100 = 3*32 + 4)"),
+    (2048, 4096, 80, "128x128 grid, 512 tiles"),
+    (1000, 1000, 300, "64x64 two-slice tiles, ragged edges"),
+    (1024, 1024, 4096, "split K: 128x128 tiles, 8 slices"),
+    (300, 260, 5000, "split K: 64x64 edge tiles, 16 slices, ragged K"),
     (1, 3001, 5003, "one row (matrix-vector)"),
     (5, 3001, 5003, "five rows"),
     (16, 1000, 777, "sixteen rows"),
@@ -74,7 +78,8 @@ def test_dispatch_padded_and_misaligned(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2051, 2055, 300), (7, 2000, 3001), (2000, 9, 3001),
-                                   (4096 + 1, 4096 + 1, 33)])
+                                   (4096 + 1, 4096 + 1, 33), (1024, 1024, 4096),
+                                   (512, 512, 8192)])
 def test_dispatch_integer_exact(M, N, K):
     """Integer entries in [-8, 8]: every partial sum is an integer far below
     2^24, so any summation order is exact and the result must equal the
@@ -87,7 +92,8 @@ def test_dispatch_integer_exact(M, N, K):
     assert np.array_equal(out.astype(np.float64), ref.ref)
 
 
-@pytest.mark.parametrize("M,N,K", [(4097, 4097, 97), (1, 4097, 4097), (4097, 2, 4097)])
+@pytest.mark.parametrize("M,N,K", [(4097, 4097, 97), (1, 4097, 4097), (4097, 2, 4097),
+                                   (1024, 1024, 4096), (1000, 1000, 300)])
 def test_dispatch_deterministic(M, N, K):
     print(f"[dispatch determinism] {M}x{N}x{K}", flush=True)
     A, B, C = inputs.make_abc(M, N, K, 9100 + K)
