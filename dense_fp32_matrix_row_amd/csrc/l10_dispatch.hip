@@ -47,9 +47,11 @@ double round_fill(int64_t tiles) {
 // The rules below were fitted to sweeps of every tile shape and slice count
 // on MI355X (dense_fp32_matrix_row_amd.autotune); the comments give the
 // measurements that decided them.
-Decomp decompose(int M, int N, int K) {
+Decomp decompose(int M, int N, int K, bool trans_a) {
   if (M <= kThin) return {Plan::kFewRows, Shape::kSmall, M, N, K};
-  if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, M, N, K};
+  // (with A stored K x M the few-columns kernel would read strided columns
+  // of A; those problems take the tiles below)
+  if (N <= kThin && !trans_a) return {Plan::kFewCols, Shape::kSmall, M, N, K};
 
   // 1. At least two 256 x 128 tiles per CU (plus a fringe of <= 16): the
   //    big tile (4096^3: 138 TFLOP/s; 4097^3 with the fringe: 127).
@@ -106,7 +108,7 @@ Decomp decompose(int M, int N, int K) {
 }
 
 Geometry geometry10(int M, int N, int K) {
-  const Decomp d = decompose(M, N, K);
+  const Decomp d = decompose(M, N, K, false);
   switch (d.plan) {
     case Plan::kFewRows: return few_rows_geometry(M, N, K);
     case Plan::kFewCols: return few_cols_geometry(M, N, K);
@@ -116,7 +118,7 @@ Geometry geometry10(int M, int N, int K) {
 }
 
 hipError_t launch10(const Problem& p, hipStream_t s) {
-  const Decomp d = decompose(p.M, p.N, p.K);
+  const Decomp d = decompose(p.M, p.N, p.K, p.trans_a);
   switch (d.plan) {
     case Plan::kFewRows: return launch_few_rows(p, s);
     case Plan::kFewCols: return launch_few_cols(p, s);
@@ -129,19 +131,20 @@ hipError_t launch10(const Problem& p, hipStream_t s) {
   grid.N = d.Nm;
   hipError_t e = launch_mfma(d.shape, grid, s);
   if (e == hipSuccess && d.Nm < p.N) {
-    // right fringe: rows [0, Mm), columns [Nm, N)
+    // right fringe: rows [0, Mm), columns [Nm, N) (B's columns are its rows
+    // when it is stored transposed)
     Problem right = p;
     right.M = d.Mm;
     right.N = p.N - d.Nm;
-    right.B = p.B + d.Nm;
+    right.B = p.B + (p.trans_b ? d.Nm * p.ldb : d.Nm);
     right.C = p.C + d.Nm;
-    e = launch_few_cols(right, s);
+    e = p.trans_a ? launch_mfma(Shape::kSmallSliced, right, s) : launch_few_cols(right, s);
   }
   if (e == hipSuccess && d.Mm < p.M) {
     // bottom fringe: rows [Mm, M), every column
     Problem bottom = p;
     bottom.M = p.M - d.Mm;
-    bottom.A = p.A + d.Mm * p.lda;
+    bottom.A = p.A + (p.trans_a ? d.Mm : d.Mm * p.lda);
     bottom.C = p.C + d.Mm * p.ldc;
     e = launch_few_rows(bottom, s);
   }

@@ -41,7 +41,10 @@ struct FewRows {
   static constexpr int KSWEEP = 64 * WAVES;
 };
 
-template <int RP>
+// TA: A stored K x M (element (r, k) at A[k * lda + r]); TB: B stored N x K
+// (element (k, n) at B[n * ldb + k]: the lane's four columns come as four
+// 128-bit reads along k and are transposed in registers).
+template <int RP, bool TA, bool TB>
 __global__ __launch_bounds__(FewRows<RP>::THREADS) void k_few_rows(Problem p,
                                                                    int64_t nblocks) {
   constexpr int WAVES = FewRows<RP>::WAVES, KSWEEP = FewRows<RP>::KSWEEP;
@@ -60,12 +63,30 @@ __global__ __launch_bounds__(FewRows<RP>::THREADS) void k_few_rows(Problem p,
 
     for (int64_t k = 64 * wave + 4 * g; k < p.K; k += KSWEEP) {
       float4 b[4];
+      if (TB) {
+        float4 v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = load4(p.B + (k + j) * p.ldb, col, p.N, k + j < p.K);
+        for (int c = 0; c < 4; ++c) v[c] = load4(p.B + (col + c) * p.ldb, k, p.K, col + c < p.N);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b[j] = make_float4(fget(v[0], j), fget(v[1], j), fget(v[2], j), fget(v[3], j));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b[j] = load4(p.B + (k + j) * p.ldb, col, p.N, k + j < p.K);
+      }
 #pragma unroll
       for (int r = 0; r < RP; ++r) {
-        const float4 a = load4(p.A + r * p.lda, k, p.K, r < p.M);
+        float4 a;
+        if (TA) {
+          const bool ok = r < p.M;
+          a = make_float4(ok && k < p.K ? p.A[k * p.lda + r] : 0.0f,
+                          ok && k + 1 < p.K ? p.A[(k + 1) * p.lda + r] : 0.0f,
+                          ok && k + 2 < p.K ? p.A[(k + 2) * p.lda + r] : 0.0f,
+                          ok && k + 3 < p.K ? p.A[(k + 3) * p.lda + r] : 0.0f);
+        } else {
+          a = load4(p.A + r * p.lda, k, p.K, r < p.M);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float av = fget(a, j);
@@ -123,7 +144,10 @@ struct FewCols {
   static constexpr int QUADS = KC / 256;            // k quads per lane per chunk
 };
 
-template <int WP>
+// TB: B stored N x K (the staged strip is then contiguous along k).  A is
+// always row-major here: with A stored K x M a wavefront's row would be a
+// strided column, so the dispatcher gives such problems to the tile kernels.
+template <int WP, bool TB>
 __global__ __launch_bounds__(kColThreads) void k_few_cols(Problem p, int64_t nblocks) {
   constexpr int KC = FewCols<WP>::KC, QUADS = FewCols<WP>::QUADS;
   __shared__ __align__(16) float Bs[WP][KC];
@@ -144,7 +168,8 @@ __global__ __launch_bounds__(kColThreads) void k_few_cols(Problem p, int64_t nbl
       __syncthreads();  // every wavefront is done with the previous chunk
       for (int e = tid; e < WP * KC; e += kColThreads) {
         const int c = e / KC, kk = e % KC;
-        Bs[c][kk] = (kc + kk < p.K && c < p.N) ? p.B[(kc + kk) * p.ldb + c] : 0.0f;
+        const bool ok = kc + kk < p.K && c < p.N;
+        Bs[c][kk] = !ok ? 0.0f : TB ? p.B[c * p.ldb + kc + kk] : p.B[(kc + kk) * p.ldb + c];
       }
       __syncthreads();
       if (has_row) {
@@ -188,22 +213,22 @@ int padded_width(int n) {
   return w;
 }
 
-template <int RP>
+template <int RP, bool TA, bool TB>
 hipError_t launch_rows_t(const Problem& p, hipStream_t s) {
   const int64_t nblocks = ceil_div(p.N, 16);
   const int64_t grid = nblocks < kMaxWorkItems / FewRows<RP>::THREADS
                            ? nblocks : kMaxWorkItems / FewRows<RP>::THREADS;
-  hipLaunchKernelGGL(k_few_rows<RP>, dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((k_few_rows<RP, TA, TB>), dim3(static_cast<unsigned>(grid)),
                      dim3(FewRows<RP>::THREADS), 0, s, p, nblocks);
   return hipGetLastError();
 }
 
-template <int WP>
+template <int WP, bool TB>
 hipError_t launch_cols_t(const Problem& p, hipStream_t s) {
   const int64_t nblocks = ceil_div(p.M, kRowsPerBlock);
   const int64_t grid = nblocks < kMaxWorkItems / kColThreads ? nblocks
                                                               : kMaxWorkItems / kColThreads;
-  hipLaunchKernelGGL(k_few_cols<WP>, dim3(static_cast<unsigned>(grid)), dim3(kColThreads), 0, s,
+  hipLaunchKernelGGL((k_few_cols<WP, TB>), dim3(static_cast<unsigned>(grid)), dim3(kColThreads), 0, s,
                      p, nblocks);
   return hipGetLastError();
 }
@@ -218,15 +243,23 @@ Geometry few_rows_geometry(int M, int N, int K) {
   return g;
 }
 
-hipError_t launch_few_rows(const Problem& p, hipStream_t s) {
+template <bool TA, bool TB>
+hipError_t launch_rows_op(const Problem& p, hipStream_t s) {
   switch (padded_width(p.M)) {
-    case 1: return launch_rows_t<1>(p, s);
-    case 2: return launch_rows_t<2>(p, s);
-    case 4: return launch_rows_t<4>(p, s);
-    case 8: return launch_rows_t<8>(p, s);
-    case 16: return launch_rows_t<16>(p, s);
+    case 1: return launch_rows_t<1, TA, TB>(p, s);
+    case 2: return launch_rows_t<2, TA, TB>(p, s);
+    case 4: return launch_rows_t<4, TA, TB>(p, s);
+    case 8: return launch_rows_t<8, TA, TB>(p, s);
+    case 16: return launch_rows_t<16, TA, TB>(p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_few_rows(const Problem& p, hipStream_t s) {
+  if (p.trans_a && p.trans_b) return launch_rows_op<true, true>(p, s);
+  if (p.trans_a) return launch_rows_op<true, false>(p, s);
+  if (p.trans_b) return launch_rows_op<false, true>(p, s);
+  return launch_rows_op<false, false>(p, s);
 }
 
 Geometry few_cols_geometry(int M, int N, int K) {
@@ -234,15 +267,21 @@ Geometry few_cols_geometry(int M, int N, int K) {
   return make_geometry(M, wp, K, kRowsPerBlock, wp, wp <= 8 ? 2048 : 1024, kColThreads);
 }
 
-hipError_t launch_few_cols(const Problem& p, hipStream_t s) {
+template <bool TB>
+hipError_t launch_cols_op(const Problem& p, hipStream_t s) {
   switch (padded_width(p.N)) {
-    case 1: return launch_cols_t<1>(p, s);
-    case 2: return launch_cols_t<2>(p, s);
-    case 4: return launch_cols_t<4>(p, s);
-    case 8: return launch_cols_t<8>(p, s);
-    case 16: return launch_cols_t<16>(p, s);
+    case 1: return launch_cols_t<1, TB>(p, s);
+    case 2: return launch_cols_t<2, TB>(p, s);
+    case 4: return launch_cols_t<4, TB>(p, s);
+    case 8: return launch_cols_t<8, TB>(p, s);
+    case 16: return launch_cols_t<16, TB>(p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_few_cols(const Problem& p, hipStream_t s) {
+  if (p.trans_a) return hipErrorInvalidValue;  // the dispatcher never sends these
+  return p.trans_b ? launch_cols_op<true>(p, s) : launch_cols_op<false>(p, s);
 }
 
 }  // namespace sgemm

@@ -23,14 +23,17 @@ const LevelDesc* level_desc(int level) {
 
 int max1(int v) { return v > 1 ? v : 1; }
 
-// Returns 0 or the negative 1-based position of the first bad argument.
+// Returns 0 or the negative 1-based position (in hip_sgemm's argument list)
+// of the first bad argument.  A stored transposed is K x M (lda >= M), B
+// stored transposed is N x K (ldb >= K).
 int validate(int M, int N, int K, float alpha, const void* A, int lda,
-             const void* B, int ldb, const void* C, int ldc) {
+             const void* B, int ldb, const void* C, int ldc, bool ta = false,
+             bool tb = false) {
   if (M < 0) return -1;
   if (N < 0) return -2;
   if (K < 0) return -3;
-  if (lda < max1(K)) return -6;
-  if (ldb < max1(N)) return -8;
+  if (lda < max1(ta ? M : K)) return -6;
+  if (ldb < max1(tb ? K : N)) return -8;
   if (ldc < max1(N)) return -11;
   const bool product = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
   if (product && A == nullptr) return -5;
@@ -133,6 +136,32 @@ int hip_sgemm_tile_split(int tile, int splits, int M, int N, int K, float alpha,
 
 int hip_sgemm_num_tiles(void) { return kNumTiles; }
 
+// 'N' / 'n' / 0: as stored; 'T' / 't' / 'C' / 'c' / 1: transposed (for real
+// data the conjugate transpose is the transpose); -1 otherwise.
+static int parse_op(int op) {
+  switch (op) {
+    case 0: case 'N': case 'n': return 0;
+    case 1: case 'T': case 't': case 'C': case 'c': return 1;
+    default: return -1;
+  }
+}
+
+int hip_sgemm_ex(int op_a, int op_b, int M, int N, int K, float alpha, const float* A,
+                 int lda, const float* B, int ldb, float beta, float* C, int ldc,
+                 hipStream_t stream) {
+  const int ta = parse_op(op_a), tb = parse_op(op_b);
+  if (ta < 0) return SGEMM_STATUS_BAD_OP_A;
+  if (tb < 0) return SGEMM_STATUS_BAD_OP_B;
+  const int bad = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc, ta, tb);
+  if (bad) return bad;
+  if (M == 0 || N == 0) return 0;
+  Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+  p.trans_a = ta != 0;
+  p.trans_b = tb != 0;
+  if (K == 0 || alpha == 0.0f) return status_of(launch_scale(p, stream));
+  return status_of(level_desc(10)->launch(p, stream));
+}
+
 const char* hip_sgemm_tile_name(int tile) {
   if (tile < 0 || tile >= kNumTiles) return nullptr;
   static const char* const names[kNumTiles] = {"256x128x16_8w", "128x128x32_4w", "128x64x16_4w",
@@ -155,13 +184,15 @@ const char* hip_sgemm_status_string(int status) {
     case -2: return "argument 2 (N) is negative";
     case -3: return "argument 3 (K) is negative";
     case -5: return "argument 5 (A) is NULL but A is read";
-    case -6: return "argument 6 (lda) is smaller than max(1, K)";
+    case -6: return "argument 6 (lda) is smaller than max(1, K) (max(1, M) for a transposed A)";
     case -7: return "argument 7 (B) is NULL but B is read";
-    case -8: return "argument 8 (ldb) is smaller than max(1, N)";
+    case -8: return "argument 8 (ldb) is smaller than max(1, N) (max(1, K) for a transposed B)";
     case -10: return "argument 10 (C) is NULL with M, N > 0";
     case -11: return "argument 11 (ldc) is smaller than max(1, N)";
     case SGEMM_STATUS_UNKNOWN_LEVEL: return "unknown level";
     case SGEMM_STATUS_UNKNOWN_CONFIG: return "unknown tile shape or split count";
+    case SGEMM_STATUS_BAD_OP_A: return "op(A) is not 'N' or 'T'";
+    case SGEMM_STATUS_BAD_OP_B: return "op(B) is not 'N' or 'T'";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

@@ -21,6 +21,10 @@ struct Problem {
   int64_t ldb;
   float* C;
   int64_t ldc;
+  // op(A) = A^T: A is stored K x M (row stride lda >= M); op(B) = B^T: B is
+  // stored N x K (ldb >= K).  Only the dispatching rung and the kernels it
+  // composes read these; levels 0-9 are reached with both false.
+  bool trans_a = false, trans_b = false;
 };
 
 // Launch geometry of one level for one shape.
@@ -154,6 +158,17 @@ int shape_bk(Shape shape);
 Geometry mfma_split_geometry(Shape shape, int M, int N, int K, int64_t k_split);
 hipError_t launch_mfma_split(Shape shape, const Problem& p, int64_t k_split, float* ws,
                              hipStream_t s);
+// The transposed orientations (l9_mfma_{tn,nt,tt}.hip): tn = A transposed,
+// nt = B transposed, tt = both.
+hipError_t launch_mfma_tn(Shape shape, const Problem& p, hipStream_t s);
+hipError_t launch_mfma_nt(Shape shape, const Problem& p, hipStream_t s);
+hipError_t launch_mfma_tt(Shape shape, const Problem& p, hipStream_t s);
+hipError_t launch_mfma_split_tn(Shape shape, const Problem& p, int64_t k_split, float* ws,
+                                hipStream_t s);
+hipError_t launch_mfma_split_nt(Shape shape, const Problem& p, int64_t k_split, float* ws,
+                                hipStream_t s);
+hipError_t launch_mfma_split_tt(Shape shape, const Problem& p, int64_t k_split, float* ws,
+                                hipStream_t s);
 // The whole split-K call: workspace from the library's stream-ordered pool,
 // the split tile kernel, the in-order reduction with the alpha/beta epilogue.
 hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStream_t s);

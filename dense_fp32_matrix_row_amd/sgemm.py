@@ -23,12 +23,14 @@ LIBRARY = os.path.join(HERE, "libsgemm.so")
 
 STATUS_UNKNOWN_LEVEL = -100
 STATUS_UNKNOWN_CONFIG = -101
+STATUS_BAD_OP_A = -102
+STATUS_BAD_OP_B = -103
 
 # Every exported symbol of include/sgemm.h.
 EXPORTS = (
     "hip_sgemm", "hip_sgemm_level", "hip_sgemm_num_levels", "hip_sgemm_level_name",
     "hip_sgemm_status_string", "hip_sgemm_auto_level", "hip_sgemm_launch_shape",
-    "hip_sgemm_tile_split", "hip_sgemm_num_tiles", "hip_sgemm_tile_name",
+    "hip_sgemm_tile_split", "hip_sgemm_num_tiles", "hip_sgemm_tile_name", "hip_sgemm_ex",
 )
 
 _lib = None
@@ -58,6 +60,8 @@ def load(path: Optional[str] = None):
     lib.hip_sgemm.argtypes = gemm_args
     lib.hip_sgemm_level.restype = i32
     lib.hip_sgemm_level.argtypes = [i32] + gemm_args
+    lib.hip_sgemm_ex.restype = i32
+    lib.hip_sgemm_ex.argtypes = [i32, i32] + gemm_args
     lib.hip_sgemm_tile_split.restype = i32
     lib.hip_sgemm_tile_split.argtypes = [i32, i32] + gemm_args
     lib.hip_sgemm_num_tiles.restype = i32
@@ -123,6 +127,21 @@ def hip_sgemm_level(level, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=
     return int(load().hip_sgemm_level(int(level), int(M), int(N), int(K), float(alpha), _addr(A),
                                       int(lda), _addr(B), int(ldb), float(beta), _addr(C),
                                       int(ldc), _stream(stream)))
+
+
+def _op(op) -> int:
+    if isinstance(op, str):
+        if len(op) != 1:
+            raise ValueError(f"op must be one character, got {op!r}")
+        return ord(op)
+    return int(op)
+
+
+def hip_sgemm_ex(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    """C <- alpha*op(A)@op(B) + beta*C; op_a / op_b are 'N' or 'T' (or 0 / 1)."""
+    return int(load().hip_sgemm_ex(_op(op_a), _op(op_b), int(M), int(N), int(K), float(alpha),
+                                   _addr(A), int(lda), _addr(B), int(ldb), float(beta), _addr(C),
+                                   int(ldc), _stream(stream)))
 
 
 def hip_sgemm_tile_split(tile, splits, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

@@ -59,6 +59,7 @@
  *                 arguments the same way (level is not counted).
  *   -100          unknown level
  *   -101          unknown tile shape or split count (hip_sgemm_tile_split)
+ *   -102, -103    op(A), op(B) not 'N' / 'T' (hip_sgemm_ex)
  *   > 0           the hipError_t the launch reported
  */
 #ifndef LIBSGEMM_SGEMM_H
@@ -72,6 +73,8 @@ extern "C" {
 
 #define SGEMM_STATUS_UNKNOWN_LEVEL (-100)
 #define SGEMM_STATUS_UNKNOWN_CONFIG (-101)
+#define SGEMM_STATUS_BAD_OP_A (-102)
+#define SGEMM_STATUS_BAD_OP_B (-103)
 
 /*
  * Best kernel for the shape: C <- alpha*A*B + beta*C.
@@ -84,6 +87,28 @@ int hip_sgemm(int M, int N, int K, float alpha,
               const float *B, int ldb,
               float beta, float *C, int ldc,
               hipStream_t stream);
+
+/*
+ * The full BLAS sgemm form: C <- alpha*op(A)*op(B) + beta*C with
+ * op(X) = X or X^T ([L04] section 5.2's op(A), op(B); row-major storage as
+ * everywhere in this library).
+ *   op_a  'N' (or 0): A is M x K, lda >= max(1, K);
+ *         'T' or 'C' (or 1): A is stored K x M and op(A) = A^T, lda >= max(1, M).
+ *   op_b  'N': B is K x N, ldb >= max(1, N);
+ *         'T' or 'C': B is stored N x K, op(B) = B^T, ldb >= max(1, K).
+ *   (lower case accepted; for real data the conjugate transpose is the
+ *   transpose.)  C is always M x N, ldc >= max(1, N), read only if beta != 0.
+ * Runs level 10's plans with the operands read in place (no transposed copy
+ * is made): the tile kernels stage either orientation into the same k-major
+ * LDS layout.  Returns hip_sgemm's status codes (argument numbers refer to
+ * hip_sgemm's positions: -6 lda, -8 ldb, ...), -102 / -103 for a bad op_a /
+ * op_b.
+ */
+int hip_sgemm_ex(int op_a, int op_b, int M, int N, int K, float alpha,
+                 const float *A, int lda,
+                 const float *B, int ldb,
+                 float beta, float *C, int ldc,
+                 hipStream_t stream);
 
 /*
  * Same operation with the rung of the optimisation ladder forced.  Every

@@ -175,3 +175,20 @@ def test_tile_split_arguments():
     # argument errors as hip_sgemm once the configuration is valid
     assert sgemm.hip_sgemm_tile_split(0, 2, 4, 4, 8, 1.0, FAKE, 7, FAKE, 4, 0.0, FAKE, 4, stream=0) == -6
     assert sgemm.hip_sgemm_tile_split(1, 2, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, stream=0) == 0
+
+
+@pytest.mark.parametrize("ops,args,status", [
+    (("X", "N"), (4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4), sgemm.STATUS_BAD_OP_A),
+    (("N", 2), (4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4), sgemm.STATUS_BAD_OP_B),
+    (("N", "N"), (4, 4, 8, 1.0, FAKE, 7, FAKE, 4, 0.0, FAKE, 4), -6),
+    (("T", "N"), (9, 4, 8, 1.0, FAKE, 8, FAKE, 4, 0.0, FAKE, 4), -6),   # A stored K x M: lda >= M
+    (("T", "N"), (9, 4, 8, 1.0, FAKE, 9, FAKE, 4, 0.0, None, 4), -10),  # lda = M is fine
+    (("N", "T"), (4, 9, 8, 1.0, FAKE, 8, FAKE, 7, 0.0, FAKE, 9), -8),   # B stored N x K: ldb >= K
+    (("n", "t"), (4, 9, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, None, 9), -10),  # ldb = K is fine
+    (("C", "c"), (-1, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4), -1),
+    ((1, 0), (0, 4, 4, 1.0, None, 1, None, 4, 0.0, None, 4), 0),         # M == 0: nothing to do
+])
+def test_ex_argument_checks(ops, args, status):
+    assert sgemm.hip_sgemm_ex(*ops, *args, stream=0) == status
+    if status < -100:
+        assert "op(" in sgemm.hip_sgemm_status_string(status)

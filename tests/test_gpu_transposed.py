@@ -1,0 +1,125 @@
+"""hip_sgemm_ex with op(A), op(B) in {N, T} through the C ABI: every level-10
+plan (thin rows / columns, whole-tile grid + fringe, ragged K, two-slice
+tiles, split K) in all four orientations against the CPU reference, with
+padded and misaligned storage and guard regions around C.
+
+The tile kernels stage either orientation into the same k-major LDS layout,
+and the thin kernels keep the same per-lane k order, so wherever the plan is
+the same for every orientation the transposed calls must reproduce the
+untransposed result bit for bit.  (With A stored transposed the
+few-columns kernel is not used -- its rows would be strided columns -- so
+shapes with N <= 16 or a right fringe take other kernels there.)
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from dense_fp32_matrix_row_amd import inputs, sgemm
+from oracle import oracle
+from tests import gpu_harness as gh
+
+pytestmark = pytest.mark.gpu
+
+BOUND = 1e-5
+OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    sgemm.load()
+
+
+def run_ex(op_a, op_b, A, B, C, alpha, beta, pads=(0, 0, 0), offs=(0, 0, 0)):
+    """A (M x K) and B (K x N) are the logical operands; they are stored as
+    given by op_a / op_b (transposed copies for 'T') with row padding."""
+    M, K = A.shape
+    N = B.shape[1]
+    sa = np.ascontiguousarray(A.T) if op_a == "T" else A
+    sb = np.ascontiguousarray(B.T) if op_b == "T" else B
+    lda = max(1, sa.shape[1]) + pads[0]
+    ldb = max(1, sb.shape[1]) + pads[1]
+    ldc = max(1, N) + pads[2]
+    case = gh.Case(M, N, K, alpha, beta, sa, sb, C, lda, ldb, ldc, *offs)
+    return gh.run(case, lambda *args: sgemm.hip_sgemm_ex(op_a, op_b, *args))
+
+
+# (M, N, K, plan, same plan in every orientation)
+SHAPES = [
+    (5, 3001, 777, "few rows", True),
+    (16, 1000, 333, "sixteen rows", True),
+    (1500, 7, 2003, "few columns (A^T: tiles)", False),
+    (2051, 2055, 300, "128x128 two-slice grid + fringe", False),
+    (4096 + 3, 4096 + 16, 40, "256x128 grid + fringe", False),
+    (2048, 2048, 100, "128x128 two-slice grid, K ragged", True),
+    (4096, 4096, 36, "256x128 grid, K ragged", True),
+    (1000, 1000, 300, "64x64 two-slice tiles, edges", True),
+    (1024, 1024, 4096, "split K, 128x128", True),
+    (300, 260, 5000, "split K, 64x64 edges", True),
+    (17, 33, 65, "odd", True),
+    (129, 65, 31, "odd", True),
+]
+
+
+@pytest.mark.parametrize("M,N,K,plan,same", SHAPES, ids=[f"{s[0]}x{s[1]}x{s[2]}" for s in SHAPES])
+def test_transposed_operands(M, N, K, plan, same):
+    print(f"[transposed] {M}x{N}x{K}: {plan}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 5100 + M + N + K)
+    ref = oracle.oracle_sgemm(A, B, C, 0.5, 3.0)
+    outs = {}
+    for op_a, op_b in OPS:
+        out, st = run_ex(op_a, op_b, A, B, C, 0.5, 3.0)
+        assert st == 0, (op_a, op_b, sgemm.hip_sgemm_status_string(st))
+        err = oracle.normalised_error(out, ref, C, 0.5, 3.0, strict=True)
+        assert err <= BOUND, (op_a, op_b, err)
+        outs[op_a + op_b] = out
+    if same:
+        for key in ("NT", "TN", "TT"):
+            assert np.array_equal(outs["NN"].view(np.uint32), outs[key].view(np.uint32)), key
+    else:
+        # B's orientation never changes the plan
+        assert np.array_equal(outs["NN"].view(np.uint32), outs["NT"].view(np.uint32))
+        assert np.array_equal(outs["TN"].view(np.uint32), outs["TT"].view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(131, 257, 515), (7, 1029, 301), (1029, 9, 301), (2051, 2053, 64)])
+def test_transposed_padded_misaligned(M, N, K):
+    """Row padding that breaks 16-byte alignment of rows and bases that are
+    only 4-byte aligned, beta = 0 with NaN in C (C must not be read)."""
+    print(f"[transposed alignment] {M}x{N}x{K}", flush=True)
+    A, B, _ = inputs.make_abc(M, N, K, 5200 + M)
+    nanC = np.full((M, N), np.nan, np.float32)
+    ref = oracle.oracle_sgemm(A, B, None, -1.5, 0.0)
+    for op_a, op_b in OPS:
+        out, st = run_ex(op_a, op_b, A, B, nanC, -1.5, 0.0, pads=(3, 5, 7), offs=(1, 2, 3))
+        assert st == 0 and np.all(np.isfinite(out)), (op_a, op_b)
+        assert oracle.normalised_error(out, ref, None, -1.5, 0.0, strict=True) <= BOUND, (op_a, op_b)
+
+
+@pytest.mark.parametrize("M,N,K", [(4097, 4097, 33), (520, 390, 3000), (3, 2000, 999)])
+def test_transposed_integer_exact(M, N, K):
+    """Integer entries: every orientation equals the reference bit for bit."""
+    print(f"[transposed integer] {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.integer_abc(M, N, K, seed=5300 + K)
+    ref = oracle.oracle_sgemm(A, B, C, 2.0, -1.0)
+    for op_a, op_b in OPS:
+        out, st = run_ex(op_a, op_b, A, B, C, 2.0, -1.0)
+        assert st == 0
+        assert np.array_equal(out.astype(np.float64), ref.ref), (op_a, op_b)
+
+
+def test_transposed_quick_returns():
+    """alpha = 0 and K = 0 give C = beta*C without reading A or B (NaN here)."""
+    M, N, K = 70, 90, 50
+    rng = np.random.default_rng(5400)
+    C = inputs.uniform_f32(rng, (M, N))
+    nanA = np.full((M, K), np.nan, np.float32)
+    nanB = np.full((K, N), np.nan, np.float32)
+    for op_a, op_b in OPS:
+        out, st = run_ex(op_a, op_b, nanA, nanB, C, 0.0, 3.0)
+        assert st == 0 and np.array_equal(out, np.float32(3.0) * C)
