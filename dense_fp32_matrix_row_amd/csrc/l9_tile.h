@@ -22,6 +22,8 @@
 // row-major B arrive 4 consecutive m / n per load and are copied as is.
 #pragma once
 
+#include <type_traits>
+
 #include "sgemm_internal.h"
 
 namespace sgemm {
@@ -42,9 +44,11 @@ constexpr int kPad = 4;      // LDS row padding (words)
 // slices' sums meet in LDS after the K loop, added in slice order).  More
 // slices put more wavefronts on each SIMD for the same tile, which hides the
 // dependent-MFMA and LDS latencies of a tile grid too small to fill the GPU
-// otherwise, without a second kernel or workspace.
+// otherwise, without a second kernel or workspace.  DEPTH 2 issues each
+// stage's global loads two K steps ahead (for tiles whose K step is shorter
+// than the memory latency).
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int UNROLL_ = BK_ / 2,
-          int GROUP_M_ = 8, bool PRIO_ = false, int KSLICE_ = 1>
+          int GROUP_M_ = 8, bool PRIO_ = false, int KSLICE_ = 1, int DEPTH_ = 1>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -53,6 +57,10 @@ struct MfmaTile {
   static constexpr int UNROLL = UNROLL_;
   static constexpr int GROUP_M = GROUP_M_;
   static constexpr bool PRIO = PRIO_;
+  // Prefetch depth: global loads of a stage are issued DEPTH K steps before
+  // it is computed (2 = two register sets alternating).
+  static constexpr int DEPTH = DEPTH_;
+  static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
 };
 
 template <int N>
@@ -105,7 +113,7 @@ struct Panel {
   static constexpr int ITERS = (E * BK / 4) / THREADS;
   static_assert(ITERS >= 1 && ITERS * THREADS * 4 == E * BK, "panel not evenly staged");
   const float* ptr[ITERS];
-  float4 reg[ITERS];
+  float4 reg[2][ITERS];  // set 1 only with prefetch depth 2
 
   // group index of (thread, s) -> (e, k) inside the panel
   __device__ static int e_of(int idx) { return KCONTIG ? idx / (BK / 4) : 4 * (idx % (E / 4)); }
@@ -120,26 +128,29 @@ struct Panel {
     }
   }
   // whole K step, whole tile
+  template <int W>
   __device__ void load_whole(int64_t k0, int64_t ld) {
 #pragma unroll
-    for (int s = 0; s < ITERS; ++s) reg[s] = ld_global4(ptr[s] + (KCONTIG ? k0 : k0 * ld));
+    for (int s = 0; s < ITERS; ++s) reg[W][s] = ld_global4(ptr[s] + (KCONTIG ? k0 : k0 * ld));
   }
   // last K step of a whole tile: k at or beyond K reads as zero
+  template <int W>
   __device__ void load_ragged_k(int64_t k0, int64_t K, int64_t ld, int tid) {
 #pragma unroll
     for (int s = 0; s < ITERS; ++s) {
       const int64_t k = k0 + k_of(tid + s * THREADS);
       if (KCONTIG) {
         const float* q = ptr[s] + k0;
-        reg[s] = make_float4(k < K ? q[0] : 0.0f, k + 1 < K ? q[1] : 0.0f,
-                             k + 2 < K ? q[2] : 0.0f, k + 3 < K ? q[3] : 0.0f);
+        reg[W][s] = make_float4(k < K ? q[0] : 0.0f, k + 1 < K ? q[1] : 0.0f,
+                                k + 2 < K ? q[2] : 0.0f, k + 3 < K ? q[3] : 0.0f);
       } else {
-        reg[s] = k < K ? ld_global4(ptr[s] + k0 * ld) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        reg[W][s] = k < K ? ld_global4(ptr[s] + k0 * ld) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       }
     }
   }
   // any K step of any tile: e0 is the tile's first row/column, ext the
   // matrix's extent in e (M or N)
+  template <int W>
   __device__ void load_edge(int64_t k0, int64_t K, int64_t ld, int64_t e0, int64_t ext,
                             int tid) {
 #pragma unroll
@@ -147,24 +158,24 @@ struct Panel {
       const int idx = tid + s * THREADS;
       const int64_t e = e0 + e_of(idx), k = k0 + k_of(idx);
       if (KCONTIG)
-        reg[s] = load4(ptr[s] - k_of(idx), k, K, e < ext);
+        reg[W][s] = load4(ptr[s] - k_of(idx), k, K, e < ext);
       else
-        reg[s] = load4(ptr[s] + k0 * ld - e, e, ext, k < K);
+        reg[W][s] = load4(ptr[s] + k0 * ld - e, e, ext, k < K);
     }
   }
-  template <int LDX>
+  template <int W, int LDX>
   __device__ void store(float (*X)[LDX], int tid) const {
 #pragma unroll
     for (int s = 0; s < ITERS; ++s) {
       const int idx = tid + s * THREADS;
       const int e = e_of(idx), k = k_of(idx);
       if (KCONTIG) {
-        X[k + 0][e] = reg[s].x;
-        X[k + 1][e] = reg[s].y;
-        X[k + 2][e] = reg[s].z;
-        X[k + 3][e] = reg[s].w;
+        X[k + 0][e] = reg[W][s].x;
+        X[k + 1][e] = reg[W][s].y;
+        X[k + 2][e] = reg[W][s].z;
+        X[k + 3][e] = reg[W][s].w;
       } else {
-        *reinterpret_cast<float4*>(&X[k][e]) = reg[s];
+        *reinterpret_cast<float4*>(&X[k][e]) = reg[W][s];
       }
     }
   }
@@ -196,9 +207,14 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
   typedef typename VecT<BLK_M>::type AFrag;
   typedef typename VecT<BLK_N>::type BFrag;
 
-  __shared__ __align__(16) float As[2][BK][LDA];
-  __shared__ __align__(16) float Bs[2][BK][LDB];
-  __shared__ __align__(16) float red[T::KSLICE > 1 ? (T::KSLICE - 1) * WAVE_TILES * PER_WAVE : 1];
+  // LDS: the two stages of A and B; with K slices, the slices' sums meet in
+  // the same memory once the K loop is over (the stages are free then).
+  constexpr int STAGE_FLOATS = 2 * BK * LDA + 2 * BK * LDB;
+  constexpr int RED_FLOATS = (T::KSLICE - 1) * WAVE_TILES * PER_WAVE;
+  __shared__ __align__(16) float smem[STAGE_FLOATS > RED_FLOATS ? STAGE_FLOATS : RED_FLOATS];
+  float (*const As)[BK][LDA] = reinterpret_cast<float (*)[BK][LDA]>(smem);
+  float (*const Bs)[BK][LDB] = reinterpret_cast<float (*)[BK][LDB]>(smem + 2 * BK * LDA);
+  float* const red = smem;
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
@@ -239,37 +255,36 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
     Panel<BN, BK, THREADS, TB> pb;
     pa.init(p.A, p.lda, row0, k_lo, tid);
     pb.init(p.B, p.ldb, col0, k_lo, tid);
-    auto load = [&](int64_t k0) {
+    // load<W>: stage at k0 into register set W; store<W>: set W into LDS
+    // stage buffer W' (W' = W with depth 2, the alternating buffer with 1).
+    typedef std::integral_constant<int, 0> Set0;
+    typedef std::integral_constant<int, 1> Set1;
+    auto load = [&](auto set, int64_t k0) {
+      constexpr int W = decltype(set)::value;
       if (MODE == kWhole || (interior && k0 + BK <= K)) {
         // whole K step inside the matrix: no bounds tests (uniform branch)
-        pa.load_whole(k0, p.lda);
-        pb.load_whole(k0, p.ldb);
+        pa.template load_whole<W>(k0, p.lda);
+        pb.template load_whole<W>(k0, p.ldb);
       } else if (MODE == kRaggedK) {
-        pa.load_ragged_k(k0, K, p.lda, tid);
-        pb.load_ragged_k(k0, K, p.ldb, tid);
+        pa.template load_ragged_k<W>(k0, K, p.lda, tid);
+        pb.template load_ragged_k<W>(k0, K, p.ldb, tid);
       } else {
-        pa.load_edge(k0, K, p.lda, row0, p.M, tid);
-        pb.load_edge(k0, K, p.ldb, col0, p.N, tid);
+        pa.template load_edge<W>(k0, K, p.lda, row0, p.M, tid);
+        pb.template load_edge<W>(k0, K, p.ldb, col0, p.N, tid);
       }
     };
-    auto store = [&](int buf) {
-      pa.store(As[buf], tid);
-      pb.store(Bs[buf], tid);
+    auto store = [&](auto set, int buf) {
+      constexpr int W = decltype(set)::value;
+      pa.template store<W>(As[buf], tid);
+      pb.template store<W>(Bs[buf], tid);
     };
-
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      const int cur = static_cast<int>(kt & 1);
-      const bool more = kt + 1 < nk;
-      if (more) load((kt + 1) * BK);
-      // PRIO: two blocks share each CU's matrix pipes and a block is only as
-      // fast as its slowest wavefront at the barrier, so a wavefront takes
-      // priority 1 while it issues MFMAs and 3 while it stores the next stage
-      // and waits at the barrier (the stragglers reach the barrier sooner),
-      // then drops to 0.  Measured on MI355X: +3 % at 4096^3 with 256 x 128
-      // tiles; it slows the small-tile shapes, which leave it off.
+    // The MFMA steps of one stage.  PRIO: two blocks share each CU's matrix
+    // pipes and a block is only as fast as its slowest wavefront at the
+    // barrier, so a wavefront takes priority 1 while it issues MFMAs (and 3
+    // while it stores the next stage and waits at the barrier, below: the
+    // stragglers reach the barrier sooner), then drops to 0.  Measured on
+    // MI355X: +3 % at 4096^3 with 256 x 128 tiles.
+    auto mfma_stage = [&](int cur) {
       if (T::PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll T::UNROLL
       for (int s = 0; s < STEPS; ++s) {
@@ -284,16 +299,50 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
                 vget<BLK_M>(af, bi), vget<BLK_N>(bf, bj), acc[bi][bj], 0, 0, 0);
       }
       if (T::PRIO) __builtin_amdgcn_s_setprio(3);
-      if (more) store(cur ^ 1);
+    };
+    auto barrier = [&]() {
       __syncthreads();
       if (T::PRIO) __builtin_amdgcn_s_setprio(0);
+    };
+
+    if (T::DEPTH == 1) {
+      load(Set0(), 0);
+      store(Set0(), 0);
+      __syncthreads();
+      for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = static_cast<int>(kt & 1);
+        const bool more = kt + 1 < nk;
+        if (more) load(Set0(), (kt + 1) * BK);
+        mfma_stage(cur);
+        if (more) store(Set0(), cur ^ 1);
+        barrier();
+      }
+    } else {
+      // Stage j lives in register set j % 2 and LDS buffer j % 2; its loads
+      // are issued at the start of step j - 2 and stored at the end of step
+      // j - 1, after the buffer's previous stage (j - 2) has been read.
+      load(Set0(), 0);
+      store(Set0(), 0);
+      if (nk > 1) load(Set1(), BK);
+      __syncthreads();
+      for (int64_t kt = 0; kt < nk; kt += 2) {
+        if (kt + 2 < nk) load(Set0(), (kt + 2) * BK);
+        mfma_stage(0);
+        if (kt + 1 < nk) store(Set1(), 1);
+        barrier();
+        if (kt + 1 >= nk) break;
+        if (kt + 3 < nk) load(Set1(), (kt + 3) * BK);
+        mfma_stage(1);
+        if (kt + 2 < nk) store(Set0(), 0);
+        barrier();
+      }
     }
 
     if (T::KSLICE > 1) {
-      // Slices 1.. hand their sums to slice 0 (lane-contiguous, conflict
-      // free); slice 0 adds them in slice order and runs the epilogue.  The
-      // next tile's reduction writes red only after that tile's K loop,
-      // whose barriers slice 0 reaches after finishing this epilogue.
+      // Slices 1.. hand their sums to slice 0 through LDS (lane-contiguous,
+      // conflict free; the K loop's last barrier has freed the stages that
+      // red overlays); slice 0 adds them in slice order and runs the
+      // epilogue.  The second barrier frees red before the next tile stages.
       if (kslice > 0) {
         float* dst = red + ((kslice - 1) * WAVE_TILES + wv) * PER_WAVE + lane;
 #pragma unroll
@@ -304,17 +353,20 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
             for (int r = 0; r < 16; ++r) dst[((bi * BLK_N + bj) * 16 + r) * 64] = acc[bi][bj][r];
       }
       __syncthreads();
-      if (kslice > 0) continue;
+      if (kslice == 0) {
 #pragma unroll
-      for (int ks = 1; ks < T::KSLICE; ++ks) {
-        const float* src = red + ((ks - 1) * WAVE_TILES + wv) * PER_WAVE + lane;
+        for (int ks = 1; ks < T::KSLICE; ++ks) {
+          const float* src = red + ((ks - 1) * WAVE_TILES + wv) * PER_WAVE + lane;
 #pragma unroll
-        for (int bi = 0; bi < BLK_M; ++bi)
+          for (int bi = 0; bi < BLK_M; ++bi)
 #pragma unroll
-          for (int bj = 0; bj < BLK_N; ++bj)
+            for (int bj = 0; bj < BLK_N; ++bj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[bi][bj][r] += src[((bi * BLK_N + bj) * 16 + r) * 64];
+              for (int r = 0; r < 16; ++r) acc[bi][bj][r] += src[((bi * BLK_N + bj) * 16 + r) * 64];
+        }
       }
+      __syncthreads();
+      if (kslice > 0) continue;
     }
 
     // Epilogue: register r of block (bi, bj) is C[row(bi, r)][col(bj)]; a
@@ -448,9 +500,12 @@ typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;
 // Two K slices per stage (8 wavefronts): for tile grids of about one block
 // per CU, where a single wavefront per SIMD leaves MFMA and LDS latency
 // exposed.  Measured on MI355X: 64 x 64 at 1024^3 +18 %, at 3072^3 +10 %;
-// 128 x 128 (2 x 2 wave tiles of 64 x 64) at 2048^3 +5 %.
+// 128 x 128 (2 x 2 wave tiles of 64 x 64) at 2048^3 +5 %.  The 64 x 64 tile
+// also prefetches two K steps ahead with raised priority around the barrier
+// (its 32-deep K step is shorter than a global load's latency): +3-4 % at
+// 768^3-3072^3; the 128 x 128 one loses 4 % with it and keeps one step.
 typedef MfmaTile<128, 128, 32, 2, 2, 16, 8, false, 2> TileLargeSliced;
-typedef MfmaTile<64, 64, 32, 2, 2, 16, 8, false, 2> TileSmallSliced;
+typedef MfmaTile<64, 64, 32, 2, 2, 16, 8, true, 2, 2> TileSmallSliced;
 constexpr int kCUs = 256;
 
 // Launch a tile shape on a problem (MODE chosen from the problem's shape).
