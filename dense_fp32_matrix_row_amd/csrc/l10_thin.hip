@@ -52,7 +52,9 @@ __global__ __launch_bounds__(FewRows<RP>::THREADS) void k_few_rows(Problem p,
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int q = lane % 4, g = lane / 4;
 
-  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+  // neighbouring column blocks read the two halves of the same 128-byte B
+  // lines: keep them on one XCD (one L2)
+  for (int64_t blk = xcd_contiguous(blockIdx.x, gridDim.x); blk < nblocks; blk += gridDim.x) {
     const int64_t c0 = blk * 16;
     const int64_t col = c0 + 4 * q;
     float acc[RP][4];
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kColThreads) void k_few_cols(Problem p, int64_t nbl
   __shared__ __align__(16) float Bs[WP][KC];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
 
-  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+  for (int64_t blk = xcd_contiguous(blockIdx.x, gridDim.x); blk < nblocks; blk += gridDim.x) {
     const int64_t row = blk * kRowsPerBlock + wave;
     const bool has_row = row < p.M;
     const float* arow = p.A + (has_row ? row : 0) * p.lda;

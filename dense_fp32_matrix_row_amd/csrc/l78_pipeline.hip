@@ -94,14 +94,6 @@ struct MapWaveTiled {
   __device__ int n_off(int h) const { return n_base + 32 * h; }
 };
 
-// Logical tile id of block `bid` among `nblocks`: XCD x (= bid % 8) gets the
-// x-th contiguous range of ids.
-__device__ __forceinline__ int64_t xcd_contiguous(int64_t bid, int64_t nblocks) {
-  const int64_t q = nblocks / 8, r = nblocks % 8;
-  const int64_t x = bid % 8, local = bid / 8;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
-}
-
 template <bool SWIZZLE, class Map>
 __device__ __forceinline__ void pipeline_tiles(const Problem& p,
                                                int64_t tiles_m,

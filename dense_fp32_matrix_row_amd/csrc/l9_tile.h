@@ -85,12 +85,6 @@ __device__ __forceinline__ float vget<4>(const float4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-__device__ __forceinline__ int64_t xcd_contiguous(int64_t bid, int64_t nblocks) {
-  const int64_t q = nblocks / 8, r = nblocks % 8;
-  const int64_t x = bid % 8, local = bid / 8;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
-}
-
 // MODE kWhole: the host guarantees M % BM == N % BN == K % BK == 0, so every
 // tile and K step is whole and the kernel carries no bounds logic (fewer
 // registers and instructions).  kRaggedK: whole M and N tiles, K not a

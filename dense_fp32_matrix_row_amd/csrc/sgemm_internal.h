@@ -68,6 +68,16 @@ inline Geometry make_geometry(int M, int N, int K, int tile_m, int tile_n,
   return g;
 }
 
+// MI355X dispatches consecutive workgroup ids round-robin to its 8 XCDs,
+// each with its own L2.  This maps block `bid` of `nblocks` to a logical id
+// such that XCD x (= bid % 8) gets the x-th contiguous range of ids, so that
+// neighbouring tiles (which share operand panels) share one L2.
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t bid, int64_t nblocks) {
+  const int64_t q = nblocks / 8, r = nblocks % 8;
+  const int64_t x = bid % 8, local = bid / 8;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
 // The epilogue of every level: alpha*acc + beta*c, with C read only when
 // beta != 0 (BLAS convention; the page kernels read C unconditionally).
 __device__ __forceinline__ float epilogue(float acc, float alpha, float beta,
