@@ -7,9 +7,13 @@
 // registers before the FMAs of step k, and stored into the other buffer
 // after them, so the HBM/L2 latency overlaps the arithmetic and one barrier
 // per step suffices: a buffer is rewritten only after the barrier that ends
-// every wavefront's reads of it.  BK = 16; A is staged transposed with rows
-// padded to 132 words (the four k-groups of the 16 rows one wavefront stages
-// then land in distinct banks).
+// every wavefront's reads of it.  BK = 8 and the k loop unrolled by 4 keep
+// the kernel at 118 VGPRs, four wavefronts per SIMD like level 6 (BK = 16
+// needed 140, three per SIMD, and ran 3.5 % slower at 4096^3).  On MI355X the
+// double buffer gains little over level 6: four resident blocks per CU
+// already overlap one block's loads with the others' FMAs, which is what the
+// double buffer buys a single block.  A is staged transposed with rows padded
+// to 132 words.
 //
 // Level 8 follows [GEMM2]'s warp-tiling section ("三级分块：block → warp →
 // thread") on wave64: the 128 x 128 block tile is split 2 x 2 into 64 x 64
@@ -31,11 +35,11 @@
 namespace sgemm {
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 16, kTM = 8, kTN = 8;
+constexpr int kBM = 128, kBN = 128, kBK = 8, kTM = 8, kTN = 8;
 constexpr int kThreads = 256;
 constexpr int kLdaT = kBM + 4;  // transposed-A row stride in LDS (words)
 constexpr int kGroupM = 8;      // tile-rows per group in the level-8 order
-constexpr int kStageIters = (kBM * kBK / 4) / kThreads;  // 2 float4 of A
+constexpr int kStageIters = (kBM * kBK / 4) / kThreads;  // 1 float4 of A and of B
 
 struct Staged {
   float4 a[kStageIters];
@@ -135,9 +139,8 @@ __device__ __forceinline__ void pipeline_tiles(const Problem& p,
       const int cur = static_cast<int>(kt & 1);
       const bool more = kt + 1 < nk;
       if (more) load_stage(st, p, row0, col0, (kt + 1) * kBK, tid);
-      // Unrolled by 4, not 16: fully unrolled, the compiler hoists all 16 k-steps
-      // of fragment reads (~256 registers, one wavefront per SIMD, nothing to
-      // hide the barrier); by 4 it needs ~140 (three wavefronts per SIMD).
+      // Unrolled by 4: fully unrolled, the compiler hoists every k-step's
+      // fragment reads above the loop (233 VGPRs, two wavefronts per SIMD).
 #pragma unroll 4
       for (int k = 0; k < kBK; ++k) {
         const float4 m0 = *reinterpret_cast<const float4*>(&As[cur][k][map.m_off(0)]);

@@ -136,13 +136,15 @@ def test_launch_shapes():
 
 def test_phase_count_rounds_up_like_the_lecture_example():
     """Lecture 4 notes, section 8 exercise 6: K = 100 with 16-wide phases needs
-    ceil(100/16) = 7 phases (the floor form would drop 4 terms).  Levels 7-9
-    stage BK = 16 and must walk exactly that many K steps."""
+    ceil(100/16) = 7 phases (the floor form would drop 4 terms).  Level 9
+    stages BK = 16 and must walk exactly that many K steps; levels 7 and 8
+    stage BK = 8 and round up the same way."""
     from tests.oracle_pins import golden
     g = golden()["phase_count"]
-    for level in (7, 8, 9):
-        shape = sgemm.hip_sgemm_launch_shape(level, 64, 64, g["K"])
-        assert shape["k_steps"] == g["phases"]
+    shape = sgemm.hip_sgemm_launch_shape(9, 64, 64, g["K"])
+    assert shape["k_steps"] == g["phases"]
+    for level in (7, 8):
+        assert sgemm.hip_sgemm_launch_shape(level, 64, 64, g["K"])["k_steps"] == -(-g["K"] // 8)
     assert sgemm.hip_sgemm_launch_shape(2, 64, 64, g["K"])["k_steps"] == -(-g["K"] // 32)
 
 
