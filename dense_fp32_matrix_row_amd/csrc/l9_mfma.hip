@@ -1,6 +1,7 @@
 // l9_mfma.hip -- level 9: the level-8 pipeline with the FMA core moved onto
-// the FP32 matrix cores (v_mfma_f32_32x32x2_f32: a 32 x 32 x 2 product, full
-// float32 inputs and accumulators, 2048 FMAs per instruction per wavefront).
+// the FP32 matrix cores (v_mfma_f32_32x32x2_f32 and v_mfma_f32_16x16x4_f32:
+// 32 x 32 x 2 and 16 x 16 x 4 products, full float32 inputs and
+// accumulators, 2048 / 1024 FMAs per instruction per wavefront).
 //
 // None of the pages programs matrix instructions for FP32 ([L04] section 5.5
 // only names them as what libraries add on top of tiling); GEMM is a dense
@@ -101,7 +102,7 @@ hipError_t launch9(const Problem& p, hipStream_t s) { return launch_mfma(pick_sh
 }  // namespace
 
 const LevelDesc* level9() {
-  static const LevelDesc d = {"L9_mfma_f32_32x32x2", geometry9, launch9};
+  static const LevelDesc d = {"L9_mfma_f32", geometry9, launch9};
   return &d;
 }
 

@@ -4,17 +4,19 @@
 //
 // Block tile BM x BN with BK-deep K steps and WAVES_M x WAVES_N wavefronts
 // (times KSLICE K slices), each owning a WTM x WTN wave tile made of
-// BLK_M x BLK_N 32 x 32 MFMA blocks of v_mfma_f32_32x32x2_f32 (full float32
-// inputs and accumulators, 2048 FMAs per instruction per wavefront).
+// BLK_M x BLK_N MFMA blocks, 32 x 32 (v_mfma_f32_32x32x2_f32, 2048 FMAs) or
+// 16 x 16 (v_mfma_f32_16x16x4_f32, 1024 FMAs); full float32 inputs and
+// accumulators either way.
 //
-// Operand layout of the 32x32x2 instruction (one block): lane l supplies
-// A[l % 32][l / 32] and B[l / 32][l % 32]; accumulator register r of lane l
-// holds C[8*(r/4) + 4*(l/32) + r%4][l % 32].  Rows and columns of the wave tile
+// Operand layout (MfmaOp below): lane l supplies A[l % DIM][l / DIM] and
+// B[l / DIM][l % DIM]; for 32 x 32 accumulator register r of lane l holds
+// C[8*(r/4) + 4*(l/32) + r%4][l % 32], for 16 x 16 C[4*(l/16) + r][l % 16].
+// Rows and columns of the wave tile
 // are interleaved over the blocks: MFMA row i of block bi is wave-tile row
 // BLK_M*i + bi (columns likewise), so the BLK_M A values a lane needs for one
 // k are adjacent in the k-major LDS tile (one 64-bit read for BLK_M = 2),
 // and a lane's BLK_N outputs of one row are adjacent in C (one 64-bit store).
-// MFMA step s of a K-phase consumes k = 2s + l/32.
+// MFMA step s of a K-phase consumes k = KPER*s + l/DIM (KPER = 2 or 4).
 //
 // LDS holds both operands k-major: As[k][m], Bs[k][n].  A row-major A (and a
 // transposed B, stored N x K) arrive 4 consecutive k per 128-bit load and
@@ -30,6 +32,32 @@ namespace sgemm {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// The two FP32 matrix instructions, one 32 x 32 or 16 x 16 block each (the
+// same 64 FLOP per SIMD per cycle): lane l supplies A[l % DIM][l / DIM] and
+// B[l / DIM][l % DIM] (KPER = 64 / DIM k values per instruction), and its
+// accumulator register r holds C[row(l / DIM, r)][l % DIM].
+template <int MS>
+struct MfmaOp;
+template <>
+struct MfmaOp<32> {  // v_mfma_f32_32x32x2_f32: 16 passes
+  static constexpr int DIM = 32, KPER = 2, REGS = 16;
+  typedef floatx16 acc_t;
+  __device__ static acc_t mma(float a, float b, const acc_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __host__ __device__ static constexpr int row(int g, int r) { return 8 * (r / 4) + 4 * g + r % 4; }
+};
+template <>
+struct MfmaOp<16> {  // v_mfma_f32_16x16x4_f32: 8 passes
+  static constexpr int DIM = 16, KPER = 4, REGS = 4;
+  typedef floatx4 acc_t;
+  __device__ static acc_t mma(float a, float b, const acc_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __host__ __device__ static constexpr int row(int g, int r) { return 4 * g + r; }
+};
 
 constexpr int kPad = 4;      // LDS row padding (words)
 
@@ -48,7 +76,7 @@ constexpr int kPad = 4;      // LDS row padding (words)
 // stage's global loads two K steps ahead (for tiles whose K step is shorter
 // than the memory latency).
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int UNROLL_ = BK_ / 2,
-          int GROUP_M_ = 8, bool PRIO_ = false, int KSLICE_ = 1, int DEPTH_ = 1>
+          int GROUP_M_ = 8, bool PRIO_ = false, int KSLICE_ = 1, int DEPTH_ = 1, int MS_ = 32>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -61,6 +89,8 @@ struct MfmaTile {
   // it is computed (2 = two register sets alternating).
   static constexpr int DEPTH = DEPTH_;
   static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
+  // Matrix instruction: 32 x 32 x 2 or 16 x 16 x 4 blocks.
+  static constexpr int MS = MS_;
 };
 
 template <int N>
@@ -190,14 +220,16 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
                                                        float* __restrict__ ws) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK, THREADS = T::THREADS;
   constexpr int WTM = BM / T::WAVES_M, WTN = BN / T::WAVES_N;
-  constexpr int BLK_M = WTM / 32, BLK_N = WTN / 32;
+  typedef MfmaOp<T::MS> Op;
+  constexpr int DIM = Op::DIM, KPER = Op::KPER, REGS = Op::REGS;
+  constexpr int BLK_M = WTM / DIM, BLK_N = WTN / DIM;
   constexpr int LDA = BM + kPad, LDB = BN + kPad;
-  static_assert(BLK_M * 32 == WTM && BLK_N * 32 == WTN, "wave tile not whole blocks");
-  static_assert(BK % 2 == 0, "MFMA steps consume k in pairs");
-  static_assert((BK / 2) % T::KSLICE == 0, "K slices must split a stage's MFMA steps evenly");
+  static_assert(BLK_M * DIM == WTM && BLK_N * DIM == WTN, "wave tile not whole blocks");
+  static_assert(BK % KPER == 0, "a stage is whole MFMA steps");
+  static_assert((BK / KPER) % T::KSLICE == 0, "K slices must split a stage's MFMA steps evenly");
   constexpr int WAVE_TILES = T::WAVES_M * T::WAVES_N;
-  constexpr int STEPS = BK / 2 / T::KSLICE;           // MFMA steps per stage per wavefront
-  constexpr int PER_WAVE = BLK_M * BLK_N * 16 * 64;   // accumulator floats per wavefront
+  constexpr int STEPS = BK / KPER / T::KSLICE;         // MFMA steps per stage per wavefront
+  constexpr int PER_WAVE = BLK_M * BLK_N * REGS * 64;  // accumulator floats per wavefront
   typedef typename VecT<BLK_M>::type AFrag;
   typedef typename VecT<BLK_N>::type BFrag;
 
@@ -214,7 +246,7 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
   const int wave = tid / 64, lane = tid % 64;
   const int kslice = wave / WAVE_TILES, wv = wave % WAVE_TILES;
   const int wm = wv / T::WAVES_N, wn = wv % T::WAVES_N;
-  const int lrow = lane % 32, khalf = lane / 32;
+  const int lrow = lane % DIM, kg = lane / DIM;  // block row/column, k within a step
   // LDS offsets (words) of this lane's fragments inside one k-row
   const int a_off = wm * WTM + BLK_M * lrow;
   const int b_off = wn * WTN + BLK_N * lrow;
@@ -234,13 +266,13 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
     const int64_t row0 = (first_m + in % gm) * BM;
     const int64_t col0 = (in / gm) * BN;
 
-    floatx16 acc[BLK_M][BLK_N];
+    typename Op::acc_t acc[BLK_M][BLK_N];
 #pragma unroll
     for (int bi = 0; bi < BLK_M; ++bi)
 #pragma unroll
       for (int bj = 0; bj < BLK_N; ++bj)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
+        for (int r = 0; r < REGS; ++r) acc[bi][bj][r] = 0.0f;
 
     // This thread's share of the A and B panels of each K step (rows of A
     // beyond M, columns of B beyond N and k beyond K read as zero).
@@ -282,15 +314,14 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
       if (T::PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll T::UNROLL
       for (int s = 0; s < STEPS; ++s) {
-        const int kk = 2 * (kslice * STEPS + s) + khalf;
+        const int kk = KPER * (kslice * STEPS + s) + kg;
         const AFrag af = *reinterpret_cast<const AFrag*>(&As[cur][kk][a_off]);
         const BFrag bf = *reinterpret_cast<const BFrag*>(&Bs[cur][kk][b_off]);
 #pragma unroll
         for (int bi = 0; bi < BLK_M; ++bi)
 #pragma unroll
           for (int bj = 0; bj < BLK_N; ++bj)
-            acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                vget<BLK_M>(af, bi), vget<BLK_N>(bf, bj), acc[bi][bj], 0, 0, 0);
+            acc[bi][bj] = Op::mma(vget<BLK_M>(af, bi), vget<BLK_N>(bf, bj), acc[bi][bj]);
       }
       if (T::PRIO) __builtin_amdgcn_s_setprio(3);
     };
@@ -344,7 +375,7 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
 #pragma unroll
           for (int bj = 0; bj < BLK_N; ++bj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dst[((bi * BLK_N + bj) * 16 + r) * 64] = acc[bi][bj][r];
+            for (int r = 0; r < REGS; ++r) dst[((bi * BLK_N + bj) * REGS + r) * 64] = acc[bi][bj][r];
       }
       __syncthreads();
       if (kslice == 0) {
@@ -356,7 +387,7 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
 #pragma unroll
             for (int bj = 0; bj < BLK_N; ++bj)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) acc[bi][bj][r] += src[((bi * BLK_N + bj) * 16 + r) * 64];
+              for (int r = 0; r < REGS; ++r) acc[bi][bj][r] += src[((bi * BLK_N + bj) * REGS + r) * 64];
         }
       }
       __syncthreads();
@@ -374,11 +405,11 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
       float* const plane = ws + split * int64_t(p.M) * p.N;
 #pragma unroll
       for (int bi = 0; bi < BLK_M; ++bi) {
-        const int64_t row_base = row0 + wm * WTM + BLK_M * 4 * khalf + bi;
+        const int64_t row_base = row0 + wm * WTM + BLK_M * Op::row(kg, 0) + bi;
         float* const w_base = plane + row_base * p.N + col;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int dr = BLK_M * (8 * (r / 4) + (r % 4));
+        for (int r = 0; r < REGS; ++r) {
+          const int dr = BLK_M * (Op::row(kg, r) - Op::row(kg, 0));
           if (!interior && row_base + dr >= p.M) continue;
           float* w = w_base + dr * p.N;
           float o[BLK_N];
@@ -397,11 +428,11 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
     }
 #pragma unroll
     for (int bi = 0; bi < BLK_M; ++bi) {
-      const int64_t row_base = row0 + wm * WTM + BLK_M * 4 * khalf + bi;
+      const int64_t row_base = row0 + wm * WTM + BLK_M * Op::row(kg, 0) + bi;
       float* const c_base = p.C + row_base * p.ldc + col;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dr = BLK_M * (8 * (r / 4) + (r % 4));
+      for (int r = 0; r < REGS; ++r) {
+        const int dr = BLK_M * (Op::row(kg, r) - Op::row(kg, 0));
         if (!interior && row_base + dr >= p.M) continue;
         float* c = c_base + dr * p.ldc;
         if (interior || vec_ok) {
@@ -487,7 +518,12 @@ hipError_t launch_split(const Problem& p, int64_t k_split, float* ws, hipStream_
 // 32-deep K steps; large ragged problems (4097^3 leaves a one-row /
 // one-column fringe of tiles) take 128 x 64, whose many small blocks soak up
 // the fringe; small problems take 64 x 64 so that more CUs get work.
-typedef MfmaTile<256, 128, 16, 4, 2, 8, 8, true> TileHuge;
+// The big tile runs 16 x 16 x 4 blocks: each wavefront's 64 x 64 wave tile is
+// 4 x 4 blocks, 16 independent accumulator chains of 8-pass instructions
+// (against 4 chains of 16-pass ones with 32 x 32 blocks); measured on
+// MI355X: 138.2 against 136.6 TFLOP/s at 4096^3, 131.8 against 128.2 at
+// 4097^3.  (The 16 x 16 form of the other tiles measured equal or slower.)
+typedef MfmaTile<256, 128, 16, 4, 2, 4, 8, true, 1, 1, 16> TileHuge;
 typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true> TileLarge;
 typedef MfmaTile<128, 64, 16, 2, 2> TileMid;
 typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;

@@ -130,7 +130,8 @@ int hip_sgemm_ex(int op_a, int op_b, int M, int N, int K, float alpha,
  *     double_buffer_gemm)
  *   8 wave tiling (block -> wave -> lane) with an XCD-aware, grouped
  *     block-to-tile order ([GEMM2] warp tiling and thread swizzling sections)
- *   9 FP32 matrix cores (v_mfma_f32_32x32x2_f32) on the level-8 pipeline
+ *   9 FP32 matrix cores (v_mfma_f32_32x32x2_f32 and v_mfma_f32_16x16x4_f32)
+ *     on the level-8 pipeline
  *  10 shape-aware dispatch, the level hip_sgemm runs: level 9's tiles over
  *     the largest whole-tile part of a problem whose M and N miss a tile
  *     multiple by at most 16, with vector-ALU kernels on the thin fringe;
@@ -181,7 +182,7 @@ const char *hip_sgemm_tile_name(int tile);
 /* Number of levels (valid levels are 0 .. hip_sgemm_num_levels()-1). */
 int hip_sgemm_num_levels(void);
 
-/* Short name of a level ("L9_mfma_f32_32x32x2", ...); NULL if unknown.  The
+/* Short name of a level ("L9_mfma_f32", ...); NULL if unknown.  The
  * string is static and owned by the library. */
 const char *hip_sgemm_level_name(int level);
 
