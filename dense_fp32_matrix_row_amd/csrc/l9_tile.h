@@ -76,7 +76,8 @@ constexpr int kPad = 4;      // LDS row padding (words)
 // stage's global loads two K steps ahead (for tiles whose K step is shorter
 // than the memory latency).
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int UNROLL_ = BK_ / 2,
-          int GROUP_M_ = 8, bool PRIO_ = false, int KSLICE_ = 1, int DEPTH_ = 1, int MS_ = 32>
+          int GROUP_M_ = 8, bool PRIO_ = false, int KSLICE_ = 1, int DEPTH_ = 1, int MS_ = 32,
+          bool QUADS_ = false>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -91,6 +92,9 @@ struct MfmaTile {
   static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
   // Matrix instruction: 32 x 32 x 2 or 16 x 16 x 4 blocks.
   static constexpr int MS = MS_;
+  // Lane map of the transposing LDS store (Panel below): quads of lanes on
+  // one row (fewer, wider global reads) or conflict-free pairs.
+  static constexpr bool QUADS = QUADS_;
 };
 
 template <int N>
@@ -132,7 +136,7 @@ constexpr int kWhole = 0, kRaggedK = 1, kEdge = 2;
 // stored K x M): group = 4 consecutive e of one k, copied as is.  Groups
 // outside the matrix (e beyond its extent, k beyond K) read as zero and are
 // never dereferenced.
-template <int E, int BK, int THREADS, bool KCONTIG>
+template <int E, int BK, int THREADS, bool KCONTIG, bool QUADS>
 struct Panel {
   static constexpr int ITERS = (E * BK / 4) / THREADS;
   static_assert(ITERS >= 1 && ITERS * THREADS * 4 == E * BK, "panel not evenly staged");
@@ -140,8 +144,24 @@ struct Panel {
   float4 reg[2][ITERS];  // set 1 only with prefetch depth 2
 
   // group index of (thread, s) -> (e, k) inside the panel
-  __device__ static int e_of(int idx) { return KCONTIG ? idx / (BK / 4) : 4 * (idx % (E / 4)); }
-  __device__ static int k_of(int idx) { return KCONTIG ? 4 * (idx % (BK / 4)) : idx / (E / 4); }
+  // With KCONTIG and QUADS, the BK/4 groups of one e go to consecutive
+  // lanes (a lane quad reads one 64-byte row segment when BK = 16).  The
+  // transposing store then has the lanes of a half-wavefront write k-rows
+  // 4q + j for every q of the same few e, and with LDX = 4 (mod 32) rows 8
+  // apart share their banks: two-way conflicts on every store.  Without
+  // QUADS a half-wavefront takes two k groups of opposite parity (rows 16
+  // banks apart) over 16 consecutive e, conflict-free, at the price of lane
+  // pairs reading 32-byte pieces.
+  static constexpr int KGROUPS = BK / 4, KPAIRS = KGROUPS / 2 > 0 ? KGROUPS / 2 : 1;
+  static_assert(QUADS || E % 16 == 0, "pair mapping stages 16 rows per half-wavefront");
+  __device__ static int e_of(int idx) {
+    if (!KCONTIG) return 4 * (idx % (E / 4));
+    return QUADS ? idx / KGROUPS : 16 * ((idx / 32) / KPAIRS) + (idx / 2) % 16;
+  }
+  __device__ static int k_of(int idx) {
+    if (!KCONTIG) return idx / (E / 4);
+    return QUADS ? 4 * (idx % KGROUPS) : 4 * (2 * ((idx / 32) % KPAIRS) + idx % 2);
+  }
 
   __device__ void init(const float* base, int64_t ld, int64_t e0, int64_t k_lo, int tid) {
 #pragma unroll
@@ -277,8 +297,8 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
     // This thread's share of the A and B panels of each K step (rows of A
     // beyond M, columns of B beyond N and k beyond K read as zero).
     const bool interior = MODE != kEdge || (row0 + BM <= p.M && col0 + BN <= p.N);
-    Panel<BM, BK, THREADS, !TA> pa;
-    Panel<BN, BK, THREADS, TB> pb;
+    Panel<BM, BK, THREADS, !TA, T::QUADS> pa;
+    Panel<BN, BK, THREADS, TB, T::QUADS> pb;
     pa.init(p.A, p.lda, row0, k_lo, tid);
     pb.init(p.B, p.ldb, col0, k_lo, tid);
     // load<W>: stage at k0 into register set W; store<W>: set W into LDS
@@ -523,7 +543,11 @@ hipError_t launch_split(const Problem& p, int64_t k_split, float* ws, hipStream_
 // (against 4 chains of 16-pass ones with 32 x 32 blocks); measured on
 // MI355X: 138.2 against 136.6 TFLOP/s at 4096^3, 131.8 against 128.2 at
 // 4097^3.  (The 16 x 16 form of the other tiles measured equal or slower.)
-typedef MfmaTile<256, 128, 16, 4, 2, 4, 8, true, 1, 1, 16> TileHuge;
+// It alone keeps the lane-quad map of the transposing store: the
+// conflict-free map costs it 1 % at 4096^3, while the other tiles gain by
+// it (64 x 64 two-slice at 1024^3: +4.5 %; 128 x 128 two-slice at 2048^3:
+// +1 %).
+typedef MfmaTile<256, 128, 16, 4, 2, 4, 8, true, 1, 1, 16, true> TileHuge;
 typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true> TileLarge;
 typedef MfmaTile<128, 64, 16, 2, 2> TileMid;
 typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;
