@@ -63,9 +63,10 @@ Decomp decompose(int M, int N, int K, bool trans_a) {
   }
 
   // 2. Deep K over a small tile grid: split K so that about two work items
-  //    per CU run (1024 x 1024 x 4096: 128 x 128 in 8 slices 94 TFLOP/s
-  //    against 80 unsplit; 2048 x 2048 x 8192: 256 x 128 in 4 slices 131
-  //    against 115; 512 x 512 x 8192: 74 against 19).  Slices stay >= 256
+  //    per CU run (1024 x 1024 x 4096: 128 x 128 in 8 slices 97 TFLOP/s
+  //    against 80 unsplit; 1024 x 1024 x 8192: 113 in 16 slices;
+  //    2048 x 2048 x 8192: 256 x 128 in 4 slices 126-131 against 115;
+  //    512 x 512 x 8192: 74-77 against 19).  Slices stay >= 256
   //    deep (512 for the big tile) and at most 16.
   const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
   if (K >= 2048 && K >= 2 * int64_t(M > N ? M : N) && tiles128 < 2 * kCUs) {

@@ -77,7 +77,7 @@ int shape_bk(Shape shape) {
 Geometry mfma_split_geometry(Shape shape, int M, int N, int K, int64_t k_split) {
   switch (shape) {
     case Shape::kHuge: return split_geometry<TileHuge>(M, N, K, k_split);
-    case Shape::kLarge: return split_geometry<TileLarge>(M, N, K, k_split);
+    case Shape::kLarge: return split_geometry<TileLargeSplit>(M, N, K, k_split);
     case Shape::kMid: return split_geometry<TileMid>(M, N, K, k_split);
     case Shape::kLargeSliced: return split_geometry<TileLargeSliced>(M, N, K, k_split);
     case Shape::kSmallSliced: return split_geometry<TileSmallSliced>(M, N, K, k_split);

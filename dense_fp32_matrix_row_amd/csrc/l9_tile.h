@@ -77,7 +77,7 @@ constexpr int kPad = 4;      // LDS row padding (words)
 // than the memory latency).
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int UNROLL_ = BK_ / 2,
           int GROUP_M_ = 8, bool PRIO_ = false, int KSLICE_ = 1, int DEPTH_ = 1, int MS_ = 32,
-          bool QUADS_ = false>
+          bool QUADS_ = false, bool EARLY_ = false>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -95,6 +95,9 @@ struct MfmaTile {
   // Lane map of the transposing LDS store (Panel below): quads of lanes on
   // one row (fewer, wider global reads) or conflict-free pairs.
   static constexpr bool QUADS = QUADS_;
+  // With DEPTH 1: store the next stage into LDS before this stage's MFMAs
+  // (and load the one after) rather than after them.
+  static constexpr bool EARLY = EARLY_;
 };
 
 template <int N>
@@ -350,7 +353,23 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
       if (T::PRIO) __builtin_amdgcn_s_setprio(0);
     };
 
-    if (T::DEPTH == 1) {
+    if (T::DEPTH == 1 && T::EARLY) {
+      // Stage kt + 1 goes from registers into LDS before stage kt's MFMAs
+      // (its buffer was released by the previous barrier) and the registers
+      // take stage kt + 2 right after: the stores' latency hides under the
+      // MFMAs instead of preceding the barrier.
+      load(Set0(), 0);
+      store(Set0(), 0);
+      if (nk > 1) load(Set0(), BK);
+      __syncthreads();
+      for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = static_cast<int>(kt & 1);
+        if (kt + 1 < nk) store(Set0(), cur ^ 1);
+        if (kt + 2 < nk) load(Set0(), (kt + 2) * BK);
+        mfma_stage(cur);
+        barrier();
+      }
+    } else if (T::DEPTH == 1) {
       load(Set0(), 0);
       store(Set0(), 0);
       __syncthreads();
@@ -559,6 +578,12 @@ typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;
 // (its 32-deep K step is shorter than a global load's latency): +3-4 % at
 // 768^3-3072^3; the 128 x 128 one loses 4 % with it and keeps one step.
 typedef MfmaTile<128, 128, 32, 2, 2, 16, 8, false, 2> TileLargeSliced;
+// The 128 x 128 tile as split-K work items (K slices of 256 to 1024) stores
+// each stage into LDS before the previous stage's MFMAs: measured on MI355X
+// +5.9 % at 1024 x 1024 x 4096 and +4 % at 1024 x 1024 x 8192, where it
+// costs the unsplit tile 1.6 % (2048 x 4096 x 2048) and the 256 x 128 tile
+// 1.5-3 %.
+typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true, 1, 1, 32, false, true> TileLargeSplit;
 typedef MfmaTile<64, 64, 32, 2, 2, 16, 8, true, 2, 2> TileSmallSliced;
 constexpr int kCUs = 256;
 
@@ -581,7 +606,7 @@ hipError_t launch_split_shape_t(Shape shape, const Problem& p, int64_t k_split, 
                                 hipStream_t s) {
   switch (shape) {
     case Shape::kHuge: return launch_split<TileHuge, TA, TB>(p, k_split, ws, s);
-    case Shape::kLarge: return launch_split<TileLarge, TA, TB>(p, k_split, ws, s);
+    case Shape::kLarge: return launch_split<TileLargeSplit, TA, TB>(p, k_split, ws, s);
     case Shape::kMid: return launch_split<TileMid, TA, TB>(p, k_split, ws, s);
     case Shape::kLargeSliced: return launch_split<TileLargeSliced, TA, TB>(p, k_split, ws, s);
     case Shape::kSmallSliced: return launch_split<TileSmallSliced, TA, TB>(p, k_split, ws, s);
