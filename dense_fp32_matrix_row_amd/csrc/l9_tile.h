@@ -59,7 +59,7 @@ struct MfmaOp<16> {  // v_mfma_f32_16x16x4_f32: 8 passes
   __host__ __device__ static constexpr int row(int g, int r) { return 4 * g + r; }
 };
 
-constexpr int kPad = 4;      // LDS row padding (words)
+constexpr int kPad = 4;      // LDS row padding (words) of the unswizzled layout
 
 // A tile configuration: BM x BN block tile, BK-deep K steps, WAVES_M x
 // WAVES_N wavefronts (each owning a (BM/WAVES_M) x (BN/WAVES_N) wave tile),
@@ -77,7 +77,7 @@ constexpr int kPad = 4;      // LDS row padding (words)
 // than the memory latency).
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int UNROLL_ = BK_ / 2,
           int GROUP_M_ = 8, bool PRIO_ = false, int KSLICE_ = 1, int DEPTH_ = 1, int MS_ = 32,
-          bool QUADS_ = false, bool EARLY_ = false>
+          bool SWZ_ = true, bool EARLY_ = false>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -92,9 +92,9 @@ struct MfmaTile {
   static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
   // Matrix instruction: 32 x 32 x 2 or 16 x 16 x 4 blocks.
   static constexpr int MS = MS_;
-  // Lane map of the transposing LDS store (Panel below): quads of lanes on
-  // one row (fewer, wider global reads) or conflict-free pairs.
-  static constexpr bool QUADS = QUADS_;
+  // LDS layout (Panel below): unpadded rows with the transposing store's
+  // columns XOR-swizzled, or rows padded by kPad words.
+  static constexpr bool SWZ = SWZ_;
   // With DEPTH 1: store the next stage into LDS before this stage's MFMAs
   // (and load the one after) rather than after them.
   static constexpr bool EARLY = EARLY_;
@@ -139,7 +139,7 @@ constexpr int kWhole = 0, kRaggedK = 1, kEdge = 2;
 // stored K x M): group = 4 consecutive e of one k, copied as is.  Groups
 // outside the matrix (e beyond its extent, k beyond K) read as zero and are
 // never dereferenced.
-template <int E, int BK, int THREADS, bool KCONTIG, bool QUADS>
+template <int E, int BK, int THREADS, bool KCONTIG, bool SWZ>
 struct Panel {
   static constexpr int ITERS = (E * BK / 4) / THREADS;
   static_assert(ITERS >= 1 && ITERS * THREADS * 4 == E * BK, "panel not evenly staged");
@@ -147,24 +147,25 @@ struct Panel {
   float4 reg[2][ITERS];  // set 1 only with prefetch depth 2
 
   // group index of (thread, s) -> (e, k) inside the panel
-  // With KCONTIG and QUADS, the BK/4 groups of one e go to consecutive
-  // lanes (a lane quad reads one 64-byte row segment when BK = 16).  The
-  // transposing store then has the lanes of a half-wavefront write k-rows
-  // 4q + j for every q of the same few e, and with LDX = 4 (mod 32) rows 8
-  // apart share their banks: two-way conflicts on every store.  Without
-  // QUADS a half-wavefront takes two k groups of opposite parity (rows 16
-  // banks apart) over 16 consecutive e, conflict-free, at the price of lane
-  // pairs reading 32-byte pieces.
-  static constexpr int KGROUPS = BK / 4, KPAIRS = KGROUPS / 2 > 0 ? KGROUPS / 2 : 1;
-  static_assert(QUADS || E % 16 == 0, "pair mapping stages 16 rows per half-wavefront");
-  __device__ static int e_of(int idx) {
-    if (!KCONTIG) return 4 * (idx % (E / 4));
-    return QUADS ? idx / KGROUPS : 16 * ((idx / 32) / KPAIRS) + (idx / 2) % 16;
-  }
-  __device__ static int k_of(int idx) {
-    if (!KCONTIG) return idx / (E / 4);
-    return QUADS ? 4 * (idx % KGROUPS) : 4 * (2 * ((idx / 32) % KPAIRS) + idx % 2);
-  }
+  // A lane quad takes the BK/4 groups of one e (a row's 64 contiguous bytes
+  // at BK = 16) with KCONTIG, or 16 consecutive e of one k otherwise.
+  __device__ static int e_of(int idx) { return KCONTIG ? idx / (BK / 4) : 4 * (idx % (E / 4)); }
+  __device__ static int k_of(int idx) { return KCONTIG ? 4 * (idx % (BK / 4)) : idx / (E / 4); }
+
+  // LDS column of element e in k-row k.  Measured on MI355X (bank-conflict
+  // counter over single access patterns): a 128-bit read whose 16-lane
+  // groups each cover 256 contiguous bytes of one row is conflict-free when
+  // the row stride is a multiple of 256 bytes and takes 4 extra cycles
+  // otherwise, and the transposing store's 32-bit writes are served as two
+  // half-wavefronts on 32 banks.  With SWZ the rows are unpadded (E words,
+  // a multiple of 64) and the store XORs the column with SWZ_STEP times the
+  // k-row's 4-row group, which spreads a half-wavefront's writes over all
+  // 32 banks; readers apply the same XOR (constant per MFMA step).  The XOR
+  // stays inside an aligned 32-word block, so 4-word groups stay whole.
+  // Without SWZ the rows are padded to E + kPad words and stored as is.
+  static constexpr int SWZ_STEP = SWZ && KCONTIG ? 128 / BK : 0;
+  static_assert(SWZ_STEP == 0 || (SWZ_STEP >= 4 && E % 64 == 0), "swizzle needs BK <= 32, E % 64 == 0");
+  __host__ __device__ static constexpr int col(int e, int k) { return e ^ (SWZ_STEP * ((k % BK) / 4)); }
 
   __device__ void init(const float* base, int64_t ld, int64_t e0, int64_t k_lo, int tid) {
 #pragma unroll
@@ -217,10 +218,11 @@ struct Panel {
       const int idx = tid + s * THREADS;
       const int e = e_of(idx), k = k_of(idx);
       if (KCONTIG) {
-        X[k + 0][e] = reg[W][s].x;
-        X[k + 1][e] = reg[W][s].y;
-        X[k + 2][e] = reg[W][s].z;
-        X[k + 3][e] = reg[W][s].w;
+        const int c = col(e, k);
+        X[k + 0][c] = reg[W][s].x;
+        X[k + 1][c] = reg[W][s].y;
+        X[k + 2][c] = reg[W][s].z;
+        X[k + 3][c] = reg[W][s].w;
       } else {
         *reinterpret_cast<float4*>(&X[k][e]) = reg[W][s];
       }
@@ -246,11 +248,13 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
   typedef MfmaOp<T::MS> Op;
   constexpr int DIM = Op::DIM, KPER = Op::KPER, REGS = Op::REGS;
   constexpr int BLK_M = WTM / DIM, BLK_N = WTN / DIM;
-  constexpr int LDA = BM + kPad, LDB = BN + kPad;
+  constexpr int LDA = BM + (T::SWZ ? 0 : kPad), LDB = BN + (T::SWZ ? 0 : kPad);
   static_assert(BLK_M * DIM == WTM && BLK_N * DIM == WTN, "wave tile not whole blocks");
   static_assert(BK % KPER == 0, "a stage is whole MFMA steps");
   static_assert((BK / KPER) % T::KSLICE == 0, "K slices must split a stage's MFMA steps evenly");
   constexpr int WAVE_TILES = T::WAVES_M * T::WAVES_N;
+  typedef Panel<BM, BK, THREADS, !TA, T::SWZ> PanelA;
+  typedef Panel<BN, BK, THREADS, TB, T::SWZ> PanelB;
   constexpr int STEPS = BK / KPER / T::KSLICE;         // MFMA steps per stage per wavefront
   constexpr int PER_WAVE = BLK_M * BLK_N * REGS * 64;  // accumulator floats per wavefront
   typedef typename VecT<BLK_M>::type AFrag;
@@ -300,8 +304,8 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
     // This thread's share of the A and B panels of each K step (rows of A
     // beyond M, columns of B beyond N and k beyond K read as zero).
     const bool interior = MODE != kEdge || (row0 + BM <= p.M && col0 + BN <= p.N);
-    Panel<BM, BK, THREADS, !TA, T::QUADS> pa;
-    Panel<BN, BK, THREADS, TB, T::QUADS> pb;
+    PanelA pa;
+    PanelB pb;
     pa.init(p.A, p.lda, row0, k_lo, tid);
     pb.init(p.B, p.ldb, col0, k_lo, tid);
     // load<W>: stage at k0 into register set W; store<W>: set W into LDS
@@ -337,9 +341,11 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
       if (T::PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll T::UNROLL
       for (int s = 0; s < STEPS; ++s) {
-        const int kk = KPER * (kslice * STEPS + s) + kg;
-        const AFrag af = *reinterpret_cast<const AFrag*>(&As[cur][kk][a_off]);
-        const BFrag bf = *reinterpret_cast<const BFrag*>(&Bs[cur][kk][b_off]);
+        // (the KPER k-rows of one MFMA step share one 4-row group, so one
+        // swizzle serves every lane)
+        const int k0 = KPER * (kslice * STEPS + s), kk = k0 + kg;
+        const AFrag af = *reinterpret_cast<const AFrag*>(&As[cur][kk][PanelA::col(a_off, k0)]);
+        const BFrag bf = *reinterpret_cast<const BFrag*>(&Bs[cur][kk][PanelB::col(b_off, k0)]);
 #pragma unroll
         for (int bi = 0; bi < BLK_M; ++bi)
 #pragma unroll
@@ -562,11 +568,11 @@ hipError_t launch_split(const Problem& p, int64_t k_split, float* ws, hipStream_
 // (against 4 chains of 16-pass ones with 32 x 32 blocks); measured on
 // MI355X: 138.2 against 136.6 TFLOP/s at 4096^3, 131.8 against 128.2 at
 // 4097^3.  (The 16 x 16 form of the other tiles measured equal or slower.)
-// It alone keeps the lane-quad map of the transposing store: the
-// conflict-free map costs it 1 % at 4096^3, while the other tiles gain by
-// it (64 x 64 two-slice at 1024^3: +4.5 %; 128 x 128 two-slice at 2048^3:
-// +1 %).
-typedef MfmaTile<256, 128, 16, 4, 2, 4, 8, true, 1, 1, 16, true> TileHuge;
+// It alone keeps padded LDS rows: the swizzled layout (conflict-free LDS
+// traffic, which gains the other tiles 1-3 %) makes the compiler keep a
+// single fragment register set in its loop and costs 0.7 % at 4096^3, and
+// its ragged-K form then needs 133 VGPRs, one block per CU: -8.5 % at 4097^3.
+typedef MfmaTile<256, 128, 16, 4, 2, 4, 8, true, 1, 1, 16, false> TileHuge;
 typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true> TileLarge;
 typedef MfmaTile<128, 64, 16, 2, 2> TileMid;
 typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;
@@ -583,7 +589,7 @@ typedef MfmaTile<128, 128, 32, 2, 2, 16, 8, false, 2> TileLargeSliced;
 // +5.9 % at 1024 x 1024 x 4096 and +4 % at 1024 x 1024 x 8192, where it
 // costs the unsplit tile 1.6 % (2048 x 4096 x 2048) and the 256 x 128 tile
 // 1.5-3 %.
-typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true, 1, 1, 32, false, true> TileLargeSplit;
+typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true, 1, 1, 32, true, true> TileLargeSplit;
 typedef MfmaTile<64, 64, 32, 2, 2, 16, 8, true, 2, 2> TileSmallSliced;
 constexpr int kCUs = 256;
 
