@@ -18,7 +18,9 @@
 // and a lane's BLK_N outputs of one row are adjacent in C (one 64-bit store).
 // MFMA step s of a K-phase consumes k = KPER*s + l/DIM (KPER = 2 or 4).
 //
-// LDS holds both operands k-major: As[k][m], Bs[k][n].  A row-major A (and a
+// LDS holds both operands k-major, k-row k of A at As[k / 4][(k % 4) * BM + m]
+// (likewise B): unpadded rows in groups of four, the groups a few words
+// apart (Panel below gives the bank arithmetic).  A row-major A (and a
 // transposed B, stored N x K) arrive 4 consecutive k per 128-bit load and
 // are transposed on their way into LDS; a transposed A (stored K x M) and a
 // row-major B arrive 4 consecutive m / n per load and are copied as is.
@@ -59,7 +61,6 @@ struct MfmaOp<16> {  // v_mfma_f32_16x16x4_f32: 8 passes
   __host__ __device__ static constexpr int row(int g, int r) { return 4 * g + r; }
 };
 
-constexpr int kPad = 4;      // LDS row padding (words) of the unswizzled layout
 
 // A tile configuration: BM x BN block tile, BK-deep K steps, WAVES_M x
 // WAVES_N wavefronts (each owning a (BM/WAVES_M) x (BN/WAVES_N) wave tile),
@@ -77,7 +78,7 @@ constexpr int kPad = 4;      // LDS row padding (words) of the unswizzled layout
 // than the memory latency).
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int UNROLL_ = BK_ / 2,
           int GROUP_M_ = 8, bool PRIO_ = false, int KSLICE_ = 1, int DEPTH_ = 1, int MS_ = 32,
-          bool SWZ_ = true, bool EARLY_ = false>
+          bool EARLY_ = false>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -92,9 +93,6 @@ struct MfmaTile {
   static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
   // Matrix instruction: 32 x 32 x 2 or 16 x 16 x 4 blocks.
   static constexpr int MS = MS_;
-  // LDS layout (Panel below): unpadded rows with the transposing store's
-  // columns XOR-swizzled, or rows padded by kPad words.
-  static constexpr bool SWZ = SWZ_;
   // With DEPTH 1: store the next stage into LDS before this stage's MFMAs
   // (and load the one after) rather than after them.
   static constexpr bool EARLY = EARLY_;
@@ -139,7 +137,7 @@ constexpr int kWhole = 0, kRaggedK = 1, kEdge = 2;
 // stored K x M): group = 4 consecutive e of one k, copied as is.  Groups
 // outside the matrix (e beyond its extent, k beyond K) read as zero and are
 // never dereferenced.
-template <int E, int BK, int THREADS, bool KCONTIG, bool SWZ>
+template <int E, int BK, int THREADS, bool KCONTIG>
 struct Panel {
   static constexpr int ITERS = (E * BK / 4) / THREADS;
   static_assert(ITERS >= 1 && ITERS * THREADS * 4 == E * BK, "panel not evenly staged");
@@ -152,20 +150,19 @@ struct Panel {
   __device__ static int e_of(int idx) { return KCONTIG ? idx / (BK / 4) : 4 * (idx % (E / 4)); }
   __device__ static int k_of(int idx) { return KCONTIG ? 4 * (idx % (BK / 4)) : idx / (E / 4); }
 
-  // LDS column of element e in k-row k.  Measured on MI355X (bank-conflict
+  // LDS layout: X[k / 4][(k % 4) * E + e] -- unpadded k-rows, groups of
+  // four k-rows GROUP words apart.  Measured on MI355X (bank-conflict
   // counter over single access patterns): a 128-bit read whose 16-lane
-  // groups each cover 256 contiguous bytes of one row is conflict-free when
-  // the row stride is a multiple of 256 bytes and takes 4 extra cycles
-  // otherwise, and the transposing store's 32-bit writes are served as two
-  // half-wavefronts on 32 banks.  With SWZ the rows are unpadded (E words,
-  // a multiple of 64) and the store XORs the column with SWZ_STEP times the
-  // k-row's 4-row group, which spreads a half-wavefront's writes over all
-  // 32 banks; readers apply the same XOR (constant per MFMA step).  The XOR
-  // stays inside an aligned 32-word block, so 4-word groups stay whole.
-  // Without SWZ the rows are padded to E + kPad words and stored as is.
-  static constexpr int SWZ_STEP = SWZ && KCONTIG ? 128 / BK : 0;
-  static_assert(SWZ_STEP == 0 || (SWZ_STEP >= 4 && E % 64 == 0), "swizzle needs BK <= 32, E % 64 == 0");
-  __host__ __device__ static constexpr int col(int e, int k) { return e ^ (SWZ_STEP * ((k % BK) / 4)); }
+  // groups each cover 256 contiguous bytes of one row -- the fragment reads
+  // -- is conflict-free when the row stride is a multiple of 256 bytes and
+  // takes 4 extra cycles otherwise, and 32-bit writes are served as two
+  // half-wavefronts on 32 banks.  An MFMA step reads k-rows of one group
+  // (row stride 4E bytes, E a multiple of 64): conflict-free.  The
+  // transposing store (KCONTIG) has a half-wavefront write the BK/4 k-groups
+  // of 128/BK consecutive e; groups 128/BK words apart put those writes on
+  // 32 different banks.
+  static constexpr int GROUP = 4 * E + (KCONTIG ? 128 / BK : 0);
+  static_assert(E % 64 == 0 && GROUP % 4 == 0, "rows of 64-word multiples, 16-byte aligned groups");
 
   __device__ void init(const float* base, int64_t ld, int64_t e0, int64_t k_lo, int tid) {
 #pragma unroll
@@ -211,20 +208,20 @@ struct Panel {
         reg[W][s] = load4(ptr[s] + k0 * ld - e, e, ext, k < K);
     }
   }
-  template <int W, int LDX>
-  __device__ void store(float (*X)[LDX], int tid) const {
+  template <int W>
+  __device__ void store(float (*X)[GROUP], int tid) const {
 #pragma unroll
     for (int s = 0; s < ITERS; ++s) {
       const int idx = tid + s * THREADS;
       const int e = e_of(idx), k = k_of(idx);
-      if (KCONTIG) {
-        const int c = col(e, k);
-        X[k + 0][c] = reg[W][s].x;
-        X[k + 1][c] = reg[W][s].y;
-        X[k + 2][c] = reg[W][s].z;
-        X[k + 3][c] = reg[W][s].w;
+      float* const g = X[k / 4];
+      if (KCONTIG) {  // k % 4 == 0: the group's four rows
+        g[0 * E + e] = reg[W][s].x;
+        g[1 * E + e] = reg[W][s].y;
+        g[2 * E + e] = reg[W][s].z;
+        g[3 * E + e] = reg[W][s].w;
       } else {
-        *reinterpret_cast<float4*>(&X[k][e]) = reg[W][s];
+        *reinterpret_cast<float4*>(&g[(k % 4) * E + e]) = reg[W][s];
       }
     }
   }
@@ -248,13 +245,13 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
   typedef MfmaOp<T::MS> Op;
   constexpr int DIM = Op::DIM, KPER = Op::KPER, REGS = Op::REGS;
   constexpr int BLK_M = WTM / DIM, BLK_N = WTN / DIM;
-  constexpr int LDA = BM + (T::SWZ ? 0 : kPad), LDB = BN + (T::SWZ ? 0 : kPad);
+  typedef Panel<BM, BK, THREADS, !TA> PanelA;
+  typedef Panel<BN, BK, THREADS, TB> PanelB;
+  constexpr int GA = PanelA::GROUP, GB = PanelB::GROUP;
   static_assert(BLK_M * DIM == WTM && BLK_N * DIM == WTN, "wave tile not whole blocks");
   static_assert(BK % KPER == 0, "a stage is whole MFMA steps");
   static_assert((BK / KPER) % T::KSLICE == 0, "K slices must split a stage's MFMA steps evenly");
   constexpr int WAVE_TILES = T::WAVES_M * T::WAVES_N;
-  typedef Panel<BM, BK, THREADS, !TA, T::SWZ> PanelA;
-  typedef Panel<BN, BK, THREADS, TB, T::SWZ> PanelB;
   constexpr int STEPS = BK / KPER / T::KSLICE;         // MFMA steps per stage per wavefront
   constexpr int PER_WAVE = BLK_M * BLK_N * REGS * 64;  // accumulator floats per wavefront
   typedef typename VecT<BLK_M>::type AFrag;
@@ -262,11 +259,11 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
 
   // LDS: the two stages of A and B; with K slices, the slices' sums meet in
   // the same memory once the K loop is over (the stages are free then).
-  constexpr int STAGE_FLOATS = 2 * BK * LDA + 2 * BK * LDB;
+  constexpr int STAGE_FLOATS = 2 * (BK / 4) * (GA + GB);
   constexpr int RED_FLOATS = (T::KSLICE - 1) * WAVE_TILES * PER_WAVE;
   __shared__ __align__(16) float smem[STAGE_FLOATS > RED_FLOATS ? STAGE_FLOATS : RED_FLOATS];
-  float (*const As)[BK][LDA] = reinterpret_cast<float (*)[BK][LDA]>(smem);
-  float (*const Bs)[BK][LDB] = reinterpret_cast<float (*)[BK][LDB]>(smem + 2 * BK * LDA);
+  float (*const As)[BK / 4][GA] = reinterpret_cast<float (*)[BK / 4][GA]>(smem);
+  float (*const Bs)[BK / 4][GB] = reinterpret_cast<float (*)[BK / 4][GB]>(smem + 2 * (BK / 4) * GA);
   float* const red = smem;
 
   const int tid = threadIdx.x;
@@ -341,11 +338,10 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
       if (T::PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll T::UNROLL
       for (int s = 0; s < STEPS; ++s) {
-        // (the KPER k-rows of one MFMA step share one 4-row group, so one
-        // swizzle serves every lane)
-        const int k0 = KPER * (kslice * STEPS + s), kk = k0 + kg;
-        const AFrag af = *reinterpret_cast<const AFrag*>(&As[cur][kk][PanelA::col(a_off, k0)]);
-        const BFrag bf = *reinterpret_cast<const BFrag*>(&Bs[cur][kk][PanelB::col(b_off, k0)]);
+        // (the KPER k-rows k0 + kg of one MFMA step lie in one group)
+        const int k0 = KPER * (kslice * STEPS + s), r = k0 % 4 + kg;
+        const AFrag af = *reinterpret_cast<const AFrag*>(&As[cur][k0 / 4][r * BM + a_off]);
+        const BFrag bf = *reinterpret_cast<const BFrag*>(&Bs[cur][k0 / 4][r * BN + b_off]);
 #pragma unroll
         for (int bi = 0; bi < BLK_M; ++bi)
 #pragma unroll
@@ -568,11 +564,7 @@ hipError_t launch_split(const Problem& p, int64_t k_split, float* ws, hipStream_
 // (against 4 chains of 16-pass ones with 32 x 32 blocks); measured on
 // MI355X: 138.2 against 136.6 TFLOP/s at 4096^3, 131.8 against 128.2 at
 // 4097^3.  (The 16 x 16 form of the other tiles measured equal or slower.)
-// It alone keeps padded LDS rows: the swizzled layout (conflict-free LDS
-// traffic, which gains the other tiles 1-3 %) makes the compiler keep a
-// single fragment register set in its loop and costs 0.7 % at 4096^3, and
-// its ragged-K form then needs 133 VGPRs, one block per CU: -8.5 % at 4097^3.
-typedef MfmaTile<256, 128, 16, 4, 2, 4, 8, true, 1, 1, 16, false> TileHuge;
+typedef MfmaTile<256, 128, 16, 4, 2, 4, 8, true, 1, 1, 16> TileHuge;
 typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true> TileLarge;
 typedef MfmaTile<128, 64, 16, 2, 2> TileMid;
 typedef MfmaTile<64, 64, 16, 2, 2> TileSmall;
@@ -589,7 +581,7 @@ typedef MfmaTile<128, 128, 32, 2, 2, 16, 8, false, 2> TileLargeSliced;
 // +5.9 % at 1024 x 1024 x 4096 and +4 % at 1024 x 1024 x 8192, where it
 // costs the unsplit tile 1.6 % (2048 x 4096 x 2048) and the 256 x 128 tile
 // 1.5-3 %.
-typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true, 1, 1, 32, true, true> TileLargeSplit;
+typedef MfmaTile<128, 128, 32, 4, 1, 16, 8, true, 1, 1, 32, true> TileLargeSplit;
 typedef MfmaTile<64, 64, 32, 2, 2, 16, 8, true, 2, 2> TileSmallSliced;
 constexpr int kCUs = 256;
 
