@@ -172,11 +172,15 @@ struct Panel {
                        : base + (k_lo + k_of(idx)) * ld + e0 + e_of(idx);
     }
   }
-  // whole K step, whole tile
+  // whole K step, whole tile (load_one: group s only)
+  template <int W>
+  __device__ void load_one(int s, int64_t k0, int64_t ld) {
+    reg[W][s] = ld_global4(ptr[s] + (KCONTIG ? k0 : k0 * ld));
+  }
   template <int W>
   __device__ void load_whole(int64_t k0, int64_t ld) {
 #pragma unroll
-    for (int s = 0; s < ITERS; ++s) reg[W][s] = ld_global4(ptr[s] + (KCONTIG ? k0 : k0 * ld));
+    for (int s = 0; s < ITERS; ++s) load_one<W>(s, k0, ld);
   }
   // last K step of a whole tile: k at or beyond K reads as zero
   template <int W>
@@ -208,22 +212,25 @@ struct Panel {
         reg[W][s] = load4(ptr[s] + k0 * ld - e, e, ext, k < K);
     }
   }
+  // group s of register set W into the LDS stage X (store_one), or all of them
+  template <int W>
+  __device__ void store_one(int s, float (*X)[GROUP], int tid) const {
+    const int idx = tid + s * THREADS;
+    const int e = e_of(idx), k = k_of(idx);
+    float* const g = X[k / 4];
+    if (KCONTIG) {  // k % 4 == 0: the group's four rows
+      g[0 * E + e] = reg[W][s].x;
+      g[1 * E + e] = reg[W][s].y;
+      g[2 * E + e] = reg[W][s].z;
+      g[3 * E + e] = reg[W][s].w;
+    } else {
+      *reinterpret_cast<float4*>(&g[(k % 4) * E + e]) = reg[W][s];
+    }
+  }
   template <int W>
   __device__ void store(float (*X)[GROUP], int tid) const {
 #pragma unroll
-    for (int s = 0; s < ITERS; ++s) {
-      const int idx = tid + s * THREADS;
-      const int e = e_of(idx), k = k_of(idx);
-      float* const g = X[k / 4];
-      if (KCONTIG) {  // k % 4 == 0: the group's four rows
-        g[0 * E + e] = reg[W][s].x;
-        g[1 * E + e] = reg[W][s].y;
-        g[2 * E + e] = reg[W][s].z;
-        g[3 * E + e] = reg[W][s].w;
-      } else {
-        *reinterpret_cast<float4*>(&g[(k % 4) * E + e]) = reg[W][s];
-      }
-    }
+    for (int s = 0; s < ITERS; ++s) store_one<W>(s, X, tid);
   }
 };
 //
@@ -471,24 +478,50 @@ __global__ __launch_bounds__(T::THREADS) void k_level9(Problem p, int64_t tiles_
     for (int bi = 0; bi < BLK_M; ++bi) {
       const int64_t row_base = row0 + wm * WTM + BLK_M * Op::row(kg, 0) + bi;
       float* const c_base = p.C + row_base * p.ldc + col;
+      auto row_in = [&](int r) {
+        return interior || row_base + BLK_M * (Op::row(kg, r) - Op::row(kg, 0)) < p.M;
+      };
+      auto c_row = [&](int r) { return c_base + BLK_M * (Op::row(kg, r) - Op::row(kg, 0)) * p.ldc; };
+      if (interior || vec_ok) {
+        // One 64- or 128-bit access per lane and row (4-byte alignment
+        // suffices).  With beta != 0 the old values of four rows are loaded
+        // before their stores: the compiler cannot move a load of C above a
+        // store to C (it cannot tell the rows apart), so loads interleaved
+        // with stores would each wait out a full memory latency (four rows
+        // at a time bounds the registers this takes).
+        if (p.beta != 0.0f) {
+          constexpr int RB = REGS < 4 ? REGS : 4;
 #pragma unroll
-      for (int r = 0; r < REGS; ++r) {
-        const int dr = BLK_M * (Op::row(kg, r) - Op::row(kg, 0));
-        if (!interior && row_base + dr >= p.M) continue;
-        float* c = c_base + dr * p.ldc;
-        if (interior || vec_ok) {
-          // one 64- or 128-bit access per lane (4-byte alignment suffices)
-          float o[BLK_N];
+          for (int r0 = 0; r0 < REGS; r0 += RB) {
+            float old[RB][BLK_N];
 #pragma unroll
-          for (int bj = 0; bj < BLK_N; ++bj) o[bj] = p.alpha * acc[bi][bj][r];
-          if (p.beta != 0.0f) {
-            float old[BLK_N];
-            __builtin_memcpy(old, c, sizeof(old));
+            for (int r = r0; r < r0 + RB; ++r)
+              if (row_in(r)) __builtin_memcpy(old[r - r0], c_row(r), sizeof(old[0]));
 #pragma unroll
-            for (int bj = 0; bj < BLK_N; ++bj) o[bj] = fmaf(p.beta, old[bj], o[bj]);
+            for (int r = r0; r < r0 + RB; ++r) {
+              if (!row_in(r)) continue;
+              float o[BLK_N];
+#pragma unroll
+              for (int bj = 0; bj < BLK_N; ++bj)
+                o[bj] = fmaf(p.beta, old[r - r0][bj], p.alpha * acc[bi][bj][r]);
+              __builtin_memcpy(c_row(r), o, sizeof(o));
+            }
           }
-          __builtin_memcpy(c, o, sizeof(o));
         } else {
+#pragma unroll
+          for (int r = 0; r < REGS; ++r) {
+            if (!row_in(r)) continue;
+            float o[BLK_N];
+#pragma unroll
+            for (int bj = 0; bj < BLK_N; ++bj) o[bj] = p.alpha * acc[bi][bj][r];
+            __builtin_memcpy(c_row(r), o, sizeof(o));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < REGS; ++r) {
+          if (!row_in(r)) continue;
+          float* c = c_row(r);
 #pragma unroll
           for (int bj = 0; bj < BLK_N; ++bj)
             if (col + bj < p.N)
