@@ -7,7 +7,8 @@
 // one fixed tiling.  This rung does the same with what the library has:
 //   - M <= 16 or N <= 16: the thin kernels (a matrix-core tile would be
 //     mostly empty rows or columns, and the problem is bound by reading the
-//     other operand);
+//     other operand; l10_thin.hip gives them one 16-row MFMA block or
+//     vector-ALU FMA chains);
 //   - a large problem whose M and N miss a multiple of the 256 x 128 (or
 //     128 x 128) tile by at most 16: whole tiles over the largest multiple,
 //     no per-element bounds logic (only the last K step masks when K is
@@ -47,11 +48,9 @@ double round_fill(int64_t tiles) {
 // The rules below were fitted to sweeps of every tile shape and slice count
 // on MI355X (dense_fp32_matrix_row_amd.autotune); the comments give the
 // measurements that decided them.
-Decomp decompose(int M, int N, int K, bool trans_a) {
+Decomp decompose(int M, int N, int K) {
   if (M <= kThin) return {Plan::kFewRows, Shape::kSmall, M, N, K};
-  // (with A stored K x M the few-columns kernel would read strided columns
-  // of A; those problems take the tiles below)
-  if (N <= kThin && !trans_a) return {Plan::kFewCols, Shape::kSmall, M, N, K};
+  if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, M, N, K};
 
   // 1. At least two 256 x 128 tiles per CU (plus a fringe of <= 16): the
   //    big tile (4096^3: 138 TFLOP/s; 4097^3 with the fringe: 127).
@@ -109,7 +108,7 @@ Decomp decompose(int M, int N, int K, bool trans_a) {
 }
 
 Geometry geometry10(int M, int N, int K) {
-  const Decomp d = decompose(M, N, K, false);
+  const Decomp d = decompose(M, N, K);
   switch (d.plan) {
     case Plan::kFewRows: return few_rows_geometry(M, N, K);
     case Plan::kFewCols: return few_cols_geometry(M, N, K);
@@ -119,7 +118,7 @@ Geometry geometry10(int M, int N, int K) {
 }
 
 hipError_t launch10(const Problem& p, hipStream_t s) {
-  const Decomp d = decompose(p.M, p.N, p.K, p.trans_a);
+  const Decomp d = decompose(p.M, p.N, p.K);
   switch (d.plan) {
     case Plan::kFewRows: return launch_few_rows(p, s);
     case Plan::kFewCols: return launch_few_cols(p, s);
@@ -139,7 +138,7 @@ hipError_t launch10(const Problem& p, hipStream_t s) {
     right.N = p.N - d.Nm;
     right.B = p.B + (p.trans_b ? d.Nm * p.ldb : d.Nm);
     right.C = p.C + d.Nm;
-    e = p.trans_a ? launch_mfma(Shape::kSmallSliced, right, s) : launch_few_cols(right, s);
+    e = launch_few_cols(right, s);
   }
   if (e == hipSuccess && d.Mm < p.M) {
     // bottom fringe: rows [Mm, M), every column

@@ -1,5 +1,5 @@
 // l10_thin.hip -- the thin-problem kernels of the dispatching rung: C blocks
-// with at most kThin (16) rows or at most kThin columns, on the vector ALUs.
+// with at most kThin (16) rows or at most kThin columns.
 //
 // A thin product reads one operand in full and does little arithmetic per
 // byte (M = 1 is a matrix-vector product), so it is HBM-bound; a matrix-core
@@ -13,6 +13,10 @@
 //   - across wavefronts, an in-order sum through LDS.
 // The order depends only on the shape, never on timing: results are
 // bit-reproducible, with no atomics and no workspace.
+//
+// Two forms: vector-ALU FMA chains (below, for one to four rows or
+// columns of short problems), and a matrix-core form for the rest, whose
+// 16-row MFMA block takes up to sixteen rows at once (further below).
 //
 // Used for problems with M <= 16 or N <= 16, and for the one- to
 // sixteen-row/column fringe left beside the matrix-core tiles of large
@@ -208,6 +212,171 @@ __global__ __launch_bounds__(kColThreads) void k_few_cols(Problem p, int64_t nbl
   }
 }
 
+// ---------------------------------------------------------------------------
+// Thin problems on the matrix cores.  One form serves both thin shapes:
+// C' = alpha * A' * B' + beta * C' with C' at most 16 rows -- C itself for
+// few rows, C^T = B^T * A^T for few columns -- where each operand is read
+// in its stored orientation:
+//   A'[r][k] = TA ? a[k * lda + r] : a[r * lda + k]
+//   B'[k][n] = TB ? b[n * ldb + k] : b[k * ldb + n]
+//   C'[r][n] = CT ? c[n * ldc + r] : c[r * ldc + n]
+// A block owns NB = 16 V columns of C' and all of K.  Its W wavefronts take
+// the K groups of 16 in turn; in a group at kb, MFMA step s (0..3) gives
+// lane group g = l / 16 the k = kb + 4 g + s, so a lane's four A' values are
+// adjacent (one 128-bit read of a row-major A' row) and, when B' is stored
+// k-contiguous, so are its four B' values of one column.  v_mfma_f32_16x16x4_f32
+// block j takes the columns n0 + V i + j (i = l % 16): with B' row-major a
+// lane's V values of one k are adjacent, and the 16 lanes of a k read 16 V
+// consecutive floats.  The wavefronts' partial sums meet in LDS and are
+// added in wavefront order; nothing depends on timing, and every
+// orientation performs the same arithmetic.
+struct Thin {
+  int M, N, K;  // of C'
+  float alpha, beta;
+  const float* a;
+  int64_t lda;
+  const float* b;
+  int64_t ldb;
+  float* c;
+  int64_t ldc;
+};
+
+constexpr int kThinWaves = 16;
+
+template <int V, bool TA, bool TB, bool CT>
+__global__ __launch_bounds__(64 * kThinWaves) void k_thin_mfma(Thin t, int64_t ntiles) {
+  typedef float floatx4 __attribute__((ext_vector_type(4)));
+  constexpr int W = kThinWaves, NB = 16 * V;
+  __shared__ float red[W][16][NB];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int i = lane % 16, g = lane / 16;
+  const bool row_ok = i < t.M;
+  for (int64_t tile = xcd_contiguous(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
+    const int64_t n0 = tile * NB, nl = n0 + V * i;  // nl: this lane's first column
+    floatx4 acc[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t kb = 16 * wave; kb < t.K; kb += 16 * W) {
+      const int64_t k = kb + 4 * g;  // steps s = 0..3 take k + s
+      float4 av;
+      if (TA) {
+        av = make_float4(row_ok && k < t.K ? t.a[k * t.lda + i] : 0.0f,
+                         row_ok && k + 1 < t.K ? t.a[(k + 1) * t.lda + i] : 0.0f,
+                         row_ok && k + 2 < t.K ? t.a[(k + 2) * t.lda + i] : 0.0f,
+                         row_ok && k + 3 < t.K ? t.a[(k + 3) * t.lda + i] : 0.0f);
+      } else {
+        av = load4(t.a + (row_ok ? i : 0) * t.lda, k, t.K, row_ok);
+      }
+      float bv[4][V];  // [step][column]
+      if (TB) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const bool ok = nl + j < t.N;
+          const float4 v = load4(t.b + (ok ? nl + j : 0) * t.ldb, k, t.K, ok);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) bv[s][j] = fget(v, s);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bool kok = k + s < t.K;
+          const float* row = t.b + (kok ? k + s : 0) * t.ldb;
+          if (V == 4) {
+            const float4 v = load4(row, nl, t.N, kok);
+            bv[s][0] = v.x;
+            bv[s][1] = v.y;
+            bv[s][2] = v.z;
+            bv[s][3] = v.w;
+          } else {
+#pragma unroll
+            for (int j = 0; j < V; ++j) bv[s][j] = kok && nl + j < t.N ? row[nl + j] : 0.0f;
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fget(av, s), bv[s][j], acc[j], 0, 0, 0);
+    }
+    // register r of block j holds C'[4 g + r][n0 + V i + j]
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][4 * g + r][V * i + j] = acc[j][r];
+    __syncthreads();
+    // consecutive threads take consecutive addresses of C
+    for (int e = tid; e < 16 * NB; e += 64 * W) {
+      const int r = CT ? e % 16 : e / NB, n = CT ? e / 16 : e % NB;
+      float sum = red[0][r][n];
+#pragma unroll
+      for (int w = 1; w < W; ++w) sum += red[w][r][n];
+      if (r < t.M && n0 + n < t.N) {
+        float* cp = CT ? t.c + (n0 + n) * t.ldc + r : t.c + r * t.ldc + n0 + n;
+        *cp = epilogue(sum, t.alpha, t.beta, cp);
+      }
+    }
+    __syncthreads();  // red is rewritten by the next tile
+  }
+}
+
+// Columns of C' per lane: the widest (1, 2, 4) that still leaves min_tiles
+// tiles; few columns (B' read along k, one 128-bit read per column) stay at
+// two at most.  Measured on MI355X (TB/s at 8192 x 8192: 16 rows 4.2-4.6,
+// 8 columns 5.7, against 2.4-2.6 on the vector ALUs).
+int thin_width(int64_t n, bool few_cols) {
+  const int64_t min_tiles = few_cols ? 256 : 512;
+  int v = 1;
+  while (v < (few_cols ? 2 : 4) && ceil_div(n, 16 * 2 * v) >= min_tiles) v *= 2;
+  return v;
+}
+
+// The vector-ALU kernels keep one to four rows (columns) of problems below
+// 8192 columns (rows), where they measured faster (1 x 4096 x 4096: 4.2
+// against 3.8 TB/s).
+bool thin_on_valu(int64_t thin, int64_t wide) { return thin <= 4 && wide < 8192; }
+
+template <int V, bool TA, bool TB, bool CT>
+hipError_t launch_thin_t(const Thin& t, hipStream_t s) {
+  const int64_t ntiles = ceil_div(t.N, 16 * V);
+  const int64_t cap = kMaxWorkItems / (64 * kThinWaves);
+  const int64_t grid = ntiles < cap ? ntiles : cap;
+  hipLaunchKernelGGL((k_thin_mfma<V, TA, TB, CT>), dim3(static_cast<unsigned>(grid)),
+                     dim3(64 * kThinWaves), 0, s, t, ntiles);
+  return hipGetLastError();
+}
+
+template <bool TA, bool TB, bool CT>
+hipError_t launch_thin_op(const Thin& t, hipStream_t s) {
+  switch (thin_width(t.N, CT)) {
+    case 1: return launch_thin_t<1, TA, TB, CT>(t, s);
+    case 2: return launch_thin_t<2, TA, TB, CT>(t, s);
+    default: return launch_thin_t<4, TA, TB, CT>(t, s);
+  }
+}
+
+template <bool CT>
+hipError_t launch_thin(const Thin& t, bool ta, bool tb, hipStream_t s) {
+  if (ta && tb) return launch_thin_op<true, true, CT>(t, s);
+  if (ta) return launch_thin_op<true, false, CT>(t, s);
+  if (tb) return launch_thin_op<false, true, CT>(t, s);
+  return launch_thin_op<false, false, CT>(t, s);
+}
+
+Geometry thin_geometry(int64_t thin_rows, int64_t n, int K, bool few_cols) {
+  const int v = thin_width(n, few_cols);
+  Geometry g;
+  g.threads = 64 * kThinWaves;
+  g.tiles = ceil_div(n, 16 * v);
+  const int64_t cap = kMaxWorkItems / g.threads;
+  g.workgroups = g.tiles < cap ? g.tiles : cap;
+  g.k_steps = ceil_div(K, 16 * kThinWaves);
+  g.tile_m = few_cols ? 16 * v : 16;
+  g.tile_n = few_cols ? 16 : 16 * v;
+  (void)thin_rows;
+  return g;
+}
+
 // Smallest instantiated width (1, 2, 4, 8, 16) that covers n.
 int padded_width(int n) {
   int w = 1;
@@ -238,6 +407,7 @@ hipError_t launch_cols_t(const Problem& p, hipStream_t s) {
 }  // namespace
 
 Geometry few_rows_geometry(int M, int N, int K) {
+  if (!thin_on_valu(M, N)) return thin_geometry(M, N, K, false);
   const int rp = padded_width(M);
   const int threads = rp <= 4 ? FewRows<4>::THREADS : FewRows<16>::THREADS;
   Geometry g = make_geometry(rp, N, K, rp, 16, rp <= 4 ? FewRows<4>::KSWEEP
@@ -258,6 +428,10 @@ hipError_t launch_rows_op(const Problem& p, hipStream_t s) {
 }
 
 hipError_t launch_few_rows(const Problem& p, hipStream_t s) {
+  if (!thin_on_valu(p.M, p.N)) {
+    const Thin t{p.M, p.N, p.K, p.alpha, p.beta, p.A, p.lda, p.B, p.ldb, p.C, p.ldc};
+    return launch_thin<false>(t, p.trans_a, p.trans_b, s);
+  }
   if (p.trans_a && p.trans_b) return launch_rows_op<true, true>(p, s);
   if (p.trans_a) return launch_rows_op<true, false>(p, s);
   if (p.trans_b) return launch_rows_op<false, true>(p, s);
@@ -265,6 +439,7 @@ hipError_t launch_few_rows(const Problem& p, hipStream_t s) {
 }
 
 Geometry few_cols_geometry(int M, int N, int K) {
+  if (!thin_on_valu(N, M)) return thin_geometry(N, M, K, true);
   const int wp = padded_width(N);
   return make_geometry(M, wp, K, kRowsPerBlock, wp, wp <= 8 ? 2048 : 1024, kColThreads);
 }
@@ -282,7 +457,13 @@ hipError_t launch_cols_op(const Problem& p, hipStream_t s) {
 }
 
 hipError_t launch_few_cols(const Problem& p, hipStream_t s) {
-  if (p.trans_a) return hipErrorInvalidValue;  // the dispatcher never sends these
+  // C^T = B^T A^T: A' = B^T (row-major B is B^T stored transposed), B' = A^T
+  // (row-major A is A^T stored transposed), C' = C^T stored transposed.
+  // The vector-ALU form reads A by rows: not for a transposed A.
+  if (p.trans_a || !thin_on_valu(p.N, p.M)) {
+    const Thin t{p.N, p.M, p.K, p.alpha, p.beta, p.B, p.ldb, p.A, p.lda, p.C, p.ldc};
+    return launch_thin<true>(t, !p.trans_b, !p.trans_a, s);
+  }
   return p.trans_b ? launch_cols_op<true>(p, s) : launch_cols_op<false>(p, s);
 }
 

@@ -124,8 +124,13 @@ def test_launch_shapes():
     # N <= 16 (one block per 16 rows)
     shape = sgemm.hip_sgemm_launch_shape(10, 1, 4097, 4097)
     assert (shape["workgroups"], shape["threads"], shape["tile_n"]) == (257, 1024, 16)
+    # (16 rows: the matrix-core form, 16 wavefronts per block of 16 columns)
     shape = sgemm.hip_sgemm_launch_shape(10, 16, 4096, 64)
-    assert (shape["workgroups"], shape["threads"], shape["tile_m"]) == (256, 512, 16)
+    assert (shape["workgroups"], shape["threads"], shape["tile_m"], shape["tile_n"]) == (256, 1024, 16, 16)
+    shape = sgemm.hip_sgemm_launch_shape(10, 16, 32768, 64)   # 64 columns per block
+    assert (shape["workgroups"], shape["tile_n"]) == (512, 64)
+    shape = sgemm.hip_sgemm_launch_shape(10, 8192, 8, 64)     # few columns: 32 rows per block
+    assert (shape["workgroups"], shape["threads"], shape["tile_m"], shape["tile_n"]) == (256, 1024, 32, 16)
     shape = sgemm.hip_sgemm_launch_shape(10, 4096, 3, 4097)
     assert (shape["workgroups"], shape["threads"], shape["tile_m"], shape["tile_n"]) == (256, 1024, 16, 4)
     assert sgemm.hip_sgemm_launch_shape(2, 4096, 4096, 4096)["threads"] == 1024

@@ -6,9 +6,10 @@ padded and misaligned storage and guard regions around C.
 The tile kernels stage either orientation into the same k-major LDS layout,
 and the thin kernels keep the same per-lane k order, so wherever the plan is
 the same for every orientation the transposed calls must reproduce the
-untransposed result bit for bit.  (With A stored transposed the
-few-columns kernel is not used -- its rows would be strided columns -- so
-shapes with N <= 16 or a right fringe take other kernels there.)
+untransposed result bit for bit.  (The vector-ALU few-columns kernel reads A
+by rows, so one to four columns with A stored transposed take the
+matrix-core thin form instead: those shapes differ between A's two
+orientations.)
 """
 
 from __future__ import annotations
@@ -53,9 +54,12 @@ def run_ex(op_a, op_b, A, B, C, alpha, beta, pads=(0, 0, 0), offs=(0, 0, 0)):
 SHAPES = [
     (5, 3001, 777, "few rows", True),
     (16, 1000, 333, "sixteen rows", True),
-    (1500, 7, 2003, "few columns (A^T: tiles)", False),
-    (2051, 2055, 300, "128x128 two-slice grid + fringe", False),
-    (4096 + 3, 4096 + 16, 40, "256x128 grid + fringe", False),
+    (1500, 7, 2003, "few columns", True),
+    (1500, 3, 2003, "three columns (A^T: matrix-core thin form)", False),
+    (2051, 2055, 300, "128x128 two-slice grid + fringe", True),
+    (4096 + 3, 4096 + 16, 40, "256x128 grid + fringe", True),
+    (8192, 8, 1000, "eight columns, two per lane", True),
+    (16, 16384, 777, "sixteen rows, two columns per lane", True),
     (2048, 2048, 100, "128x128 two-slice grid, K ragged", True),
     (4096, 4096, 36, "256x128 grid, K ragged", True),
     (1000, 1000, 300, "64x64 two-slice tiles, edges", True),
