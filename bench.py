@@ -68,7 +68,7 @@ def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_fp32_matrix_row_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
+        if name.endswith((".hip", ".h", ".inc")):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

@@ -12,7 +12,9 @@
 //   - a large problem whose M and N miss a multiple of the 256 x 128 (or
 //     128 x 128) tile by at most 16: whole tiles over the largest multiple,
 //     no per-element bounds logic (only the last K step masks when K is
-//     ragged), plus the thin kernels on the fringe.  At 4097^3 this replaces
+//     ragged), plus the thin kernels on the fringe.  Whole 256 x 128 tiles
+//     with row-major operands and K % 16 == 0 run l10_kloop.hip, the same
+//     tile with its K loop scheduled by hand.  At 4097^3 this replaces
 //     level 9's 2145 edge-checked 128 x 64 tiles by the 512 whole 256 x 128
 //     tiles of 4096^3 (exactly two per CU) and two one-element-wide strips;
 //   - a deep K over a small tile grid: split K (l10_splitk.hip);
@@ -122,14 +124,14 @@ hipError_t launch10(const Problem& p, hipStream_t s) {
   switch (d.plan) {
     case Plan::kFewRows: return launch_few_rows(p, s);
     case Plan::kFewCols: return launch_few_cols(p, s);
-    case Plan::kTiles: return launch_mfma(d.shape, p, s);
+    case Plan::kTiles: return launch_tiles(d.shape, p, s);
     case Plan::kSplitK: return launch_splitk(d.shape, d.k_split, p, s);
     case Plan::kTilesWithFringe: break;
   }
   Problem grid = p;
   grid.M = d.Mm;
   grid.N = d.Nm;
-  hipError_t e = launch_mfma(d.shape, grid, s);
+  hipError_t e = launch_tiles(d.shape, grid, s);
   if (e == hipSuccess && d.Nm < p.N) {
     // right fringe: rows [0, Mm), columns [Nm, N) (B's columns are its rows
     // when it is stored transposed)

@@ -130,7 +130,7 @@ int hip_sgemm_tile_split(int tile, int splits, int M, int N, int K, float alpha,
   if (K == 0 || alpha == 0.0f) return status_of(launch_scale(p, stream));
   const Shape shape = tile_shape(tile);
   const int64_t k_split = k_split_for(K, splits, shape_bk(shape));
-  if (k_split >= K) return status_of(launch_mfma(shape, p, stream));
+  if (k_split >= K) return status_of(launch_tiles(shape, p, stream));
   return status_of(launch_splitk(shape, k_split, p, stream));
 }
 

@@ -1,0 +1,120 @@
+"""Level 10's 256 x 128 whole-tile kernel with the K loop in assembly
+(l10_kloop.hip) through the C ABI: K step counts that exercise each path of
+the loop (one step, pairs only, pairs plus the odd step, long loops), a
+fringe around the whole-tile grid, padded and 4-byte-aligned storage,
+beta = 0 over NaN, integer data (bit-exact against the reference), the
+tile-forcing entry point on grids too small for the dispatch rule, and
+bit-identity with level 9's compiled loop on the same tile.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from dense_fp32_matrix_row_amd import inputs, sgemm
+from oracle import oracle
+from tests import gpu_harness as gh
+
+pytestmark = pytest.mark.gpu
+
+BOUND = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    sgemm.load()
+
+
+def _rows(M):
+    """Rows sampled for the reference: both ends of the first and last tile
+    row, rows of every wavefront row and lane group, the middle."""
+    return sorted({0, 1, 15, 16, 63, 64, 127, 128, 255, 256, M // 2, M // 2 + 77,
+                   M - 257, M - 256, M - 2, M - 1})
+
+
+# (M, N, K, what): all have at least 512 whole 256 x 128 tiles, so level 10
+# takes the assembly loop for the grid
+SHAPES = [
+    (4096, 4096, 16, "one K step (no pair)"),
+    (4096, 4096, 32, "one pair"),
+    (4096, 4096, 48, "pair + odd step"),
+    (4096, 4096, 272, "8 pairs + odd step"),
+    (8192, 2048, 1024, "64 K-step pairs, 8192 rows"),
+    (4096 + 5, 4096 + 9, 80, "grid + 5-row / 9-column fringe"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,what", SHAPES, ids=[s[3] for s in SHAPES])
+def test_kloop_matches_reference(M, N, K, what):
+    print(f"[kloop] {M}x{N}x{K}: {what}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 12000 + M + N + K)
+    rows = _rows(M)
+    for alpha, beta in [(0.5, 3.0), (1.0, 0.0)]:
+        out, st = gh.run(gh.Case(M, N, K, alpha, beta, A, B, C), 10)
+        assert st == 0, sgemm.hip_sgemm_status_string(st)
+        ref = oracle.oracle_sgemm(A[rows], B, C[rows], alpha, beta)
+        err = oracle.normalised_error(out[rows], ref, C[rows], alpha, beta, strict=True)
+        assert err <= BOUND, (alpha, beta, err)
+
+
+def test_kloop_padded_misaligned_nan_c():
+    """lda = K + 3, ldb = N + 5, ldc = N + 7 and bases 4, 8, 12 bytes past a
+    16-byte boundary: every 128-bit load and store is misaligned; beta = 0
+    with NaN in C (C must not be read)."""
+    M, N, K = 4096, 4096, 64
+    print(f"[kloop alignment] {M}x{N}x{K}", flush=True)
+    A, B, _ = inputs.make_abc(M, N, K, 12500)
+    nanC = np.full((M, N), np.nan, np.float32)
+    out, st = gh.run(gh.Case(M, N, K, -1.5, 0.0, A, B, nanC, K + 3, N + 5, N + 7, 1, 2, 3), 10)
+    assert st == 0 and np.all(np.isfinite(out))
+    rows = _rows(M)
+    ref = oracle.oracle_sgemm(A[rows], B, None, -1.5, 0.0)
+    assert oracle.normalised_error(out[rows], ref, None, -1.5, 0.0, strict=True) <= BOUND
+
+
+def test_kloop_integer_exact():
+    """Integer entries: every sum is exact in any order, so all of C must
+    equal the reference bit for bit (every tile, lane and register)."""
+    M, N, K = 4096, 4096, 48
+    print(f"[kloop integer] {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.integer_abc(M, N, K, seed=12600)
+    out, st = gh.run(gh.Case(M, N, K, 2.0, -1.0, A, B, C), 10)
+    assert st == 0
+    assert np.array_equal(out.astype(np.float64), oracle.oracle_sgemm(A, B, C, 2.0, -1.0).ref)
+
+
+@pytest.mark.parametrize("K", [48, 1040])
+def test_kloop_bit_identical_to_level9(K):
+    """Level 9 runs the same 256 x 128 tile with the compiled K loop: same
+    blocks, same operands per MFMA, same k order, so the same bits."""
+    M = N = 4096
+    print(f"[kloop vs level 9] {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 12700 + K)
+    res = gh.Resident(A, B, C)
+    l9, st9 = res.call(9, 0.5, 3.0)
+    l10, st10 = res.call(10, 0.5, 3.0)
+    again, st = res.call(10, 0.5, 3.0)
+    assert st9 == st10 == st == 0
+    assert np.array_equal(l9.view(np.uint32), l10.view(np.uint32))
+    assert np.array_equal(l10.view(np.uint32), again.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 128, 16), (512, 384, 144), (768, 256, 1008),
+                                   (256, 128, 40)])
+def test_tile_api_whole_tiles(M, N, K):
+    """hip_sgemm_tile_split(0, 1) takes the assembly loop on any whole-tile
+    grid with K % 16 == 0 (and the compiled tile otherwise, as for K = 40)."""
+    print(f"[kloop tile api] {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 12800 + M + K)
+
+    def call(*args):
+        return sgemm.hip_sgemm_tile_split(0, 1, *args)
+    out, st = gh.run(gh.Case(M, N, K, 0.5, 3.0, A, B, C), call)
+    assert st == 0
+    ref = oracle.oracle_sgemm(A, B, C, 0.5, 3.0)
+    assert oracle.normalised_error(out, ref, C, 0.5, 3.0, strict=True) <= BOUND
