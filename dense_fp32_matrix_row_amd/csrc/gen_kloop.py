@@ -9,6 +9,10 @@ analysis against cuBLAS) puts the last 15-20 % of an FP32 GEMM in exactly
 this instruction-level ordering, out of reach of C++; its double-buffering
 section gives the overlap this loop implements.
 
+Stage 0 is the first K % 16 k (a whole stage when K % 16 == 0), zero-padded,
+and is put into LDS buffer 0 by the kernel's C++ part; the loop starts by
+loading stage 1 at that offset, so every stage it loads is whole.
+
 Register map (the kernel pins these with asm operand constraints/clobbers):
   v[0:63]   accumulators: 16 blocks of 16 x 16 (block b = 4 i + j at
             v[4b : 4b+3], i = A block, j = B block)
@@ -109,8 +113,9 @@ def k_step(cur: int) -> list[str]:
 
 
 def program() -> list[str]:
-    prologue = [*LOADS, *ADVANCE, "s_waitcnt vmcnt(0)", *stage_stores(0), "s_waitcnt lgkmcnt(0)",
-                *LOADS, *ADVANCE, "s_barrier", *frag_reads(FE, 0, 0)]
+    # stage 0 (the ragged remainder of K, or a whole stage) is stored into
+    # buffer 0 by the kernel's C++ part just before this statement
+    prologue = ["s_waitcnt lgkmcnt(0)", *LOADS, *ADVANCE, "s_barrier", *frag_reads(FE, 0, 0)]
     pairs = ["s_cmp_eq_u32 %[pairs], 0", "s_cbranch_scc1 .Lkloop_odd_%=", ".Lkloop_pair_%=:",
              *k_step(0), *k_step(1),
              "s_sub_u32 %[pairs], %[pairs], 1", "s_cmp_lg_u32 %[pairs], 0",

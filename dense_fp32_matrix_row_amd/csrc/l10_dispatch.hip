@@ -13,8 +13,8 @@
 //     128 x 128) tile by at most 16: whole tiles over the largest multiple,
 //     no per-element bounds logic (only the last K step masks when K is
 //     ragged), plus the thin kernels on the fringe.  Whole 256 x 128 tiles
-//     with row-major operands and K % 16 == 0 run l10_kloop.hip, the same
-//     tile with its K loop scheduled by hand.  At 4097^3 this replaces
+//     with row-major operands run l10_kloop.hip, the same tile with its K
+//     loop scheduled by hand.  At 4097^3 this replaces
 //     level 9's 2145 edge-checked 128 x 64 tiles by the 512 whole 256 x 128
 //     tiles of 4096^3 (exactly two per CU) and two one-element-wide strips;
 //   - a deep K over a small tile grid: split K (l10_splitk.hip);

@@ -10,16 +10,19 @@
 // is the difference between level 9's compiled loop and this one on the
 // same tile (4096^3: 138.7 against 152 TFLOP/s on MI355X).
 //
+// The first stage holds the K % 16 leftover k (a whole stage when
+// K % 16 == 0), loaded with per-element bounds here in C++ and stored into
+// LDS buffer 0 before the loop; every stage the loop loads is then whole.
 // The loop reads A and B through buffer resources whose record counts end
-// at the last element the tile may use, so the loads a K loop issues past
-// its last stage (the prefetch of stages K/16 and K/16 + 1) read zeros or
-// elements of the same matrix, never beyond it; their values are stored
-// into the idle LDS buffer and not used.  Every stage inside K is whole,
-// so the kernel takes K % 16 == 0 only (the template kernel handles ragged
-// K), row-major A and B, and every buffer offset below 2^31.
+// at the last element the tile may use, so the loads it issues past the
+// last stage (two stages of prefetch) read zeros or elements of the same
+// matrix, never beyond it; they land in the idle LDS buffer unused.  The
+// kernel takes row-major A and B and byte offsets below 2^31.
 //
-// Results are bit-identical to level 9's tile: the same blocks, the same
-// operand values per MFMA and the same k order per accumulator.
+// With K % 16 == 0 the results are bit-identical to level 9's tile (the
+// same blocks, the same operand values per MFMA, the same k order per
+// accumulator); with a ragged K, level 9 takes the partial stage last and
+// this kernel first, so the k order differs.
 #include "l10_kloop.inc"
 #include "sgemm_internal.h"
 
@@ -79,9 +82,28 @@ __global__ __launch_bounds__(kThreads) void k_kloop(Problem p, int64_t tiles_m, 
   const uint32_t rA = base + static_cast<uint32_t>((kg * kBM + wm * 64 + 4 * lrow) * 4);
   const uint32_t rB = base + 2 * kAStage + static_cast<uint32_t>((kg * kBN + wn * 64 + 4 * lrow) * 4);
   const uint32_t stepB = static_cast<uint32_t>(kBK * ldb * 4);
-  uint32_t sA = 0, sB = 0;
-  uint32_t pairs = static_cast<uint32_t>(p.K / (2 * kBK));
-  const uint32_t odd = static_cast<uint32_t>((p.K / kBK) % 2);
+  // stage 0: k < k0 (the same thread-to-element map as the loop's stages)
+  const int k0 = p.K % kBK ? p.K % kBK : kBK;
+  {
+    float* const lds = reinterpret_cast<float*>(smem);
+    const float* const arow = p.A + (row0 + tid / 4) * lda;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4 v = load4(arow + h * 128 * lda, 4 * (tid % 4), k0, true);
+      float* const dst = lds + (tid % 4) * kAGroup + tid / 4 + 128 * h;
+      dst[0] = v.x;
+      dst[kBM] = v.y;
+      dst[2 * kBM] = v.z;
+      dst[3 * kBM] = v.w;
+    }
+    const int kb = tid / 32;
+    const float4 bv = load4(p.B + (kb < k0 ? kb : 0) * ldb + col0, 4 * (tid % 32), kBN, kb < k0);
+    *reinterpret_cast<float4*>(lds + 2 * kAStage / 4 + tid * 4) = bv;
+  }
+  uint32_t sA = static_cast<uint32_t>(k0 * 4), sB = static_cast<uint32_t>(k0 * ldb * 4);
+  const int stages = (p.K + kBK - 1) / kBK;
+  uint32_t pairs = static_cast<uint32_t>(stages / 2);
+  const uint32_t odd = static_cast<uint32_t>(stages % 2);
   floatx16 a0 = {}, a1 = {}, a2 = {}, a3 = {};
   asm volatile(SGEMM_KLOOP_ASM
                : "+{v[0:15]}"(a0), "+{v[16:31]}"(a1), "+{v[32:47]}"(a2), "+{v[48:63]}"(a3),
@@ -126,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void k_kloop(Problem p, int64_t tiles_m, 
 
 bool kloop_fits(const Problem& p) {
   if (p.trans_a || p.trans_b || p.M <= 0 || p.N <= 0) return false;
-  if (p.M % kBM || p.N % kBN || p.K < kBK || p.K % kBK) return false;
+  if (p.M % kBM || p.N % kBN || p.K < 1) return false;
   // largest byte offset of a load (record counts, plus the two stages the
   // loop prefetches past K) stays below 2^31
   const int64_t lim = int64_t(1) << 31;

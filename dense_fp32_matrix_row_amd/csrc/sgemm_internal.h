@@ -162,8 +162,8 @@ TileDims shape_dims(Shape shape);
 Geometry mfma_geometry(Shape shape, int M, int N, int K);
 hipError_t launch_mfma(Shape shape, const Problem& p, hipStream_t s);
 // Level 10's 256 x 128 whole-tile kernel with its K loop in assembly
-// (l10_kloop.hip): row-major operands, M % 256 == N % 128 == K % 16 == 0,
-// buffer offsets below 2^31.  launch_tiles runs it where it fits and the
+// (l10_kloop.hip): row-major operands, M % 256 == N % 128 == 0, buffer
+// offsets below 2^31.  launch_tiles runs it where it fits and the
 // shape is Huge, else the template kernel.
 bool kloop_fits(const Problem& p);
 hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s);

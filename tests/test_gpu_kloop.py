@@ -1,10 +1,11 @@
 """Level 10's 256 x 128 whole-tile kernel with the K loop in assembly
 (l10_kloop.hip) through the C ABI: K step counts that exercise each path of
 the loop (one step, pairs only, pairs plus the odd step, long loops), a
-fringe around the whole-tile grid, padded and 4-byte-aligned storage,
-beta = 0 over NaN, integer data (bit-exact against the reference), the
-tile-forcing entry point on grids too small for the dispatch rule, and
-bit-identity with level 9's compiled loop on the same tile.
+ragged first stage (K % 16 != 0), a fringe around the whole-tile grid,
+padded and 4-byte-aligned storage, beta = 0 over NaN, integer data
+(bit-exact against the reference), the tile-forcing entry point on grids
+too small for the dispatch rule, and bit-identity with level 9's compiled
+loop on the same tile when K % 16 == 0.
 """
 
 from __future__ import annotations
@@ -46,6 +47,10 @@ SHAPES = [
     (4096, 4096, 272, "8 pairs + odd step"),
     (8192, 2048, 1024, "64 K-step pairs, 8192 rows"),
     (4096 + 5, 4096 + 9, 80, "grid + 5-row / 9-column fringe"),
+    (4096, 4096, 5, "K = 5: one ragged stage"),
+    (4096, 4096, 21, "ragged stage + one whole stage"),
+    (4096, 4096, 1001, "ragged stage (9) + 62 whole stages"),
+    (4096 + 1, 4096 + 1, 4097, "4097^3: ragged stage (1) + 256 whole stages, fringe"),
 ]
 
 
@@ -105,10 +110,10 @@ def test_kloop_bit_identical_to_level9(K):
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 128, 16), (512, 384, 144), (768, 256, 1008),
-                                   (256, 128, 40)])
+                                   (256, 128, 40), (300, 128, 40)])
 def test_tile_api_whole_tiles(M, N, K):
     """hip_sgemm_tile_split(0, 1) takes the assembly loop on any whole-tile
-    grid with K % 16 == 0 (and the compiled tile otherwise, as for K = 40)."""
+    grid (and the compiled tile otherwise, as for M = 300)."""
     print(f"[kloop tile api] {M}x{N}x{K}", flush=True)
     A, B, C = inputs.make_abc(M, N, K, 12800 + M + K)
 

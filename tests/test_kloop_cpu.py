@@ -91,6 +91,21 @@ def _stage_stores(buf):
     return written
 
 
+def test_first_stage_map_matches_the_loop():
+    """Stage 0 is stored by the kernel's C++ part (A word (tid % 4) * A_GROUP
+    + tid / 4 + 128 h + 256 c, B float4 at word 4 tid of the B region, both
+    as in l10_kloop.hip) into buffer 0: it must put every element where the
+    loop's own stores into buffer 0 put it."""
+    written = _stage_stores(0)
+    for tid in range(512):
+        for h in range(2):
+            for c in range(4):
+                word = (tid % 4) * G.A_GROUP + tid // 4 + 128 * h + G.BM * c
+                assert written[4 * word] == ("A", tid // 4 + 128 * h, 4 * (tid % 4) + c)
+        for c in range(4):
+            assert written[A_END + 16 * tid + 4 * c] == ("B", tid // 32, 4 * (tid % 32) + c)
+
+
 @pytest.mark.parametrize("buf", [0, 1])
 def test_fragment_reads_find_their_operands(buf):
     written = _stage_stores(buf)
@@ -116,7 +131,7 @@ def test_fragment_reads_find_their_operands(buf):
 def test_loop_structure():
     prog = G.program()
     mfmas = [l for l in prog if l.startswith("v_mfma")]
-    # prologue reads no MFMA; a pair of K steps and the odd step: 3 x 64
+    # the prologue issues no MFMA; a pair of K steps and the odd step: 3 x 64
     assert len(mfmas) == 3 * 64
     # every accumulator block gets exactly four MFMAs per K step, one per step s
     for b in range(16):
