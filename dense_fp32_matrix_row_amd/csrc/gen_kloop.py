@@ -1,36 +1,45 @@
-"""Write l10_kloop.inc: the K loop of the 256 x 128 whole-tile kernel
+"""Write l10_kloop.inc: the K loops of level 10's whole-tile kernels
 (l10_kloop.hip) as GCN assembly text for gfx950.
 
-The kernel's C++ part sets up addresses and runs the epilogue; this loop is
-emitted instruction by instruction so that the order of the matrix, LDS and
-global-memory instructions is the one chosen here rather than the
-compiler's.  [CP04] (section on boundary conditions and limits, the gap
-analysis against cuBLAS) puts the last 15-20 % of an FP32 GEMM in exactly
-this instruction-level ordering, out of reach of C++; its double-buffering
-section gives the overlap this loop implements.
+The kernels' C++ part sets up addresses, stores the first stage and runs
+the epilogue; each loop is emitted instruction by instruction so that the
+order of the matrix, LDS and global-memory instructions is the one chosen
+here rather than the compiler's.  [CP04] (section on boundary conditions
+and limits, the gap analysis against cuBLAS) puts the last 15-20 % of an
+FP32 GEMM in exactly this instruction-level ordering, out of reach of C++;
+its double-buffering section gives the overlap these loops implement.
+
+Two tiles, both of 64 x 64 wavefront tiles (4 x 4 blocks of
+v_mfma_f32_16x16x4_f32) over a 128-column block tile with 16-deep stages:
+  256 x 128, eight wavefronts (4 x 2), two blocks per CU: one stage of
+            global prefetch (the other block's wavefronts cover the wait);
+  128 x 128, four wavefronts (2 x 2), one wavefront per SIMD where one
+            block runs per CU: two stages of global prefetch in two
+            register sets.
 
 Stage 0 is the first K % 16 k (a whole stage when K % 16 == 0), zero-padded,
 and is put into LDS buffer 0 by the kernel's C++ part; the loop starts by
 loading stage 1 at that offset, so every stage it loads is whole.
 
-Register map (the kernel pins these with asm operand constraints/clobbers):
+Register map (the kernels pin these with asm operand constraints/clobbers):
   v[0:63]   accumulators: 16 blocks of 16 x 16 (block b = 4 i + j at
             v[4b : 4b+3], i = A block, j = B block)
   v[64:71]  fragment set E: A operands of blocks i = 0..3 (v64..v67) and B
             operands of blocks j = 0..3 (v68..v71) for one MFMA step
   v[72:79]  fragment set O, the same for the alternate step
-  v[80:91]  the next stage's global loads (two A float4s, one B float4)
+  v[80:..]  global-load staging: per set, the A float4s then the B float4s
+            of one stage (12 words for 256 x 128, 16 for 128 x 128)
 
-One K step (16 deep) per wavefront: four MFMA steps s = 0..3 of 16
-v_mfma_f32_16x16x4_f32 each, step s reading k = 4 s + lane / 16.  Step s
-runs on one fragment set while the other set receives step s + 1 (128-bit
-LDS reads issued after the step's first MFMA); the stage after next is
-stored into the free LDS buffer during step 0 and its successor's global
-loads go out during step 1; the barrier sits halfway through step 3, after
-which step 0 of the next stage is read from the other buffer, so the LDS
-latency after a barrier hides under the remaining eight MFMAs.  Loop
-bookkeeping is scalar (buffer offsets in SGPRs, LDS offsets immediate), so
-the loop issues no vector-ALU instruction besides the MFMAs.
+One K step (16 deep) per wavefront: four MFMA steps s = 0..3 of 16 MFMAs,
+step s reading k = 4 s + lane / 16.  Step s runs on one fragment set while
+the other set receives step s + 1 (128-bit LDS reads issued after the
+step's first MFMA); the next stage is stored from its staging set into the
+free LDS buffer during step 0 and the same set is reloaded (with the stage
+one or two further on) during step 1; the barrier sits halfway through
+step 3, after which step 0 of the next stage is read from the other buffer,
+so the LDS latency after a barrier hides under the remaining eight MFMAs.
+Loop bookkeeping is scalar (buffer offsets in SGPRs, LDS offsets
+immediate), so the loop issues no vector-ALU instruction besides the MFMAs.
 
 Run as a script to rewrite l10_kloop.inc; tests check that the committed
 file equals what this script emits.
@@ -40,99 +49,159 @@ from __future__ import annotations
 
 import os
 
-BM, BN, BK = 256, 128, 16
-A_GROUP = 4 * BM + 8           # floats per four-k group of an A stage (8 words of pad)
-A_STAGE = 16640                # bytes per A stage: 4 groups, rounded up to 65 * 256
+BN, BK = 128, 16
 B_STAGE = BK * BN * 4          # bytes per B stage
-assert 4 * A_GROUP * 4 <= A_STAGE and A_STAGE % 256 == 0
 FE, FO = 64, 72                # fragment sets
+STAGING = 80                   # first staging register
 
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "l10_kloop.inc")
 
 
-def mfma(b: int, fs: int) -> str:
-    i, j = divmod(b, 4)
-    return f"v_mfma_f32_16x16x4_f32 v[{4*b}:{4*b+3}], v{fs+i}, v{fs+4+j}, v[{4*b}:{4*b+3}]"
+class Tile:
+    """One block tile: BM rows, WAVES_M x 2 wavefronts, DEPTH staging sets."""
+
+    STEPS = 4                                         # MFMA steps per stage
+
+    def __init__(self, bm: int, waves_m: int, depth: int):
+        self.BM, self.WAVES_M, self.DEPTH = bm, waves_m, depth
+        self.THREADS = 64 * 2 * waves_m
+        self.A_GROUP = 4 * bm + 8                     # floats per four-k group (8 words of pad)
+        self.A_STAGE = -(-4 * self.A_GROUP * 4 // 256) * 256   # bytes, a whole number of 256
+        self.A_LOADS = bm * BK // 4 // self.THREADS   # A float4s per thread per stage
+        self.B_LOADS = BK * BN // 4 // self.THREADS   # B float4s per thread per stage
+        self.SET = 4 * (self.A_LOADS + self.B_LOADS)  # staging words per set
+        self.LDS = 2 * self.A_STAGE + 2 * B_STAGE
+        assert self.A_LOADS * self.THREADS * 4 == bm * BK and self.B_LOADS * self.THREADS * 4 == BK * BN
+        assert bm % 64 == 0 and self.THREADS % 256 == 0
+        assert STAGING + depth * self.SET <= 128
+
+    @property
+    def name(self) -> str:
+        return f"{self.BM}"
+
+    def last_vgpr(self) -> int:
+        return STAGING + self.DEPTH * self.SET - 1
+
+    # -- instruction builders ------------------------------------------------
+    def mfma(self, b: int, fs: int) -> str:
+        i, j = divmod(b, 4)
+        return f"v_mfma_f32_16x16x4_f32 v[{4*b}:{4*b+3}], v{fs+i}, v{fs+4+j}, v[{4*b}:{4*b+3}]"
+
+    def frag_reads(self, fs: int, s: int, buf: int) -> list[str]:
+        """MFMA step s of LDS buffer buf into fragment set fs."""
+        return [f"ds_read_b128 v[{fs}:{fs+3}], %[rA] offset:{s * self.A_GROUP * 4 + buf * self.A_STAGE}",
+                f"ds_read_b128 v[{fs+4}:{fs+7}], %[rB] offset:{s * 4 * BN * 4 + buf * B_STAGE}"]
+
+    def set_base(self, st: int) -> int:
+        return STAGING + st * self.SET
+
+    def loads(self, st: int) -> list[str]:
+        """One stage into staging set st (A float4 h: row tid/4 + h THREADS/4;
+        B float4 h: k-row tid/32 + h THREADS/32), then advance the offsets."""
+        r = self.set_base(st)
+        out = [f"buffer_load_dwordx4 v[{r + 4*h}:{r + 4*h + 3}], %[oA{h}], %[rsA], %[sA] offen"
+               for h in range(self.A_LOADS)]
+        rb = r + 4 * self.A_LOADS
+        out += [f"buffer_load_dwordx4 v[{rb + 4*h}:{rb + 4*h + 3}], %[oB{h}], %[rsB], %[sB] offen"
+                for h in range(self.B_LOADS)]
+        return out
+
+    ADVANCE = ["s_add_u32 %[sA], %[sA], 64", "s_add_u32 %[sB], %[sB], %[stepB]"]
+
+    def stage_stores(self, st: int, buf: int) -> list[str]:
+        """Staging set st into LDS buffer buf: each A float4 holds k = 4 q ..
+        4 q + 3 of one row and goes to four k-rows of group q (BM floats
+        apart, in 256-byte units), its h-th copy THREADS / 4 rows further;
+        each B float4 is one 16-byte piece of a k-row."""
+        r, u = self.set_base(st), buf * (self.A_STAGE // 256)
+        step = self.BM // 64          # 256-byte units between k-rows of a group
+        hrow = self.THREADS // 256    # 256-byte units between the A float4s' rows
+        out = []
+        for h in range(self.A_LOADS):
+            for c0, c1 in ((0, 1), (2, 3)):
+                out.append(f"ds_write2st64_b32 %[wA], v{r + 4*h + c0}, v{r + 4*h + c1} "
+                           f"offset0:{u + c0 * step + h * hrow} offset1:{u + c1 * step + h * hrow}")
+        rb = r + 4 * self.A_LOADS
+        for h in range(self.B_LOADS):
+            out.append(f"ds_write_b128 %[wB], v[{rb + 4*h}:{rb + 4*h + 3}] "
+                       f"offset:{buf * B_STAGE + h * (self.THREADS // 32) * BN * 4}")
+        return out
+
+    # -- the loop ------------------------------------------------------------
+    def k_step(self, cur: int) -> list[str]:
+        """One K step on LDS buffer cur (stage n with n % 2 == cur); on entry
+        set E is being read with MFMA step 0 of stage n and stage n + 1 is
+        in flight in staging set (n + 1) % DEPTH (with DEPTH 2, stage n + 2
+        in the other set behind it)."""
+        nxt = 1 - cur
+        st = nxt % self.DEPTH
+        per_stage = self.A_LOADS + self.B_LOADS
+        sets = (FE, FO)
+        stores = self.stage_stores(st, nxt)
+        loads = self.loads(st)
+        assert len(stores) <= 12 and len(loads) + 1 < 8
+        out = []
+        for ss in range(self.STEPS):
+            fs, fn = sets[ss % 2], sets[(ss + 1) % 2]
+            mf = [self.mfma(b, fs) for b in range(16)]
+            # work placed after MFMA i of this step
+            extra: dict[int, list[str]] = {}
+            if ss == 0:
+                # stage n + 1 complete (its set's loads are the older ones in
+                # flight), then stored into the free buffer
+                extra.setdefault(3, []).append(f"s_waitcnt vmcnt({per_stage * (self.DEPTH - 1)})")
+                for i, ins in enumerate(stores):
+                    extra.setdefault(4 + i, []).append(ins)
+            if ss == 1:
+                # the stores have completed (lgkmcnt(0) at this step's start),
+                # so the staging set may take stage n + 1 + DEPTH
+                for i, ins in enumerate(loads):
+                    extra.setdefault(1 + i, []).append(ins)
+                extra.setdefault(len(loads) + 1, []).extend(self.ADVANCE)
+            out.append("s_waitcnt lgkmcnt(0)")
+            last = ss == self.STEPS - 1
+            for b in range(16):
+                if last and b == 8:
+                    # every wavefront's reads of this buffer and stores of the
+                    # next are complete here (lgkmcnt(0) at the step's start)
+                    out += ["s_barrier", *self.frag_reads(fn, 0, nxt)]
+                out.append(mf[b])
+                if not last and b == 0:
+                    out += self.frag_reads(fn, ss + 1, cur)
+                out += extra.get(b, [])
+        return out
+
+    def program(self) -> list[str]:
+        # stage 0 was stored into buffer 0 by the kernel's C++ part just
+        # before this statement; stages 1 .. DEPTH go into sets 1 % DEPTH ..
+        prologue = ["s_waitcnt lgkmcnt(0)"]
+        for j in range(1, self.DEPTH + 1):
+            prologue += [*self.loads(j % self.DEPTH), *self.ADVANCE]
+        prologue += ["s_barrier", *self.frag_reads(FE, 0, 0)]
+        pairs = ["s_cmp_eq_u32 %[pairs], 0", "s_cbranch_scc1 .Lkloop_odd_%=", ".Lkloop_pair_%=:",
+                 *self.k_step(0), *self.k_step(1),
+                 "s_sub_u32 %[pairs], %[pairs], 1", "s_cmp_lg_u32 %[pairs], 0",
+                 "s_cbranch_scc1 .Lkloop_pair_%="]
+        odd = [".Lkloop_odd_%=:", "s_cmp_eq_u32 %[odd], 0", "s_cbranch_scc1 .Lkloop_end_%=",
+               *self.k_step(0), ".Lkloop_end_%=:"]
+        # drain every load (the staging and fragment registers are free after
+        # the asm statement) and give the last MFMAs' results the wait states
+        # a vector read of them needs
+        tail = ["s_waitcnt vmcnt(0) lgkmcnt(0)", "s_nop 7", "s_nop 7"]
+        return prologue + pairs + odd + tail
 
 
-def frag_reads(fs: int, s: int, buf: int) -> list[str]:
-    """MFMA step s of LDS buffer buf into fragment set fs."""
-    return [f"ds_read_b128 v[{fs}:{fs+3}], %[rA] offset:{s * A_GROUP * 4 + buf * A_STAGE}",
-            f"ds_read_b128 v[{fs+4}:{fs+7}], %[rB] offset:{s * 2048 + buf * B_STAGE}"]
-
-
-def stage_stores(buf: int) -> list[str]:
-    """v[80:91] into LDS buffer buf: each A float4 holds k = 4 q .. 4 q + 3 of
-    one row and goes to four rows of group q (256 floats = 4 * 256 bytes
-    apart, st64 units); the second A float4 is 128 rows (2 units) further;
-    the B float4 is one 16-byte piece of a k-row."""
-    u = buf * (A_STAGE // 256)
-    return [f"ds_write2st64_b32 %[wA], v80, v81 offset0:{u + 0} offset1:{u + 4}",
-            f"ds_write2st64_b32 %[wA], v82, v83 offset0:{u + 8} offset1:{u + 12}",
-            f"ds_write2st64_b32 %[wA], v84, v85 offset0:{u + 2} offset1:{u + 6}",
-            f"ds_write2st64_b32 %[wA], v86, v87 offset0:{u + 10} offset1:{u + 14}",
-            f"ds_write_b128 %[wB], v[88:91] offset:{buf * B_STAGE}"]
-
-
-LOADS = ["buffer_load_dwordx4 v[80:83], %[oA0], %[rsA], %[sA] offen",
-         "buffer_load_dwordx4 v[84:87], %[oA1], %[rsA], %[sA] offen",
-         "buffer_load_dwordx4 v[88:91], %[oB], %[rsB], %[sB] offen"]
-ADVANCE = ["s_add_u32 %[sA], %[sA], 64", "s_add_u32 %[sB], %[sB], %[stepB]"]
-
-
-def k_step(cur: int) -> list[str]:
-    """One K step on LDS buffer cur; on entry set E is being read with step 0
-    of this stage and v[80:91] are loading the next stage."""
-    nxt = 1 - cur
-    out = ["s_waitcnt lgkmcnt(0)", mfma(0, FE), *frag_reads(FO, 1, cur)]
-    out += [mfma(b, FE) for b in (1, 2, 3)]
-    out.append("s_waitcnt vmcnt(0)")
-    stores = stage_stores(nxt)
-    for b in range(4, 16):
-        out.append(mfma(b, FE))
-        if b < 4 + len(stores):
-            out.append(stores[b - 4])
-    # step 1 (set O); the stores above have completed once this wait is over,
-    # so v[80:91] may take the stage after next
-    out += ["s_waitcnt lgkmcnt(0)", mfma(0, FO), *frag_reads(FE, 2, cur)]
-    for b in range(1, 16):
-        out.append(mfma(b, FO))
-        if b <= len(LOADS):
-            out.append(LOADS[b - 1])
-        if b == len(LOADS) + 1:
-            out += ADVANCE
-    # step 2 (set E)
-    out += ["s_waitcnt lgkmcnt(0)", mfma(0, FE), *frag_reads(FO, 3, cur)]
-    out += [mfma(b, FE) for b in range(1, 16)]
-    # step 3 (set O): every wavefront's reads of this buffer and stores of
-    # the next are complete at the barrier (lgkmcnt(0) before it)
-    out += ["s_waitcnt lgkmcnt(0)"] + [mfma(b, FO) for b in range(8)]
-    out += ["s_barrier", *frag_reads(FE, 0, nxt)]
-    out += [mfma(b, FO) for b in range(8, 16)]
-    return out
-
-
-def program() -> list[str]:
-    # stage 0 (the ragged remainder of K, or a whole stage) is stored into
-    # buffer 0 by the kernel's C++ part just before this statement
-    prologue = ["s_waitcnt lgkmcnt(0)", *LOADS, *ADVANCE, "s_barrier", *frag_reads(FE, 0, 0)]
-    pairs = ["s_cmp_eq_u32 %[pairs], 0", "s_cbranch_scc1 .Lkloop_odd_%=", ".Lkloop_pair_%=:",
-             *k_step(0), *k_step(1),
-             "s_sub_u32 %[pairs], %[pairs], 1", "s_cmp_lg_u32 %[pairs], 0",
-             "s_cbranch_scc1 .Lkloop_pair_%="]
-    odd = [".Lkloop_odd_%=:", "s_cmp_eq_u32 %[odd], 0", "s_cbranch_scc1 .Lkloop_end_%=",
-           *k_step(0), ".Lkloop_end_%=:"]
-    # drain every load (v[64:91] are free after the asm statement) and give
-    # the last MFMAs' results the wait states a vector read of them needs
-    tail = ["s_waitcnt vmcnt(0) lgkmcnt(0)", "s_nop 7", "s_nop 7"]
-    return prologue + pairs + odd + tail
+TILES = [Tile(256, 4, 1), Tile(128, 2, 2)]
 
 
 def render() -> str:
-    lines = ["// Generated by gen_kloop.py (the K loop of l10_kloop.hip); do not edit.",
-             "#define SGEMM_KLOOP_ASM \\"]
-    lines += [f'  "{ins}\\n" \\' for ins in program()]
-    lines.append('  ""')
+    lines = ["// Generated by gen_kloop.py (the K loops of l10_kloop.hip); do not edit."]
+    for t in TILES:
+        lines.append(f"#define SGEMM_KLOOP_ASM_{t.name} \\")
+        lines += [f'  "{ins}\\n" \\' for ins in t.program()]
+        lines.append('  ""')
+        regs = ", ".join(f'"v{r}"' for r in range(FE, t.last_vgpr() + 1))
+        lines.append(f"#define SGEMM_KLOOP_CLOBBERS_{t.name} {regs}")
     return "\n".join(lines) + "\n"
 
 

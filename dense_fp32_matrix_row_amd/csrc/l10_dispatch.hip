@@ -50,7 +50,9 @@ double round_fill(int64_t tiles) {
 // The rules below were fitted to sweeps of every tile shape and slice count
 // on MI355X (dense_fp32_matrix_row_amd.autotune); the comments give the
 // measurements that decided them.
-Decomp decompose(int M, int N, int K) {
+// row_major: neither operand transposed (the assembly-loop kernels take
+// only that orientation).
+Decomp decompose(int M, int N, int K, bool row_major) {
   if (M <= kThin) return {Plan::kFewRows, Shape::kSmall, M, N, K};
   if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, M, N, K};
 
@@ -91,13 +93,16 @@ Decomp decompose(int M, int N, int K) {
   }
 
   // 3. 128 x 128 tiles (plus a fringe of <= 16) when they fill whole rounds
-  //    of CUs: with two K slices at about one round (2048^3: 115 against
-  //    110 unsliced), unsliced beyond (2048 x 4096: 124).
+  //    of CUs: row-major, the assembly-loop tile (2048^3: 123-130 against
+  //    105-122 for any compiled tile; 2048 x 4096: 142-146); transposed, the
+  //    compiled tile with two K slices at about one round (2048^3: 115
+  //    against 110 unsliced), unsliced beyond (2048 x 4096: 124).
   {
     const int mr = M % 128, nr = N % 128;
     const int64_t tiles = int64_t((M - mr) / 128) * ((N - nr) / 128);
     if (mr <= kThin && nr <= kThin && tiles >= kCUs && round_fill(tiles) >= 0.9) {
-      const Shape shape = tiles <= kCUs + kCUs / 8 ? Shape::kLargeSliced : Shape::kLarge;
+      const Shape shape =
+          !row_major && tiles <= kCUs + kCUs / 8 ? Shape::kLargeSliced : Shape::kLarge;
       return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, shape, M - mr, N - nr, K};
     }
   }
@@ -110,17 +115,17 @@ Decomp decompose(int M, int N, int K) {
 }
 
 Geometry geometry10(int M, int N, int K) {
-  const Decomp d = decompose(M, N, K);
+  const Decomp d = decompose(M, N, K, true);
   switch (d.plan) {
     case Plan::kFewRows: return few_rows_geometry(M, N, K);
     case Plan::kFewCols: return few_cols_geometry(M, N, K);
     case Plan::kSplitK: return mfma_split_geometry(d.shape, M, N, K, d.k_split);
-    default: return mfma_geometry(d.shape, d.Mm, d.Nm, K);
+    default: return tiles_geometry(d.shape, d.Mm, d.Nm, K);
   }
 }
 
 hipError_t launch10(const Problem& p, hipStream_t s) {
-  const Decomp d = decompose(p.M, p.N, p.K);
+  const Decomp d = decompose(p.M, p.N, p.K, !p.trans_a && !p.trans_b);
   switch (d.plan) {
     case Plan::kFewRows: return launch_few_rows(p, s);
     case Plan::kFewCols: return launch_few_cols(p, s);

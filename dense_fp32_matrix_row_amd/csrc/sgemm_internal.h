@@ -161,12 +161,13 @@ Shape pick_shape(int M, int N);  // level 9's own choice for a problem
 TileDims shape_dims(Shape shape);
 Geometry mfma_geometry(Shape shape, int M, int N, int K);
 hipError_t launch_mfma(Shape shape, const Problem& p, hipStream_t s);
-// Level 10's 256 x 128 whole-tile kernel with its K loop in assembly
-// (l10_kloop.hip): row-major operands, M % 256 == N % 128 == 0, buffer
-// offsets below 2^31.  launch_tiles runs it where it fits and the
-// shape is Huge, else the template kernel.
-bool kloop_fits(const Problem& p);
+// Level 10's whole-tile kernels with their K loop in assembly
+// (l10_kloop.hip), for the Huge (256 x 128) and Large (128 x 128) shapes:
+// row-major operands, M and N multiples of the tile, buffer offsets below
+// 2^31.  launch_tiles runs one where it fits, else the template kernel.
+bool kloop_fits(Shape shape, const Problem& p);
 hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s);
+Geometry tiles_geometry(Shape shape, int M, int N, int K);  // of launch_tiles, dense row-major
 // Split K over the same tiles: the K range is cut into slices of k_split
 // (a multiple of the shape's BK) and each (tile, slice) is one work item
 // that stores raw float32 sums into its slice's M x N plane of ws.

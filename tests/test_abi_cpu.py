@@ -101,12 +101,12 @@ def test_launch_shapes():
     assert shape == {"workgroups": 512, "threads": 512, "k_steps": 257, "tile_m": 256, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(10, 4096 + 16, 4096 + 16, 100)
     assert (shape["workgroups"], shape["tile_m"], shape["tile_n"]) == (512, 256, 128)
-    # ... or the 128 x 128 tile with two K slices (8 wavefronts) when there
-    # are about one round of them ...
+    # ... or the 128 x 128 tile (the assembly loop: 4 wavefronts, 16-deep
+    # stages) when they fill whole rounds of CUs ...
     shape = sgemm.hip_sgemm_launch_shape(10, 2051, 2055, 300)
-    assert shape == {"workgroups": 256, "threads": 512, "k_steps": 10, "tile_m": 128, "tile_n": 128}
+    assert shape == {"workgroups": 256, "threads": 256, "k_steps": 19, "tile_m": 128, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(10, 2048, 4096, 2048)
-    assert shape == {"workgroups": 512, "threads": 256, "k_steps": 64, "tile_m": 128, "tile_n": 128}
+    assert shape == {"workgroups": 512, "threads": 256, "k_steps": 128, "tile_m": 128, "tile_n": 128}
     # ... split K for a deep K over a small grid: 8 slices of 512 over the
     # 64 tiles of 128 x 128 at 1024 x 1024 x 4096, 4 slices of 2048 over the
     # 128 tiles of 256 x 128 at 2048 x 2048 x 8192 ...

@@ -109,17 +109,78 @@ def test_kloop_bit_identical_to_level9(K):
     assert np.array_equal(l10.view(np.uint32), again.view(np.uint32))
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 128, 16), (512, 384, 144), (768, 256, 1008),
-                                   (256, 128, 40), (300, 128, 40)])
-def test_tile_api_whole_tiles(M, N, K):
-    """hip_sgemm_tile_split(0, 1) takes the assembly loop on any whole-tile
-    grid (and the compiled tile otherwise, as for M = 300)."""
-    print(f"[kloop tile api] {M}x{N}x{K}", flush=True)
-    A, B, C = inputs.make_abc(M, N, K, 12800 + M + K)
+# tile ids of hip_sgemm_tile_split with an assembly loop: 0 = 256 x 128,
+# 1 = 128 x 128
+TILE_SHAPES = {0: (256, 128), 1: (128, 128)}
+
+
+@pytest.mark.parametrize("tile", sorted(TILE_SHAPES))
+@pytest.mark.parametrize("gm,gn,K", [(1, 1, 16), (2, 3, 144), (3, 2, 1008), (1, 1, 40), (2, 2, 7),
+                                     (2, 1, 33), (4, 4, 4097)])
+def test_tile_api_whole_tiles(tile, gm, gn, K):
+    """hip_sgemm_tile_split(tile, 1) takes the assembly loop on a grid of
+    gm x gn whole tiles: one stage, odd and even stage counts, ragged first
+    stages; an extra row outside whole tiles falls back to the compiled
+    tile (checked as well)."""
+    bm, bn = TILE_SHAPES[tile]
+    for M, N in ((gm * bm, gn * bn), (gm * bm + 1, gn * bn)):
+        print(f"[kloop tile api] tile {tile}: {M}x{N}x{K}", flush=True)
+        A, B, C = inputs.make_abc(M, N, K, 12800 + M + K + tile)
+
+        def call(*args):
+            return sgemm.hip_sgemm_tile_split(tile, 1, *args)
+        out, st = gh.run(gh.Case(M, N, K, 0.5, 3.0, A, B, C), call)
+        assert st == 0
+        ref = oracle.oracle_sgemm(A, B, C, 0.5, 3.0)
+        assert oracle.normalised_error(out, ref, C, 0.5, 3.0, strict=True) <= BOUND
+
+
+@pytest.mark.parametrize("tile", sorted(TILE_SHAPES))
+def test_tile_api_padded_misaligned_nan_c(tile):
+    bm, bn = TILE_SHAPES[tile]
+    M, N, K = 2 * bm, 3 * bn, 75
+    print(f"[kloop tile api alignment] tile {tile}: {M}x{N}x{K}", flush=True)
+    A, B, _ = inputs.make_abc(M, N, K, 12900 + tile)
+    nanC = np.full((M, N), np.nan, np.float32)
 
     def call(*args):
-        return sgemm.hip_sgemm_tile_split(0, 1, *args)
-    out, st = gh.run(gh.Case(M, N, K, 0.5, 3.0, A, B, C), call)
+        return sgemm.hip_sgemm_tile_split(tile, 1, *args)
+    out, st = gh.run(gh.Case(M, N, K, -1.5, 0.0, A, B, nanC, K + 3, N + 5, N + 7, 1, 2, 3), call)
+    assert st == 0 and np.all(np.isfinite(out))
+    ref = oracle.oracle_sgemm(A, B, None, -1.5, 0.0)
+    assert oracle.normalised_error(out, ref, None, -1.5, 0.0, strict=True) <= BOUND
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 2048), (2048, 2048, 2053), (2048, 4096, 1024),
+                                   (2048 + 3, 2048 + 11, 500)])
+def test_dispatch_128_tiles(M, N, K):
+    """Level 10 on 128 x 128 grids (one or more tiles per CU, plus fringes)
+    takes the 128 x 128 assembly loop."""
+    print(f"[kloop 128] {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 13000 + M + N + K)
+    rows = _rows(M)
+    out, st = gh.run(gh.Case(M, N, K, 0.5, 3.0, A, B, C), 10)
     assert st == 0
-    ref = oracle.oracle_sgemm(A, B, C, 0.5, 3.0)
-    assert oracle.normalised_error(out, ref, C, 0.5, 3.0, strict=True) <= BOUND
+    ref = oracle.oracle_sgemm(A[rows], B, C[rows], 0.5, 3.0)
+    assert oracle.normalised_error(out[rows], ref, C[rows], 0.5, 3.0, strict=True) <= BOUND
+
+
+def test_loops_deterministic_and_agree():
+    """Both loops are deterministic and give each output the same chain of
+    MFMAs over the same k (16-deep stages, k = 4 s + lane / 16 in MFMA step
+    s), so their results agree bit for bit."""
+    M = N = 2048
+    K = 512
+    A, B, C = inputs.make_abc(M, N, K, 13100)
+    outs = []
+    for tile in (0, 1):
+        def call(*args, tile=tile):
+            return sgemm.hip_sgemm_tile_split(tile, 1, *args)
+        a, st1 = gh.run(gh.Case(M, N, K, 0.5, 3.0, A, B, C), call)
+        b, st2 = gh.run(gh.Case(M, N, K, 0.5, 3.0, A, B, C), call)
+        assert st1 == st2 == 0
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), tile
+        outs.append(a)
+    # tiles 0 and 1 accumulate every output in the same order (16-deep
+    # stages, k = 4 s + lane/16 per MFMA step, one chain per block)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
