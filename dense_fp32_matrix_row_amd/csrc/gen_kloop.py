@@ -10,7 +10,10 @@ FP32 GEMM in exactly this instruction-level ordering, out of reach of C++;
 its double-buffering section gives the overlap these loops implement.
 
 Two tiles, both of 64 x 64 wavefront tiles (4 x 4 blocks of
-v_mfma_f32_16x16x4_f32) over a 128-column block tile with 16-deep stages:
+v_mfma_f32_16x16x4_f32) over a 128-column block tile with 16-deep stages,
+each in the four operand orientations (only the stage loads and stores
+differ: a row-major A and a transposed B are transposed into LDS, a
+transposed A and a row-major B are stored whole):
   256 x 128, eight wavefronts (4 x 2), two blocks per CU: one stage of
             global prefetch (the other block's wavefronts cover the wait);
   128 x 128, four wavefronts (2 x 2), one wavefront per SIMD where one
@@ -50,34 +53,44 @@ from __future__ import annotations
 import os
 
 BN, BK = 128, 16
-B_STAGE = BK * BN * 4          # bytes per B stage
 FE, FO = 64, 72                # fragment sets
 STAGING = 80                   # first staging register
 
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "l10_kloop.inc")
 
 
+def _round256(n: int) -> int:
+    return -(-n // 256) * 256
+
+
 class Tile:
-    """One block tile: BM rows, WAVES_M x 2 wavefronts, DEPTH staging sets."""
+    """One block tile: BM rows, WAVES_M x 2 wavefronts, DEPTH staging sets,
+    operands as stored (TA: A given transposed, K x M; TB: B given
+    transposed, N x K)."""
 
     STEPS = 4                                         # MFMA steps per stage
 
-    def __init__(self, bm: int, waves_m: int, depth: int):
-        self.BM, self.WAVES_M, self.DEPTH = bm, waves_m, depth
+    def __init__(self, bm: int, waves_m: int, depth: int, ta: bool = False, tb: bool = False):
+        self.BM, self.WAVES_M, self.DEPTH, self.TA, self.TB = bm, waves_m, depth, ta, tb
         self.THREADS = 64 * 2 * waves_m
-        self.A_GROUP = 4 * bm + 8                     # floats per four-k group (8 words of pad)
-        self.A_STAGE = -(-4 * self.A_GROUP * 4 // 256) * 256   # bytes, a whole number of 256
+        # floats per four-k group: 8 words of pad where the stage store
+        # transposes (a row-major A, a transposed B), so that its 32-bit
+        # writes hit 32 different banks per half-wavefront
+        self.A_GROUP = 4 * bm + (0 if ta else 8)
+        self.B_GROUP = 4 * BN + (8 if tb else 0)
+        self.A_STAGE = _round256(4 * self.A_GROUP * 4)   # bytes, a whole number of 256
+        self.B_STAGE = _round256(4 * self.B_GROUP * 4)
         self.A_LOADS = bm * BK // 4 // self.THREADS   # A float4s per thread per stage
         self.B_LOADS = BK * BN // 4 // self.THREADS   # B float4s per thread per stage
         self.SET = 4 * (self.A_LOADS + self.B_LOADS)  # staging words per set
-        self.LDS = 2 * self.A_STAGE + 2 * B_STAGE
+        self.LDS = 2 * self.A_STAGE + 2 * self.B_STAGE
         assert self.A_LOADS * self.THREADS * 4 == bm * BK and self.B_LOADS * self.THREADS * 4 == BK * BN
         assert bm % 64 == 0 and self.THREADS % 256 == 0
         assert STAGING + depth * self.SET <= 128
 
     @property
     def name(self) -> str:
-        return f"{self.BM}"
+        return f"{self.BM}_{'T' if self.TA else 'N'}{'T' if self.TB else 'N'}"
 
     def last_vgpr(self) -> int:
         return STAGING + self.DEPTH * self.SET - 1
@@ -90,14 +103,15 @@ class Tile:
     def frag_reads(self, fs: int, s: int, buf: int) -> list[str]:
         """MFMA step s of LDS buffer buf into fragment set fs."""
         return [f"ds_read_b128 v[{fs}:{fs+3}], %[rA] offset:{s * self.A_GROUP * 4 + buf * self.A_STAGE}",
-                f"ds_read_b128 v[{fs+4}:{fs+7}], %[rB] offset:{s * 4 * BN * 4 + buf * B_STAGE}"]
+                f"ds_read_b128 v[{fs+4}:{fs+7}], %[rB] offset:{s * self.B_GROUP * 4 + buf * self.B_STAGE}"]
 
     def set_base(self, st: int) -> int:
         return STAGING + st * self.SET
 
     def loads(self, st: int) -> list[str]:
-        """One stage into staging set st (A float4 h: row tid/4 + h THREADS/4;
-        B float4 h: k-row tid/32 + h THREADS/32), then advance the offsets."""
+        """One stage into staging set st: A float4s first, then B float4s
+        (which elements each thread loads is set by the kernel's per-thread
+        offsets; see stage_stores)."""
         r = self.set_base(st)
         out = [f"buffer_load_dwordx4 v[{r + 4*h}:{r + 4*h + 3}], %[oA{h}], %[rsA], %[sA] offen"
                for h in range(self.A_LOADS)]
@@ -106,25 +120,48 @@ class Tile:
                 for h in range(self.B_LOADS)]
         return out
 
-    ADVANCE = ["s_add_u32 %[sA], %[sA], 64", "s_add_u32 %[sB], %[sB], %[stepB]"]
+    ADVANCE = ["s_add_u32 %[sA], %[sA], %[stepA]", "s_add_u32 %[sB], %[sB], %[stepB]"]
+
+    @staticmethod
+    def _transposing(w: str, r: int, u: int, row_units: int, copy_units: int, copies: int) -> list[str]:
+        """Float4s v[r + 4h ..] that each hold k = 4 q .. 4 q + 3 of one m
+        (n) go to four k-rows of group q, row_units 256-byte units apart;
+        copy h is copy_units further."""
+        out = []
+        for h in range(copies):
+            for c0, c1 in ((0, 1), (2, 3)):
+                out.append(f"ds_write2st64_b32 %[{w}], v{r + 4*h + c0}, v{r + 4*h + c1} "
+                           f"offset0:{u + c0 * row_units + h * copy_units} "
+                           f"offset1:{u + c1 * row_units + h * copy_units}")
+        return out
 
     def stage_stores(self, st: int, buf: int) -> list[str]:
-        """Staging set st into LDS buffer buf: each A float4 holds k = 4 q ..
-        4 q + 3 of one row and goes to four k-rows of group q (BM floats
-        apart, in 256-byte units), its h-th copy THREADS / 4 rows further;
-        each B float4 is one 16-byte piece of a k-row."""
-        r, u = self.set_base(st), buf * (self.A_STAGE // 256)
-        step = self.BM // 64          # 256-byte units between k-rows of a group
-        hrow = self.THREADS // 256    # 256-byte units between the A float4s' rows
-        out = []
-        for h in range(self.A_LOADS):
-            for c0, c1 in ((0, 1), (2, 3)):
-                out.append(f"ds_write2st64_b32 %[wA], v{r + 4*h + c0}, v{r + 4*h + c1} "
-                           f"offset0:{u + c0 * step + h * hrow} offset1:{u + c1 * step + h * hrow}")
+        """Staging set st into LDS buffer buf.  A row-major A's float4 holds
+        k = 4 q .. 4 q + 3 of one row (thread: row tid/4, q = tid%4; copy h
+        THREADS/4 rows on) and is transposed into four k-rows of group q; a
+        transposed A's float4 holds four rows of one k-row (thread: k-row
+        tid/(BM/4), rows 4 (tid%(BM/4)) ..; copy h 8 k-rows = 2 groups on)
+        and is stored whole.  B likewise: row-major, four columns of one
+        k-row (k-row tid/32, columns 4 (tid%32) ..; copy h THREADS/32 k-rows
+        on), stored whole; transposed, k = 4 q .. of one column (column
+        tid/4, q = tid%4; copy h THREADS/4 columns on), transposed."""
+        r = self.set_base(st)
         rb = r + 4 * self.A_LOADS
-        for h in range(self.B_LOADS):
-            out.append(f"ds_write_b128 %[wB], v[{rb + 4*h}:{rb + 4*h + 3}] "
-                       f"offset:{buf * B_STAGE + h * (self.THREADS // 32) * BN * 4}")
+        out = []
+        if self.TA:
+            for h in range(self.A_LOADS):
+                out.append(f"ds_write_b128 %[wA], v[{r + 4*h}:{r + 4*h + 3}] "
+                           f"offset:{buf * self.A_STAGE + h * 2 * self.A_GROUP * 4}")
+        else:
+            out += self._transposing("wA", r, buf * (self.A_STAGE // 256), self.BM // 64,
+                                     self.THREADS // 256, self.A_LOADS)
+        if self.TB:
+            out += self._transposing("wB", rb, buf * (self.B_STAGE // 256), BN // 64,
+                                     self.THREADS // 256, self.B_LOADS)
+        else:
+            for h in range(self.B_LOADS):
+                out.append(f"ds_write_b128 %[wB], v[{rb + 4*h}:{rb + 4*h + 3}] "
+                           f"offset:{buf * self.B_STAGE + h * (self.THREADS // 32) * BN * 4}")
         return out
 
     # -- the loop ------------------------------------------------------------
@@ -191,7 +228,8 @@ class Tile:
         return prologue + pairs + odd + tail
 
 
-TILES = [Tile(256, 4, 1), Tile(128, 2, 2)]
+TILES = [Tile(bm, wm, depth, ta, tb) for bm, wm, depth in ((256, 4, 1), (128, 2, 2))
+         for ta in (False, True) for tb in (False, True)]
 
 
 def render() -> str:

@@ -12,9 +12,9 @@
 //   - a large problem whose M and N miss a multiple of the 256 x 128 (or
 //     128 x 128) tile by at most 16: whole tiles over the largest multiple,
 //     no per-element bounds logic (only the last K step masks when K is
-//     ragged), plus the thin kernels on the fringe.  Whole 256 x 128 tiles
-//     with row-major operands run l10_kloop.hip, the same tile with its K
-//     loop scheduled by hand.  At 4097^3 this replaces
+//     ragged), plus the thin kernels on the fringe.  Whole 256 x 128 and
+//     128 x 128 tiles run l10_kloop.hip, the same tiles with their K loop
+//     scheduled by hand.  At 4097^3 this replaces
 //     level 9's 2145 edge-checked 128 x 64 tiles by the 512 whole 256 x 128
 //     tiles of 4096^3 (exactly two per CU) and two one-element-wide strips;
 //   - a deep K over a small tile grid: split K (l10_splitk.hip);
@@ -50,9 +50,7 @@ double round_fill(int64_t tiles) {
 // The rules below were fitted to sweeps of every tile shape and slice count
 // on MI355X (dense_fp32_matrix_row_amd.autotune); the comments give the
 // measurements that decided them.
-// row_major: neither operand transposed (the assembly-loop kernels take
-// only that orientation).
-Decomp decompose(int M, int N, int K, bool row_major) {
+Decomp decompose(int M, int N, int K) {
   if (M <= kThin) return {Plan::kFewRows, Shape::kSmall, M, N, K};
   if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, M, N, K};
 
@@ -93,17 +91,13 @@ Decomp decompose(int M, int N, int K, bool row_major) {
   }
 
   // 3. 128 x 128 tiles (plus a fringe of <= 16) when they fill whole rounds
-  //    of CUs: row-major, the assembly-loop tile (2048^3: 123-130 against
-  //    105-122 for any compiled tile; 2048 x 4096: 142-146); transposed, the
-  //    compiled tile with two K slices at about one round (2048^3: 115
-  //    against 110 unsliced), unsliced beyond (2048 x 4096: 124).
+  //    of CUs: the assembly-loop tile (2048^3: 123-140 against 105-122 for
+  //    any compiled tile; 2048 x 4096: 142-146).
   {
     const int mr = M % 128, nr = N % 128;
     const int64_t tiles = int64_t((M - mr) / 128) * ((N - nr) / 128);
     if (mr <= kThin && nr <= kThin && tiles >= kCUs && round_fill(tiles) >= 0.9) {
-      const Shape shape =
-          !row_major && tiles <= kCUs + kCUs / 8 ? Shape::kLargeSliced : Shape::kLarge;
-      return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, shape, M - mr, N - nr, K};
+      return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, Shape::kLarge, M - mr, N - nr, K};
     }
   }
 
@@ -115,7 +109,7 @@ Decomp decompose(int M, int N, int K, bool row_major) {
 }
 
 Geometry geometry10(int M, int N, int K) {
-  const Decomp d = decompose(M, N, K, true);
+  const Decomp d = decompose(M, N, K);
   switch (d.plan) {
     case Plan::kFewRows: return few_rows_geometry(M, N, K);
     case Plan::kFewCols: return few_cols_geometry(M, N, K);
@@ -125,7 +119,7 @@ Geometry geometry10(int M, int N, int K) {
 }
 
 hipError_t launch10(const Problem& p, hipStream_t s) {
-  const Decomp d = decompose(p.M, p.N, p.K, !p.trans_a && !p.trans_b);
+  const Decomp d = decompose(p.M, p.N, p.K);
   switch (d.plan) {
     case Plan::kFewRows: return launch_few_rows(p, s);
     case Plan::kFewCols: return launch_few_cols(p, s);

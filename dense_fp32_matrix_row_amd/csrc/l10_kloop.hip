@@ -3,27 +3,33 @@
 // 16 x 16 blocks, 16-deep K steps, double-buffered group-padded LDS,
 // interleaved block rows and columns; eight or four wavefronts) with the K
 // loop written as assembly (l10_kloop.inc, emitted by gen_kloop.py, which
-// documents the schedule and the register map).
+// documents the schedule and the register map), for each orientation of
+// the operands.
 //
 // [CP04] (section on boundary conditions and limits) attributes the last
 // 15-20 % between a hand-written FP32 GEMM and the vendor library to
 // instruction-level scheduling that compiled C++ does not reach; here that
 // is the difference between level 9's compiled loop and this one on the
-// same tile (4096^3: 138.7 against 152 TFLOP/s on MI355X).
+// same tile (4096^3: 138.5 against 150-152 TFLOP/s on MI355X).
 //
 // The first stage holds the K % 16 leftover k (a whole stage when
 // K % 16 == 0), loaded with per-element bounds here in C++ and stored into
 // LDS buffer 0 before the loop; every stage the loop loads is then whole.
 // The loop reads A and B through buffer resources whose record counts end
 // at the last element the tile may use, so the loads it issues past the
-// last stage (two stages of prefetch) read zeros or elements of the same
-// matrix, never beyond it; they land in the idle LDS buffer unused.  The
-// kernel takes row-major A and B and byte offsets below 2^31.
+// last stage (one or two stages of prefetch) read zeros or elements of the
+// same matrix, never beyond it; they land in the idle LDS buffer unused.
+// Byte offsets must stay below 2^31 (kloop_fits).
 //
-// With K % 16 == 0 the 256 x 128 kernel's results are bit-identical to
-// level 9's tile of that shape (the same blocks, the same operand values
-// per MFMA, the same k order per accumulator); with a ragged K, level 9
-// takes the partial stage last and this kernel first.
+// LDS holds both operands k-major whatever their storage (as level 9's
+// tile): a row-major A and a transposed B arrive four k per 128-bit load
+// and are transposed on their way in (into groups padded by 8 words), a
+// transposed A and a row-major B arrive four m / n per load and are stored
+// whole.  The fragments, the MFMAs and so the results are the same in every
+// orientation.  With K % 16 == 0 they are bit-identical to level 9's
+// 256 x 128 tile (the same blocks, the same operand values per MFMA, the
+// same k order per accumulator); with a ragged K, level 9 takes the partial
+// stage last and this kernel first.
 #include "l10_kloop.inc"
 #include "sgemm_internal.h"
 
@@ -34,18 +40,22 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
+constexpr int round256(int n) { return (n + 255) / 256 * 256; }
+
 // The tile constants gen_kloop.py builds each loop for.
-template <int BM_>
+template <int BM_, bool TA_, bool TB_>
 struct KTile {
   static constexpr int BM = BM_, BN = 128, BK = 16, GROUP_M = 8;
+  static constexpr bool TA = TA_, TB = TB_;
   static constexpr int WAVES_M = BM / 64, THREADS = 64 * 2 * WAVES_M;
-  static constexpr int A_GROUP = 4 * BM + 8;                          // floats per four-k group of A
-  static constexpr int A_STAGE = (4 * A_GROUP * 4 + 255) / 256 * 256;  // bytes per A stage
-  static constexpr int B_STAGE = BK * BN * 4;                          // bytes per B stage
+  static constexpr int A_GROUP = 4 * BM + (TA ? 0 : 8);  // floats per four-k group
+  static constexpr int B_GROUP = 4 * BN + (TB ? 8 : 0);
+  static constexpr int A_STAGE = round256(4 * A_GROUP * 4);  // bytes per stage
+  static constexpr int B_STAGE = round256(4 * B_GROUP * 4);
   static constexpr int LDS = 2 * A_STAGE + 2 * B_STAGE;
   static constexpr int A_LOADS = BM * BK / 4 / THREADS, B_LOADS = BK * BN / 4 / THREADS;
-  static constexpr int PREFETCH = BM == 256 ? 1 : 2;  // stages loaded ahead of the one stored
   static_assert(A_LOADS == 2 && (B_LOADS == 1 || B_LOADS == 2), "thread-to-element map");
+  static_assert(THREADS / (BM / 4) == 8, "a transposed A's second float4 is 8 k-rows on");
 };
 
 // Raw buffer resource (stride 0): loads at byte offsets >= bytes return 0.
@@ -62,14 +72,44 @@ __device__ __forceinline__ intx4 buffer_resource(const float* base, uint32_t byt
 #define SGEMM_KLOOP_OPERANDS                                                               \
   : "+{v[0:15]}"(a0), "+{v[16:31]}"(a1), "+{v[32:47]}"(a2), "+{v[48:63]}"(a3), [sA] "+s"(sA), \
     [sB] "+s"(sB), [pairs] "+s"(pairs)                                                     \
-  : [rsA] "s"(rsA), [rsB] "s"(rsB), [oA0] "v"(oA0), [oA1] "v"(oA1), [oB0] "v"(oB0),        \
-    [oB1] "v"(oB1), [wA] "v"(wA), [wB] "v"(wB), [rA] "v"(rA), [rB] "v"(rB),                \
-    [stepB] "s"(stepB), [odd] "s"(odd)
+  : [rsA] "s"(rsA), [rsB] "s"(rsB), [oA0] "v"(oA[0]), [oA1] "v"(oA[1]), [oB0] "v"(oB[0]),  \
+    [oB1] "v"(oB[1]), [wA] "v"(wA), [wB] "v"(wB), [rA] "v"(rA), [rB] "v"(rB),              \
+    [stepA] "s"(stepA), [stepB] "s"(stepB), [odd] "s"(odd)
 
-template <int BM>
-__global__ __launch_bounds__(KTile<BM>::THREADS) void k_kloop(Problem p, int64_t tiles_m,
-                                                             int64_t tiles_n) {
-  typedef KTile<BM> T;
+#define SGEMM_KLOOP_RUN(NAME) \
+  asm volatile(SGEMM_KLOOP_ASM_##NAME SGEMM_KLOOP_OPERANDS : SGEMM_KLOOP_CLOBBERS_##NAME, "memory", "scc")
+
+// Per-thread element maps of one stage (the loop's loads and stores, and
+// the C++ first stage, use the same ones).  Element h of a thread:
+//   A row-major:  row tid/4 + h THREADS/4, k 4 (tid%4) .. +3
+//   A transposed: k-row tid/(BM/4) + 8 h, rows 4 (tid%(BM/4)) .. +3
+//   B row-major:  k-row tid/32 + h THREADS/32, columns 4 (tid%32) .. +3
+//   B transposed: column tid/4 + h THREADS/4, k 4 (tid%4) .. +3
+template <class T>
+__device__ __forceinline__ void a_map(int tid, int h, int& row, int& k) {
+  if (T::TA) {
+    k = tid / (T::BM / 4) + 8 * h;
+    row = 4 * (tid % (T::BM / 4));
+  } else {
+    row = tid / 4 + h * (T::THREADS / 4);
+    k = 4 * (tid % 4);
+  }
+}
+template <class T>
+__device__ __forceinline__ void b_map(int tid, int h, int& k, int& col) {
+  if (T::TB) {
+    col = tid / 4 + h * (T::THREADS / 4);
+    k = 4 * (tid % 4);
+  } else {
+    k = tid / 32 + h * (T::THREADS / 32);
+    col = 4 * (tid % 32);
+  }
+}
+
+template <int BM, bool TA, bool TB>
+__global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem p, int64_t tiles_m,
+                                                                       int64_t tiles_n) {
+  typedef KTile<BM, TA, TB> T;
   __shared__ __align__(16) char smem[T::LDS];
   // tile order: XCD-contiguous ranges, grouped by GROUP_M rows of tiles
   const int64_t t = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -83,60 +123,102 @@ __global__ __launch_bounds__(KTile<BM>::THREADS) void k_kloop(Problem p, int64_t
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int wm = wave / 2, wn = wave % 2, lrow = lane % 16, kg = lane / 16;
   const int64_t lda = p.lda, ldb = p.ldb;
-  // A: rows row0 .. row0 + BM - 1, k < K; B: k < K, columns col0 .. col0 + 127
-  const intx4 rsA = buffer_resource(p.A + row0 * lda, static_cast<uint32_t>(((BM - 1) * lda + p.K) * 4));
-  const intx4 rsB = buffer_resource(p.B + col0, static_cast<uint32_t>(((p.K - 1) * ldb + T::BN) * 4));
-  // loads of a stage: A float4 h at row tid/4 + h THREADS/4, k 4 (tid%4) ..;
-  // B float4 h at k-row tid/32 + h THREADS/32, columns 4 (tid%32) ..
-  constexpr int AROWS = T::THREADS / 4, BROWS = T::THREADS / 32;
-  const uint32_t oA0 = static_cast<uint32_t>(((tid / 4) * lda + 4 * (tid % 4)) * 4);
-  const uint32_t oA1 = oA0 + static_cast<uint32_t>(AROWS * lda * 4);
-  const uint32_t oB0 = static_cast<uint32_t>(((tid / 32) * ldb + 4 * (tid % 32)) * 4);
-  const uint32_t oB1 = oB0 + static_cast<uint32_t>(BROWS * ldb * 4);
-  // LDS: A stage k-row k at group k/4, word (k%4)*BM + m; B k-row k at
-  // word 128 k; fragments of step s at group s (A) / k-row 4 s (B), lane
-  // reading the four interleaved rows (columns) 4 lrow .. 4 lrow + 3 of its
-  // wave tile at k-row kg of the step
-  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)smem));
-  const uint32_t wA = base + static_cast<uint32_t>(((tid % 4) * T::A_GROUP + tid / 4) * 4);
-  const uint32_t wB = base + 2 * T::A_STAGE + static_cast<uint32_t>(tid * 16);
-  const uint32_t rA = base + static_cast<uint32_t>((kg * BM + wm * 64 + 4 * lrow) * 4);
-  const uint32_t rB = base + 2 * T::A_STAGE + static_cast<uint32_t>((kg * T::BN + wn * 64 + 4 * lrow) * 4);
-  const uint32_t stepB = static_cast<uint32_t>(T::BK * ldb * 4);
-  // stage 0: k < k0 (the same thread-to-element map as the loop's stages)
-  const int k0 = p.K % T::BK ? p.K % T::BK : T::BK;
-  {
-    float* const lds = reinterpret_cast<float*>(smem);
-    const float* const arow = p.A + (row0 + tid / 4) * lda;
+  // The tile's part of A (rows row0 .. row0 + BM - 1, k < K) and of B
+  // (k < K, columns col0 .. col0 + 127), as stored: element (m, k) of the
+  // tile's A at a_base[m a_rs + k a_ks], element (k, n) of B at
+  // b_base[k b_ks + n b_cs].
+  const float* const a_base = TA ? p.A + row0 : p.A + row0 * lda;
+  const float* const b_base = TB ? p.B + col0 * ldb : p.B + col0;
+  const int64_t a_rs = TA ? 1 : lda, a_ks = TA ? lda : 1;
+  const int64_t b_ks = TB ? 1 : ldb, b_cs = TB ? ldb : 1;
+  const intx4 rsA =
+      buffer_resource(a_base, static_cast<uint32_t>(((BM - 1) * a_rs + (p.K - 1) * a_ks + 1) * 4));
+  const intx4 rsB =
+      buffer_resource(b_base, static_cast<uint32_t>(((p.K - 1) * b_ks + (T::BN - 1) * b_cs + 1) * 4));
+  uint32_t oA[2], oB[2] = {0, 0};
 #pragma unroll
-    for (int h = 0; h < T::A_LOADS; ++h) {
-      const float4 v = load4(arow + h * AROWS * lda, 4 * (tid % 4), k0, true);
-      float* const dst = lds + (tid % 4) * T::A_GROUP + tid / 4 + AROWS * h;
+  for (int h = 0; h < T::A_LOADS; ++h) {
+    int row, k;
+    a_map<T>(tid, h, row, k);
+    oA[h] = static_cast<uint32_t>((row * a_rs + k * a_ks) * 4);
+  }
+#pragma unroll
+  for (int h = 0; h < T::B_LOADS; ++h) {
+    int k, col;
+    b_map<T>(tid, h, k, col);
+    oB[h] = static_cast<uint32_t>((k * b_ks + col * b_cs) * 4);
+  }
+  // LDS: A stage k-row k at group k/4, word (k%4)*BM + m; B k-row k at
+  // group k/4, word (k%4)*128 + n.  Stores start at element 0 of the
+  // thread's map (element 1 is an immediate away); fragments of step s sit
+  // in group s, a lane reading the four interleaved rows (columns)
+  // 4 lrow .. 4 lrow + 3 of its wave tile at k-row kg of the step.
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)smem));
+  float* const lds_a = reinterpret_cast<float*>(smem);
+  float* const lds_b = reinterpret_cast<float*>(smem + 2 * T::A_STAGE);
+  int a_row0, a_k0, b_k0, b_col0;
+  a_map<T>(tid, 0, a_row0, a_k0);
+  b_map<T>(tid, 0, b_k0, b_col0);
+  const int wa_word = (a_k0 / 4) * T::A_GROUP + (a_k0 % 4) * BM + a_row0;
+  const int wb_word = (b_k0 / 4) * T::B_GROUP + (b_k0 % 4) * T::BN + b_col0;
+  const uint32_t wA = base + static_cast<uint32_t>(wa_word * 4);
+  const uint32_t wB = base + 2 * T::A_STAGE + static_cast<uint32_t>(wb_word * 4);
+  const uint32_t rA = base + static_cast<uint32_t>((kg * BM + wm * 64 + 4 * lrow) * 4);
+  const uint32_t rB =
+      base + 2 * T::A_STAGE + static_cast<uint32_t>((kg * T::BN + wn * 64 + 4 * lrow) * 4);
+  const uint32_t stepA = static_cast<uint32_t>(T::BK * a_ks * 4);
+  const uint32_t stepB = static_cast<uint32_t>(T::BK * b_ks * 4);
+
+  // stage 0: k < k0, into buffer 0 through the same element maps
+  const int k0 = p.K % T::BK ? p.K % T::BK : T::BK;
+  const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int h = 0; h < T::A_LOADS; ++h) {
+    int row, k;
+    a_map<T>(tid, h, row, k);
+    if (TA) {
+      // four rows of k-row k: whole or nothing
+      const float4 v = k < k0 ? ld_global4(a_base + k * lda + row) : zero;
+      *reinterpret_cast<float4*>(lds_a + (k / 4) * T::A_GROUP + (k % 4) * BM + row) = v;
+    } else {
+      // k .. k + 3 of one row, each below k0 or zero
+      const float4 v = load4(a_base + row * lda, k, k0, true);
+      float* const dst = lds_a + (k / 4) * T::A_GROUP + row;
       dst[0] = v.x;
       dst[BM] = v.y;
       dst[2 * BM] = v.z;
       dst[3 * BM] = v.w;
     }
+  }
 #pragma unroll
-    for (int h = 0; h < T::B_LOADS; ++h) {
-      const int kb = tid / 32 + BROWS * h;
-      const float4 bv = load4(p.B + (kb < k0 ? kb : 0) * ldb + col0, 4 * (tid % 32), T::BN, kb < k0);
-      *reinterpret_cast<float4*>(lds + 2 * T::A_STAGE / 4 + (tid + T::THREADS * h) * 4) = bv;
+  for (int h = 0; h < T::B_LOADS; ++h) {
+    int k, col;
+    b_map<T>(tid, h, k, col);
+    if (TB) {
+      const float4 v = load4(b_base + col * ldb, k, k0, true);
+      float* const dst = lds_b + (k / 4) * T::B_GROUP + col;
+      dst[0] = v.x;
+      dst[T::BN] = v.y;
+      dst[2 * T::BN] = v.z;
+      dst[3 * T::BN] = v.w;
+    } else {
+      const float4 v = k < k0 ? ld_global4(b_base + k * ldb + col) : zero;
+      *reinterpret_cast<float4*>(lds_b + (k / 4) * T::B_GROUP + (k % 4) * T::BN + col) = v;
     }
   }
-  uint32_t sA = static_cast<uint32_t>(k0 * 4), sB = static_cast<uint32_t>(k0 * ldb * 4);
+  uint32_t sA = static_cast<uint32_t>(k0 * a_ks * 4), sB = static_cast<uint32_t>(k0 * b_ks * 4);
   const int stages = (p.K + T::BK - 1) / T::BK;
   uint32_t pairs = static_cast<uint32_t>(stages / 2);
   const uint32_t odd = static_cast<uint32_t>(stages % 2);
   floatx16 a0 = {}, a1 = {}, a2 = {}, a3 = {};
-  if constexpr (BM == 256) {
-    asm volatile(SGEMM_KLOOP_ASM_256 SGEMM_KLOOP_OPERANDS
-                 : SGEMM_KLOOP_CLOBBERS_256, "memory", "scc");
-  } else {
-    static_assert(BM == 128, "one loop per tile");
-    asm volatile(SGEMM_KLOOP_ASM_128 SGEMM_KLOOP_OPERANDS
-                 : SGEMM_KLOOP_CLOBBERS_128, "memory", "scc");
-  }
+  if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_RUN(256_NN);
+  else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_RUN(256_NT);
+  else if constexpr (BM == 256 && !TB) SGEMM_KLOOP_RUN(256_TN);
+  else if constexpr (BM == 256) SGEMM_KLOOP_RUN(256_TT);
+  else if constexpr (!TA && !TB) SGEMM_KLOOP_RUN(128_NN);
+  else if constexpr (!TA) SGEMM_KLOOP_RUN(128_NT);
+  else if constexpr (!TB) SGEMM_KLOOP_RUN(128_TN);
+  else SGEMM_KLOOP_RUN(128_TT);
 
   // Block (i, j) register r holds C[row0 + 64 wm + 16 kg + 4 r + i]
   // [col0 + 64 wn + 4 lrow + j]: for each (r, i) a lane owns four adjacent
@@ -169,22 +251,31 @@ __global__ __launch_bounds__(KTile<BM>::THREADS) void k_kloop(Problem p, int64_t
 
 template <int BM>
 bool fits(const Problem& p) {
-  typedef KTile<BM> T;
-  if (p.trans_a || p.trans_b || p.M <= 0 || p.N <= 0) return false;
-  if (p.M % BM || p.N % T::BN || p.K < 1) return false;
+  if (p.M <= 0 || p.N <= 0 || p.M % BM || p.N % 128 || p.K < 1) return false;
   // largest byte offset of a load (record counts, plus the stages the loop
-  // prefetches past K) stays below 2^31
-  const int64_t lim = int64_t(1) << 31, past = p.K + (T::PREFETCH + 1) * T::BK;
-  return ((BM - 1) * p.lda + past) * 4 < lim && (past * p.ldb + T::BN) * 4 < lim;
+  // prefetches past K: one for the 256-row tile, two for the 128-row one)
+  // stays below 2^31
+  const int64_t lim = int64_t(1) << 31, past = p.K + ((BM == 256 ? 1 : 2) + 1) * 16;
+  const int64_t a_end = p.trans_a ? past * p.lda + BM : (BM - 1) * p.lda + past;
+  const int64_t b_end = p.trans_b ? 127 * p.ldb + past : past * p.ldb + 128;
+  return a_end * 4 < lim && b_end * 4 < lim;
+}
+
+template <int BM, bool TA, bool TB>
+hipError_t launch_t(const Problem& p, hipStream_t s) {
+  typedef KTile<BM, TA, TB> T;
+  const int64_t tm = p.M / BM, tn = p.N / T::BN;
+  hipLaunchKernelGGL((k_kloop<BM, TA, TB>), dim3(static_cast<unsigned>(tm * tn)), dim3(T::THREADS),
+                     0, s, p, tm, tn);
+  return hipGetLastError();
 }
 
 template <int BM>
 hipError_t launch(const Problem& p, hipStream_t s) {
-  typedef KTile<BM> T;
-  const int64_t tm = p.M / BM, tn = p.N / T::BN;
-  hipLaunchKernelGGL(k_kloop<BM>, dim3(static_cast<unsigned>(tm * tn)), dim3(T::THREADS), 0, s, p,
-                     tm, tn);
-  return hipGetLastError();
+  if (p.trans_a && p.trans_b) return launch_t<BM, true, true>(p, s);
+  if (p.trans_a) return launch_t<BM, true, false>(p, s);
+  if (p.trans_b) return launch_t<BM, false, true>(p, s);
+  return launch_t<BM, false, false>(p, s);
 }
 
 }  // namespace
@@ -206,8 +297,8 @@ Geometry tiles_geometry(Shape shape, int M, int N, int K) {
   p.ldb = N;
   p.ldc = N;
   if (!kloop_fits(shape, p)) return mfma_geometry(shape, M, N, K);
-  return shape == Shape::kHuge ? make_geometry(M, N, K, 256, 128, 16, KTile<256>::THREADS)
-                               : make_geometry(M, N, K, 128, 128, 16, KTile<128>::THREADS);
+  return shape == Shape::kHuge ? make_geometry(M, N, K, 256, 128, 16, 512)
+                               : make_geometry(M, N, K, 128, 128, 16, 256);
 }
 
 hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s) {

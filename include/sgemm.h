@@ -160,9 +160,9 @@ int hip_sgemm_level(int level, int M, int N, int K, float alpha,
  *           sums in slice order, then applies alpha and beta ([GEMM2]
  *           size-sweep section: split-K, a tiled GEMM plus a reduce kernel).
  *           splits = 1, or a slice covering all of K, is the unsplit kernel
- *           (for tile 0 on whole tiles and row-major operands, level 10's
- *           version of it with the K loop in assembly; the same results
- *           bit for bit when K % 16 == 0).
+ *           (for tiles 0 and 1 on whole tiles, level 10's version of them
+ *           with the K loop in assembly; for tile 0 the same results bit
+ *           for bit when K % 16 == 0).
  * Split K needs S x M x N floats of workspace: the library takes it from a
  * stream-ordered memory pool of its own (one per device, created on first
  * use, memory kept cached until the process ends), allocated and released on

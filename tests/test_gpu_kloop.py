@@ -135,6 +135,36 @@ def test_tile_api_whole_tiles(tile, gm, gn, K):
         assert oracle.normalised_error(out, ref, C, 0.5, 3.0, strict=True) <= BOUND
 
 
+OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 48), (4096, 4096, 1001), (2048, 2048, 300),
+                                   (2048 + 7, 2048 + 9, 77)])
+def test_kloop_every_orientation_bit_identical(M, N, K):
+    """Every orientation of the operands runs the same loop on the same LDS
+    contents (only the stage loads and stores differ), so all four give the
+    same bits; they are checked against the reference as well."""
+    print(f"[kloop orientations] {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 13200 + M + K)
+    rows = _rows(M)
+    ref = oracle.oracle_sgemm(A[rows], B, C[rows], 0.5, 3.0)
+    outs = {}
+    for op_a, op_b in OPS:
+        sa = np.ascontiguousarray(A.T) if op_a == "T" else A
+        sb = np.ascontiguousarray(B.T) if op_b == "T" else B
+        case = gh.Case(M, N, K, 0.5, 3.0, sa, sb, C, sa.shape[1] + 1, sb.shape[1] + 3, N + 2)
+
+        def call(*args, op_a=op_a, op_b=op_b):
+            return sgemm.hip_sgemm_ex(op_a, op_b, *args)
+        out, st = gh.run(case, call)
+        assert st == 0
+        err = oracle.normalised_error(out[rows], ref, C[rows], 0.5, 3.0, strict=True)
+        assert err <= BOUND, (op_a, op_b, err)
+        outs[op_a + op_b] = out
+    for key in ("NT", "TN", "TT"):
+        assert np.array_equal(outs["NN"].view(np.uint32), outs[key].view(np.uint32)), key
+
+
 @pytest.mark.parametrize("tile", sorted(TILE_SHAPES))
 def test_tile_api_padded_misaligned_nan_c(tile):
     bm, bn = TILE_SHAPES[tile]

@@ -9,11 +9,7 @@ the same for every orientation the transposed calls must reproduce the
 untransposed result bit for bit.  Where it is not, the expected identities
 are narrower: the vector-ALU few-columns kernel reads A by rows, so one to
 four columns with A stored transposed take the matrix-core thin form (B's
-orientation never changes the plan there); and the untransposed call runs
-the assembly-loop 128 x 128 tile where the transposed ones run the compiled
-tile with two K slices (different summation order), so only the three
-transposed calls agree.  (The assembly-loop 256 x 128 tile and the compiled
-one sum in the same order, up to exact zeros, when K % 4 == 0.)
+orientation never changes the plan there).
 """
 
 from __future__ import annotations
@@ -55,17 +51,17 @@ def run_ex(op_a, op_b, A, B, C, alpha, beta, pads=(0, 0, 0), offs=(0, 0, 0)):
 
 
 # (M, N, K, plan, which results must be bit-identical: "all" four, "b" =
-# B's orientation does not matter, "t" = the three transposed calls)
+# B's orientation does not matter)
 SHAPES = [
     (5, 3001, 777, "few rows", "all"),
     (16, 1000, 333, "sixteen rows", "all"),
     (1500, 7, 2003, "few columns", "all"),
     (1500, 3, 2003, "three columns (A^T: matrix-core thin form)", "b"),
-    (2051, 2055, 300, "128x128 grid + fringe (A, B row-major: assembly loop)", "t"),
+    (2051, 2055, 300, "128x128 grid + fringe", "all"),
     (4096 + 3, 4096 + 16, 40, "256x128 grid + fringe", "all"),
     (8192, 8, 1000, "eight columns, two per lane", "all"),
     (16, 16384, 777, "sixteen rows, two columns per lane", "all"),
-    (2048, 2048, 100, "128x128 grid, K ragged (row-major: assembly loop)", "t"),
+    (2048, 2048, 100, "128x128 grid, K ragged", "all"),
     (4096, 4096, 36, "256x128 grid, K ragged", "all"),
     (1000, 1000, 300, "64x64 two-slice tiles, edges", "all"),
     (1024, 1024, 4096, "split K, 128x128", "all"),
@@ -87,8 +83,7 @@ def test_transposed_operands(M, N, K, plan, same):
         err = oracle.normalised_error(out, ref, C, 0.5, 3.0, strict=True)
         assert err <= BOUND, (op_a, op_b, err)
         outs[op_a + op_b] = out
-    groups = {"all": [("NN", "NT", "TN", "TT")], "b": [("NN", "NT"), ("TN", "TT")],
-              "t": [("NT", "TN", "TT")]}[same]
+    groups = {"all": [("NN", "NT", "TN", "TT")], "b": [("NN", "NT"), ("TN", "TT")]}[same]
     for group in groups:
         for key in group[1:]:
             assert np.array_equal(outs[group[0]].view(np.uint32), outs[key].view(np.uint32)), (group[0], key)

@@ -1,5 +1,5 @@
 """Host-side checks of the assembly K loops of l10_kloop.hip (no GPU), for
-each tile gen_kloop.py builds a loop for.
+each tile and operand orientation gen_kloop.py builds a loop for.
 
 The loop text is emitted by gen_kloop.py; the committed l10_kloop.inc must
 be exactly that output.  Its LDS traffic is then replayed on the CPU from
@@ -39,13 +39,41 @@ def test_committed_loop_matches_generator():
         assert f.read() == G.render()
 
 
-# Base addresses (bytes) of l10_kloop.hip, per thread tid = 64 wave + lane.
+# Per-thread element maps and base addresses of l10_kloop.hip (restated from
+# the kernel): element h of thread tid is
+#   A row-major:  row tid/4 + h THREADS/4, k 4 (tid%4) + c
+#   A transposed: k-row tid/(BM/4) + 8 h, row 4 (tid%(BM/4)) + c
+#   B row-major:  k-row tid/32 + h THREADS/32, column 4 (tid%32) + c
+#   B transposed: column tid/4 + h THREADS/4, k 4 (tid%4) + c
+def a_elem(t, tid, h, c):
+    if t.TA:
+        return ("A", 4 * (tid % (t.BM // 4)) + c, tid // (t.BM // 4) + 8 * h)
+    return ("A", tid // 4 + h * t.THREADS // 4, 4 * (tid % 4) + c)
+
+
+def b_elem(t, tid, h, c):
+    if t.TB:
+        return ("B", 4 * (tid % 4) + c, tid // 4 + h * t.THREADS // 4)
+    return ("B", tid // 32 + h * t.THREADS // 32, 4 * (tid % 32) + c)
+
+
+def a_word(t, m, k):
+    """LDS word of A element (m, k): k-row k at group k/4, word (k%4) BM + m."""
+    return (k // 4) * t.A_GROUP + (k % 4) * t.BM + m
+
+
+def b_word(t, k, n):
+    return 2 * t.A_STAGE // 4 + (k // 4) * t.B_GROUP + (k % 4) * G.BN + n
+
+
 def w_a(t, tid):
-    return ((tid % 4) * t.A_GROUP + tid // 4) * 4
+    _, m, k = a_elem(t, tid, 0, 0)
+    return 4 * a_word(t, m, k)
 
 
 def w_b(t, tid):
-    return 2 * t.A_STAGE + tid * 16
+    _, k, n = b_elem(t, tid, 0, 0)
+    return 4 * b_word(t, k, n)
 
 
 def _wave(t, tid):
@@ -67,75 +95,70 @@ def r_b(t, tid):
 def _stage_stores(t, st, buf):
     """{byte address: ('A', row, k) or ('B', k, col)} written by one stage's
     stores from staging set st into buffer buf, replayed from the emitted
-    instructions."""
+    instructions (their registers and immediate offsets)."""
     written = {}
     a_end = 2 * t.A_STAGE
     base = t.set_base(st)
     lines = t.stage_stores(st, buf)
-    a_lines = [l for l in lines if l.startswith("ds_write2st64_b32")]
-    b_lines = [l for l in lines if l.startswith("ds_write_b128")]
-    assert len(a_lines) == 2 * t.A_LOADS and len(b_lines) == t.B_LOADS
     for tid in range(t.THREADS):
-        # staging words: A float4 h (row tid/4 + h THREADS/4, k = 4 (tid%4) + c),
-        # then B float4 h (k-row tid/32 + h THREADS/32, columns 4 (tid%32) + c)
         regs = {}
         for h in range(t.A_LOADS):
             for c in range(4):
-                regs[base + 4 * h + c] = ("A", tid // 4 + h * t.THREADS // 4, 4 * (tid % 4) + c)
+                regs[base + 4 * h + c] = a_elem(t, tid, h, c)
         for h in range(t.B_LOADS):
             for c in range(4):
-                regs[base + 4 * t.A_LOADS + 4 * h + c] = ("B", tid // 32 + h * t.THREADS // 32,
-                                                          4 * (tid % 32) + c)
-        for line in a_lines:
-            m = re.match(r"ds_write2st64_b32 %\[wA\], v(\d+), v(\d+) offset0:(\d+) offset1:(\d+)", line)
-            r0, r1, o0, o1 = (int(x) for x in m.groups())
-            for reg, off in ((r0, o0), (r1, o1)):
-                addr = w_a(t, tid) + 256 * off
-                assert 0 <= addr and addr + 4 <= a_end, (tid, line)
-                assert addr not in written, ("store overlap", tid, line)
+                regs[base + 4 * t.A_LOADS + 4 * h + c] = b_elem(t, tid, h, c)
+        for line in lines:
+            m2 = re.match(r"ds_write2st64_b32 %\[w([AB])\], v(\d+), v(\d+) offset0:(\d+) offset1:(\d+)$", line)
+            m4 = re.match(r"ds_write_b128 %\[w([AB])\], v\[(\d+):(\d+)\] offset:(\d+)$", line)
+            assert m2 or m4, line
+            if m2:
+                op, r0, r1, o0, o1 = m2.group(1), *(int(x) for x in m2.groups()[1:])
+                pieces = [(r0, 256 * o0), (r1, 256 * o1)]
+            else:
+                op, r0, r3, off = m4.group(1), *(int(x) for x in m4.groups()[1:])
+                assert r3 == r0 + 3
+                pieces = [(r0 + c, off + 4 * c) for c in range(4)]
+            start = w_a(t, tid) if op == "A" else w_b(t, tid)
+            lo, hi = (0, a_end) if op == "A" else (a_end, t.LDS)
+            for reg, off in pieces:
+                addr = start + off
+                assert lo <= addr and addr + 4 <= hi, (t.name, tid, line)
+                assert addr not in written, ("store overlap", t.name, tid, line)
+                assert regs[reg][0] == op, (t.name, line)
                 written[addr] = regs[reg]
-        for line in b_lines:
-            m = re.match(r"ds_write_b128 %\[wB\], v\[(\d+):(\d+)\] offset:(\d+)", line)
-            r0, r3, off = (int(x) for x in m.groups())
-            assert r3 == r0 + 3
-            for c in range(4):
-                addr = w_b(t, tid) + off + 4 * c
-                assert a_end <= addr and addr + 4 <= t.LDS, tid
-                assert addr not in written
-                written[addr] = regs[r0 + c]
     return written
 
 
-@pytest.mark.parametrize("bm", sorted(TILES))
-def test_first_stage_map_matches_the_loop(bm):
-    """Stage 0 is stored by the kernel's C++ part (A word (tid % 4) A_GROUP +
-    tid / 4 + h THREADS/4 + BM c, B float4 h at word 4 (tid + h THREADS) of
-    the B region, both as in l10_kloop.hip) into buffer 0: it must put every
-    element where the loop's own stores into buffer 0 put it."""
-    t = TILES[bm]
+@pytest.mark.parametrize("name", sorted(TILES))
+def test_first_stage_map_matches_the_loop(name):
+    """Stage 0 is stored by the kernel's C++ part through the same element
+    maps into buffer 0 (A (m, k) at word (k/4) A_GROUP + (k%4) BM + m, B
+    (k, n) likewise): it must put every element where the loop's own stores
+    into buffer 0 put it."""
+    t = TILES[name]
     written = _stage_stores(t, 0, 0)
-    a_end = 2 * t.A_STAGE
     for tid in range(t.THREADS):
         for h in range(t.A_LOADS):
             for c in range(4):
-                word = (tid % 4) * t.A_GROUP + tid // 4 + h * t.THREADS // 4 + t.BM * c
-                assert written[4 * word] == ("A", tid // 4 + h * t.THREADS // 4, 4 * (tid % 4) + c)
+                e = a_elem(t, tid, h, c)
+                assert written[4 * a_word(t, e[1], e[2])] == e
         for h in range(t.B_LOADS):
             for c in range(4):
-                assert written[a_end + 16 * (tid + h * t.THREADS) + 4 * c] == (
-                    "B", tid // 32 + h * t.THREADS // 32, 4 * (tid % 32) + c)
+                e = b_elem(t, tid, h, c)
+                assert written[4 * b_word(t, e[1], e[2])] == e
 
 
-@pytest.mark.parametrize("bm", sorted(TILES))
+@pytest.mark.parametrize("name", sorted(TILES))
 @pytest.mark.parametrize("buf", [0, 1])
-def test_fragment_reads_find_their_operands(bm, buf):
-    t = TILES[bm]
+def test_fragment_reads_find_their_operands(name, buf):
+    t = TILES[name]
     a_end = 2 * t.A_STAGE
     for st in range(t.DEPTH):
         written = _stage_stores(t, st, buf)
         # a whole stage lands: BM x 16 A words and 16 x 128 B words
         assert len(written) == t.BM * 16 + 16 * G.BN
-        for s in range(t.STEPS):
+        for s in range(4):
             lines = t.frag_reads(64, s, buf)
             offs = [int(re.search(r"offset:(\d+)", l).group(1)) for l in lines]
             for tid in range(t.THREADS):
@@ -151,9 +174,30 @@ def test_fragment_reads_find_their_operands(bm, buf):
                     assert written[b_addr] == ("B", k, wn * 64 + 4 * lrow + e), (s, tid, e)
 
 
-@pytest.mark.parametrize("bm", sorted(TILES))
-def test_loop_structure(bm):
-    t = TILES[bm]
+def _bank_conflict_free_32bit(addrs):
+    """The 32 words of one half-wavefront's 32-bit write lie in 32 different
+    banks (bank = word mod 64)."""
+    return len({(a // 4) % 64 for a in addrs}) == len(addrs)
+
+
+@pytest.mark.parametrize("name", sorted(TILES))
+def test_transposing_stores_hit_distinct_banks(name):
+    """Each half-wavefront of a 32-bit transposing store writes 32 different
+    banks (the padded groups' purpose)."""
+    t = TILES[name]
+    for line in t.stage_stores(0, 0):
+        m2 = re.match(r"ds_write2st64_b32 %\[w([AB])\], v\d+, v\d+ offset0:(\d+) offset1:\d+$", line)
+        if not m2:
+            continue
+        op, o0 = m2.group(1), int(m2.group(2))
+        for first in range(0, t.THREADS, 32):
+            addrs = [(w_a(t, tid) if op == "A" else w_b(t, tid)) + 256 * o0 for tid in range(first, first + 32)]
+            assert _bank_conflict_free_32bit(addrs), (name, line, first)
+
+
+@pytest.mark.parametrize("name", sorted(TILES))
+def test_loop_structure(name):
+    t = TILES[name]
     prog = t.program()
     mfmas = [l for l in prog if l.startswith("v_mfma")]
     # the prologue issues no MFMA; a pair of K steps and the odd step: 3 x 64
@@ -173,13 +217,13 @@ def test_loop_structure(bm):
             assert int(r) <= t.last_vgpr()
 
 
-@pytest.mark.parametrize("bm", sorted(TILES))
-def test_staging_sets_are_waited_for_before_their_stores(bm):
+@pytest.mark.parametrize("name", sorted(TILES))
+def test_staging_sets_are_waited_for_before_their_stores(name):
     """With DEPTH staging sets, the loop's stores of stage n + 1 follow a
     vmcnt wait that leaves at most the younger DEPTH - 1 stages' loads in
     flight, and each set is reloaded only after an lgkmcnt(0) that follows
     its stores (the stores have read the registers)."""
-    t = TILES[bm]
+    t = TILES[name]
     per_stage = t.A_LOADS + t.B_LOADS
     for cur in (0, 1):
         step = t.k_step(cur)
