@@ -113,7 +113,7 @@ Geometry geometry10(int M, int N, int K) {
   switch (d.plan) {
     case Plan::kFewRows: return few_rows_geometry(M, N, K);
     case Plan::kFewCols: return few_cols_geometry(M, N, K);
-    case Plan::kSplitK: return mfma_split_geometry(d.shape, M, N, K, d.k_split);
+    case Plan::kSplitK: return tiles_split_geometry(d.shape, M, N, K, d.k_split);
     default: return tiles_geometry(d.shape, d.Mm, d.Nm, K);
   }
 }

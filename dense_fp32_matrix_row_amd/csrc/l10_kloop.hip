@@ -106,13 +106,25 @@ __device__ __forceinline__ void b_map(int tid, int h, int& k, int& col) {
   }
 }
 
-template <int BM, bool TA, bool TB>
+// SPLIT (split K): work item i is K slice i / ntiles, k in
+// [slice k_split, min(K, (slice + 1) k_split)), of tile i % ntiles, and
+// stores its raw sums (no alpha, beta or C) into plane `slice` of ws, an
+// M x N row-major array per slice; the reduction kernel adds the planes in
+// slice order.
+template <int BM, bool TA, bool TB, bool SPLIT>
 __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem p, int64_t tiles_m,
-                                                                       int64_t tiles_n) {
+                                                                       int64_t tiles_n,
+                                                                       int64_t k_split,
+                                                                       float* __restrict__ ws) {
   typedef KTile<BM, TA, TB> T;
   __shared__ __align__(16) char smem[T::LDS];
+  const int64_t ntiles = tiles_m * tiles_n;
+  const int64_t item = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int64_t t = SPLIT ? item % ntiles : item;
+  const int64_t slice = SPLIT ? item / ntiles : 0;
+  const int64_t k_lo = slice * k_split;
+  const int K = SPLIT ? static_cast<int>(p.K - k_lo < k_split ? p.K - k_lo : k_split) : p.K;
   // tile order: XCD-contiguous ranges, grouped by GROUP_M rows of tiles
-  const int64_t t = xcd_contiguous(blockIdx.x, gridDim.x);
   const int64_t group = T::GROUP_M * tiles_n;
   const int64_t first_m = (t / group) * T::GROUP_M;
   const int64_t gm = tiles_m - first_m < T::GROUP_M ? tiles_m - first_m : T::GROUP_M;
@@ -123,18 +135,18 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int wm = wave / 2, wn = wave % 2, lrow = lane % 16, kg = lane / 16;
   const int64_t lda = p.lda, ldb = p.ldb;
-  // The tile's part of A (rows row0 .. row0 + BM - 1, k < K) and of B
-  // (k < K, columns col0 .. col0 + 127), as stored: element (m, k) of the
-  // tile's A at a_base[m a_rs + k a_ks], element (k, n) of B at
-  // b_base[k b_ks + n b_cs].
-  const float* const a_base = TA ? p.A + row0 : p.A + row0 * lda;
-  const float* const b_base = TB ? p.B + col0 * ldb : p.B + col0;
+  // The tile's part of A (rows row0 .. row0 + BM - 1, k_lo <= k < k_lo + K)
+  // and of B (those k, columns col0 .. col0 + 127), as stored: element
+  // (m, k_lo + k) of A at a_base[m a_rs + k a_ks], element (k_lo + k, n) of
+  // B at b_base[k b_ks + n b_cs].
   const int64_t a_rs = TA ? 1 : lda, a_ks = TA ? lda : 1;
   const int64_t b_ks = TB ? 1 : ldb, b_cs = TB ? ldb : 1;
+  const float* const a_base = p.A + row0 * a_rs + k_lo * a_ks;
+  const float* const b_base = p.B + col0 * b_cs + k_lo * b_ks;
   const intx4 rsA =
-      buffer_resource(a_base, static_cast<uint32_t>(((BM - 1) * a_rs + (p.K - 1) * a_ks + 1) * 4));
+      buffer_resource(a_base, static_cast<uint32_t>(((BM - 1) * a_rs + (K - 1) * a_ks + 1) * 4));
   const intx4 rsB =
-      buffer_resource(b_base, static_cast<uint32_t>(((p.K - 1) * b_ks + (T::BN - 1) * b_cs + 1) * 4));
+      buffer_resource(b_base, static_cast<uint32_t>(((K - 1) * b_ks + (T::BN - 1) * b_cs + 1) * 4));
   uint32_t oA[2], oB[2] = {0, 0};
 #pragma unroll
   for (int h = 0; h < T::A_LOADS; ++h) {
@@ -170,7 +182,7 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
   const uint32_t stepB = static_cast<uint32_t>(T::BK * b_ks * 4);
 
   // stage 0: k < k0, into buffer 0 through the same element maps
-  const int k0 = p.K % T::BK ? p.K % T::BK : T::BK;
+  const int k0 = K % T::BK ? K % T::BK : T::BK;
   const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int h = 0; h < T::A_LOADS; ++h) {
@@ -207,7 +219,7 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
     }
   }
   uint32_t sA = static_cast<uint32_t>(k0 * a_ks * 4), sB = static_cast<uint32_t>(k0 * b_ks * 4);
-  const int stages = (p.K + T::BK - 1) / T::BK;
+  const int stages = (K + T::BK - 1) / T::BK;
   uint32_t pairs = static_cast<uint32_t>(stages / 2);
   const uint32_t odd = static_cast<uint32_t>(stages % 2);
   floatx16 a0 = {}, a1 = {}, a2 = {}, a3 = {};
@@ -225,6 +237,17 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
   // outputs of one row.  With beta != 0 the four rows of one r are read
   // before any is written (the loads cannot move above earlier stores).
   const floatx16 acc[4] = {a0, a1, a2, a3};
+  if (SPLIT) {
+    float* const w = ws + slice * int64_t(p.M) * p.N + (row0 + wm * 64 + 16 * kg) * p.N + col0 +
+                     wn * 64 + 4 * lrow;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st_global4(w + (4 * r + i) * int64_t(p.N),
+                   make_float4(acc[i][r], acc[i][4 + r], acc[i][8 + r], acc[i][12 + r]));
+    return;
+  }
   const float alpha = p.alpha, beta = p.beta;
   float* const cw = p.C + (row0 + wm * 64 + 16 * kg) * p.ldc + col0 + wn * 64 + 4 * lrow;
 #pragma unroll
@@ -261,21 +284,22 @@ bool fits(const Problem& p) {
   return a_end * 4 < lim && b_end * 4 < lim;
 }
 
-template <int BM, bool TA, bool TB>
-hipError_t launch_t(const Problem& p, hipStream_t s) {
+template <int BM, bool TA, bool TB, bool SPLIT>
+hipError_t launch_t(const Problem& p, int64_t k_split, float* ws, hipStream_t s) {
   typedef KTile<BM, TA, TB> T;
   const int64_t tm = p.M / BM, tn = p.N / T::BN;
-  hipLaunchKernelGGL((k_kloop<BM, TA, TB>), dim3(static_cast<unsigned>(tm * tn)), dim3(T::THREADS),
-                     0, s, p, tm, tn);
+  const int64_t items = tm * tn * (SPLIT ? ceil_div(p.K, k_split) : 1);
+  hipLaunchKernelGGL((k_kloop<BM, TA, TB, SPLIT>), dim3(static_cast<unsigned>(items)),
+                     dim3(T::THREADS), 0, s, p, tm, tn, k_split, ws);
   return hipGetLastError();
 }
 
-template <int BM>
-hipError_t launch(const Problem& p, hipStream_t s) {
-  if (p.trans_a && p.trans_b) return launch_t<BM, true, true>(p, s);
-  if (p.trans_a) return launch_t<BM, true, false>(p, s);
-  if (p.trans_b) return launch_t<BM, false, true>(p, s);
-  return launch_t<BM, false, false>(p, s);
+template <int BM, bool SPLIT>
+hipError_t launch(const Problem& p, int64_t k_split, float* ws, hipStream_t s) {
+  if (p.trans_a && p.trans_b) return launch_t<BM, true, true, SPLIT>(p, k_split, ws, s);
+  if (p.trans_a) return launch_t<BM, true, false, SPLIT>(p, k_split, ws, s);
+  if (p.trans_b) return launch_t<BM, false, true, SPLIT>(p, k_split, ws, s);
+  return launch_t<BM, false, false, SPLIT>(p, k_split, ws, s);
 }
 
 }  // namespace
@@ -303,7 +327,32 @@ Geometry tiles_geometry(Shape shape, int M, int N, int K) {
 
 hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s) {
   if (!kloop_fits(shape, p)) return launch_mfma(shape, p, s);
-  return shape == Shape::kHuge ? launch<256>(p, s) : launch<128>(p, s);
+  return shape == Shape::kHuge ? launch<256, false>(p, p.K, nullptr, s)
+                               : launch<128, false>(p, p.K, nullptr, s);
+}
+
+Geometry tiles_split_geometry(Shape shape, int M, int N, int K, int64_t k_split) {
+  Problem p{};
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.lda = K;
+  p.ldb = N;
+  p.ldc = N;
+  if (!kloop_fits(shape, p)) return mfma_split_geometry(shape, M, N, K, k_split);
+  const int bm = shape == Shape::kHuge ? 256 : 128;
+  Geometry g = make_geometry(M, N, K, bm, 128, 16, bm == 256 ? 512 : 256);
+  g.tiles *= ceil_div(K, k_split);
+  g.workgroups = g.tiles;
+  g.k_steps = ceil_div(k_split, 16);
+  return g;
+}
+
+hipError_t launch_tiles_split(Shape shape, const Problem& p, int64_t k_split, float* ws,
+                              hipStream_t s) {
+  if (!kloop_fits(shape, p)) return launch_mfma_split(shape, p, k_split, ws, s);
+  return shape == Shape::kHuge ? launch<256, true>(p, k_split, ws, s)
+                               : launch<128, true>(p, k_split, ws, s);
 }
 
 }  // namespace sgemm

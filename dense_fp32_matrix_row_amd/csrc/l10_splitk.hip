@@ -105,7 +105,7 @@ hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStre
   void* ws = nullptr;
   e = hipMallocFromPoolAsync(&ws, bytes, pool, s);
   if (e != hipSuccess) return e;
-  e = launch_mfma_split(shape, p, k_split, static_cast<float*>(ws), s);
+  e = launch_tiles_split(shape, p, k_split, static_cast<float*>(ws), s);
   if (e == hipSuccess) e = launch_reduce(static_cast<const float*>(ws), splits, p, s);
   const hipError_t f = hipFreeAsync(ws, s);
   return e != hipSuccess ? e : f;

@@ -168,6 +168,11 @@ hipError_t launch_mfma(Shape shape, const Problem& p, hipStream_t s);
 bool kloop_fits(Shape shape, const Problem& p);
 hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s);
 Geometry tiles_geometry(Shape shape, int M, int N, int K);  // of launch_tiles, dense row-major
+// The same kernels over K slices (see launch_mfma_split): work item (tile,
+// slice) stores raw sums into plane `slice` of ws.
+hipError_t launch_tiles_split(Shape shape, const Problem& p, int64_t k_split, float* ws,
+                              hipStream_t s);
+Geometry tiles_split_geometry(Shape shape, int M, int N, int K, int64_t k_split);
 // Split K over the same tiles: the K range is cut into slices of k_split
 // (a multiple of the shape's BK) and each (tile, slice) is one work item
 // that stores raw float32 sums into its slice's M x N plane of ws.

@@ -109,9 +109,10 @@ def test_launch_shapes():
     assert shape == {"workgroups": 512, "threads": 256, "k_steps": 128, "tile_m": 128, "tile_n": 128}
     # ... split K for a deep K over a small grid: 8 slices of 512 over the
     # 64 tiles of 128 x 128 at 1024 x 1024 x 4096, 4 slices of 2048 over the
-    # 128 tiles of 256 x 128 at 2048 x 2048 x 8192 ...
+    # 128 tiles of 256 x 128 at 2048 x 2048 x 8192 (both on the assembly
+    # loops: 16-deep stages) ...
     shape = sgemm.hip_sgemm_launch_shape(10, 1024, 1024, 4096)
-    assert shape == {"workgroups": 512, "threads": 256, "k_steps": 16, "tile_m": 128, "tile_n": 128}
+    assert shape == {"workgroups": 512, "threads": 256, "k_steps": 32, "tile_m": 128, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(10, 2048, 2048, 8192)
     assert shape == {"workgroups": 512, "threads": 512, "k_steps": 128, "tile_m": 256, "tile_n": 128}
     # ... and otherwise 64 x 64 tiles with two K slices (1024^3, 3072^3, and

@@ -214,3 +214,61 @@ def test_loops_deterministic_and_agree():
     # tiles 0 and 1 accumulate every output in the same order (16-deep
     # stages, k = 4 s + lane/16 per MFMA step, one chain per block)
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("tile", sorted(TILE_SHAPES))
+@pytest.mark.parametrize("splits", [2, 3, 7])
+def test_kloop_split_k(tile, splits):
+    """hip_sgemm_tile_split(tile, splits) on whole tiles runs the assembly
+    loops over K slices (each slice's first stage takes its own K % 16
+    leftover; the last slice is short) and the in-order reduction."""
+    bm, bn = TILE_SHAPES[tile]
+    M, N, K = 2 * bm, 3 * bn, 1001
+    print(f"[kloop split] tile {tile} {M}x{N}x{K} in {splits}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 13300 + tile + splits)
+
+    def call(*args):
+        return sgemm.hip_sgemm_tile_split(tile, splits, *args)
+    out, st = gh.run(gh.Case(M, N, K, 0.5, 3.0, A, B, C), call)
+    assert st == 0
+    ref = oracle.oracle_sgemm(A, B, C, 0.5, 3.0)
+    assert oracle.normalised_error(out, ref, C, 0.5, 3.0, strict=True) <= BOUND
+
+
+@pytest.mark.parametrize("tile", sorted(TILE_SHAPES))
+def test_kloop_split_k_integer_exact_deterministic(tile):
+    bm, bn = TILE_SHAPES[tile]
+    M, N, K = 2 * bm, 2 * bn, 1500
+    A, B, C = inputs.integer_abc(M, N, K, seed=13400 + tile)
+    ref = oracle.oracle_sgemm(A, B, C, 2.0, -1.0)
+
+    def call(*args):
+        return sgemm.hip_sgemm_tile_split(tile, 6, *args)
+    first, st = gh.run(gh.Case(M, N, K, 2.0, -1.0, A, B, C), call)
+    again, st2 = gh.run(gh.Case(M, N, K, 2.0, -1.0, A, B, C), call)
+    assert st == st2 == 0
+    assert np.array_equal(first.astype(np.float64), ref.ref)
+    assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+
+
+def test_kloop_split_k_every_orientation():
+    """Level 10's split plan (1024 x 1024 x 4096: 8 slices of 128 x 128
+    tiles) in every orientation: the same bits, within the bound."""
+    M, N, K = 1024, 1024, 4096
+    print(f"[kloop split orientations] {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 13500)
+    rows = _rows(M)
+    ref = oracle.oracle_sgemm(A[rows], B, C[rows], 1.0, 1.0)
+    outs = {}
+    for op_a, op_b in OPS:
+        sa = np.ascontiguousarray(A.T) if op_a == "T" else A
+        sb = np.ascontiguousarray(B.T) if op_b == "T" else B
+
+        def call(*args, op_a=op_a, op_b=op_b):
+            return sgemm.hip_sgemm_ex(op_a, op_b, *args)
+        out, st = gh.run(gh.Case(M, N, K, 1.0, 1.0, sa, sb, C, sa.shape[1], sb.shape[1], N), call)
+        assert st == 0
+        assert oracle.normalised_error(out[rows], ref, C[rows], 1.0, 1.0, strict=True) <= BOUND
+        outs[op_a + op_b] = out
+    for key in ("NT", "TN", "TT"):
+        assert np.array_equal(outs["NN"].view(np.uint32), outs[key].view(np.uint32)), key
