@@ -63,14 +63,14 @@ Decomp decompose(int M, int N, int K) {
       return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, Shape::kHuge, M - mr, N - nr, K};
   }
 
-  // 2. Deep K over a small tile grid: split K so that about two work items
-  //    per CU run (1024 x 1024 x 4096: 128 x 128 in 8 slices 97 TFLOP/s
-  //    against 80 unsplit; 1024 x 1024 x 8192: 113 in 16 slices;
-  //    2048 x 2048 x 8192: 256 x 128 in 4 slices 126-131 against 115;
-  //    512 x 512 x 8192: 74-77 against 19).  Slices stay >= 256
-  //    deep (512 for the big tile) and at most 16.
+  // 2. Deep K over less than one round of 128 x 128 tiles: split K so that
+  //    about two work items per CU run (1024 x 1024 x 4096: 128 x 128 in
+  //    8 slices 108 TFLOP/s against 38 unsplit; 1024 x 1024 x 8192: 127-128
+  //    in 4-8 slices; 512 x 512 x 8192: 84-88 against 9).  Slices stay
+  //    >= 256 deep (512 for the big tile) and at most 16.  (A full round,
+  //    2048 x 2048 x 8192, runs unsplit: 148.5 against 144 in 2-4 slices.)
   const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
-  if (K >= 2048 && K >= 2 * int64_t(M > N ? M : N) && tiles128 < 2 * kCUs) {
+  if (K >= 2048 && K >= 2 * int64_t(M > N ? M : N) && tiles128 < kCUs) {
     Shape shape = Shape::kSmall;
     int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64), min_slice = 256;
     if (M % 256 == 0 && N % 128 == 0 && int64_t(M / 256) * (N / 128) >= 64) {
@@ -99,6 +99,26 @@ Decomp decompose(int M, int N, int K) {
     if (mr <= kThin && nr <= kThin && tiles >= kCUs && round_fill(tiles) >= 0.9) {
       return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, Shape::kLarge, M - mr, N - nr, K};
     }
+  }
+
+  // 3b. A whole grid of >= 128 such tiles whose last round is partly idle:
+  //     split K into s <= 4 slices, the s with the fewest rounds of work
+  //     items per slice depth (ceil(tiles s / CUs) / s; ties to fewer
+  //     slices): 3072^3 in 4 slices 135.6 against 119.7 for the 64 x 64
+  //     tile (rule 4) and 113.6 unsplit; 1536^3 in 3 slices 91.0 against
+  //     83.6 and 79.7.  (Below 128 tiles the 64 x 64 tile wins: 1024^3
+  //     77.7 against at most 54 for split 128 x 128 tiles.)
+  if (M % 128 == 0 && N % 128 == 0 && tiles128 >= 128 && K >= 1024) {
+    int best = 1;
+    double best_cost = double(ceil_div(tiles128, kCUs));
+    for (int s = 2; s <= 4; ++s) {
+      const double cost = double(ceil_div(tiles128 * s, kCUs)) / s;
+      if (cost < best_cost - 1e-9) {
+        best = s;
+        best_cost = cost;
+      }
+    }
+    if (best > 1) return {Plan::kSplitK, Shape::kLarge, M, N, k_split_for(K, best, 16)};
   }
 
   // 4. Everything else: 64 x 64 tiles with two K slices, up to three blocks

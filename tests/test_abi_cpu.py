@@ -107,17 +107,23 @@ def test_launch_shapes():
     assert shape == {"workgroups": 256, "threads": 256, "k_steps": 19, "tile_m": 128, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(10, 2048, 4096, 2048)
     assert shape == {"workgroups": 512, "threads": 256, "k_steps": 128, "tile_m": 128, "tile_n": 128}
-    # ... split K for a deep K over a small grid: 8 slices of 512 over the
-    # 64 tiles of 128 x 128 at 1024 x 1024 x 4096, 4 slices of 2048 over the
-    # 128 tiles of 256 x 128 at 2048 x 2048 x 8192 (both on the assembly
-    # loops: 16-deep stages) ...
+    # ... split K for a deep K over less than one round of tiles: 8 slices
+    # of 512 over the 64 tiles of 128 x 128 at 1024 x 1024 x 4096 (assembly
+    # loop: 16-deep stages), while a full round (2048 x 2048 x 8192) runs
+    # unsplit ...
     shape = sgemm.hip_sgemm_launch_shape(10, 1024, 1024, 4096)
     assert shape == {"workgroups": 512, "threads": 256, "k_steps": 32, "tile_m": 128, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(10, 2048, 2048, 8192)
-    assert shape == {"workgroups": 512, "threads": 512, "k_steps": 128, "tile_m": 256, "tile_n": 128}
-    # ... and otherwise 64 x 64 tiles with two K slices (1024^3, 3072^3, and
+    assert shape == {"workgroups": 256, "threads": 256, "k_steps": 512, "tile_m": 128, "tile_n": 128}
+    # ... and over a whole 128 x 128 grid whose last round would be partly
+    # idle: 3072^3 (576 tiles) in 4 slices, 1536^3 (144 tiles) in 3 ...
+    shape = sgemm.hip_sgemm_launch_shape(10, 3072, 3072, 3072)
+    assert shape == {"workgroups": 576 * 4, "threads": 256, "k_steps": 48, "tile_m": 128, "tile_n": 128}
+    shape = sgemm.hip_sgemm_launch_shape(10, 1536, 1536, 1536)
+    assert shape == {"workgroups": 144 * 3, "threads": 256, "k_steps": 32, "tile_m": 128, "tile_n": 128}
+    # ... and otherwise 64 x 64 tiles with two K slices (1024^3, 3000^3, and
     # shapes whose fringe would be wider than 16)
-    for M, N, K in [(1024, 1024, 1024), (3072, 3072, 3072), (4096 + 17, 4096, 64)]:
+    for M, N, K in [(1024, 1024, 1024), (3000, 3000, 3000), (4096 + 17, 4096, 64)]:
         shape = sgemm.hip_sgemm_launch_shape(10, M, N, K)
         assert shape == {"workgroups": -(-M // 64) * -(-N // 64), "threads": 512,
                          "k_steps": -(-K // 32), "tile_m": 64, "tile_n": 64}
