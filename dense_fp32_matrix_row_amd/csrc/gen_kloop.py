@@ -52,7 +52,6 @@ from __future__ import annotations
 
 import os
 
-BN, BK = 128, 16
 FE, FO = 64, 72                # fragment sets
 STAGING = 80                   # first staging register
 
@@ -64,36 +63,49 @@ def _round256(n: int) -> int:
 
 
 class Tile:
-    """One block tile: BM rows, WAVES_M x 2 wavefronts, DEPTH staging sets,
-    operands as stored (TA: A given transposed, K x M; TB: B given
-    transposed, N x K)."""
+    """One block tile of BM x BN, 64 x 64 wavefront tiles (WAVES_M x WAVES_N
+    of them, each shared by KSLICES wavefronts that split every stage's MFMA
+    steps), BK-deep stages, DEPTH staging register sets, operands as stored
+    (TA: A given transposed, K x M; TB: B given transposed, N x K)."""
 
-    STEPS = 4                                         # MFMA steps per stage
-
-    def __init__(self, bm: int, waves_m: int, depth: int, ta: bool = False, tb: bool = False):
-        self.BM, self.WAVES_M, self.DEPTH, self.TA, self.TB = bm, waves_m, depth, ta, tb
-        self.THREADS = 64 * 2 * waves_m
-        # floats per four-k group: 8 words of pad where the stage store
+    def __init__(self, bm: int, bn: int, bk: int, waves_m: int, waves_n: int, kslices: int,
+                 depth: int, ta: bool = False, tb: bool = False):
+        self.BM, self.BN, self.BK = bm, bn, bk
+        self.WAVES_M, self.WAVES_N, self.KSLICES, self.DEPTH = waves_m, waves_n, kslices, depth
+        self.TA, self.TB = ta, tb
+        self.THREADS = 64 * waves_m * waves_n * kslices
+        self.GROUPS = bk // 4                         # four-k groups (MFMA steps) per stage
+        self.STEPS = self.GROUPS // kslices           # MFMA steps per stage per wavefront
+        # floats per four-k group: a few words of pad where the stage store
         # transposes (a row-major A, a transposed B), so that its 32-bit
         # writes hit 32 different banks per half-wavefront
-        self.A_GROUP = 4 * bm + (0 if ta else 8)
-        self.B_GROUP = 4 * BN + (8 if tb else 0)
-        self.A_STAGE = _round256(4 * self.A_GROUP * 4)   # bytes, a whole number of 256
-        self.B_STAGE = _round256(4 * self.B_GROUP * 4)
-        self.A_LOADS = bm * BK // 4 // self.THREADS   # A float4s per thread per stage
-        self.B_LOADS = BK * BN // 4 // self.THREADS   # B float4s per thread per stage
+        pad = 8 if bk == 16 else 4
+        self.A_GROUP = 4 * bm + (0 if ta else pad)
+        self.B_GROUP = 4 * bn + (pad if tb else 0)
+        self.A_STAGE = _round256(self.GROUPS * self.A_GROUP * 4)   # bytes, a whole number of 256
+        self.B_STAGE = _round256(self.GROUPS * self.B_GROUP * 4)
+        self.A_LOADS = bm * bk // 4 // self.THREADS   # A float4s per thread per stage
+        self.B_LOADS = bk * bn // 4 // self.THREADS   # B float4s per thread per stage
         self.SET = 4 * (self.A_LOADS + self.B_LOADS)  # staging words per set
         self.LDS = 2 * self.A_STAGE + 2 * self.B_STAGE
-        assert self.A_LOADS * self.THREADS * 4 == bm * BK and self.B_LOADS * self.THREADS * 4 == BK * BN
-        assert bm % 64 == 0 and self.THREADS % 256 == 0
-        assert STAGING + depth * self.SET <= 128
+        assert bm == 64 * waves_m and bn == 64 * waves_n and self.STEPS >= 2
+        assert self.A_LOADS * self.THREADS * 4 == bm * bk and self.B_LOADS * self.THREADS * 4 == bk * bn
+        assert STAGING + depth * self.SET <= 256
 
     @property
     def name(self) -> str:
-        return f"{self.BM}_{'T' if self.TA else 'N'}{'T' if self.TB else 'N'}"
+        return f"{self.BM}x{self.BN}_{'T' if self.TA else 'N'}{'T' if self.TB else 'N'}"
 
     def last_vgpr(self) -> int:
         return STAGING + self.DEPTH * self.SET - 1
+
+    # -- per-thread element maps (restated by the kernel and the tests) ------
+    def a_per(self) -> int:
+        """A float4s per row (row-major A) or per k-row (transposed A)."""
+        return self.BM // 4 if self.TA else self.BK // 4
+
+    def b_per(self) -> int:
+        return self.BK // 4 if self.TB else self.BN // 4
 
     # -- instruction builders ------------------------------------------------
     def mfma(self, b: int, fs: int) -> str:
@@ -101,7 +113,9 @@ class Tile:
         return f"v_mfma_f32_16x16x4_f32 v[{4*b}:{4*b+3}], v{fs+i}, v{fs+4+j}, v[{4*b}:{4*b+3}]"
 
     def frag_reads(self, fs: int, s: int, buf: int) -> list[str]:
-        """MFMA step s of LDS buffer buf into fragment set fs."""
+        """MFMA step s (of this wavefront's slice) of LDS buffer buf into
+        fragment set fs; the kernel's base addresses point at the slice's
+        first group."""
         return [f"ds_read_b128 v[{fs}:{fs+3}], %[rA] offset:{s * self.A_GROUP * 4 + buf * self.A_STAGE}",
                 f"ds_read_b128 v[{fs+4}:{fs+7}], %[rB] offset:{s * self.B_GROUP * 4 + buf * self.B_STAGE}"]
 
@@ -123,60 +137,84 @@ class Tile:
     ADVANCE = ["s_add_u32 %[sA], %[sA], %[stepA]", "s_add_u32 %[sB], %[sB], %[stepB]"]
 
     @staticmethod
-    def _transposing(w: str, r: int, u: int, row_units: int, copy_units: int, copies: int) -> list[str]:
+    def _transposing(w: str, r: int, buf: int, stage: int, row: int, copy: int, copies: int) -> list[str]:
         """Float4s v[r + 4h ..] that each hold k = 4 q .. 4 q + 3 of one m
-        (n) go to four k-rows of group q, row_units 256-byte units apart;
-        copy h is copy_units further."""
+        (n) go to four k-rows of group q, `row` words apart; copy h is
+        h `copy` words further.  Offsets in 256-byte units where every one
+        is a whole number of them (ds_write2st64_b32, the buffer as an
+        offset), else in words (ds_write2_b32, the buffer by its own base
+        register)."""
         out = []
-        for h in range(copies):
-            for c0, c1 in ((0, 1), (2, 3)):
-                out.append(f"ds_write2st64_b32 %[{w}], v{r + 4*h + c0}, v{r + 4*h + c1} "
-                           f"offset0:{u + c0 * row_units + h * copy_units} "
-                           f"offset1:{u + c1 * row_units + h * copy_units}")
+        if row % 64 == 0 and copy % 64 == 0:
+            u = buf * (stage // 256)
+            for h in range(copies):
+                for c0, c1 in ((0, 1), (2, 3)):
+                    out.append(f"ds_write2st64_b32 %[{w}], v{r + 4*h + c0}, v{r + 4*h + c1} "
+                               f"offset0:{u + (c0 * row + h * copy) // 64} "
+                               f"offset1:{u + (c1 * row + h * copy) // 64}")
+        else:
+            base = w if buf == 0 else w + "1"
+            for h in range(copies):
+                for c0, c1 in ((0, 1), (2, 3)):
+                    o0, o1 = c0 * row + h * copy, c1 * row + h * copy
+                    assert o1 <= 255
+                    out.append(f"ds_write2_b32 %[{base}], v{r + 4*h + c0}, v{r + 4*h + c1} "
+                               f"offset0:{o0} offset1:{o1}")
         return out
 
     def stage_stores(self, st: int, buf: int) -> list[str]:
-        """Staging set st into LDS buffer buf.  A row-major A's float4 holds
-        k = 4 q .. 4 q + 3 of one row (thread: row tid/4, q = tid%4; copy h
-        THREADS/4 rows on) and is transposed into four k-rows of group q; a
-        transposed A's float4 holds four rows of one k-row (thread: k-row
-        tid/(BM/4), rows 4 (tid%(BM/4)) ..; copy h 8 k-rows = 2 groups on)
-        and is stored whole.  B likewise: row-major, four columns of one
-        k-row (k-row tid/32, columns 4 (tid%32) ..; copy h THREADS/32 k-rows
-        on), stored whole; transposed, k = 4 q .. of one column (column
-        tid/4, q = tid%4; copy h THREADS/4 columns on), transposed."""
+        """Staging set st into LDS buffer buf.  Element maps (copy h of
+        thread tid; per = float4s per row or k-row, a_per / b_per):
+          A row-major:  row tid/per + h THREADS/per, k 4 (tid%per) .. +3:
+                        transposed into four k-rows of a group;
+          A transposed: k-row tid/per + h THREADS/per, rows 4 (tid%per) ..:
+                        stored whole;
+          B row-major:  k-row tid/per + h THREADS/per, columns 4 (tid%per) ..:
+                        stored whole;
+          B transposed: column tid/per + h THREADS/per, k 4 (tid%per) .. +3:
+                        transposed."""
         r = self.set_base(st)
         rb = r + 4 * self.A_LOADS
         out = []
         if self.TA:
+            dk = self.THREADS // self.a_per()
+            assert dk % 4 == 0
             for h in range(self.A_LOADS):
                 out.append(f"ds_write_b128 %[wA], v[{r + 4*h}:{r + 4*h + 3}] "
-                           f"offset:{buf * self.A_STAGE + h * 2 * self.A_GROUP * 4}")
+                           f"offset:{buf * self.A_STAGE + h * (dk // 4) * self.A_GROUP * 4}")
         else:
-            out += self._transposing("wA", r, buf * (self.A_STAGE // 256), self.BM // 64,
-                                     self.THREADS // 256, self.A_LOADS)
+            out += self._transposing("wA", r, buf, self.A_STAGE, self.BM,
+                                     self.THREADS // self.a_per(), self.A_LOADS)
         if self.TB:
-            out += self._transposing("wB", rb, buf * (self.B_STAGE // 256), BN // 64,
-                                     self.THREADS // 256, self.B_LOADS)
+            out += self._transposing("wB", rb, buf, self.B_STAGE, self.BN,
+                                     self.THREADS // self.b_per(), self.B_LOADS)
         else:
+            dk = self.THREADS // self.b_per()
+            assert dk % 4 == 0
             for h in range(self.B_LOADS):
                 out.append(f"ds_write_b128 %[wB], v[{rb + 4*h}:{rb + 4*h + 3}] "
-                           f"offset:{buf * self.B_STAGE + h * (self.THREADS // 32) * BN * 4}")
+                           f"offset:{buf * self.B_STAGE + h * (dk // 4) * self.B_GROUP * 4}")
         return out
 
     # -- the loop ------------------------------------------------------------
     def k_step(self, cur: int) -> list[str]:
-        """One K step on LDS buffer cur (stage n with n % 2 == cur); on entry
-        set E is being read with MFMA step 0 of stage n and stage n + 1 is
-        in flight in staging set (n + 1) % DEPTH (with DEPTH 2, stage n + 2
-        in the other set behind it)."""
+        """One K step (stage) on LDS buffer cur (stage n with n % 2 == cur);
+        on entry set E is being read with this wavefront's first MFMA step
+        of stage n and stage n + 1 is in flight in staging set
+        (n + 1) % DEPTH (with DEPTH 2, stage n + 2 in the other set behind
+        it)."""
         nxt = 1 - cur
         st = nxt % self.DEPTH
         per_stage = self.A_LOADS + self.B_LOADS
         sets = (FE, FO)
         stores = self.stage_stores(st, nxt)
         loads = self.loads(st)
-        assert len(stores) <= 12 and len(loads) + 1 < 8
+        assert len(loads) + 1 < 16
+        # stores after MFMAs 4..15 of the first step (spread when more than 12)
+        store_at: dict[int, list[str]] = {}
+        for i, ins in enumerate(stores):
+            slot = 4 + i if len(stores) <= 12 else 4 + i * 12 // len(stores)
+            store_at.setdefault(slot, []).append(ins)
         out = []
         for ss in range(self.STEPS):
             fs, fn = sets[ss % 2], sets[(ss + 1) % 2]
@@ -187,8 +225,8 @@ class Tile:
                 # stage n + 1 complete (its set's loads are the older ones in
                 # flight), then stored into the free buffer
                 extra.setdefault(3, []).append(f"s_waitcnt vmcnt({per_stage * (self.DEPTH - 1)})")
-                for i, ins in enumerate(stores):
-                    extra.setdefault(4 + i, []).append(ins)
+                for slot, ins in store_at.items():
+                    extra.setdefault(slot, []).extend(ins)
             if ss == 1:
                 # the stores have completed (lgkmcnt(0) at this step's start),
                 # so the staging set may take stage n + 1 + DEPTH
@@ -228,8 +266,9 @@ class Tile:
         return prologue + pairs + odd + tail
 
 
-TILES = [Tile(bm, wm, depth, ta, tb) for bm, wm, depth in ((256, 4, 1), (128, 2, 2))
-         for ta in (False, True) for tb in (False, True)]
+# (BM, BN, BK, WAVES_M, WAVES_N, KSLICES, DEPTH)
+SHAPES = [(256, 128, 16, 4, 2, 1, 1), (128, 128, 16, 2, 2, 1, 2), (64, 64, 64, 1, 1, 4, 2)]
+TILES = [Tile(*shape, ta, tb) for shape in SHAPES for ta in (False, True) for tb in (False, True)]
 
 
 def render() -> str:

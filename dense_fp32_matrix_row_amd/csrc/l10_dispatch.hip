@@ -17,10 +17,11 @@
 //     scheduled by hand.  At 4097^3 this replaces
 //     level 9's 2145 edge-checked 128 x 64 tiles by the 512 whole 256 x 128
 //     tiles of 4096^3 (exactly two per CU) and two one-element-wide strips;
+//   - the tile shape whose grid fills the CUs best: 128 x 128 tiles, or the
+//     64 x 64 tile whose 64-deep stages are split over four wavefronts
+//     (l10_kloop.hip);
 //   - a deep K over a small tile grid: split K (l10_splitk.hip);
-//   - anything else: the tile shape whose grid fills the CUs best, with two
-//     K slices per stage where one block per CU would leave each SIMD a
-//     single wavefront.
+//   - anything else: compiled 64 x 64 tiles with two K slices per stage.
 // Every output element is computed by exactly one tile or thin kernel (or,
 // split, by one reduction over its slices); the regions are disjoint, so
 // the launches need no ordering beyond the stream's.
@@ -55,7 +56,7 @@ Decomp decompose(int M, int N, int K) {
   if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, M, N, K};
 
   // 1. At least two 256 x 128 tiles per CU (plus a fringe of <= 16): the
-  //    big tile (4096^3: 138 TFLOP/s; 4097^3 with the fringe: 127).
+  //    big tile (4096^3: 150-152 TFLOP/s; 4097^3 with the fringe: 143).
   {
     const int mr = M % 256, nr = N % 128;
     const int64_t tiles = int64_t((M - mr) / 256) * ((N - nr) / 128);
@@ -63,16 +64,50 @@ Decomp decompose(int M, int N, int K) {
       return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, Shape::kHuge, M - mr, N - nr, K};
   }
 
-  // 2. Deep K over less than one round of 128 x 128 tiles: split K so that
-  //    about two work items per CU run (1024 x 1024 x 4096: 128 x 128 in
-  //    8 slices 108 TFLOP/s against 38 unsplit; 1024 x 1024 x 8192: 127-128
-  //    in 4-8 slices; 512 x 512 x 8192: 84-88 against 9).  Slices stay
-  //    >= 256 deep (512 for the big tile) and at most 16.  (A full round,
-  //    2048 x 2048 x 8192, runs unsplit: 148.5 against 144 in 2-4 slices.)
+  // 2. 128 x 128 tiles (plus a fringe of <= 16) that fill whole rounds of
+  //    CUs, or one round at least 70 % full (2048^3: 140.8 against 132.6
+  //    for the 64 x 64 tile below; 1792^3, 196 tiles: 108.5 against 100.7;
+  //    2048 x 4096: 147; 1024 x 4096 x 1024: 130 against 119).
+  {
+    const int mr = M % 128, nr = N % 128;
+    const int64_t tiles = int64_t((M - mr) / 128) * ((N - nr) / 128);
+    const bool fills = tiles >= kCUs ? round_fill(tiles) >= 0.9 : tiles * 10 >= kCUs * 7;
+    if (mr <= kThin && nr <= kThin && fills)
+      return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, Shape::kLarge, M - mr, N - nr, K};
+  }
+
+  // 3. A whole grid of >= 64 tiles of 64 x 64: the deep-stage 64 x 64
+  //    loop (four K-slice wavefronts per tile; two blocks fit a CU), which
+  //    balances over the CUs where bigger tiles leave a round partly idle
+  //    (1024^3: 89.3 against 76.5 for the best compiled tile; 1280^3: 91.5;
+  //    1536^3: 94.7; 3072^3: 140.6 against 135.2 for 128 x 128 tiles in 4
+  //    K parts; 3584^3: 135.3; 1024 x 2048 x 4096: 133.8; 1024 x 1024 x
+  //    8192: 130.5 against 128 for split 128 x 128 tiles).  A deep K over
+  //    less than one round of these tiles is split into the most parts
+  //    (<= 16, each >= 256 deep) that keep at most two work items per CU:
+  //    512 x 512 x 8192 (64 tiles) in 8 parts 85.8 (in 4: 87.0);
+  //    768 x 768 x 4096 (144 tiles) in 3: 82.7 against 70.2 before.
+  const int64_t tiles64 = ceil_div(M, 64) * ceil_div(N, 64);
+  if (M % 64 == 0 && N % 64 == 0 && tiles64 >= 64) {
+    if (K >= 2048 && K >= 2 * int64_t(M > N ? M : N) && tiles64 < kCUs) {
+      int64_t parts = 2 * kCUs / tiles64;
+      if (parts > 16) parts = 16;
+      if (parts > K / 256) parts = K / 256;
+      if (parts >= 2) {
+        const int64_t k_split = k_split_for(K, parts, shape_bk(Shape::kSmallDeep));
+        if (k_split < K) return {Plan::kSplitK, Shape::kSmallDeep, M, N, k_split};
+      }
+    }
+    return {Plan::kTiles, Shape::kSmallDeep, M, N, K};
+  }
+
+  // 4. Deep K over less than one round of 128 x 128 tiles, M or N not a
+  //    multiple of 64: split K on compiled tiles so that about two work
+  //    items per CU run (slices >= 256 deep (512 for the big tile), <= 16).
   const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
   if (K >= 2048 && K >= 2 * int64_t(M > N ? M : N) && tiles128 < kCUs) {
     Shape shape = Shape::kSmall;
-    int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64), min_slice = 256;
+    int64_t tiles = tiles64, min_slice = 256;
     if (M % 256 == 0 && N % 128 == 0 && int64_t(M / 256) * (N / 128) >= 64) {
       shape = Shape::kHuge;
       tiles = int64_t(M / 256) * (N / 128);
@@ -90,41 +125,9 @@ Decomp decompose(int M, int N, int K) {
     }
   }
 
-  // 3. 128 x 128 tiles (plus a fringe of <= 16) when they fill whole rounds
-  //    of CUs: the assembly-loop tile (2048^3: 123-140 against 105-122 for
-  //    any compiled tile; 2048 x 4096: 142-146).
-  {
-    const int mr = M % 128, nr = N % 128;
-    const int64_t tiles = int64_t((M - mr) / 128) * ((N - nr) / 128);
-    if (mr <= kThin && nr <= kThin && tiles >= kCUs && round_fill(tiles) >= 0.9) {
-      return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, Shape::kLarge, M - mr, N - nr, K};
-    }
-  }
-
-  // 3b. A whole grid of >= 128 such tiles whose last round is partly idle:
-  //     split K into s <= 4 slices, the s with the fewest rounds of work
-  //     items per slice depth (ceil(tiles s / CUs) / s; ties to fewer
-  //     slices): 3072^3 in 4 slices 135.6 against 119.7 for the 64 x 64
-  //     tile (rule 4) and 113.6 unsplit; 1536^3 in 3 slices 91.0 against
-  //     83.6 and 79.7.  (Below 128 tiles the 64 x 64 tile wins: 1024^3
-  //     77.7 against at most 54 for split 128 x 128 tiles.)
-  if (M % 128 == 0 && N % 128 == 0 && tiles128 >= 128 && K >= 1024) {
-    int best = 1;
-    double best_cost = double(ceil_div(tiles128, kCUs));
-    for (int s = 2; s <= 4; ++s) {
-      const double cost = double(ceil_div(tiles128 * s, kCUs)) / s;
-      if (cost < best_cost - 1e-9) {
-        best = s;
-        best_cost = cost;
-      }
-    }
-    if (best > 1) return {Plan::kSplitK, Shape::kLarge, M, N, k_split_for(K, best, 16)};
-  }
-
-  // 4. Everything else: 64 x 64 tiles with two K slices, up to three blocks
-  //    per CU (1024^3: 66 against 56 unsliced; 3072^3: 115 against 73 for
-  //    128 x 128 tiles, whose 576 tiles leave the third round 1/4 full;
-  //    it beats the 128 x 64 tile at every size measured, 512^3 to 4096^3).
+  // 5. Everything else: compiled 64 x 64 tiles with two K slices, up to
+  //    three blocks per CU (3000^3: 101.5; 256^3: 3.2; it beats the
+  //    128 x 64 tile at every size measured, 512^3 to 4096^3).
   return {Plan::kTiles, Shape::kSmallSliced, M, N, K};
 }
 

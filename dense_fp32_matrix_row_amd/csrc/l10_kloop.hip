@@ -1,10 +1,14 @@
-// l10_kloop.hip -- level 10's kernels for whole 256 x 128 and 128 x 128
-// tiles: level 9's tile structure (64 x 64 wavefront tiles of 4 x 4
-// 16 x 16 blocks, 16-deep K steps, double-buffered group-padded LDS,
-// interleaved block rows and columns; eight or four wavefronts) with the K
-// loop written as assembly (l10_kloop.inc, emitted by gen_kloop.py, which
-// documents the schedule and the register map), for each orientation of
-// the operands.
+// l10_kloop.hip -- level 10's kernels for whole 256 x 128, 128 x 128 and
+// 64 x 64 tiles: level 9's tile structure (64 x 64 wavefront tiles of 4 x 4
+// 16 x 16 blocks, double-buffered group-padded LDS, interleaved block rows
+// and columns) with the K loop written as assembly (l10_kloop.inc, emitted
+// by gen_kloop.py, which documents the schedule and the register map), for
+// each orientation of the operands.  The 256 x 128 and 128 x 128 tiles take
+// 16-deep stages, one wavefront per wave tile; the 64 x 64 tile takes
+// 64-deep stages split over four wavefronts (each runs four of a stage's
+// sixteen MFMA steps for the whole tile), whose sums meet in LDS after the
+// loop, so that a tile with one wavefront per SIMD still has 64 MFMAs per
+// wavefront between barriers.
 //
 // [CP04] (section on boundary conditions and limits) attributes the last
 // 15-20 % between a hand-written FP32 GEMM and the vendor library to
@@ -43,19 +47,30 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr int round256(int n) { return (n + 255) / 256 * 256; }
 
 // The tile constants gen_kloop.py builds each loop for.
-template <int BM_, bool TA_, bool TB_>
+template <int BM_, int BN_, int BK_, int KS_, bool TA_, bool TB_>
 struct KTile {
-  static constexpr int BM = BM_, BN = 128, BK = 16, GROUP_M = 8;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, KS = KS_, GROUP_M = 8;
   static constexpr bool TA = TA_, TB = TB_;
-  static constexpr int WAVES_M = BM / 64, THREADS = 64 * 2 * WAVES_M;
-  static constexpr int A_GROUP = 4 * BM + (TA ? 0 : 8);  // floats per four-k group
-  static constexpr int B_GROUP = 4 * BN + (TB ? 8 : 0);
-  static constexpr int A_STAGE = round256(4 * A_GROUP * 4);  // bytes per stage
-  static constexpr int B_STAGE = round256(4 * B_GROUP * 4);
-  static constexpr int LDS = 2 * A_STAGE + 2 * B_STAGE;
+  static constexpr int WAVES_M = BM / 64, WAVES_N = BN / 64, WAVE_TILES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVE_TILES * KS;
+  static constexpr int GROUPS = BK / 4, STEPS = GROUPS / KS;  // MFMA steps per stage / per slice
+  static constexpr int PAD = BK == 16 ? 8 : 4;  // words between four-k groups, transposing stores
+  static constexpr int A_GROUP = 4 * BM + (TA ? 0 : PAD);  // floats per four-k group
+  static constexpr int B_GROUP = 4 * BN + (TB ? PAD : 0);
+  static constexpr int A_STAGE = round256(GROUPS * A_GROUP * 4);  // bytes per stage
+  static constexpr int B_STAGE = round256(GROUPS * B_GROUP * 4);
+  static constexpr int STAGES_LDS = 2 * A_STAGE + 2 * B_STAGE;
+  // K slices: each wavefront finishes 4 / KS block rows of its wave tile
+  // and receives them from the other slices through LDS after the loop
+  static constexpr int RED_FLOATS = KS > 1 ? WAVE_TILES * KS * KS * (4 / KS) * 16 * 64 : 0;
+  static constexpr int LDS = STAGES_LDS > 4 * RED_FLOATS ? STAGES_LDS : 4 * RED_FLOATS;
   static constexpr int A_LOADS = BM * BK / 4 / THREADS, B_LOADS = BK * BN / 4 / THREADS;
-  static_assert(A_LOADS == 2 && (B_LOADS == 1 || B_LOADS == 2), "thread-to-element map");
-  static_assert(THREADS / (BM / 4) == 8, "a transposed A's second float4 is 8 k-rows on");
+  static constexpr int A_PER = TA ? BM / 4 : BK / 4;  // float4s per (k-)row of A as stored
+  static constexpr int B_PER = TB ? BK / 4 : BN / 4;
+  static constexpr int PREFETCH = BM * BN >= 256 * 128 ? 1 : 2;  // stages loaded ahead
+  static_assert(A_LOADS >= 1 && A_LOADS <= 4 && B_LOADS >= 1 && B_LOADS <= 4, "loads per stage");
+  static_assert(THREADS % A_PER == 0 && THREADS % B_PER == 0, "whole rows per load round");
+  static_assert(4 % KS == 0 && STEPS >= 2, "K slices");
 };
 
 // Raw buffer resource (stride 0): loads at byte offsets >= bytes return 0.
@@ -69,60 +84,66 @@ __device__ __forceinline__ intx4 buffer_resource(const float* base, uint32_t byt
   return r;
 }
 
-#define SGEMM_KLOOP_OPERANDS                                                               \
+// The asm operands: the 16-deep tiles load two float4s of each operand per
+// thread and stage (at most), the 64-deep tile four, and it also takes
+// each buffer's own store base (its 32-bit stores cannot reach the second
+// buffer by an immediate).  Unused inputs would still occupy registers.
+#define SGEMM_KLOOP_OUTPUTS                                                                \
   : "+{v[0:15]}"(a0), "+{v[16:31]}"(a1), "+{v[32:47]}"(a2), "+{v[48:63]}"(a3), [sA] "+s"(sA), \
-    [sB] "+s"(sB), [pairs] "+s"(pairs)                                                     \
-  : [rsA] "s"(rsA), [rsB] "s"(rsB), [oA0] "v"(oA[0]), [oA1] "v"(oA[1]), [oB0] "v"(oB[0]),  \
-    [oB1] "v"(oB[1]), [wA] "v"(wA), [wB] "v"(wB), [rA] "v"(rA), [rB] "v"(rB),              \
-    [stepA] "s"(stepA), [stepB] "s"(stepB), [odd] "s"(odd)
-
-#define SGEMM_KLOOP_RUN(NAME) \
-  asm volatile(SGEMM_KLOOP_ASM_##NAME SGEMM_KLOOP_OPERANDS : SGEMM_KLOOP_CLOBBERS_##NAME, "memory", "scc")
+    [sB] "+s"(sB), [pairs] "+s"(pairs)
+#define SGEMM_KLOOP_INPUTS                                                                 \
+  [rsA] "s"(rsA), [rsB] "s"(rsB), [oA0] "v"(oA[0]), [oA1] "v"(oA[1]), [oB0] "v"(oB[0]),    \
+      [wA] "v"(wA), [wB] "v"(wB), [rA] "v"(rA), [rB] "v"(rB), [stepA] "s"(stepA),          \
+      [stepB] "s"(stepB), [odd] "s"(odd)
+#define SGEMM_KLOOP_RUN(NAME)                                                                 \
+  asm volatile(SGEMM_KLOOP_ASM_##NAME SGEMM_KLOOP_OUTPUTS : SGEMM_KLOOP_INPUTS, [oB1] "v"(oB[1]) \
+               : SGEMM_KLOOP_CLOBBERS_##NAME, "memory", "scc")
+#define SGEMM_KLOOP_RUN_ONE_B(NAME)                                                          \
+  asm volatile(SGEMM_KLOOP_ASM_##NAME SGEMM_KLOOP_OUTPUTS : SGEMM_KLOOP_INPUTS               \
+               : SGEMM_KLOOP_CLOBBERS_##NAME, "memory", "scc")
+#define SGEMM_KLOOP_RUN_DEEP(NAME)                                                             \
+  asm volatile(SGEMM_KLOOP_ASM_##NAME SGEMM_KLOOP_OUTPUTS                                      \
+               : SGEMM_KLOOP_INPUTS, [oB1] "v"(oB[1]), [oA2] "v"(oA[2]), [oA3] "v"(oA[3]),      \
+                 [oB2] "v"(oB[2]), [oB3] "v"(oB[3]), [wA1] "v"(wA + T::A_STAGE),               \
+                 [wB1] "v"(wB + T::B_STAGE)                                                    \
+               : SGEMM_KLOOP_CLOBBERS_##NAME, "memory", "scc")
 
 // Per-thread element maps of one stage (the loop's loads and stores, and
-// the C++ first stage, use the same ones).  Element h of a thread:
-//   A row-major:  row tid/4 + h THREADS/4, k 4 (tid%4) .. +3
-//   A transposed: k-row tid/(BM/4) + 8 h, rows 4 (tid%(BM/4)) .. +3
-//   B row-major:  k-row tid/32 + h THREADS/32, columns 4 (tid%32) .. +3
-//   B transposed: column tid/4 + h THREADS/4, k 4 (tid%4) .. +3
+// the C++ first stage, use the same ones).  Element h of a thread, with
+// per = float4s per row (k-row) of the operand as stored (A_PER, B_PER):
+//   A row-major:  row tid/per + h THREADS/per, k 4 (tid%per) .. +3
+//   A transposed: k-row tid/per + h THREADS/per, rows 4 (tid%per) .. +3
+//   B row-major:  k-row tid/per + h THREADS/per, columns 4 (tid%per) .. +3
+//   B transposed: column tid/per + h THREADS/per, k 4 (tid%per) .. +3
 template <class T>
 __device__ __forceinline__ void a_map(int tid, int h, int& row, int& k) {
-  if (T::TA) {
-    k = tid / (T::BM / 4) + 8 * h;
-    row = 4 * (tid % (T::BM / 4));
-  } else {
-    row = tid / 4 + h * (T::THREADS / 4);
-    k = 4 * (tid % 4);
-  }
+  const int major = tid / T::A_PER + h * (T::THREADS / T::A_PER), minor = 4 * (tid % T::A_PER);
+  row = T::TA ? minor : major;
+  k = T::TA ? major : minor;
 }
 template <class T>
 __device__ __forceinline__ void b_map(int tid, int h, int& k, int& col) {
-  if (T::TB) {
-    col = tid / 4 + h * (T::THREADS / 4);
-    k = 4 * (tid % 4);
-  } else {
-    k = tid / 32 + h * (T::THREADS / 32);
-    col = 4 * (tid % 32);
-  }
+  const int major = tid / T::B_PER + h * (T::THREADS / T::B_PER), minor = 4 * (tid % T::B_PER);
+  k = T::TB ? minor : major;
+  col = T::TB ? major : minor;
 }
 
-// SPLIT (split K): work item i is K slice i / ntiles, k in
-// [slice k_split, min(K, (slice + 1) k_split)), of tile i % ntiles, and
-// stores its raw sums (no alpha, beta or C) into plane `slice` of ws, an
-// M x N row-major array per slice; the reduction kernel adds the planes in
-// slice order.
-template <int BM, bool TA, bool TB, bool SPLIT>
-__global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem p, int64_t tiles_m,
-                                                                       int64_t tiles_n,
-                                                                       int64_t k_split,
-                                                                       float* __restrict__ ws) {
-  typedef KTile<BM, TA, TB> T;
+// SPLIT (split K): work item i is K part i / ntiles, k in
+// [part k_split, min(K, (part + 1) k_split)), of tile i % ntiles, and
+// stores its raw sums (no alpha, beta or C) into plane `part` of ws, an
+// M x N row-major array per part; the reduction kernel adds the planes in
+// part order.
+template <class T, bool SPLIT>
+__global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m, int64_t tiles_n,
+                                                      int64_t k_split, float* __restrict__ ws) {
+  constexpr int BM = T::BM;
+  constexpr bool TA = T::TA, TB = T::TB;
   __shared__ __align__(16) char smem[T::LDS];
   const int64_t ntiles = tiles_m * tiles_n;
   const int64_t item = xcd_contiguous(blockIdx.x, gridDim.x);
   const int64_t t = SPLIT ? item % ntiles : item;
-  const int64_t slice = SPLIT ? item / ntiles : 0;
-  const int64_t k_lo = slice * k_split;
+  const int64_t part = SPLIT ? item / ntiles : 0;  // split-K part
+  const int64_t k_lo = part * k_split;
   const int K = SPLIT ? static_cast<int>(p.K - k_lo < k_split ? p.K - k_lo : k_split) : p.K;
   // tile order: XCD-contiguous ranges, grouped by GROUP_M rows of tiles
   const int64_t group = T::GROUP_M * tiles_n;
@@ -133,10 +154,11 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
   const int64_t col0 = (in / gm) * T::BN;
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int wm = wave / 2, wn = wave % 2, lrow = lane % 16, kg = lane / 16;
+  const int slice = wave / T::WAVE_TILES, wv = wave % T::WAVE_TILES;
+  const int wm = wv / T::WAVES_N, wn = wv % T::WAVES_N, lrow = lane % 16, kg = lane / 16;
   const int64_t lda = p.lda, ldb = p.ldb;
   // The tile's part of A (rows row0 .. row0 + BM - 1, k_lo <= k < k_lo + K)
-  // and of B (those k, columns col0 .. col0 + 127), as stored: element
+  // and of B (those k, columns col0 .. col0 + BN - 1), as stored: element
   // (m, k_lo + k) of A at a_base[m a_rs + k a_ks], element (k_lo + k, n) of
   // B at b_base[k b_ks + n b_cs].
   const int64_t a_rs = TA ? 1 : lda, a_ks = TA ? lda : 1;
@@ -147,7 +169,7 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
       buffer_resource(a_base, static_cast<uint32_t>(((BM - 1) * a_rs + (K - 1) * a_ks + 1) * 4));
   const intx4 rsB =
       buffer_resource(b_base, static_cast<uint32_t>(((K - 1) * b_ks + (T::BN - 1) * b_cs + 1) * 4));
-  uint32_t oA[2], oB[2] = {0, 0};
+  uint32_t oA[4] = {0, 0, 0, 0}, oB[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int h = 0; h < T::A_LOADS; ++h) {
     int row, k;
@@ -161,10 +183,11 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
     oB[h] = static_cast<uint32_t>((k * b_ks + col * b_cs) * 4);
   }
   // LDS: A stage k-row k at group k/4, word (k%4)*BM + m; B k-row k at
-  // group k/4, word (k%4)*128 + n.  Stores start at element 0 of the
-  // thread's map (element 1 is an immediate away); fragments of step s sit
-  // in group s, a lane reading the four interleaved rows (columns)
-  // 4 lrow .. 4 lrow + 3 of its wave tile at k-row kg of the step.
+  // group k/4, word (k%4)*BN + n.  Stores start at element 0 of the
+  // thread's map (the others are immediates away); fragments of MFMA step
+  // s sit in group s, a lane reading the four interleaved rows (columns)
+  // 4 lrow .. 4 lrow + 3 of its wave tile at k-row kg of the step; a K
+  // slice's steps start at group slice * STEPS.
   const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)smem));
   float* const lds_a = reinterpret_cast<float*>(smem);
   float* const lds_b = reinterpret_cast<float*>(smem + 2 * T::A_STAGE);
@@ -175,9 +198,11 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
   const int wb_word = (b_k0 / 4) * T::B_GROUP + (b_k0 % 4) * T::BN + b_col0;
   const uint32_t wA = base + static_cast<uint32_t>(wa_word * 4);
   const uint32_t wB = base + 2 * T::A_STAGE + static_cast<uint32_t>(wb_word * 4);
-  const uint32_t rA = base + static_cast<uint32_t>((kg * BM + wm * 64 + 4 * lrow) * 4);
-  const uint32_t rB =
-      base + 2 * T::A_STAGE + static_cast<uint32_t>((kg * T::BN + wn * 64 + 4 * lrow) * 4);
+  const int g0 = slice * T::STEPS;
+  const uint32_t rA =
+      base + static_cast<uint32_t>((g0 * T::A_GROUP + kg * BM + wm * 64 + 4 * lrow) * 4);
+  const uint32_t rB = base + 2 * T::A_STAGE +
+                      static_cast<uint32_t>((g0 * T::B_GROUP + kg * T::BN + wn * 64 + 4 * lrow) * 4);
   const uint32_t stepA = static_cast<uint32_t>(T::BK * a_ks * 4);
   const uint32_t stepB = static_cast<uint32_t>(T::BK * b_ks * 4);
 
@@ -223,29 +248,71 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
   uint32_t pairs = static_cast<uint32_t>(stages / 2);
   const uint32_t odd = static_cast<uint32_t>(stages % 2);
   floatx16 a0 = {}, a1 = {}, a2 = {}, a3 = {};
-  if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_RUN(256_NN);
-  else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_RUN(256_NT);
-  else if constexpr (BM == 256 && !TB) SGEMM_KLOOP_RUN(256_TN);
-  else if constexpr (BM == 256) SGEMM_KLOOP_RUN(256_TT);
-  else if constexpr (!TA && !TB) SGEMM_KLOOP_RUN(128_NN);
-  else if constexpr (!TA) SGEMM_KLOOP_RUN(128_NT);
-  else if constexpr (!TB) SGEMM_KLOOP_RUN(128_TN);
-  else SGEMM_KLOOP_RUN(128_TT);
+  if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_RUN_ONE_B(256x128_NN);
+  else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_RUN_ONE_B(256x128_NT);
+  else if constexpr (BM == 256 && !TB) SGEMM_KLOOP_RUN_ONE_B(256x128_TN);
+  else if constexpr (BM == 256) SGEMM_KLOOP_RUN_ONE_B(256x128_TT);
+  else if constexpr (BM == 128 && !TA && !TB) SGEMM_KLOOP_RUN(128x128_NN);
+  else if constexpr (BM == 128 && !TA) SGEMM_KLOOP_RUN(128x128_NT);
+  else if constexpr (BM == 128 && !TB) SGEMM_KLOOP_RUN(128x128_TN);
+  else if constexpr (BM == 128) SGEMM_KLOOP_RUN(128x128_TT);
+  else if constexpr (!TA && !TB) SGEMM_KLOOP_RUN_DEEP(64x64_NN);
+  else if constexpr (!TA) SGEMM_KLOOP_RUN_DEEP(64x64_NT);
+  else if constexpr (!TB) SGEMM_KLOOP_RUN_DEEP(64x64_TN);
+  else SGEMM_KLOOP_RUN_DEEP(64x64_TT);
+  floatx16 acc[4] = {a0, a1, a2, a3};
+
+  // K slices: slice s finishes block rows i with i / (4 / KS) == s.  Every
+  // wavefront writes the block rows the others finish into LDS (lane-
+  // contiguous, conflict free; the stage buffers are free once every
+  // wavefront has left the loop), then adds what it receives in slice
+  // order: ((p_0 + p_1) + p_2) + p_3, the same order for every output.
+  int ilo = 0, ihi = 4;
+  if constexpr (T::KS > 1) {
+    constexpr int RPS = 4 / T::KS;  // block rows per slice
+    float* const red = reinterpret_cast<float*>(smem);
+    // red[wave tile][destination slice][source slice][row][register][lane]
+    auto at = [&](int dst, int src, int row, int e) {
+      return (((((wv * T::KS + dst) * T::KS + src) * RPS + row) * 16 + e) * 64) + lane;
+    };
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int dst = i / RPS;
+      if (dst == slice) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[at(dst, slice, i % RPS, e)] = acc[i][e];
+    }
+    __syncthreads();
+    ilo = slice * RPS;
+    ihi = ilo + RPS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < ilo || i >= ihi) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float sum = slice == 0 ? acc[i][e] : red[at(slice, 0, i % RPS, e)];
+#pragma unroll
+        for (int src = 1; src < T::KS; ++src) sum += src == slice ? acc[i][e] : red[at(slice, src, i % RPS, e)];
+        acc[i][e] = sum;
+      }
+    }
+  }
 
   // Block (i, j) register r holds C[row0 + 64 wm + 16 kg + 4 r + i]
   // [col0 + 64 wn + 4 lrow + j]: for each (r, i) a lane owns four adjacent
-  // outputs of one row.  With beta != 0 the four rows of one r are read
-  // before any is written (the loads cannot move above earlier stores).
-  const floatx16 acc[4] = {a0, a1, a2, a3};
+  // outputs of one row.  With beta != 0 the rows of one r are read before
+  // any is written (the loads cannot move above earlier stores).
   if (SPLIT) {
-    float* const w = ws + slice * int64_t(p.M) * p.N + (row0 + wm * 64 + 16 * kg) * p.N + col0 +
+    float* const w = ws + part * int64_t(p.M) * p.N + (row0 + wm * 64 + 16 * kg) * p.N + col0 +
                      wn * 64 + 4 * lrow;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        st_global4(w + (4 * r + i) * int64_t(p.N),
-                   make_float4(acc[i][r], acc[i][4 + r], acc[i][8 + r], acc[i][12 + r]));
+        if (i >= ilo && i < ihi)
+          st_global4(w + (4 * r + i) * int64_t(p.N),
+                     make_float4(acc[i][r], acc[i][4 + r], acc[i][8 + r], acc[i][12 + r]));
     return;
   }
   const float alpha = p.alpha, beta = p.beta;
@@ -255,10 +322,12 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
     float4 old[4];
     if (beta != 0.0f) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) old[i] = ld_global4(cw + (4 * r + i) * p.ldc);
+      for (int i = 0; i < 4; ++i)
+        if (i >= ilo && i < ihi) old[i] = ld_global4(cw + (4 * r + i) * p.ldc);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      if (i < ilo || i >= ihi) continue;
       float4 v = make_float4(alpha * acc[i][r], alpha * acc[i][4 + r], alpha * acc[i][8 + r],
                              alpha * acc[i][12 + r]);
       if (beta != 0.0f) {
@@ -272,44 +341,57 @@ __global__ __launch_bounds__((KTile<BM, TA, TB>::THREADS)) void k_kloop(Problem 
   }
 }
 
-template <int BM>
+template <class T>
 bool fits(const Problem& p) {
-  if (p.M <= 0 || p.N <= 0 || p.M % BM || p.N % 128 || p.K < 1) return false;
+  if (p.trans_a != T::TA || p.trans_b != T::TB) return false;
+  if (p.M <= 0 || p.N <= 0 || p.M % T::BM || p.N % T::BN || p.K < 1) return false;
   // largest byte offset of a load (record counts, plus the stages the loop
-  // prefetches past K: one for the 256-row tile, two for the 128-row one)
-  // stays below 2^31
-  const int64_t lim = int64_t(1) << 31, past = p.K + ((BM == 256 ? 1 : 2) + 1) * 16;
-  const int64_t a_end = p.trans_a ? past * p.lda + BM : (BM - 1) * p.lda + past;
-  const int64_t b_end = p.trans_b ? 127 * p.ldb + past : past * p.ldb + 128;
+  // prefetches past K) stays below 2^31
+  const int64_t lim = int64_t(1) << 31, past = p.K + (T::PREFETCH + 1) * T::BK;
+  const int64_t a_end = T::TA ? past * p.lda + T::BM : (T::BM - 1) * p.lda + past;
+  const int64_t b_end = T::TB ? (T::BN - 1) * p.ldb + past : past * p.ldb + T::BN;
   return a_end * 4 < lim && b_end * 4 < lim;
 }
 
-template <int BM, bool TA, bool TB, bool SPLIT>
+template <class T, bool SPLIT>
 hipError_t launch_t(const Problem& p, int64_t k_split, float* ws, hipStream_t s) {
-  typedef KTile<BM, TA, TB> T;
-  const int64_t tm = p.M / BM, tn = p.N / T::BN;
+  const int64_t tm = p.M / T::BM, tn = p.N / T::BN;
   const int64_t items = tm * tn * (SPLIT ? ceil_div(p.K, k_split) : 1);
-  hipLaunchKernelGGL((k_kloop<BM, TA, TB, SPLIT>), dim3(static_cast<unsigned>(items)),
-                     dim3(T::THREADS), 0, s, p, tm, tn, k_split, ws);
+  hipLaunchKernelGGL((k_kloop<T, SPLIT>), dim3(static_cast<unsigned>(items)), dim3(T::THREADS), 0, s,
+                     p, tm, tn, k_split, ws);
   return hipGetLastError();
 }
 
-template <int BM, bool SPLIT>
-hipError_t launch(const Problem& p, int64_t k_split, float* ws, hipStream_t s) {
-  if (p.trans_a && p.trans_b) return launch_t<BM, true, true, SPLIT>(p, k_split, ws, s);
-  if (p.trans_a) return launch_t<BM, true, false, SPLIT>(p, k_split, ws, s);
-  if (p.trans_b) return launch_t<BM, false, true, SPLIT>(p, k_split, ws, s);
-  return launch_t<BM, false, false, SPLIT>(p, k_split, ws, s);
+// The tile of each shape (orientation as given); f(tile type) is called
+// with the one that applies.
+template <int BM, int BN, int BK, int KS, class F>
+auto with_orientation(const Problem& p, F f) {
+  if (p.trans_a && p.trans_b) return f(KTile<BM, BN, BK, KS, true, true>());
+  if (p.trans_a) return f(KTile<BM, BN, BK, KS, true, false>());
+  if (p.trans_b) return f(KTile<BM, BN, BK, KS, false, true>());
+  return f(KTile<BM, BN, BK, KS, false, false>());
 }
+
+template <class F>
+auto with_tile(Shape shape, const Problem& p, F f) {
+  switch (shape) {
+    case Shape::kHuge: return with_orientation<256, 128, 16, 1>(p, f);
+    case Shape::kLarge: return with_orientation<128, 128, 16, 1>(p, f);
+    default: return with_orientation<64, 64, 64, 4>(p, f);
+  }
+}
+
+bool has_loop(Shape shape) {
+  return shape == Shape::kHuge || shape == Shape::kLarge || shape == Shape::kSmallDeep;
+}
+
+// The compiled tile that stands in where a loop kernel does not fit.
+Shape compiled(Shape shape) { return shape == Shape::kSmallDeep ? Shape::kSmallSliced : shape; }
 
 }  // namespace
 
 bool kloop_fits(Shape shape, const Problem& p) {
-  switch (shape) {
-    case Shape::kHuge: return fits<256>(p);
-    case Shape::kLarge: return fits<128>(p);
-    default: return false;
-  }
+  return has_loop(shape) && with_tile(shape, p, [&](auto t) { return fits<decltype(t)>(p); });
 }
 
 Geometry tiles_geometry(Shape shape, int M, int N, int K) {
@@ -320,15 +402,16 @@ Geometry tiles_geometry(Shape shape, int M, int N, int K) {
   p.lda = K;
   p.ldb = N;
   p.ldc = N;
-  if (!kloop_fits(shape, p)) return mfma_geometry(shape, M, N, K);
-  return shape == Shape::kHuge ? make_geometry(M, N, K, 256, 128, 16, 512)
-                               : make_geometry(M, N, K, 128, 128, 16, 256);
+  if (!kloop_fits(shape, p)) return mfma_geometry(compiled(shape), M, N, K);
+  return with_tile(shape, p, [&](auto t) {
+    typedef decltype(t) T;
+    return make_geometry(M, N, K, T::BM, T::BN, T::BK, T::THREADS);
+  });
 }
 
 hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s) {
-  if (!kloop_fits(shape, p)) return launch_mfma(shape, p, s);
-  return shape == Shape::kHuge ? launch<256, false>(p, p.K, nullptr, s)
-                               : launch<128, false>(p, p.K, nullptr, s);
+  if (!kloop_fits(shape, p)) return launch_mfma(compiled(shape), p, s);
+  return with_tile(shape, p, [&](auto t) { return launch_t<decltype(t), false>(p, p.K, nullptr, s); });
 }
 
 Geometry tiles_split_geometry(Shape shape, int M, int N, int K, int64_t k_split) {
@@ -339,20 +422,21 @@ Geometry tiles_split_geometry(Shape shape, int M, int N, int K, int64_t k_split)
   p.lda = K;
   p.ldb = N;
   p.ldc = N;
-  if (!kloop_fits(shape, p)) return mfma_split_geometry(shape, M, N, K, k_split);
-  const int bm = shape == Shape::kHuge ? 256 : 128;
-  Geometry g = make_geometry(M, N, K, bm, 128, 16, bm == 256 ? 512 : 256);
-  g.tiles *= ceil_div(K, k_split);
-  g.workgroups = g.tiles;
-  g.k_steps = ceil_div(k_split, 16);
-  return g;
+  if (!kloop_fits(shape, p)) return mfma_split_geometry(compiled(shape), M, N, K, k_split);
+  return with_tile(shape, p, [&](auto t) {
+    typedef decltype(t) T;
+    Geometry g = make_geometry(M, N, K, T::BM, T::BN, T::BK, T::THREADS);
+    g.tiles *= ceil_div(K, k_split);
+    g.workgroups = g.tiles;
+    g.k_steps = ceil_div(k_split, T::BK);
+    return g;
+  });
 }
 
 hipError_t launch_tiles_split(Shape shape, const Problem& p, int64_t k_split, float* ws,
                               hipStream_t s) {
-  if (!kloop_fits(shape, p)) return launch_mfma_split(shape, p, k_split, ws, s);
-  return shape == Shape::kHuge ? launch<256, true>(p, k_split, ws, s)
-                               : launch<128, true>(p, k_split, ws, s);
+  if (!kloop_fits(shape, p)) return launch_mfma_split(compiled(shape), p, k_split, ws, s);
+  return with_tile(shape, p, [&](auto t) { return launch_t<decltype(t), true>(p, k_split, ws, s); });
 }
 
 }  // namespace sgemm

@@ -70,6 +70,9 @@ int shape_bk(Shape shape) {
     case Shape::kMid: return TileMid::BK;
     case Shape::kLargeSliced: return TileLargeSliced::BK;
     case Shape::kSmallSliced: return TileSmallSliced::BK;
+    // level 10's 64 x 64 loop tile: 64-deep stages (also a multiple of the
+    // BK of the compiled tile that stands in for it)
+    case Shape::kSmallDeep: return 64;
     default: return TileSmall::BK;
   }
 }

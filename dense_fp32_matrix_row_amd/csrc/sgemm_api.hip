@@ -70,11 +70,12 @@ int run(const LevelDesc* lv, int M, int N, int K, float alpha, const float* A,
   return status_of(lv->launch(p, stream));
 }
 
-constexpr int kNumTiles = 6;
+constexpr int kNumTiles = 7;
 
 Shape tile_shape(int tile) {
-  static const Shape shapes[kNumTiles] = {Shape::kHuge,  Shape::kLarge,       Shape::kMid,
-                                          Shape::kSmall, Shape::kLargeSliced, Shape::kSmallSliced};
+  static const Shape shapes[kNumTiles] = {Shape::kHuge,        Shape::kLarge,      Shape::kMid,
+                                          Shape::kSmall,       Shape::kLargeSliced, Shape::kSmallSliced,
+                                          Shape::kSmallDeep};
   return shapes[tile];
 }
 
@@ -166,7 +167,7 @@ const char* hip_sgemm_tile_name(int tile) {
   if (tile < 0 || tile >= kNumTiles) return nullptr;
   static const char* const names[kNumTiles] = {"256x128x16_8w", "128x128x32_4w", "128x64x16_4w",
                                                "64x64x16_4w", "128x128x32_8w_2slices",
-                                               "64x64x32_8w_2slices"};
+                                               "64x64x32_8w_2slices", "64x64x64_4w_4slices"};
   return names[tile];
 }
 

@@ -151,8 +151,10 @@ hipError_t launch_scale(const Problem& p, hipStream_t stream);
 // Level 9's matrix-core tile shapes, which the dispatching rung composes:
 // Huge 256 x 128, Large 128 x 128, Mid 128 x 64, Small 64 x 64 block tiles,
 // and 128 x 128 / 64 x 64 tiles whose stages are cut into two K slices
-// (twice the wavefronts per tile; their sums meet in LDS).
-enum class Shape { kHuge, kLarge, kMid, kSmall, kLargeSliced, kSmallSliced };
+// (twice the wavefronts per tile; their sums meet in LDS).  SmallDeep is
+// level 10's 64 x 64 assembly-loop tile (64-deep stages over four K-slice
+// wavefronts); where that kernel does not fit, SmallSliced stands in.
+enum class Shape { kHuge, kLarge, kMid, kSmall, kLargeSliced, kSmallSliced, kSmallDeep };
 struct TileDims {
   int bm, bn;         // block tile
   int64_t min_tiles;  // tiles a problem needs before level 9 picks the shape
@@ -162,9 +164,10 @@ TileDims shape_dims(Shape shape);
 Geometry mfma_geometry(Shape shape, int M, int N, int K);
 hipError_t launch_mfma(Shape shape, const Problem& p, hipStream_t s);
 // Level 10's whole-tile kernels with their K loop in assembly
-// (l10_kloop.hip), for the Huge (256 x 128) and Large (128 x 128) shapes,
-// any operand orientation: M and N multiples of the tile, buffer offsets
-// below 2^31.  launch_tiles runs one where it fits, else the template kernel.
+// (l10_kloop.hip), for the Huge (256 x 128), Large (128 x 128) and
+// SmallDeep (64 x 64) shapes, any operand orientation: M and N multiples of
+// the tile, buffer offsets below 2^31.  launch_tiles runs one where it
+// fits, else the compiled tile kernel.
 bool kloop_fits(Shape shape, const Problem& p);
 hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s);
 Geometry tiles_geometry(Shape shape, int M, int N, int K);  // of launch_tiles, dense row-major

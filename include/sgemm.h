@@ -154,6 +154,8 @@ int hip_sgemm_level(int level, int M, int N, int K, float alpha,
  *           128 x 128 (BK 32, 4), 128 x 64 (BK 16, 4), 64 x 64 (BK 16, 4),
  *           and with each stage cut into two K slices whose sums meet in LDS
  *           (twice the wavefronts): 128 x 128 (BK 32, 8), 64 x 64 (BK 32, 8);
+ *           6: level 10's 64 x 64 assembly-loop tile (BK 64 split over four
+ *           wavefronts; where it does not fit, tile 5 stands in);
  *   splits  >= 1: the K range is cut into about `splits` slices (each a
  *           multiple of the tile's BK; ceil(K / slice) of them run) that
  *           compute separately, and a second kernel adds the slices' float32

@@ -102,28 +102,30 @@ def test_launch_shapes():
     shape = sgemm.hip_sgemm_launch_shape(10, 4096 + 16, 4096 + 16, 100)
     assert (shape["workgroups"], shape["tile_m"], shape["tile_n"]) == (512, 256, 128)
     # ... or the 128 x 128 tile (the assembly loop: 4 wavefronts, 16-deep
-    # stages) when they fill whole rounds of CUs ...
+    # stages) when they fill whole rounds of CUs, or one round >= 70 % ...
     shape = sgemm.hip_sgemm_launch_shape(10, 2051, 2055, 300)
     assert shape == {"workgroups": 256, "threads": 256, "k_steps": 19, "tile_m": 128, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(10, 2048, 4096, 2048)
     assert shape == {"workgroups": 512, "threads": 256, "k_steps": 128, "tile_m": 128, "tile_n": 128}
-    # ... split K for a deep K over less than one round of tiles: 8 slices
-    # of 512 over the 64 tiles of 128 x 128 at 1024 x 1024 x 4096 (assembly
-    # loop: 16-deep stages), while a full round (2048 x 2048 x 8192) runs
-    # unsplit ...
-    shape = sgemm.hip_sgemm_launch_shape(10, 1024, 1024, 4096)
-    assert shape == {"workgroups": 512, "threads": 256, "k_steps": 32, "tile_m": 128, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(10, 2048, 2048, 8192)
     assert shape == {"workgroups": 256, "threads": 256, "k_steps": 512, "tile_m": 128, "tile_n": 128}
-    # ... and over a whole 128 x 128 grid whose last round would be partly
-    # idle: 3072^3 (576 tiles) in 4 slices, 1536^3 (144 tiles) in 3 ...
-    shape = sgemm.hip_sgemm_launch_shape(10, 3072, 3072, 3072)
-    assert shape == {"workgroups": 576 * 4, "threads": 256, "k_steps": 48, "tile_m": 128, "tile_n": 128}
-    shape = sgemm.hip_sgemm_launch_shape(10, 1536, 1536, 1536)
-    assert shape == {"workgroups": 144 * 3, "threads": 256, "k_steps": 32, "tile_m": 128, "tile_n": 128}
-    # ... and otherwise 64 x 64 tiles with two K slices (1024^3, 3000^3, and
-    # shapes whose fringe would be wider than 16)
-    for M, N, K in [(1024, 1024, 1024), (3000, 3000, 3000), (4096 + 17, 4096, 64)]:
+    shape = sgemm.hip_sgemm_launch_shape(10, 1792, 1792, 1792)
+    assert shape == {"workgroups": 196, "threads": 256, "k_steps": 112, "tile_m": 128, "tile_n": 128}
+    # ... or, on a whole grid of >= 64 tiles of 64 x 64, the deep-stage
+    # 64 x 64 loop (4 K-slice wavefronts, 64-deep stages) ...
+    for M, N, K in [(1024, 1024, 1024), (1536, 1536, 1536), (3072, 3072, 3072),
+                    (1024, 1024, 4096), (512, 512, 512)]:
+        shape = sgemm.hip_sgemm_launch_shape(10, M, N, K)
+        assert shape == {"workgroups": (M // 64) * (N // 64), "threads": 256,
+                         "k_steps": -(-K // 64), "tile_m": 64, "tile_n": 64}, (M, N, K)
+    # ... split into K parts when K is deep and there is less than one round
+    # of those tiles: at most two work items per CU (512 x 512 x 8192: 64
+    # tiles in 8 parts of 1024) ...
+    shape = sgemm.hip_sgemm_launch_shape(10, 512, 512, 8192)
+    assert shape == {"workgroups": 64 * 8, "threads": 256, "k_steps": 16, "tile_m": 64, "tile_n": 64}
+    # ... and otherwise compiled 64 x 64 tiles with two K slices (3000^3,
+    # 256^3, and shapes whose fringe would be wider than 16)
+    for M, N, K in [(3000, 3000, 3000), (256, 256, 256), (4096 + 17, 4096, 64)]:
         shape = sgemm.hip_sgemm_launch_shape(10, M, N, K)
         assert shape == {"workgroups": -(-M // 64) * -(-N // 64), "threads": 512,
                          "k_steps": -(-K // 32), "tile_m": 64, "tile_n": 64}
@@ -176,14 +178,15 @@ def test_tile32_geometry_matches_the_six_level_example():
 
 
 def test_tile_split_arguments():
-    assert sgemm.hip_sgemm_num_tiles() == 6
+    assert sgemm.hip_sgemm_num_tiles() == 7
     names = [sgemm.hip_sgemm_tile_name(t) for t in range(4)]
     assert names[0].startswith("256x128") and names[3].startswith("64x64")
-    names = [sgemm.hip_sgemm_tile_name(t) for t in range(6)]
+    names = [sgemm.hip_sgemm_tile_name(t) for t in range(7)]
     assert names[4].startswith("128x128") and names[5].startswith("64x64") and "2slices" in names[5]
-    assert sgemm.hip_sgemm_tile_name(6) is None and sgemm.hip_sgemm_tile_name(-1) is None
+    assert names[6].startswith("64x64x64") and "4slices" in names[6]
+    assert sgemm.hip_sgemm_tile_name(7) is None and sgemm.hip_sgemm_tile_name(-1) is None
     args = (4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4)
-    for tile, splits in [(-1, 1), (6, 1), (0, 0), (1, -3)]:
+    for tile, splits in [(-1, 1), (7, 1), (0, 0), (1, -3)]:
         assert sgemm.hip_sgemm_tile_split(tile, splits, *args, stream=0) == sgemm.STATUS_UNKNOWN_CONFIG
     assert "split" in sgemm.hip_sgemm_status_string(sgemm.STATUS_UNKNOWN_CONFIG)
     # argument errors as hip_sgemm once the configuration is valid

@@ -110,8 +110,8 @@ def test_kloop_bit_identical_to_level9(K):
 
 
 # tile ids of hip_sgemm_tile_split with an assembly loop: 0 = 256 x 128,
-# 1 = 128 x 128
-TILE_SHAPES = {0: (256, 128), 1: (128, 128)}
+# 1 = 128 x 128, 6 = 64 x 64 (64-deep stages, four K-slice wavefronts)
+TILE_SHAPES = {0: (256, 128), 1: (128, 128), 6: (64, 64)}
 
 
 @pytest.mark.parametrize("tile", sorted(TILE_SHAPES))
@@ -196,14 +196,15 @@ def test_dispatch_128_tiles(M, N, K):
 
 
 def test_loops_deterministic_and_agree():
-    """Both loops are deterministic and give each output the same chain of
-    MFMAs over the same k (16-deep stages, k = 4 s + lane / 16 in MFMA step
-    s), so their results agree bit for bit."""
+    """Every loop is deterministic; the 256 x 128 and 128 x 128 loops give
+    each output the same chain of MFMAs over the same k (16-deep stages,
+    k = 4 s + lane / 16 in MFMA step s), so their results agree bit for
+    bit."""
     M = N = 2048
     K = 512
     A, B, C = inputs.make_abc(M, N, K, 13100)
     outs = []
-    for tile in (0, 1):
+    for tile in (0, 1, 6):
         def call(*args, tile=tile):
             return sgemm.hip_sgemm_tile_split(tile, 1, *args)
         a, st1 = gh.run(gh.Case(M, N, K, 0.5, 3.0, A, B, C), call)
@@ -212,7 +213,8 @@ def test_loops_deterministic_and_agree():
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), tile
         outs.append(a)
     # tiles 0 and 1 accumulate every output in the same order (16-deep
-    # stages, k = 4 s + lane/16 per MFMA step, one chain per block)
+    # stages, k = 4 s + lane/16 per MFMA step, one chain per block); tile 6
+    # adds four K slices' chains, another order
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
 

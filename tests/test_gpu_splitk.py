@@ -15,7 +15,7 @@ from tests import gpu_harness as gh
 pytestmark = pytest.mark.gpu
 
 BOUND = 1e-5
-TILES = range(6)
+TILES = range(7)
 
 
 @pytest.fixture(scope="session", autouse=True)

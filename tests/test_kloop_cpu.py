@@ -3,12 +3,13 @@ each tile and operand orientation gen_kloop.py builds a loop for.
 
 The loop text is emitted by gen_kloop.py; the committed l10_kloop.inc must
 be exactly that output.  Its LDS traffic is then replayed on the CPU from
-the emitted instructions themselves (their immediate offsets) and the
-kernel's per-thread base addresses, restated here from l10_kloop.hip:
-every access must stay inside the block's LDS allocation and inside its
-operand's region, and the word each MFMA operand read finds must be the one
-the stage stores put there for that (row, k) or (k, column) -- the loop's
-layout is consistent with the operand map the epilogue assumes.
+the emitted instructions themselves (their registers and immediate offsets)
+and the kernel's per-thread element maps and base addresses, restated here
+from l10_kloop.hip: every access must stay inside the block's LDS
+allocation and inside its operand's region, every stage store must land
+where the k-major layout puts its element, and the word each MFMA operand
+read finds must be the one stored there for that (row, k) or (k, column) --
+the loop's layout is consistent with the operand map the epilogue assumes.
 """
 
 from __future__ import annotations
@@ -39,22 +40,23 @@ def test_committed_loop_matches_generator():
         assert f.read() == G.render()
 
 
-# Per-thread element maps and base addresses of l10_kloop.hip (restated from
-# the kernel): element h of thread tid is
-#   A row-major:  row tid/4 + h THREADS/4, k 4 (tid%4) + c
-#   A transposed: k-row tid/(BM/4) + 8 h, row 4 (tid%(BM/4)) + c
-#   B row-major:  k-row tid/32 + h THREADS/32, column 4 (tid%32) + c
-#   B transposed: column tid/4 + h THREADS/4, k 4 (tid%4) + c
+# Per-thread element maps of l10_kloop.hip (restated from the kernel):
+# element h, component c of thread tid, with per = float4s per row (k-row)
+# of the operand as stored:
+#   A row-major:  row tid/per + h THREADS/per, k 4 (tid%per) + c
+#   A transposed: k-row tid/per + h THREADS/per, row 4 (tid%per) + c
+#   B row-major:  k-row tid/per + h THREADS/per, column 4 (tid%per) + c
+#   B transposed: column tid/per + h THREADS/per, k 4 (tid%per) + c
 def a_elem(t, tid, h, c):
-    if t.TA:
-        return ("A", 4 * (tid % (t.BM // 4)) + c, tid // (t.BM // 4) + 8 * h)
-    return ("A", tid // 4 + h * t.THREADS // 4, 4 * (tid % 4) + c)
+    per = t.BM // 4 if t.TA else t.BK // 4
+    major, minor = tid // per + h * (t.THREADS // per), 4 * (tid % per) + c
+    return ("A", minor, major) if t.TA else ("A", major, minor)
 
 
 def b_elem(t, tid, h, c):
-    if t.TB:
-        return ("B", 4 * (tid % 4) + c, tid // 4 + h * t.THREADS // 4)
-    return ("B", tid // 32 + h * t.THREADS // 32, 4 * (tid % 32) + c)
+    per = t.BK // 4 if t.TB else t.BN // 4
+    major, minor = tid // per + h * (t.THREADS // per), 4 * (tid % per) + c
+    return ("B", minor, major) if t.TB else ("B", major, minor)
 
 
 def a_word(t, m, k):
@@ -63,7 +65,7 @@ def a_word(t, m, k):
 
 
 def b_word(t, k, n):
-    return 2 * t.A_STAGE // 4 + (k // 4) * t.B_GROUP + (k % 4) * G.BN + n
+    return 2 * t.A_STAGE // 4 + (k // 4) * t.B_GROUP + (k % 4) * t.BN + n
 
 
 def w_a(t, tid):
@@ -77,25 +79,52 @@ def w_b(t, tid):
 
 
 def _wave(t, tid):
-    """(wm, wn, lrow, kg) of a thread."""
+    """(K slice, wm, wn, lrow, kg) of a thread."""
     wave, lane = divmod(tid, 64)
-    return wave // 2, wave % 2, lane % 16, lane // 16
+    slice_, wv = divmod(wave, t.WAVES_M * t.WAVES_N)
+    return slice_, wv // t.WAVES_N, wv % t.WAVES_N, lane % 16, lane // 16
 
 
 def r_a(t, tid):
-    wm, _, lrow, kg = _wave(t, tid)
-    return (kg * t.BM + wm * 64 + 4 * lrow) * 4
+    slice_, wm, _, lrow, kg = _wave(t, tid)
+    return (slice_ * t.STEPS * t.A_GROUP + kg * t.BM + wm * 64 + 4 * lrow) * 4
 
 
 def r_b(t, tid):
-    _, wn, lrow, kg = _wave(t, tid)
-    return 2 * t.A_STAGE + (kg * G.BN + wn * 64 + 4 * lrow) * 4
+    slice_, _, wn, lrow, kg = _wave(t, tid)
+    return 2 * t.A_STAGE + (slice_ * t.STEPS * t.B_GROUP + kg * t.BN + wn * 64 + 4 * lrow) * 4
+
+
+STORE_2ST64 = re.compile(r"ds_write2st64_b32 %\[w([AB])\], v(\d+), v(\d+) offset0:(\d+) offset1:(\d+)$")
+STORE_2 = re.compile(r"ds_write2_b32 %\[w([AB])(1?)\], v(\d+), v(\d+) offset0:(\d+) offset1:(\d+)$")
+STORE_128 = re.compile(r"ds_write_b128 %\[w([AB])\], v\[(\d+):(\d+)\] offset:(\d+)$")
+
+
+def _pieces(t, tid, line):
+    """(operand, [(register, byte address)]) of one store instruction."""
+    m = STORE_2ST64.match(line)
+    if m:
+        op, r0, r1, o0, o1 = m.group(1), *(int(x) for x in m.groups()[1:])
+        start = w_a(t, tid) if op == "A" else w_b(t, tid)
+        return op, [(r0, start + 256 * o0), (r1, start + 256 * o1)]
+    m = STORE_2.match(line)
+    if m:
+        op, second, r0, r1, o0, o1 = m.group(1), m.group(2), *(int(x) for x in m.groups()[2:])
+        start = w_a(t, tid) if op == "A" else w_b(t, tid)
+        if second:  # the second buffer's base register
+            start += t.A_STAGE if op == "A" else t.B_STAGE
+        return op, [(r0, start + 4 * o0), (r1, start + 4 * o1)]
+    m = STORE_128.match(line)
+    assert m, line
+    op, r0, r3, off = m.group(1), *(int(x) for x in m.groups()[1:])
+    assert r3 == r0 + 3
+    start = w_a(t, tid) if op == "A" else w_b(t, tid)
+    return op, [(r0 + c, start + off + 4 * c) for c in range(4)]
 
 
 def _stage_stores(t, st, buf):
     """{byte address: ('A', row, k) or ('B', k, col)} written by one stage's
-    stores from staging set st into buffer buf, replayed from the emitted
-    instructions (their registers and immediate offsets)."""
+    stores from staging set st into buffer buf."""
     written = {}
     a_end = 2 * t.A_STAGE
     base = t.set_base(st)
@@ -109,20 +138,10 @@ def _stage_stores(t, st, buf):
             for c in range(4):
                 regs[base + 4 * t.A_LOADS + 4 * h + c] = b_elem(t, tid, h, c)
         for line in lines:
-            m2 = re.match(r"ds_write2st64_b32 %\[w([AB])\], v(\d+), v(\d+) offset0:(\d+) offset1:(\d+)$", line)
-            m4 = re.match(r"ds_write_b128 %\[w([AB])\], v\[(\d+):(\d+)\] offset:(\d+)$", line)
-            assert m2 or m4, line
-            if m2:
-                op, r0, r1, o0, o1 = m2.group(1), *(int(x) for x in m2.groups()[1:])
-                pieces = [(r0, 256 * o0), (r1, 256 * o1)]
-            else:
-                op, r0, r3, off = m4.group(1), *(int(x) for x in m4.groups()[1:])
-                assert r3 == r0 + 3
-                pieces = [(r0 + c, off + 4 * c) for c in range(4)]
-            start = w_a(t, tid) if op == "A" else w_b(t, tid)
-            lo, hi = (0, a_end) if op == "A" else (a_end, t.LDS)
-            for reg, off in pieces:
-                addr = start + off
+            op, pieces = _pieces(t, tid, line)
+            lo, hi = (buf * t.A_STAGE, (buf + 1) * t.A_STAGE) if op == "A" else \
+                     (a_end + buf * t.B_STAGE, a_end + (buf + 1) * t.B_STAGE)
+            for reg, addr in pieces:
                 assert lo <= addr and addr + 4 <= hi, (t.name, tid, line)
                 assert addr not in written, ("store overlap", t.name, tid, line)
                 assert regs[reg][0] == op, (t.name, line)
@@ -131,22 +150,19 @@ def _stage_stores(t, st, buf):
 
 
 @pytest.mark.parametrize("name", sorted(TILES))
-def test_first_stage_map_matches_the_loop(name):
-    """Stage 0 is stored by the kernel's C++ part through the same element
-    maps into buffer 0 (A (m, k) at word (k/4) A_GROUP + (k%4) BM + m, B
-    (k, n) likewise): it must put every element where the loop's own stores
-    into buffer 0 put it."""
+@pytest.mark.parametrize("buf", [0, 1])
+def test_stage_stores_follow_the_layout(name, buf):
+    """Every staged element lands at its k-major word, whole stage, no
+    overlap (buffer 0 is also where the C++ first stage stores: the same
+    element maps and the same words)."""
     t = TILES[name]
-    written = _stage_stores(t, 0, 0)
-    for tid in range(t.THREADS):
-        for h in range(t.A_LOADS):
-            for c in range(4):
-                e = a_elem(t, tid, h, c)
-                assert written[4 * a_word(t, e[1], e[2])] == e
-        for h in range(t.B_LOADS):
-            for c in range(4):
-                e = b_elem(t, tid, h, c)
-                assert written[4 * b_word(t, e[1], e[2])] == e
+    for st in range(t.DEPTH):
+        written = _stage_stores(t, st, buf)
+        assert len(written) == t.BM * t.BK + t.BK * t.BN
+        for addr, e in written.items():
+            word = a_word(t, e[1], e[2]) if e[0] == "A" else b_word(t, e[1], e[2])
+            shift = buf * (t.A_STAGE if e[0] == "A" else t.B_STAGE)
+            assert addr == 4 * word + shift, (name, e)
 
 
 @pytest.mark.parametrize("name", sorted(TILES))
@@ -154,24 +170,30 @@ def test_first_stage_map_matches_the_loop(name):
 def test_fragment_reads_find_their_operands(name, buf):
     t = TILES[name]
     a_end = 2 * t.A_STAGE
-    for st in range(t.DEPTH):
-        written = _stage_stores(t, st, buf)
-        # a whole stage lands: BM x 16 A words and 16 x 128 B words
-        assert len(written) == t.BM * 16 + 16 * G.BN
-        for s in range(4):
-            lines = t.frag_reads(64, s, buf)
-            offs = [int(re.search(r"offset:(\d+)", l).group(1)) for l in lines]
-            for tid in range(t.THREADS):
-                wm, wn, lrow, kg = _wave(t, tid)
-                k = 4 * s + kg
-                for e in range(4):
-                    a_addr = r_a(t, tid) + offs[0] + 4 * e
-                    b_addr = r_b(t, tid) + offs[1] + 4 * e
-                    assert 0 <= a_addr and a_addr + 4 <= a_end
-                    assert a_end <= b_addr and b_addr + 4 <= t.LDS
-                    # block e of the lane: A row 4 lrow + e, B column 4 lrow + e
-                    assert written[a_addr] == ("A", wm * 64 + 4 * lrow + e, k), (s, tid, e)
-                    assert written[b_addr] == ("B", k, wn * 64 + 4 * lrow + e), (s, tid, e)
+    written = _stage_stores(t, 0, buf)
+    for s in range(t.STEPS):
+        lines = t.frag_reads(64, s, buf)
+        offs = [int(re.search(r"offset:(\d+)", l).group(1)) for l in lines]
+        for tid in range(t.THREADS):
+            slice_, wm, wn, lrow, kg = _wave(t, tid)
+            k = 4 * (slice_ * t.STEPS + s) + kg
+            for e in range(4):
+                a_addr = r_a(t, tid) + offs[0] + 4 * e
+                b_addr = r_b(t, tid) + offs[1] + 4 * e
+                assert 0 <= a_addr and a_addr + 4 <= a_end
+                assert a_end <= b_addr and b_addr + 4 <= t.LDS
+                # block e of the lane: A row 4 lrow + e, B column 4 lrow + e
+                assert written[a_addr] == ("A", wm * 64 + 4 * lrow + e, k), (s, tid, e)
+                assert written[b_addr] == ("B", k, wn * 64 + 4 * lrow + e), (s, tid, e)
+
+
+@pytest.mark.parametrize("name", sorted(TILES))
+def test_k_slices_cover_every_step_once(name):
+    """The wavefronts that share a wave tile take disjoint runs of a stage's
+    MFMA steps that together cover all of them."""
+    t = TILES[name]
+    steps = sorted(sl * t.STEPS + s for sl in range(t.KSLICES) for s in range(t.STEPS))
+    assert steps == list(range(t.GROUPS))
 
 
 def _bank_conflict_free_32bit(addrs):
@@ -186,12 +208,10 @@ def test_transposing_stores_hit_distinct_banks(name):
     banks (the padded groups' purpose)."""
     t = TILES[name]
     for line in t.stage_stores(0, 0):
-        m2 = re.match(r"ds_write2st64_b32 %\[w([AB])\], v\d+, v\d+ offset0:(\d+) offset1:\d+$", line)
-        if not m2:
+        if line.startswith("ds_write_b128"):
             continue
-        op, o0 = m2.group(1), int(m2.group(2))
         for first in range(0, t.THREADS, 32):
-            addrs = [(w_a(t, tid) if op == "A" else w_b(t, tid)) + 256 * o0 for tid in range(first, first + 32)]
+            addrs = [_pieces(t, tid, line)[1][0][1] for tid in range(first, first + 32)]
             assert _bank_conflict_free_32bit(addrs), (name, line, first)
 
 
@@ -200,11 +220,12 @@ def test_loop_structure(name):
     t = TILES[name]
     prog = t.program()
     mfmas = [l for l in prog if l.startswith("v_mfma")]
-    # the prologue issues no MFMA; a pair of K steps and the odd step: 3 x 64
-    assert len(mfmas) == 3 * 64
-    # every accumulator block gets exactly four MFMAs per K step, one per step s
+    # the prologue issues no MFMA; a pair of K steps and the odd step, each
+    # STEPS MFMA steps of 16
+    assert len(mfmas) == 3 * 16 * t.STEPS
+    # every accumulator block gets one MFMA per step
     for b in range(16):
-        assert sum(1 for l in mfmas if l.startswith(f"v_mfma_f32_16x16x4_f32 v[{4*b}:")) == 12
+        assert sum(1 for l in mfmas if l.startswith(f"v_mfma_f32_16x16x4_f32 v[{4*b}:")) == 3 * t.STEPS
     # one barrier per K step, plus the prologue's
     assert sum(1 for l in prog if l == "s_barrier") == 4
     # no instruction of the loop writes memory other than LDS
