@@ -115,7 +115,21 @@ class Problem:
             c.copy_(self.dC0)
 
 
-def run_timed(prob: Problem, level, steps: int, warmup: int):
+def warm_until(call, n: int, min_ms: float):
+    """n calls, then more until at least min_ms of back-to-back calls (host
+    clock, checked every 10 calls): the clocks ramp up from idle over tens
+    of milliseconds, which a few calls of a short kernel do not cover."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < n or (min_ms > 0 and (time.perf_counter() - t0) * 1e3 < min_ms):
+        call(i)
+        i += 1
+        if i % 10 == 0:
+            torch.cuda.synchronize()
+
+
+def run_timed(prob: Problem, level, steps: int, warmup: int, min_warm_ms: float = 0.0):
     """Warm-up and timed calls on the current stream.  Returns (ms_per_step
     from the host clock over the whole timed region, mean kernel ms from the
     per-launch HIP events)."""
@@ -134,8 +148,7 @@ def run_timed(prob: Problem, level, steps: int, warmup: int):
 
     prob.refill()
     torch.cuda.synchronize()
-    for i in range(warmup):
-        call(prob.copies[i % len(prob.copies)])
+    warm_until(lambda i: call(prob.copies[i % len(prob.copies)]), warmup, min_warm_ms)
     prob.refill()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -199,7 +212,7 @@ def device_info():
     return info
 
 
-def vendor_timed(prob: Problem, steps: int, warmup: int):
+def vendor_timed(prob: Problem, steps: int, warmup: int, min_warm_ms: float = 0.0):
     """The same call through torch.addmm on FP32 tensors (rocBLAS/hipBLASLt,
     TF32 off): a context figure for the vendor library, never a dependency of
     libsgemm.  Returns the mean kernel ms from HIP events, like run_timed."""
@@ -209,8 +222,8 @@ def vendor_timed(prob: Problem, steps: int, warmup: int):
     stream = torch.cuda.current_stream()
     prob.refill()
     torch.cuda.synchronize()
-    for i in range(warmup):
-        prob.copies[i % len(prob.copies)].addmm_(prob.dA, prob.dB, beta=w.beta, alpha=w.alpha)
+    warm_until(lambda i: prob.copies[i % len(prob.copies)].addmm_(prob.dA, prob.dB, beta=w.beta,
+                                                                 alpha=w.alpha), warmup, min_warm_ms)
     prob.refill()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -223,10 +236,10 @@ def vendor_timed(prob: Problem, steps: int, warmup: int):
     return sum(a.elapsed_time(b) for a, b in ev) / steps
 
 
-def bench_one(w, level, steps, warmup, prob=None):
+def bench_one(w, level, steps, warmup, prob=None, min_warm_ms=0.0):
     from dense_fp32_matrix_row_amd import sgemm
     prob = prob or Problem(w, max(steps, warmup, 1))
-    ms, kms = run_timed(prob, level, steps, warmup)
+    ms, kms = run_timed(prob, level, steps, warmup, min_warm_ms)
     eff_level = level if level is not None else sgemm.hip_sgemm_auto_level(
         w.M, w.N, w.K, prob.dA, w.K, prob.dB, w.N, prob.dC0, w.N)
     name = sgemm.hip_sgemm_level_name(eff_level)
@@ -270,7 +283,8 @@ def main():
                     slow = lv <= 1 and wl.M >= 2048
                     st = min(steps, 3) if slow else min(steps, 20)
                     wu = 1 if slow else min(warmup, 10)
-                    _, ms, kms, _, name = bench_one(wl, lv, st, wu, prob)
+                    # short kernels: at least 30 ms of calls before timing
+                    _, ms, kms, _, name = bench_one(wl, lv, st, wu, prob, 0.0 if slow else 30.0)
                     tf = wl.flops / (kms * 1e-3) / 1e12
                     rec = {"workload": wl.name, "level": lv, "level_name": name, "steps": st,
                            "warmup": wu, "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
@@ -280,7 +294,7 @@ def main():
                     f.flush()
                     print(f"[ladder] {wl.name} L{lv} {name}: {kms:.4f} ms, {rec['tflops']} TFLOPS",
                           flush=True)
-                vms = vendor_timed(prob, min(steps, 20), min(warmup, 10))
+                vms = vendor_timed(prob, min(steps, 20), min(warmup, 10), 30.0)
                 tf = wl.flops / (vms * 1e-3) / 1e12
                 f.write(json.dumps({"workload": wl.name, "level": "vendor",
                                     "level_name": "torch.addmm (rocBLAS/hipBLASLt, FP32)",
