@@ -249,7 +249,10 @@ class Tile:
     def program(self) -> list[str]:
         # stage 0 was stored into buffer 0 by the kernel's C++ part just
         # before this statement; stages 1 .. DEPTH go into sets 1 % DEPTH ..
-        prologue = ["s_waitcnt lgkmcnt(0)"]
+        # The compiler cannot see into the statement, so the wait states a
+        # buffer load needs after a vector-ALU write of its descriptor or
+        # offset SGPRs (5 on gfx9) come first, whatever precedes it.
+        prologue = ["s_nop 4", "s_waitcnt lgkmcnt(0)"]
         for j in range(1, self.DEPTH + 1):
             prologue += [*self.loads(j % self.DEPTH), *self.ADVANCE]
         prologue += ["s_barrier", *self.frag_reads(FE, 0, 0)]

@@ -9,19 +9,13 @@
 //     mostly empty rows or columns, and the problem is bound by reading the
 //     other operand; l10_thin.hip gives them one 16-row MFMA block or
 //     vector-ALU FMA chains);
-//   - a large problem whose M and N miss a multiple of the 256 x 128 (or
-//     128 x 128) tile by at most 16: whole tiles over the largest multiple,
-//     no per-element bounds logic (only the last K step masks when K is
-//     ragged), plus the thin kernels on the fringe.  Whole 256 x 128 and
-//     128 x 128 tiles run l10_kloop.hip, the same tiles with their K loop
-//     scheduled by hand.  At 4097^3 this replaces
-//     level 9's 2145 edge-checked 128 x 64 tiles by the 512 whole 256 x 128
-//     tiles of 4096^3 (exactly two per CU) and two one-element-wide strips;
-//   - the tile shape whose grid fills the CUs best: 128 x 128 tiles, or the
-//     64 x 64 tile whose 64-deep stages are split over four wavefronts
-//     (l10_kloop.hip);
-//   - a deep K over a small tile grid: split K (l10_splitk.hip);
-//   - anything else: compiled 64 x 64 tiles with two K slices per stage.
+//   - a deep K over a small grid: split K (l10_splitk.hip);
+//   - otherwise one of the three assembly-loop tiles of l10_kloop.hip
+//     (256 x 128, 128 x 128, 64 x 64), the one that leaves the busiest CU
+//     the least work, with partial edge tiles, or whole tiles plus the thin
+//     kernels on a fringe of <= 16 rows / columns (at 4097^3: the 512 whole
+//     tiles of 4096^3 and two one-element strips);
+//   - tiny problems: compiled 64 x 64 tiles with two K slices per stage.
 // Every output element is computed by exactly one tile or thin kernel (or,
 // split, by one reduction over its slices); the regions are disjoint, so
 // the launches need no ordering beyond the stream's.
@@ -55,79 +49,90 @@ Decomp decompose(int M, int N, int K) {
   if (M <= kThin) return {Plan::kFewRows, Shape::kSmall, M, N, K};
   if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, M, N, K};
 
-  // 1. At least two 256 x 128 tiles per CU (plus a fringe of <= 16): the
-  //    big tile (4096^3: 150-152 TFLOP/s; 4097^3 with the fringe: 143).
-  {
-    const int mr = M % 256, nr = N % 128;
-    const int64_t tiles = int64_t((M - mr) / 256) * ((N - nr) / 128);
-    if (mr <= kThin && nr <= kThin && tiles >= 2 * kCUs)
-      return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, Shape::kHuge, M - mr, N - nr, K};
-  }
-
-  // 2. 128 x 128 tiles (plus a fringe of <= 16) that fill whole rounds of
-  //    CUs, or one round at least 70 % full (2048^3: 140.8 against 132.6
-  //    for the 64 x 64 tile below; 1792^3, 196 tiles: 108.5 against 100.7;
-  //    2048 x 4096: 147; 1024 x 4096 x 1024: 130 against 119).
-  {
-    const int mr = M % 128, nr = N % 128;
-    const int64_t tiles = int64_t((M - mr) / 128) * ((N - nr) / 128);
-    const bool fills = tiles >= kCUs ? round_fill(tiles) >= 0.9 : tiles * 10 >= kCUs * 7;
-    if (mr <= kThin && nr <= kThin && fills)
-      return {mr || nr ? Plan::kTilesWithFringe : Plan::kTiles, Shape::kLarge, M - mr, N - nr, K};
-  }
-
-  // 3. A whole grid of >= 64 tiles of 64 x 64: the deep-stage 64 x 64
-  //    loop (four K-slice wavefronts per tile; two blocks fit a CU), which
-  //    balances over the CUs where bigger tiles leave a round partly idle
-  //    (1024^3: 89.3 against 76.5 for the best compiled tile; 1280^3: 91.5;
-  //    1536^3: 94.7; 3072^3: 140.6 against 135.2 for 128 x 128 tiles in 4
-  //    K parts; 3584^3: 135.3; 1024 x 2048 x 4096: 133.8; 1024 x 1024 x
-  //    8192: 130.5 against 128 for split 128 x 128 tiles).  A deep K over
-  //    less than one round of these tiles is split into the most parts
-  //    (<= 16, each >= 256 deep) that keep at most two work items per CU:
-  //    512 x 512 x 8192 (64 tiles) in 8 parts 85.8 (in 4: 87.0);
-  //    768 x 768 x 4096 (144 tiles) in 3: 82.7 against 70.2 before.
   const int64_t tiles64 = ceil_div(M, 64) * ceil_div(N, 64);
-  if (M % 64 == 0 && N % 64 == 0 && tiles64 >= 64) {
-    if (K >= 2048 && K >= 2 * int64_t(M > N ? M : N) && tiles64 < kCUs) {
-      int64_t parts = 2 * kCUs / tiles64;
-      if (parts > 16) parts = 16;
-      if (parts > K / 256) parts = K / 256;
-      if (parts >= 2) {
-        const int64_t k_split = k_split_for(K, parts, shape_bk(Shape::kSmallDeep));
-        if (k_split < K) return {Plan::kSplitK, Shape::kSmallDeep, M, N, k_split};
+  const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
+  const bool deep = K >= 2048 && K >= 2 * int64_t(M > N ? M : N);
+
+  // 1. A deep K over less than one round of 64 x 64 tiles (but >= 64 of
+  //    them): the 64 x 64 assembly loop split into the most K parts (<= 16,
+  //    each >= 256 deep) that keep at most two work items per CU
+  //    (l10_splitk.hip: workspace planes from the library's pool, an
+  //    in-order reduction applying alpha and beta): 512 x 512 x 8192 (64
+  //    tiles) in 8 parts 85.8 TFLOP/s (in 4: 87.0); 768 x 768 x 4096 (144
+  //    tiles) in 3: 82.7 against 70.2 on compiled tiles.
+  if (deep && tiles64 >= 64 && tiles64 < kCUs) {
+    int64_t parts = 2 * kCUs / tiles64;
+    if (parts > 16) parts = 16;
+    if (parts > K / 256) parts = K / 256;
+    if (parts >= 2) {
+      const int64_t k_split = k_split_for(K, parts, shape_bk(Shape::kSmallDeep));
+      if (k_split < K) return {Plan::kSplitK, Shape::kSmallDeep, M, N, k_split};
+    }
+  }
+
+  // 2. A grid of >= 64 tiles of 64 x 64: whichever of the three
+  //    assembly-loop tiles leaves the busiest CU the least work,
+  //    ceil(tiles / CUs) x tile area / efficiency, the efficiency measured
+  //    for that tile at that many tiles per CU (256 x 128: 0.955 from two
+  //    per CU, 0.85 with one; 128 x 128: 0.935 / 0.895; 64 x 64, 64-deep
+  //    stages over four K-slice wavefronts: 0.89).  The 256 x 128 and
+  //    128 x 128 tiles count whole tiles only when M and N miss a multiple
+  //    by at most 16 (the rest goes to the thin kernels: 4097^3 on 512 tiles
+  //    of 256 x 128 and two one-element strips, 143-144 against 114 for the
+  //    vendor BLAS), and partial edge tiles otherwise.  Picks on the
+  //    sweeps: 256 x 128 at 4096^3 (150-152), 4000^3 (145 against 137 for
+  //    64 x 64), 5000 x 3000 x 2000 (133.5); 128 x 128 at 2048^3 (140-141
+  //    against 132.6), 1792^3 (109 against 100), 2048 x 4096, 1024 x 4096 x
+  //    1024 (130 against 119), 2048 x 2048 x 8192 (148), 6000^3 (145.4);
+  //    64 x 64 at 1024^3 (89-93 against <= 80 for compiled tiles), 1536^3
+  //    (94.7), 2500^3 (114.8), 3000^3 (132.8; compiled: 101.6), 3072^3
+  //    (140.6), 3584^3 (135.3), 4608^3 (140.2 against 128.5 for 648 tiles
+  //    of 256 x 128), 5120^3 (146.2 against 119.2 for 800), 1024 x 1024 x
+  //    4096 / 8192 (123 / 130.5).
+  if (tiles64 >= 64) {
+    struct Candidate {
+      Shape shape;
+      int bm, bn;
+      double eff_one, eff_more;  // efficiency with one / several tiles per CU
+    };
+    static const Candidate candidates[] = {{Shape::kHuge, 256, 128, 0.85, 0.955},
+                                           {Shape::kLarge, 128, 128, 0.895, 0.935},
+                                           {Shape::kSmallDeep, 64, 64, 0.89, 0.89}};
+    Decomp best{Plan::kTiles, Shape::kSmallDeep, M, N, K};
+    double best_cost = 0.0;
+    for (const Candidate& c : candidates) {
+      const int mr = M % c.bm, nr = N % c.bn;
+      const bool fringe = c.shape != Shape::kSmallDeep && mr <= kThin && nr <= kThin &&
+                          M - mr > 0 && N - nr > 0;
+      const int Mm = fringe ? M - mr : M, Nm = fringe ? N - nr : N;
+      const int64_t per_cu = ceil_div(ceil_div(Mm, c.bm) * ceil_div(Nm, c.bn), kCUs);
+      const double cost = double(per_cu) * c.bm * c.bn / (per_cu > 1 ? c.eff_more : c.eff_one);
+      if (best_cost == 0.0 || cost < best_cost) {
+        const Plan plan = fringe && (mr || nr) ? Plan::kTilesWithFringe : Plan::kTiles;
+        best = {plan, c.shape, Mm, Nm, K};
+        best_cost = cost;
       }
     }
-    return {Plan::kTiles, Shape::kSmallDeep, M, N, K};
+    return best;
   }
 
-  // 4. Deep K over less than one round of 128 x 128 tiles, M or N not a
-  //    multiple of 64: split K on compiled tiles so that about two work
-  //    items per CU run (slices >= 256 deep (512 for the big tile), <= 16).
-  const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
-  if (K >= 2048 && K >= 2 * int64_t(M > N ? M : N) && tiles128 < kCUs) {
-    Shape shape = Shape::kSmall;
-    int64_t tiles = tiles64, min_slice = 256;
-    if (M % 256 == 0 && N % 128 == 0 && int64_t(M / 256) * (N / 128) >= 64) {
-      shape = Shape::kHuge;
-      tiles = int64_t(M / 256) * (N / 128);
-      min_slice = 512;
-    } else if (tiles128 >= 16) {
-      shape = Shape::kLarge;
-      tiles = tiles128;
-    }
+  // 3. Deep K over fewer than 64 tiles of 64 x 64: split K on compiled
+  //    tiles so that about two work items per CU run (slices >= 256 deep,
+  //    <= 16).
+  if (deep && tiles128 < kCUs) {
+    const Shape shape = tiles128 >= 16 ? Shape::kLarge : Shape::kSmall;
+    const int64_t tiles = shape == Shape::kLarge ? tiles128 : tiles64;
     int64_t splits = ceil_div(2 * kCUs, tiles);
     if (splits > 16) splits = 16;
-    if (splits > K / min_slice) splits = K / min_slice;
+    if (splits > K / 256) splits = K / 256;
     if (splits >= 2) {
       const int64_t k_split = k_split_for(K, splits, shape_bk(shape));
       if (k_split < K) return {Plan::kSplitK, shape, M, N, k_split};
     }
   }
 
-  // 5. Everything else: compiled 64 x 64 tiles with two K slices, up to
-  //    three blocks per CU (3000^3: 101.5; 256^3: 3.2; it beats the
-  //    128 x 64 tile at every size measured, 512^3 to 4096^3).
+  // 4. Everything else (fewer than 64 tiles of 64 x 64): compiled 64 x 64
+  //    tiles with two K slices (256^3: 3.2 against 3.0 for the loop tile).
   return {Plan::kTiles, Shape::kSmallSliced, M, N, K};
 }
 

@@ -23,7 +23,9 @@
 // at the last element the tile may use, so the loads it issues past the
 // last stage (one or two stages of prefetch) read zeros or elements of the
 // same matrix, never beyond it; they land in the idle LDS buffer unused.
-// Byte offsets must stay below 2^31 (kloop_fits).
+// Byte offsets must stay below 2^31 (kloop_fits).  Tiles at the bottom and
+// right edges cover fewer rows / columns; their record counts stop at the
+// last row / column of the matrix and their epilogue stores only inside it.
 //
 // LDS holds both operands k-major whatever their storage (as level 9's
 // tile): a row-major A and a transposed B arrive four k per 128-bit load
@@ -153,22 +155,30 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   const int64_t row0 = (first_m + in % gm) * BM;
   const int64_t col0 = (in / gm) * T::BN;
 
+  // rows / columns of C this tile covers (fewer than BM / BN at the edges)
+  const int rows = static_cast<int>(p.M - row0 < BM ? p.M - row0 : BM);
+  const int cols = static_cast<int>(p.N - col0 < T::BN ? p.N - col0 : T::BN);
+  const bool whole = rows == BM && cols == T::BN;
+
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int slice = wave / T::WAVE_TILES, wv = wave % T::WAVE_TILES;
   const int wm = wv / T::WAVES_N, wn = wv % T::WAVES_N, lrow = lane % 16, kg = lane / 16;
   const int64_t lda = p.lda, ldb = p.ldb;
-  // The tile's part of A (rows row0 .. row0 + BM - 1, k_lo <= k < k_lo + K)
-  // and of B (those k, columns col0 .. col0 + BN - 1), as stored: element
+  // The tile's part of A (rows row0 .. row0 + rows - 1, k_lo <= k < k_lo + K)
+  // and of B (those k, columns col0 .. col0 + cols - 1), as stored: element
   // (m, k_lo + k) of A at a_base[m a_rs + k a_ks], element (k_lo + k, n) of
-  // B at b_base[k b_ks + n b_cs].
+  // B at b_base[k b_ks + n b_cs].  The record counts end at the last of
+  // these elements: at an edge tile the loads of rows (columns) beyond M
+  // (N) read zeros, or elements of the same operand that only ever meet
+  // outputs beyond M (N), which are not stored.
   const int64_t a_rs = TA ? 1 : lda, a_ks = TA ? lda : 1;
   const int64_t b_ks = TB ? 1 : ldb, b_cs = TB ? ldb : 1;
   const float* const a_base = p.A + row0 * a_rs + k_lo * a_ks;
   const float* const b_base = p.B + col0 * b_cs + k_lo * b_ks;
   const intx4 rsA =
-      buffer_resource(a_base, static_cast<uint32_t>(((BM - 1) * a_rs + (K - 1) * a_ks + 1) * 4));
+      buffer_resource(a_base, static_cast<uint32_t>(((rows - 1) * a_rs + (K - 1) * a_ks + 1) * 4));
   const intx4 rsB =
-      buffer_resource(b_base, static_cast<uint32_t>(((K - 1) * b_ks + (T::BN - 1) * b_cs + 1) * 4));
+      buffer_resource(b_base, static_cast<uint32_t>(((K - 1) * b_ks + (cols - 1) * b_cs + 1) * 4));
   uint32_t oA[4] = {0, 0, 0, 0}, oB[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int h = 0; h < T::A_LOADS; ++h) {
@@ -206,20 +216,20 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   const uint32_t stepA = static_cast<uint32_t>(T::BK * a_ks * 4);
   const uint32_t stepB = static_cast<uint32_t>(T::BK * b_ks * 4);
 
-  // stage 0: k < k0, into buffer 0 through the same element maps
+  // stage 0: k < k0, into buffer 0 through the same element maps (zeros
+  // beyond k0 and beyond the tile's rows / columns)
   const int k0 = K % T::BK ? K % T::BK : T::BK;
-  const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int h = 0; h < T::A_LOADS; ++h) {
     int row, k;
     a_map<T>(tid, h, row, k);
     if (TA) {
-      // four rows of k-row k: whole or nothing
-      const float4 v = k < k0 ? ld_global4(a_base + k * lda + row) : zero;
+      // rows row .. row + 3 of k-row k
+      const float4 v = load4(a_base + (k < k0 ? k : 0) * lda, row, rows, k < k0);
       *reinterpret_cast<float4*>(lds_a + (k / 4) * T::A_GROUP + (k % 4) * BM + row) = v;
     } else {
-      // k .. k + 3 of one row, each below k0 or zero
-      const float4 v = load4(a_base + row * lda, k, k0, true);
+      // k .. k + 3 of one row
+      const float4 v = load4(a_base + (row < rows ? row : 0) * lda, k, k0, row < rows);
       float* const dst = lds_a + (k / 4) * T::A_GROUP + row;
       dst[0] = v.x;
       dst[BM] = v.y;
@@ -232,14 +242,14 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
     int k, col;
     b_map<T>(tid, h, k, col);
     if (TB) {
-      const float4 v = load4(b_base + col * ldb, k, k0, true);
+      const float4 v = load4(b_base + (col < cols ? col : 0) * ldb, k, k0, col < cols);
       float* const dst = lds_b + (k / 4) * T::B_GROUP + col;
       dst[0] = v.x;
       dst[T::BN] = v.y;
       dst[2 * T::BN] = v.z;
       dst[3 * T::BN] = v.w;
     } else {
-      const float4 v = k < k0 ? ld_global4(b_base + k * ldb + col) : zero;
+      const float4 v = load4(b_base + (k < k0 ? k : 0) * ldb, col, cols, k < k0);
       *reinterpret_cast<float4*>(lds_b + (k / 4) * T::B_GROUP + (k % 4) * T::BN + col) = v;
     }
   }
@@ -302,21 +312,40 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   // Block (i, j) register r holds C[row0 + 64 wm + 16 kg + 4 r + i]
   // [col0 + 64 wn + 4 lrow + j]: for each (r, i) a lane owns four adjacent
   // outputs of one row.  With beta != 0 the rows of one r are read before
-  // any is written (the loads cannot move above earlier stores).
+  // any is written (the loads cannot move above earlier stores).  Edge
+  // tiles store only rows below M and columns below N.
+  const int r_lane = wm * 64 + 16 * kg, c_lane = wn * 64 + 4 * lrow;  // within the tile
   if (SPLIT) {
-    float* const w = ws + part * int64_t(p.M) * p.N + (row0 + wm * 64 + 16 * kg) * p.N + col0 +
-                     wn * 64 + 4 * lrow;
+    float* const w = ws + part * int64_t(p.M) * p.N + (row0 + r_lane) * p.N + col0 + c_lane;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < ilo || i >= ihi || r_lane + 4 * r + i >= rows) continue;
+        const float4 v = make_float4(acc[i][r], acc[i][4 + r], acc[i][8 + r], acc[i][12 + r]);
+        float* const wr = w + (4 * r + i) * int64_t(p.N);
+        if (whole || c_lane + 3 < cols) {
+          st_global4(wr, v);
+        } else {
+          if (c_lane + 0 < cols) wr[0] = v.x;
+          if (c_lane + 1 < cols) wr[1] = v.y;
+          if (c_lane + 2 < cols) wr[2] = v.z;
+        }
+      }
+    return;
+  }
+  const float alpha = p.alpha, beta = p.beta;
+  float* const cw = p.C + (row0 + r_lane) * p.ldc + col0 + c_lane;
+  if (!whole) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (i >= ilo && i < ihi)
-          st_global4(w + (4 * r + i) * int64_t(p.N),
-                     make_float4(acc[i][r], acc[i][4 + r], acc[i][8 + r], acc[i][12 + r]));
+        if (i >= ilo && i < ihi && r_lane + 4 * r + i < rows)
+          store4(cw + (4 * r + i) * p.ldc, c_lane, cols,
+                 make_float4(acc[i][r], acc[i][4 + r], acc[i][8 + r], acc[i][12 + r]), alpha, beta);
     return;
   }
-  const float alpha = p.alpha, beta = p.beta;
-  float* const cw = p.C + (row0 + wm * 64 + 16 * kg) * p.ldc + col0 + wn * 64 + 4 * lrow;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float4 old[4];
@@ -344,7 +373,7 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
 template <class T>
 bool fits(const Problem& p) {
   if (p.trans_a != T::TA || p.trans_b != T::TB) return false;
-  if (p.M <= 0 || p.N <= 0 || p.M % T::BM || p.N % T::BN || p.K < 1) return false;
+  if (p.M <= 0 || p.N <= 0 || p.K < 1) return false;
   // largest byte offset of a load (record counts, plus the stages the loop
   // prefetches past K) stays below 2^31
   const int64_t lim = int64_t(1) << 31, past = p.K + (T::PREFETCH + 1) * T::BK;
@@ -355,7 +384,7 @@ bool fits(const Problem& p) {
 
 template <class T, bool SPLIT>
 hipError_t launch_t(const Problem& p, int64_t k_split, float* ws, hipStream_t s) {
-  const int64_t tm = p.M / T::BM, tn = p.N / T::BN;
+  const int64_t tm = ceil_div(p.M, T::BM), tn = ceil_div(p.N, T::BN);
   const int64_t items = tm * tn * (SPLIT ? ceil_div(p.K, k_split) : 1);
   hipLaunchKernelGGL((k_kloop<T, SPLIT>), dim3(static_cast<unsigned>(items)), dim3(T::THREADS), 0, s,
                      p, tm, tn, k_split, ws);

@@ -111,21 +111,22 @@ def test_launch_shapes():
     assert shape == {"workgroups": 256, "threads": 256, "k_steps": 512, "tile_m": 128, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(10, 1792, 1792, 1792)
     assert shape == {"workgroups": 196, "threads": 256, "k_steps": 112, "tile_m": 128, "tile_n": 128}
-    # ... or, on a whole grid of >= 64 tiles of 64 x 64, the deep-stage
-    # 64 x 64 loop (4 K-slice wavefronts, 64-deep stages) ...
+    # ... or, on a grid of >= 64 tiles of 64 x 64 (edge tiles partial), the
+    # deep-stage 64 x 64 loop (4 K-slice wavefronts, 64-deep stages) ...
     for M, N, K in [(1024, 1024, 1024), (1536, 1536, 1536), (3072, 3072, 3072),
-                    (1024, 1024, 4096), (512, 512, 512)]:
+                    (1024, 1024, 4096), (512, 512, 512), (3000, 3000, 3000),
+                    (4096 + 17, 4096, 64), (1000, 700, 300)]:
         shape = sgemm.hip_sgemm_launch_shape(10, M, N, K)
-        assert shape == {"workgroups": (M // 64) * (N // 64), "threads": 256,
+        assert shape == {"workgroups": -(-M // 64) * -(-N // 64), "threads": 256,
                          "k_steps": -(-K // 64), "tile_m": 64, "tile_n": 64}, (M, N, K)
     # ... split into K parts when K is deep and there is less than one round
     # of those tiles: at most two work items per CU (512 x 512 x 8192: 64
     # tiles in 8 parts of 1024) ...
     shape = sgemm.hip_sgemm_launch_shape(10, 512, 512, 8192)
     assert shape == {"workgroups": 64 * 8, "threads": 256, "k_steps": 16, "tile_m": 64, "tile_n": 64}
-    # ... and otherwise compiled 64 x 64 tiles with two K slices (3000^3,
-    # 256^3, and shapes whose fringe would be wider than 16)
-    for M, N, K in [(3000, 3000, 3000), (256, 256, 256), (4096 + 17, 4096, 64)]:
+    # ... and otherwise (fewer than 64 such tiles) compiled 64 x 64 tiles
+    # with two K slices
+    for M, N, K in [(256, 256, 256), (300, 500, 100)]:
         shape = sgemm.hip_sgemm_launch_shape(10, M, N, K)
         assert shape == {"workgroups": -(-M // 64) * -(-N // 64), "threads": 512,
                          "k_steps": -(-K // 32), "tile_m": 64, "tile_n": 64}

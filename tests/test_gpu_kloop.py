@@ -120,8 +120,7 @@ TILE_SHAPES = {0: (256, 128), 1: (128, 128), 6: (64, 64)}
 def test_tile_api_whole_tiles(tile, gm, gn, K):
     """hip_sgemm_tile_split(tile, 1) takes the assembly loop on a grid of
     gm x gn whole tiles: one stage, odd and even stage counts, ragged first
-    stages; an extra row outside whole tiles falls back to the compiled
-    tile (checked as well)."""
+    stages; and with one extra row, a partial bottom edge."""
     bm, bn = TILE_SHAPES[tile]
     for M, N in ((gm * bm, gn * bn), (gm * bm + 1, gn * bn)):
         print(f"[kloop tile api] tile {tile}: {M}x{N}x{K}", flush=True)
@@ -274,3 +273,67 @@ def test_kloop_split_k_every_orientation():
         outs[op_a + op_b] = out
     for key in ("NT", "TN", "TT"):
         assert np.array_equal(outs["NN"].view(np.uint32), outs[key].view(np.uint32)), key
+
+
+EDGE_SHAPES = [(1000, 700, 300), (3000, 3000, 77), (65, 4097, 129), (4097, 65, 33), (777, 1029, 1000),
+               (2049, 2047, 16)]
+
+
+@pytest.mark.parametrize("tile", sorted(TILE_SHAPES))
+@pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
+def test_kloop_edge_tiles_every_orientation(tile, M, N, K):
+    """Grids whose bottom and right tiles are partial: the loads past M / N
+    read zeros or elements only out-of-range outputs use, the epilogue
+    stores only inside the matrix (the harness's guard regions and padding
+    check that), and every orientation gives the same bits."""
+    print(f"[kloop edges] tile {tile} {M}x{N}x{K}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 13600 + M + N + K + tile)
+    rows = [r for r in _rows(M) if 0 <= r < M]
+    ref = oracle.oracle_sgemm(A[rows], B, C[rows], 0.5, 3.0)
+    outs = {}
+    for op_a, op_b in OPS:
+        sa = np.ascontiguousarray(A.T) if op_a == "T" else A
+        sb = np.ascontiguousarray(B.T) if op_b == "T" else B
+        case = gh.Case(M, N, K, 0.5, 3.0, sa, sb, C, sa.shape[1] + 3, sb.shape[1] + 1, N + 5)
+
+        def call(*args, op_a=op_a, op_b=op_b):
+            if op_a == "N" and op_b == "N":
+                return sgemm.hip_sgemm_tile_split(tile, 1, *args)
+            return sgemm.hip_sgemm_ex(op_a, op_b, *args)
+        out, st = gh.run(case, call)
+        assert st == 0
+        err = oracle.normalised_error(out[rows], ref, C[rows], 0.5, 3.0, strict=True)
+        assert err <= BOUND, (op_a, op_b, err)
+        outs[op_a + op_b] = out
+    if tile == 6:
+        # level 10 (hip_sgemm_ex) takes the same 64 x 64 loop on these grids
+        for key in ("NT", "TN", "TT"):
+            assert np.array_equal(outs["NN"].view(np.uint32), outs[key].view(np.uint32)), key
+
+
+@pytest.mark.parametrize("tile", sorted(TILE_SHAPES))
+def test_kloop_edge_tiles_nan_c_misaligned(tile):
+    M, N, K = 1000, 700, 300
+    A, B, _ = inputs.make_abc(M, N, K, 13700 + tile)
+    nanC = np.full((M, N), np.nan, np.float32)
+
+    def call(*args):
+        return sgemm.hip_sgemm_tile_split(tile, 1, *args)
+    out, st = gh.run(gh.Case(M, N, K, -1.5, 0.0, A, B, nanC, K + 3, N + 5, N + 7, 1, 2, 3), call)
+    assert st == 0 and np.all(np.isfinite(out))
+    ref = oracle.oracle_sgemm(A, B, None, -1.5, 0.0)
+    assert oracle.normalised_error(out, ref, None, -1.5, 0.0, strict=True) <= BOUND
+
+
+@pytest.mark.parametrize("tile", sorted(TILE_SHAPES))
+def test_kloop_edge_tiles_integer_exact_and_split(tile):
+    """Integer data on a partial grid, unsplit and in 3 K parts: exact."""
+    M, N, K = 600, 520, 1300
+    A, B, C = inputs.integer_abc(M, N, K, seed=13800 + tile)
+    ref = oracle.oracle_sgemm(A, B, C, 1.0, -1.0)
+    for splits in (1, 3):
+        def call(*args, splits=splits):
+            return sgemm.hip_sgemm_tile_split(tile, splits, *args)
+        out, st = gh.run(gh.Case(M, N, K, 1.0, -1.0, A, B, C), call)
+        assert st == 0
+        assert np.array_equal(out.astype(np.float64), ref.ref), splits
