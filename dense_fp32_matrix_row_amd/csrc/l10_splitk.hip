@@ -20,7 +20,11 @@
 // pool that the library creates per device on first use and keeps for the
 // life of the process (release threshold: never), allocated and freed on the
 // caller's stream around the two kernels.  Concurrent calls on other
-// streams therefore never share a workspace.
+// streams therefore never share a workspace.  On a stream being captured
+// into a graph the pool is not touched (it can be neither created nor
+// configured during a capture): the workspace is then a stream-ordered
+// allocation from the device's default pool, which the capture records as
+// a graph memory node.
 #include <mutex>
 
 #include "sgemm_internal.h"
@@ -99,11 +103,18 @@ hipError_t launch_reduce(const float* ws, int64_t splits, const Problem& p, hipS
 hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStream_t s) {
   const int64_t splits = ceil_div(p.K, k_split);
   const size_t bytes = size_t(splits) * size_t(p.M) * size_t(p.N) * sizeof(float);
-  hipMemPool_t pool = nullptr;
-  hipError_t e = pool_for_current_device(&pool);
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &capture);
   if (e != hipSuccess) return e;
   void* ws = nullptr;
-  e = hipMallocFromPoolAsync(&ws, bytes, pool, s);
+  if (capture == hipStreamCaptureStatusActive) {
+    e = hipMallocAsync(&ws, bytes, s);
+  } else {
+    hipMemPool_t pool = nullptr;
+    e = pool_for_current_device(&pool);
+    if (e != hipSuccess) return e;
+    e = hipMallocFromPoolAsync(&ws, bytes, pool, s);
+  }
   if (e != hipSuccess) return e;
   e = launch_tiles_split(shape, p, k_split, static_cast<float*>(ws), s);
   if (e == hipSuccess) e = launch_reduce(static_cast<const float*>(ws), splits, p, s);

@@ -25,14 +25,18 @@
  *
  * Ownership and concurrency
  *   The caller owns every buffer; A, B and C are device pointers (HBM of the
- *   current HIP device).  The library allocates nothing, keeps no state and
- *   needs no handle; calls on different streams may run concurrently.  C must
- *   not overlap A or B (undefined, unchecked, as in BLAS).
+ *   current HIP device).  The only memory the library takes is split K's
+ *   workspace (level 10 splits K for deep problems with few output tiles;
+ *   see hip_sgemm_tile_split for where it comes from); it keeps no other
+ *   state and needs no handle; calls on different streams may run
+ *   concurrently.  C must not overlap A or B (undefined, unchecked, as in
+ *   BLAS).
  *
  * Asynchrony
- *   Every call enqueues its kernel on `stream` (0 = the null stream) and
- *   returns without synchronising.  Argument errors are detected on the host
- *   before anything is enqueued.
+ *   Every call enqueues its kernels on `stream` (0 = the null stream) and
+ *   returns without synchronising; a stream under graph capture records
+ *   them, and the graph replays the call.  Argument errors are detected on
+ *   the host before anything is enqueued.
  *
  * Conventions where the pages are silent (BLAS conventions)
  *   - M == 0 or N == 0: nothing is launched, returns 0.
@@ -168,7 +172,9 @@ int hip_sgemm_level(int level, int M, int N, int K, float alpha,
  * Split K needs S x M x N floats of workspace: the library takes it from a
  * stream-ordered memory pool of its own (one per device, created on first
  * use, memory kept cached until the process ends), allocated and released on
- * `stream` around the two kernels; concurrent calls never share it.  Results
+ * `stream` around the two kernels; concurrent calls never share it.  On a
+ * stream under graph capture it is a stream-ordered allocation from the
+ * device's default pool instead (recorded as a graph memory node).  Results
  * are bit-reproducible for a given (tile, splits, shape).  Other arguments,
  * quick returns and status codes as hip_sgemm; -101 for a bad tile or
  * splits < 1.
