@@ -210,10 +210,14 @@ class Tile:
         stores = self.stage_stores(st, nxt)
         loads = self.loads(st)
         assert len(loads) + 1 < 16
-        # stores after MFMAs 4..15 of the first step (spread when more than 12)
+        # stores after MFMAs 1..12 of the first step (spread when more than
+        # 12), so that the last one has three MFMAs to complete in before the
+        # next step's lgkmcnt(0): with one wavefront per SIMD nothing else
+        # would cover that wait (measured: 1024 x 1024 x 4096 on the 64 x 64
+        # tile 122 -> 125 TFLOP/s against stores after MFMAs 4..15)
         store_at: dict[int, list[str]] = {}
         for i, ins in enumerate(stores):
-            slot = 4 + i if len(stores) <= 12 else 4 + i * 12 // len(stores)
+            slot = 1 + i if len(stores) <= 12 else 1 + i * 12 // len(stores)
             store_at.setdefault(slot, []).append(ins)
         out = []
         for ss in range(self.STEPS):
@@ -224,7 +228,7 @@ class Tile:
             if ss == 0:
                 # stage n + 1 complete (its set's loads are the older ones in
                 # flight), then stored into the free buffer
-                extra.setdefault(3, []).append(f"s_waitcnt vmcnt({per_stage * (self.DEPTH - 1)})")
+                extra.setdefault(0, []).append(f"s_waitcnt vmcnt({per_stage * (self.DEPTH - 1)})")
                 for slot, ins in store_at.items():
                     extra.setdefault(slot, []).extend(ins)
             if ss == 1:
