@@ -21,8 +21,10 @@ transposed A and a row-major B are stored whole):
             register sets.
 
 Stage 0 is the first K % 16 k (a whole stage when K % 16 == 0), zero-padded,
-and is put into LDS buffer 0 by the kernel's C++ part; the loop starts by
-loading stage 1 at that offset, so every stage it loads is whole.
+and is put into LDS buffer 0 by the kernel's C++ part; every stage the
+assembly loads (from stage 1 on, at that offset) is whole.  Each tile has
+two statements: a prelude that requests stages 1 .. DEPTH, issued before the
+C++ part's stage-0 loads so that the latencies overlap, and the loop.
 
 Register map (the kernels pin these with asm operand constraints/clobbers):
   v[0:63]   accumulators: 16 blocks of 16 x 16 (block b = 4 i + j at
@@ -250,16 +252,26 @@ class Tile:
                 out += extra.get(b, [])
         return out
 
-    def program(self) -> list[str]:
-        # stage 0 was stored into buffer 0 by the kernel's C++ part just
-        # before this statement; stages 1 .. DEPTH go into sets 1 % DEPTH ..
-        # The compiler cannot see into the statement, so the wait states a
-        # buffer load needs after a vector-ALU write of its descriptor or
-        # offset SGPRs (5 on gfx9) come first, whatever precedes it.
-        prologue = ["s_nop 4", "s_waitcnt lgkmcnt(0)"]
+    def prelude(self) -> list[str]:
+        """The first statement: stages 1 .. DEPTH requested into staging sets
+        1 % DEPTH .., before the kernel's C++ part loads stage 0, so that
+        their memory latencies overlap (one round trip before the loop
+        instead of two).  The compiler cannot see into the statement, so the
+        wait states a buffer load needs after a vector-ALU write of its
+        descriptor or offset SGPRs (5 on gfx9) come first, whatever precedes
+        it.  The loads are still in flight when the statement ends: the
+        staging registers are its outputs, and the loop statement's inputs,
+        pinned to the same registers."""
+        out = ["s_nop 4"]
         for j in range(1, self.DEPTH + 1):
-            prologue += [*self.loads(j % self.DEPTH), *self.ADVANCE]
-        prologue += ["s_barrier", *self.frag_reads(FE, 0, 0)]
+            out += [*self.loads(j % self.DEPTH), *self.ADVANCE]
+        return out
+
+    def program(self) -> list[str]:
+        # stage 0 was stored into buffer 0 by the kernel's C++ part between
+        # the prelude and this statement; its stores complete, then the
+        # barrier makes every wavefront's visible
+        prologue = ["s_waitcnt lgkmcnt(0)", "s_barrier", *self.frag_reads(FE, 0, 0)]
         pairs = ["s_cmp_eq_u32 %[pairs], 0", "s_cbranch_scc1 .Lkloop_odd_%=", ".Lkloop_pair_%=:",
                  *self.k_step(0), *self.k_step(1),
                  "s_sub_u32 %[pairs], %[pairs], 1", "s_cmp_lg_u32 %[pairs], 0",
@@ -281,10 +293,19 @@ TILES = [Tile(*shape, ta, tb) for shape in SHAPES for ta in (False, True) for tb
 def render() -> str:
     lines = ["// Generated by gen_kloop.py (the K loops of l10_kloop.hip); do not edit."]
     for t in TILES:
-        lines.append(f"#define SGEMM_KLOOP_ASM_{t.name} \\")
-        lines += [f'  "{ins}\\n" \\' for ins in t.program()]
-        lines.append('  ""')
-        regs = ", ".join(f'"v{r}"' for r in range(FE, t.last_vgpr() + 1))
+        for macro, prog in (("PRE", t.prelude()), ("ASM", t.program())):
+            lines.append(f"#define SGEMM_KLOOP_{macro}_{t.name} \\")
+            lines += [f'  "{ins}\\n" \\' for ins in prog]
+            lines.append('  ""')
+        # staging registers: outputs of the prelude (written by loads still
+        # in flight, so early-clobber: no input may share them), then
+        # read-write operands of the loop; the fragment sets are clobbers
+        quads = range(t.DEPTH * t.SET // 4)
+        out = ", ".join(f'"=&{{v[{STAGING + 4*q}:{STAGING + 4*q + 3}]}}"(stg[{q}])' for q in quads)
+        io = ", ".join(f'"+{{v[{STAGING + 4*q}:{STAGING + 4*q + 3}]}}"(stg[{q}])' for q in quads)
+        lines.append(f"#define SGEMM_KLOOP_STAGING_OUT_{t.name} {out}")
+        lines.append(f"#define SGEMM_KLOOP_STAGING_IO_{t.name} {io}")
+        regs = ", ".join(f'"v{r}"' for r in range(FE, STAGING))
         lines.append(f"#define SGEMM_KLOOP_CLOBBERS_{t.name} {regs}")
     return "\n".join(lines) + "\n"
 

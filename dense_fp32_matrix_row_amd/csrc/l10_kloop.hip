@@ -16,9 +16,11 @@
 // is the difference between level 9's compiled loop and this one on the
 // same tile (4096^3: 138.5 against 150-152 TFLOP/s on MI355X).
 //
-// The first stage holds the K % 16 leftover k (a whole stage when
-// K % 16 == 0), loaded with per-element bounds here in C++ and stored into
+// The first stage holds the K % BK leftover k (a whole stage when
+// K % BK == 0), loaded with per-element bounds here in C++ and stored into
 // LDS buffer 0 before the loop; every stage the loop loads is then whole.
+// The loop's first stages are requested by a prelude statement before the
+// C++ loads of stage 0, so both memory latencies overlap.
 // The loop reads A and B through buffer resources whose record counts end
 // at the last element the tile may use, so the loads it issues past the
 // last stage (one or two stages of prefetch) read zeros or elements of the
@@ -43,6 +45,7 @@ namespace sgemm {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
@@ -96,26 +99,30 @@ __device__ __forceinline__ intx4 buffer_resource(const float* base, uint32_t byt
 // thread and stage (at most), the 64-deep tile four, and it also takes
 // each buffer's own store base (its 32-bit stores cannot reach the second
 // buffer by an immediate).  Unused inputs would still occupy registers.
-#define SGEMM_KLOOP_OUTPUTS                                                                \
-  : "+{v[0:15]}"(a0), "+{v[16:31]}"(a1), "+{v[32:47]}"(a2), "+{v[48:63]}"(a3), [sA] "+s"(sA), \
-    [sB] "+s"(sB), [pairs] "+s"(pairs)
-#define SGEMM_KLOOP_INPUTS                                                                 \
+// Two statements per tile: the prelude (stages 1 .. PREFETCH requested into
+// the staging registers, its outputs) and the loop (the staging registers
+// read-write, the accumulators pinned to v0 .. v63).
+#define SGEMM_KLOOP_LOAD_INPUTS                                                            \
   [rsA] "s"(rsA), [rsB] "s"(rsB), [oA0] "v"(oA[0]), [oA1] "v"(oA[1]), [oB0] "v"(oB[0]),    \
-      [wA] "v"(wA), [wB] "v"(wB), [rA] "v"(rA), [rB] "v"(rB), [stepA] "s"(stepA),          \
-      [stepB] "s"(stepB), [odd] "s"(odd)
-#define SGEMM_KLOOP_RUN(NAME)                                                                 \
-  asm volatile(SGEMM_KLOOP_ASM_##NAME SGEMM_KLOOP_OUTPUTS : SGEMM_KLOOP_INPUTS, [oB1] "v"(oB[1]) \
+      [stepA] "s"(stepA), [stepB] "s"(stepB)
+#define SGEMM_KLOOP_TWO_B , [oB1] "v"(oB[1])
+#define SGEMM_KLOOP_ONE_B
+#define SGEMM_KLOOP_DEEP \
+  , [oB1] "v"(oB[1]), [oA2] "v"(oA[2]), [oA3] "v"(oA[3]), [oB2] "v"(oB[2]), [oB3] "v"(oB[3])
+#define SGEMM_KLOOP_DEEP_STORES , [wA1] "v"(wA + T::A_STAGE), [wB1] "v"(wB + T::B_STAGE)
+#define SGEMM_KLOOP_PRELUDE(NAME, LOADS)                                                  \
+  asm volatile(SGEMM_KLOOP_PRE_##NAME                                                     \
+               : SGEMM_KLOOP_STAGING_OUT_##NAME, [sA] "+s"(sA), [sB] "+s"(sB)             \
+               : SGEMM_KLOOP_LOAD_INPUTS LOADS                                            \
+               : "memory", "scc")
+#define SGEMM_KLOOP_LOOP(NAME, LOADS, STORES)                                             \
+  asm volatile(SGEMM_KLOOP_ASM_##NAME                                                     \
+               : "+{v[0:15]}"(a0), "+{v[16:31]}"(a1), "+{v[32:47]}"(a2), "+{v[48:63]}"(a3), \
+                 [sA] "+s"(sA), [sB] "+s"(sB), [pairs] "+s"(pairs),                       \
+                 SGEMM_KLOOP_STAGING_IO_##NAME                                            \
+               : SGEMM_KLOOP_LOAD_INPUTS LOADS STORES, [wA] "v"(wA), [wB] "v"(wB),       \
+                 [rA] "v"(rA), [rB] "v"(rB), [odd] "s"(odd)                               \
                : SGEMM_KLOOP_CLOBBERS_##NAME, "memory", "scc")
-#define SGEMM_KLOOP_RUN_ONE_B(NAME)                                                          \
-  asm volatile(SGEMM_KLOOP_ASM_##NAME SGEMM_KLOOP_OUTPUTS : SGEMM_KLOOP_INPUTS               \
-               : SGEMM_KLOOP_CLOBBERS_##NAME, "memory", "scc")
-#define SGEMM_KLOOP_RUN_DEEP(NAME)                                                             \
-  asm volatile(SGEMM_KLOOP_ASM_##NAME SGEMM_KLOOP_OUTPUTS                                      \
-               : SGEMM_KLOOP_INPUTS, [oB1] "v"(oB[1]), [oA2] "v"(oA[2]), [oA3] "v"(oA[3]),      \
-                 [oB2] "v"(oB[2]), [oB3] "v"(oB[3]), [wA1] "v"(wA + T::A_STAGE),               \
-                 [wB1] "v"(wB + T::B_STAGE)                                                    \
-               : SGEMM_KLOOP_CLOBBERS_##NAME, "memory", "scc")
-
 // Per-thread element maps of one stage (the loop's loads and stores, and
 // the C++ first stage, use the same ones).  Element h of a thread, with
 // per = float4s per row (k-row) of the operand as stored (A_PER, B_PER):
@@ -181,10 +188,10 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   const int64_t b_ks = TB ? 1 : ldb, b_cs = TB ? ldb : 1;
   const float* const a_base = p.A + row0 * a_rs + k_lo * a_ks;
   const float* const b_base = p.B + col0 * b_cs + k_lo * b_ks;
-  const intx4 rsA =
-      buffer_resource(a_base, static_cast<uint32_t>(((rows - 1) * a_rs + (K - 1) * a_ks + 1) * 4));
-  const intx4 rsB =
-      buffer_resource(b_base, static_cast<uint32_t>(((K - 1) * b_ks + (cols - 1) * b_cs + 1) * 4));
+  const uint32_t a_bytes = static_cast<uint32_t>(((rows - 1) * a_rs + (K - 1) * a_ks + 1) * 4);
+  const uint32_t b_bytes = static_cast<uint32_t>(((K - 1) * b_ks + (cols - 1) * b_cs + 1) * 4);
+  const intx4 rsA = buffer_resource(a_base, a_bytes);
+  const intx4 rsB = buffer_resource(b_base, b_bytes);
   uint32_t oA[4] = {0, 0, 0, 0}, oB[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int h = 0; h < T::A_LOADS; ++h) {
@@ -222,25 +229,104 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   const uint32_t stepA = static_cast<uint32_t>(T::BK * a_ks * 4);
   const uint32_t stepB = static_cast<uint32_t>(T::BK * b_ks * 4);
 
-  // stage 0: k < k0, into buffer 0 through the same element maps (zeros
-  // beyond k0 and beyond the tile's rows / columns)
+  // stages 1 .. PREFETCH requested first (their loads stay in flight in the
+  // staging registers), then stage 0: k < k0, into buffer 0 through the
+  // same element maps (zeros beyond k0 and beyond the tile's rows /
+  // columns); the two latencies overlap
   const int k0 = K % T::BK ? K % T::BK : T::BK;
+  uint32_t sA = static_cast<uint32_t>(k0 * a_ks * 4), sB = static_cast<uint32_t>(k0 * b_ks * 4);
+  floatx4 stg[T::PREFETCH * (T::A_LOADS + T::B_LOADS)];
+  if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_PRELUDE(256x128_NN, SGEMM_KLOOP_ONE_B);
+  else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_PRELUDE(256x128_NT, SGEMM_KLOOP_ONE_B);
+  else if constexpr (BM == 256 && !TB) SGEMM_KLOOP_PRELUDE(256x128_TN, SGEMM_KLOOP_ONE_B);
+  else if constexpr (BM == 256) SGEMM_KLOOP_PRELUDE(256x128_TT, SGEMM_KLOOP_ONE_B);
+  else if constexpr (BM == 128 && !TA && !TB) SGEMM_KLOOP_PRELUDE(128x128_NN, SGEMM_KLOOP_TWO_B);
+  else if constexpr (BM == 128 && !TA) SGEMM_KLOOP_PRELUDE(128x128_NT, SGEMM_KLOOP_TWO_B);
+  else if constexpr (BM == 128 && !TB) SGEMM_KLOOP_PRELUDE(128x128_TN, SGEMM_KLOOP_TWO_B);
+  else if constexpr (BM == 128) SGEMM_KLOOP_PRELUDE(128x128_TT, SGEMM_KLOOP_TWO_B);
+  else if constexpr (!TA && !TB) SGEMM_KLOOP_PRELUDE(64x64_NN, SGEMM_KLOOP_DEEP);
+  else if constexpr (!TA) SGEMM_KLOOP_PRELUDE(64x64_NT, SGEMM_KLOOP_DEEP);
+  else if constexpr (!TB) SGEMM_KLOOP_PRELUDE(64x64_TN, SGEMM_KLOOP_DEEP);
+  else SGEMM_KLOOP_PRELUDE(64x64_TT, SGEMM_KLOOP_DEEP);
+  // Stage 0 with buffer loads, all issued before the first LDS store (one
+  // memory round trip, overlapping the prelude's); what lies outside the
+  // stage (k >= k0) or the tile (rows, cols) is read at an offset beyond the
+  // record count, which returns 0.  Whole tiles with k0 % 4 == 0 (a
+  // uniform test) take each float4 whole or not at all (128-bit loads);
+  // otherwise every element is its own 32-bit load.  The compiler sees
+  // these loads and waits only as far as each store needs.
+  constexpr uint32_t kOutside = 0x80000000u;  // beyond every record count (< 2^31)
+  const __amdgpu_buffer_rsrc_t ra0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a_base), 0, static_cast<int>(a_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(b_base), 0, static_cast<int>(b_bytes), 0x00020000);
+  float av[T::A_LOADS][4], bv[T::B_LOADS][4];
+  if (k0 % 4 == 0 && whole) {
+#pragma unroll
+    for (int h = 0; h < T::A_LOADS; ++h) {
+      int row, k;
+      a_map<T>(tid, h, row, k);
+      const uint32_t off = k < k0 ? static_cast<uint32_t>((row * a_rs + k * a_ks) * 4) : kOutside;
+      const float4 v =
+          __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ra0, off, 0, 0));
+      av[h][0] = v.x;
+      av[h][1] = v.y;
+      av[h][2] = v.z;
+      av[h][3] = v.w;
+    }
+#pragma unroll
+    for (int h = 0; h < T::B_LOADS; ++h) {
+      int k, col;
+      b_map<T>(tid, h, k, col);
+      const uint32_t off = k < k0 ? static_cast<uint32_t>((k * b_ks + col * b_cs) * 4) : kOutside;
+      const float4 v =
+          __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rb0, off, 0, 0));
+      bv[h][0] = v.x;
+      bv[h][1] = v.y;
+      bv[h][2] = v.z;
+      bv[h][3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < T::A_LOADS; ++h) {
+      int row, k;
+      a_map<T>(tid, h, row, k);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // a transposed A holds rows row .. row + 3 of k-row k, a row-major A
+        // k .. k + 3 of row `row`
+        const int r = TA ? row + c : row, kk = TA ? k : k + c;
+        const uint32_t off =
+            r < rows && kk < k0 ? static_cast<uint32_t>((r * a_rs + kk * a_ks) * 4) : kOutside;
+        av[h][c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra0, off, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < T::B_LOADS; ++h) {
+      int k, col;
+      b_map<T>(tid, h, k, col);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // a transposed B holds k .. k + 3 of column col, a row-major B
+        // columns col .. col + 3 of k-row k
+        const int kk = TB ? k + c : k, cc = TB ? col : col + c;
+        const uint32_t off =
+            cc < cols && kk < k0 ? static_cast<uint32_t>((kk * b_ks + cc * b_cs) * 4) : kOutside;
+        bv[h][c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb0, off, 0, 0));
+      }
+    }
+  }
 #pragma unroll
   for (int h = 0; h < T::A_LOADS; ++h) {
     int row, k;
     a_map<T>(tid, h, row, k);
     if (TA) {
-      // rows row .. row + 3 of k-row k
-      const float4 v = load4(a_base + (k < k0 ? k : 0) * lda, row, rows, k < k0);
-      *reinterpret_cast<float4*>(lds_a + (k / 4) * T::A_GROUP + (k % 4) * BM + row) = v;
+      *reinterpret_cast<float4*>(lds_a + (k / 4) * T::A_GROUP + (k % 4) * BM + row) =
+          make_float4(av[h][0], av[h][1], av[h][2], av[h][3]);
     } else {
-      // k .. k + 3 of one row
-      const float4 v = load4(a_base + (row < rows ? row : 0) * lda, k, k0, row < rows);
       float* const dst = lds_a + (k / 4) * T::A_GROUP + row;
-      dst[0] = v.x;
-      dst[BM] = v.y;
-      dst[2 * BM] = v.z;
-      dst[3 * BM] = v.w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[c * BM] = av[h][c];
     }
   }
 #pragma unroll
@@ -248,34 +334,30 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
     int k, col;
     b_map<T>(tid, h, k, col);
     if (TB) {
-      const float4 v = load4(b_base + (col < cols ? col : 0) * ldb, k, k0, col < cols);
       float* const dst = lds_b + (k / 4) * T::B_GROUP + col;
-      dst[0] = v.x;
-      dst[T::BN] = v.y;
-      dst[2 * T::BN] = v.z;
-      dst[3 * T::BN] = v.w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[c * T::BN] = bv[h][c];
     } else {
-      const float4 v = load4(b_base + (k < k0 ? k : 0) * ldb, col, cols, k < k0);
-      *reinterpret_cast<float4*>(lds_b + (k / 4) * T::B_GROUP + (k % 4) * T::BN + col) = v;
+      *reinterpret_cast<float4*>(lds_b + (k / 4) * T::B_GROUP + (k % 4) * T::BN + col) =
+          make_float4(bv[h][0], bv[h][1], bv[h][2], bv[h][3]);
     }
   }
-  uint32_t sA = static_cast<uint32_t>(k0 * a_ks * 4), sB = static_cast<uint32_t>(k0 * b_ks * 4);
   const int stages = (K + T::BK - 1) / T::BK;
   uint32_t pairs = static_cast<uint32_t>(stages / 2);
   const uint32_t odd = static_cast<uint32_t>(stages % 2);
   floatx16 a0 = {}, a1 = {}, a2 = {}, a3 = {};
-  if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_RUN_ONE_B(256x128_NN);
-  else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_RUN_ONE_B(256x128_NT);
-  else if constexpr (BM == 256 && !TB) SGEMM_KLOOP_RUN_ONE_B(256x128_TN);
-  else if constexpr (BM == 256) SGEMM_KLOOP_RUN_ONE_B(256x128_TT);
-  else if constexpr (BM == 128 && !TA && !TB) SGEMM_KLOOP_RUN(128x128_NN);
-  else if constexpr (BM == 128 && !TA) SGEMM_KLOOP_RUN(128x128_NT);
-  else if constexpr (BM == 128 && !TB) SGEMM_KLOOP_RUN(128x128_TN);
-  else if constexpr (BM == 128) SGEMM_KLOOP_RUN(128x128_TT);
-  else if constexpr (!TA && !TB) SGEMM_KLOOP_RUN_DEEP(64x64_NN);
-  else if constexpr (!TA) SGEMM_KLOOP_RUN_DEEP(64x64_NT);
-  else if constexpr (!TB) SGEMM_KLOOP_RUN_DEEP(64x64_TN);
-  else SGEMM_KLOOP_RUN_DEEP(64x64_TT);
+  if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_LOOP(256x128_NN, SGEMM_KLOOP_ONE_B, );
+  else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_LOOP(256x128_NT, SGEMM_KLOOP_ONE_B, );
+  else if constexpr (BM == 256 && !TB) SGEMM_KLOOP_LOOP(256x128_TN, SGEMM_KLOOP_ONE_B, );
+  else if constexpr (BM == 256) SGEMM_KLOOP_LOOP(256x128_TT, SGEMM_KLOOP_ONE_B, );
+  else if constexpr (BM == 128 && !TA && !TB) SGEMM_KLOOP_LOOP(128x128_NN, SGEMM_KLOOP_TWO_B, );
+  else if constexpr (BM == 128 && !TA) SGEMM_KLOOP_LOOP(128x128_NT, SGEMM_KLOOP_TWO_B, );
+  else if constexpr (BM == 128 && !TB) SGEMM_KLOOP_LOOP(128x128_TN, SGEMM_KLOOP_TWO_B, );
+  else if constexpr (BM == 128) SGEMM_KLOOP_LOOP(128x128_TT, SGEMM_KLOOP_TWO_B, );
+  else if constexpr (!TA && !TB) SGEMM_KLOOP_LOOP(64x64_NN, SGEMM_KLOOP_DEEP, SGEMM_KLOOP_DEEP_STORES);
+  else if constexpr (!TA) SGEMM_KLOOP_LOOP(64x64_NT, SGEMM_KLOOP_DEEP, SGEMM_KLOOP_DEEP_STORES);
+  else if constexpr (!TB) SGEMM_KLOOP_LOOP(64x64_TN, SGEMM_KLOOP_DEEP, SGEMM_KLOOP_DEEP_STORES);
+  else SGEMM_KLOOP_LOOP(64x64_TT, SGEMM_KLOOP_DEEP, SGEMM_KLOOP_DEEP_STORES);
   floatx16 acc[4] = {a0, a1, a2, a3};
 
   // K slices: slice s finishes block rows i with i / (4 / KS) == s.  Every
