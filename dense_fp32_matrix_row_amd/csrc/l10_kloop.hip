@@ -54,10 +54,9 @@ constexpr int round256(int n) { return (n + 255) / 256 * 256; }
 // The tile constants gen_kloop.py builds each loop for.
 // GROUP_M: rows of tiles per group of the tile order, so that one XCD's
 // contiguous run of tiles (its L2) covers GROUP_M tile rows.  The 256 x 128
-// tile runs 64 tiles per XCD at once; a 16-deep stage of a row-major A is
-// half a 128-byte line per row, and the fabric fetches of A measure about
-// twice its bytes, so 4 x 16 tiles (A 1024 rows, B 2048 columns) fetch the
-// least: 605 MB per call at 4096^3 against 741 MB for 8 x 8, same time.
+// tile runs 64 tiles per XCD at once; 4 x 16 of them (A 1024 rows, B 2048
+// columns) measured the fewest fabric fetches at 4096^3: 605 MB per call
+// against 741 MB for 8 x 8 and 739 MB for 2 x 32, at the same time.
 template <int BM_, int BN_, int BK_, int KS_, bool TA_, bool TB_>
 struct KTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, KS = KS_, GROUP_M = BM == 256 ? 4 : 8;
