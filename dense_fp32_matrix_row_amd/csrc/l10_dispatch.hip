@@ -9,13 +9,14 @@
 //     mostly empty rows or columns, and the problem is bound by reading the
 //     other operand; l10_thin.hip gives them one 16-row MFMA block or
 //     vector-ALU FMA chains);
-//   - a deep K over a small grid: split K (l10_splitk.hip);
+//   - a deep K over 64-255 tiles of 64 x 64: split K (l10_splitk.hip);
 //   - otherwise one of the three assembly-loop tiles of l10_kloop.hip
 //     (256 x 128, 128 x 128, 64 x 64), the one that leaves the busiest CU
 //     the least work, with partial edge tiles, or whole tiles plus the thin
 //     kernels on a fringe of <= 16 rows / columns (at 4097^3: the 512 whole
 //     tiles of 4096^3 and two one-element strips);
-//   - tiny problems: compiled 64 x 64 tiles with two K slices per stage.
+//   - small problems (fewer than 64 tiles of 64 x 64): the thin matrix-core
+//     kernel over 16-row panels of C.
 // Every output element is computed by exactly one tile or thin kernel (or,
 // split, by one reduction over its slices); the regions are disjoint, so
 // the launches need no ordering beyond the stream's.
@@ -24,7 +25,7 @@
 namespace sgemm {
 namespace {
 
-enum class Plan { kFewRows, kFewCols, kTiles, kTilesWithFringe, kSplitK };
+enum class Plan { kFewRows, kFewCols, kTiles, kTilesWithFringe, kSplitK, kThinPanels };
 
 struct Decomp {
   Plan plan;
@@ -50,7 +51,6 @@ Decomp decompose(int M, int N, int K) {
   if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, M, N, K};
 
   const int64_t tiles64 = ceil_div(M, 64) * ceil_div(N, 64);
-  const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
   const bool deep = K >= 2048 && K >= 2 * int64_t(M > N ? M : N);
 
   // 1. A deep K over less than one round of 64 x 64 tiles (but >= 64 of
@@ -116,24 +116,15 @@ Decomp decompose(int M, int N, int K) {
     return best;
   }
 
-  // 3. Deep K over fewer than 64 tiles of 64 x 64: split K on compiled
-  //    tiles so that about two work items per CU run (slices >= 256 deep,
-  //    <= 16).
-  if (deep && tiles128 < kCUs) {
-    const Shape shape = tiles128 >= 16 ? Shape::kLarge : Shape::kSmall;
-    const int64_t tiles = shape == Shape::kLarge ? tiles128 : tiles64;
-    int64_t splits = ceil_div(2 * kCUs, tiles);
-    if (splits > 16) splits = 16;
-    if (splits > K / 256) splits = K / 256;
-    if (splits >= 2) {
-      const int64_t k_split = k_split_for(K, splits, shape_bk(shape));
-      if (k_split < K) return {Plan::kSplitK, shape, M, N, k_split};
-    }
-  }
-
-  // 4. Everything else (fewer than 64 tiles of 64 x 64): compiled 64 x 64
-  //    tiles with two K slices (256^3: 3.2 against 3.0 for the loop tile).
-  return {Plan::kTiles, Shape::kSmallSliced, M, N, K};
+  // 3. Everything else (fewer than 64 tiles of 64 x 64, any K): the thin
+  //    matrix-core kernel over 16-row panels of C, its columns in blocks of
+  //    16 (64 when there are many), K over sixteen wavefronts per block, so
+  //    that the grid has panels x column blocks workgroups instead of a few
+  //    dozen tiles.  Against compiled 64 x 64 tiles (and, for deep K, their
+  //    split): 256^3 10.4 -> 6.1 us, 400^3 17.2 -> 8.4, 200 x 300 x 2000
+  //    57.8 -> 10.8, 128 x 512 x 4096 24.7 -> 16.7, 300 x 300 x 3000
+  //    31.5 -> 23.2; 256 x 256 x 8192 and 200 x 200 x 16384 the same.
+  return {Plan::kThinPanels, Shape::kSmallSliced, M, N, K};
 }
 
 Geometry geometry10(int M, int N, int K) {
@@ -142,6 +133,7 @@ Geometry geometry10(int M, int N, int K) {
     case Plan::kFewRows: return few_rows_geometry(M, N, K);
     case Plan::kFewCols: return few_cols_geometry(M, N, K);
     case Plan::kSplitK: return tiles_split_geometry(d.shape, M, N, K, d.k_split);
+    case Plan::kThinPanels: return thin_panels_geometry(M, N, K);
     default: return tiles_geometry(d.shape, d.Mm, d.Nm, K);
   }
 }
@@ -153,6 +145,7 @@ hipError_t launch10(const Problem& p, hipStream_t s) {
     case Plan::kFewCols: return launch_few_cols(p, s);
     case Plan::kTiles: return launch_tiles(d.shape, p, s);
     case Plan::kSplitK: return launch_splitk(d.shape, d.k_split, p, s);
+    case Plan::kThinPanels: return launch_thin_panels(p, s);
     case Plan::kTilesWithFringe: break;
   }
   Problem grid = p;

@@ -242,11 +242,20 @@ struct Thin {
 };
 
 constexpr int kThinWaves = 16;
+constexpr int64_t kMaxPanels = 65535;  // grid y limit: panels of 16 rows of C'
 
 template <int V, bool TA, bool TB, bool CT>
-__global__ __launch_bounds__(64 * kThinWaves) void k_thin_mfma(Thin t, int64_t ntiles) {
+__global__ __launch_bounds__(64 * kThinWaves) void k_thin_mfma(Thin whole, int64_t ntiles) {
   typedef float floatx4 __attribute__((ext_vector_type(4)));
   constexpr int W = kThinWaves, NB = 16 * V;
+  // blockIdx.y: the panel of 16 rows of C' this block works on (one panel
+  // for thin problems; several for small ones, whose 64 x 64 tiles would
+  // leave most CUs idle)
+  const int64_t panel = blockIdx.y, r0 = 16 * panel;
+  Thin t = whole;
+  t.M = static_cast<int>(whole.M - r0 < 16 ? whole.M - r0 : 16);
+  t.a = TA ? whole.a + r0 : whole.a + r0 * whole.lda;
+  t.c = CT ? whole.c + r0 : whole.c + r0 * whole.ldc;
   __shared__ float red[W][16][NB];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int i = lane % 16, g = lane / 16;
@@ -341,7 +350,10 @@ hipError_t launch_thin_t(const Thin& t, hipStream_t s) {
   const int64_t ntiles = ceil_div(t.N, 16 * V);
   const int64_t cap = kMaxWorkItems / (64 * kThinWaves);
   const int64_t grid = ntiles < cap ? ntiles : cap;
-  hipLaunchKernelGGL((k_thin_mfma<V, TA, TB, CT>), dim3(static_cast<unsigned>(grid)),
+  const int64_t panels = ceil_div(t.M, 16);
+  if (panels > kMaxPanels) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_thin_mfma<V, TA, TB, CT>),
+                     dim3(static_cast<unsigned>(grid), static_cast<unsigned>(panels)),
                      dim3(64 * kThinWaves), 0, s, t, ntiles);
   return hipGetLastError();
 }
@@ -365,15 +377,16 @@ hipError_t launch_thin(const Thin& t, bool ta, bool tb, hipStream_t s) {
 
 Geometry thin_geometry(int64_t thin_rows, int64_t n, int K, bool few_cols) {
   const int v = thin_width(n, few_cols);
+  const int64_t panels = ceil_div(thin_rows, 16);
   Geometry g;
   g.threads = 64 * kThinWaves;
-  g.tiles = ceil_div(n, 16 * v);
+  const int64_t per_panel = ceil_div(n, 16 * v);
   const int64_t cap = kMaxWorkItems / g.threads;
-  g.workgroups = g.tiles < cap ? g.tiles : cap;
+  g.tiles = per_panel * panels;
+  g.workgroups = (per_panel < cap ? per_panel : cap) * panels;
   g.k_steps = ceil_div(K, 16 * kThinWaves);
   g.tile_m = few_cols ? 16 * v : 16;
   g.tile_n = few_cols ? 16 : 16 * v;
-  (void)thin_rows;
   return g;
 }
 
@@ -454,6 +467,13 @@ hipError_t launch_cols_op(const Problem& p, hipStream_t s) {
     case 16: return launch_cols_t<16, TB>(p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+Geometry thin_panels_geometry(int M, int N, int K) { return thin_geometry(M, N, K, false); }
+
+hipError_t launch_thin_panels(const Problem& p, hipStream_t s) {
+  const Thin t{p.M, p.N, p.K, p.alpha, p.beta, p.A, p.lda, p.B, p.ldb, p.C, p.ldc};
+  return launch_thin<false>(t, p.trans_a, p.trans_b, s);
 }
 
 hipError_t launch_few_cols(const Problem& p, hipStream_t s) {

@@ -211,6 +211,10 @@ Geometry few_rows_geometry(int M, int N, int K);
 hipError_t launch_few_rows(const Problem& p, hipStream_t s);  // needs M <= kThin
 Geometry few_cols_geometry(int M, int N, int K);
 hipError_t launch_few_cols(const Problem& p, hipStream_t s);  // needs N <= kThin
+// Small problems on the thin matrix-core kernel: 16-row panels of C, each
+// panel's columns in blocks of 16-64, K over sixteen wavefronts per block.
+Geometry thin_panels_geometry(int M, int N, int K);
+hipError_t launch_thin_panels(const Problem& p, hipStream_t s);  // needs M <= 16 * 65535
 
 // The rungs (host-side descriptors).
 const LevelDesc* level0();

@@ -124,12 +124,13 @@ def test_launch_shapes():
     # tiles in 8 parts of 1024) ...
     shape = sgemm.hip_sgemm_launch_shape(10, 512, 512, 8192)
     assert shape == {"workgroups": 64 * 8, "threads": 256, "k_steps": 16, "tile_m": 64, "tile_n": 64}
-    # ... and otherwise (fewer than 64 such tiles) compiled 64 x 64 tiles
-    # with two K slices
-    for M, N, K in [(256, 256, 256), (300, 500, 100)]:
+    # ... and otherwise (fewer than 64 such tiles, any K) the thin
+    # matrix-core kernel over 16-row panels: one block of 16 wavefronts per
+    # panel and 16 columns, K in steps of 16 x 16
+    for M, N, K in [(256, 256, 256), (300, 500, 100), (128, 512, 4096), (17, 300, 4096)]:
         shape = sgemm.hip_sgemm_launch_shape(10, M, N, K)
-        assert shape == {"workgroups": -(-M // 64) * -(-N // 64), "threads": 512,
-                         "k_steps": -(-K // 32), "tile_m": 64, "tile_n": 64}
+        assert shape == {"workgroups": -(-M // 16) * -(-N // 16), "threads": 1024,
+                         "k_steps": -(-K // 256), "tile_m": 16, "tile_n": 16}, (M, N, K)
     # ... and the thin kernels for M <= 16 (one block per 16 columns) or
     # N <= 16 (one block per 16 rows)
     shape = sgemm.hip_sgemm_launch_shape(10, 1, 4097, 4097)

@@ -29,7 +29,7 @@ SHAPES = [
     (1, 4097, 1000, 1.0, 1.0),      # few rows, vector ALUs
     (3000, 3, 700, 2.0, -1.0),      # few columns, vector ALUs
     (16, 8192, 512, 1.0, 0.5),      # thin, matrix cores
-    (300, 500, 100, 1.0, 0.0),      # compiled 64 x 64 tiles
+    (300, 500, 100, 1.0, 0.0),      # small: thin kernel over 16-row panels
 ]
 
 
