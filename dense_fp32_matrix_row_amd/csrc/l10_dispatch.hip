@@ -15,8 +15,8 @@
 //     the least work, with partial edge tiles, or whole tiles plus the thin
 //     kernels on a fringe of <= 16 rows / columns (at 4097^3: the 512 whole
 //     tiles of 4096^3 and two one-element strips);
-//   - small problems (fewer than 64 tiles of 64 x 64): the thin matrix-core
-//     kernel over 16-row panels of C.
+//   - small problems (fewer than 128 tiles of 64 x 64): the thin
+//     matrix-core kernel over 16-row panels of C.
 // Every output element is computed by exactly one tile or thin kernel (or,
 // split, by one reduction over its slices); the regions are disjoint, so
 // the launches need no ordering beyond the stream's.
@@ -70,7 +70,7 @@ Decomp decompose(int M, int N, int K) {
     }
   }
 
-  // 2. A grid of >= 64 tiles of 64 x 64: whichever of the three
+  // 2. A grid of >= 128 tiles of 64 x 64: whichever of the three
   //    assembly-loop tiles leaves the busiest CU the least work,
   //    ceil(tiles / CUs) x tile area / efficiency, the efficiency measured
   //    for that tile at that many tiles per CU (256 x 128: 0.955 from two
@@ -89,7 +89,7 @@ Decomp decompose(int M, int N, int K) {
   //    (140.6), 3584^3 (135.3), 4608^3 (140.2 against 128.5 for 648 tiles
   //    of 256 x 128), 5120^3 (146.2 against 119.2 for 800), 1024 x 1024 x
   //    4096 / 8192 (123 / 130.5).
-  if (tiles64 >= 64) {
+  if (tiles64 >= 128) {
     struct Candidate {
       Shape shape;
       int bm, bn;
@@ -116,7 +116,8 @@ Decomp decompose(int M, int N, int K) {
     return best;
   }
 
-  // 3. Everything else (fewer than 64 tiles of 64 x 64, any K): the thin
+  // 3. Everything else (fewer than 128 tiles of 64 x 64, and for a deep K
+  //    fewer than 64): the thin
   //    matrix-core kernel over 16-row panels of C, its columns in blocks of
   //    16 (64 when there are many), K over sixteen wavefronts per block, so
   //    that the grid has panels x column blocks workgroups instead of a few
@@ -124,6 +125,9 @@ Decomp decompose(int M, int N, int K) {
   //    split): 256^3 10.4 -> 6.1 us, 400^3 17.2 -> 8.4, 200 x 300 x 2000
   //    57.8 -> 10.8, 128 x 512 x 4096 24.7 -> 16.7, 300 x 300 x 3000
   //    31.5 -> 23.2; 256 x 256 x 8192 and 200 x 200 x 16384 the same.
+  //    Against 64 x 64 loop tiles at 64-127 of them: 512^3 14.3 -> 11.3 us,
+  //    600^3 17.3 -> 15.6, 512 x 512 x 1536 28.8 -> 21.5 (at 144 and more,
+  //    768^3 and 900^3, the loop tiles are faster).
   return {Plan::kThinPanels, Shape::kSmallSliced, M, N, K};
 }
 

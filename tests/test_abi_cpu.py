@@ -111,10 +111,10 @@ def test_launch_shapes():
     assert shape == {"workgroups": 256, "threads": 256, "k_steps": 512, "tile_m": 128, "tile_n": 128}
     shape = sgemm.hip_sgemm_launch_shape(10, 1792, 1792, 1792)
     assert shape == {"workgroups": 196, "threads": 256, "k_steps": 112, "tile_m": 128, "tile_n": 128}
-    # ... or, on a grid of >= 64 tiles of 64 x 64 (edge tiles partial), the
+    # ... or, on a grid of >= 128 tiles of 64 x 64 (edge tiles partial), the
     # deep-stage 64 x 64 loop (4 K-slice wavefronts, 64-deep stages) ...
     for M, N, K in [(1024, 1024, 1024), (1536, 1536, 1536), (3072, 3072, 3072),
-                    (1024, 1024, 4096), (512, 512, 512), (3000, 3000, 3000),
+                    (1024, 1024, 4096), (768, 768, 768), (3000, 3000, 3000),
                     (4096 + 17, 4096, 64), (1000, 700, 300)]:
         shape = sgemm.hip_sgemm_launch_shape(10, M, N, K)
         assert shape == {"workgroups": -(-M // 64) * -(-N // 64), "threads": 256,
@@ -124,10 +124,11 @@ def test_launch_shapes():
     # tiles in 8 parts of 1024) ...
     shape = sgemm.hip_sgemm_launch_shape(10, 512, 512, 8192)
     assert shape == {"workgroups": 64 * 8, "threads": 256, "k_steps": 16, "tile_m": 64, "tile_n": 64}
-    # ... and otherwise (fewer than 64 such tiles, any K) the thin
+    # ... and otherwise (fewer than 128 such tiles, or 64 for a deep K) the thin
     # matrix-core kernel over 16-row panels: one block of 16 wavefronts per
     # panel and 16 columns, K in steps of 16 x 16
-    for M, N, K in [(256, 256, 256), (300, 500, 100), (128, 512, 4096), (17, 300, 4096)]:
+    for M, N, K in [(256, 256, 256), (300, 500, 100), (128, 512, 4096), (17, 300, 4096),
+                    (512, 512, 512), (700, 500, 800)]:
         shape = sgemm.hip_sgemm_launch_shape(10, M, N, K)
         assert shape == {"workgroups": -(-M // 16) * -(-N // 16), "threads": 1024,
                          "k_steps": -(-K // 256), "tile_m": 16, "tile_n": 16}, (M, N, K)
