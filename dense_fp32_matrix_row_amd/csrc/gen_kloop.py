@@ -27,6 +27,8 @@ two statements: a prelude that requests stages 1 .. DEPTH, issued before the
 C++ part's stage-0 loads so that the latencies overlap, and the loop.
 
 Register map (the kernels pin these with asm operand constraints/clobbers):
+  s[60:63], s[64:67]  buffer resources of A and B, based at the next stage
+            to load, record counts ending at the tile's last element
   v[0:63]   accumulators: 16 blocks of 16 x 16 (block b = 4 i + j at
             v[4b : 4b+3], i = A block, j = B block)
   v[64:71]  fragment set E: A operands of blocks i = 0..3 (v64..v67) and B
@@ -43,7 +45,7 @@ free LDS buffer during step 0 and the same set is reloaded (with the stage
 one or two further on) during step 1; the barrier sits halfway through
 step 3, after which step 0 of the next stage is read from the other buffer,
 so the LDS latency after a barrier hides under the remaining eight MFMAs.
-Loop bookkeeping is scalar (buffer offsets in SGPRs, LDS offsets
+Loop bookkeeping is scalar (buffer resources advanced in SGPRs, LDS offsets
 immediate), so the loop issues no vector-ALU instruction besides the MFMAs.
 
 Run as a script to rewrite l10_kloop.inc; tests check that the committed
@@ -56,6 +58,7 @@ import os
 
 FE, FO = 64, 72                # fragment sets
 STAGING = 80                   # first staging register
+RES_A, RES_B = 60, 64          # buffer resources of A and B: s[60:63], s[64:67]
 
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "l10_kloop.inc")
 
@@ -129,14 +132,23 @@ class Tile:
         (which elements each thread loads is set by the kernel's per-thread
         offsets; see stage_stores)."""
         r = self.set_base(st)
-        out = [f"buffer_load_dwordx4 v[{r + 4*h}:{r + 4*h + 3}], %[oA{h}], %[rsA], %[sA] offen"
+        out = [f"buffer_load_dwordx4 v[{r + 4*h}:{r + 4*h + 3}], %[oA{h}], s[{RES_A}:{RES_A + 3}], 0 offen"
                for h in range(self.A_LOADS)]
         rb = r + 4 * self.A_LOADS
-        out += [f"buffer_load_dwordx4 v[{rb + 4*h}:{rb + 4*h + 3}], %[oB{h}], %[rsB], %[sB] offen"
+        out += [f"buffer_load_dwordx4 v[{rb + 4*h}:{rb + 4*h + 3}], %[oB{h}], s[{RES_B}:{RES_B + 3}], 0 offen"
                 for h in range(self.B_LOADS)]
         return out
 
-    ADVANCE = ["s_add_u32 %[sA], %[sA], %[stepA]", "s_add_u32 %[sB], %[sB], %[stepB]"]
+    # The next stage of each operand: the resource's base moves one stage on
+    # (48-bit address: carry into the high word) and its record count drops
+    # by as much, stopping at 0.  The loads carry no scalar offset, so the
+    # range check, which covers the per-thread offset, bounds every load by
+    # the operand's last element whatever the hardware does with a scalar
+    # offset: a stage loaded past K reads zeros without touching memory.
+    ADVANCE = [f"s_add_u32 s{RES_A}, s{RES_A}, %[stepA]", f"s_addc_u32 s{RES_A + 1}, s{RES_A + 1}, 0",
+               f"s_sub_u32 s{RES_A + 2}, s{RES_A + 2}, %[stepA]", f"s_cselect_b32 s{RES_A + 2}, 0, s{RES_A + 2}",
+               f"s_add_u32 s{RES_B}, s{RES_B}, %[stepB]", f"s_addc_u32 s{RES_B + 1}, s{RES_B + 1}, 0",
+               f"s_sub_u32 s{RES_B + 2}, s{RES_B + 2}, %[stepB]", f"s_cselect_b32 s{RES_B + 2}, 0, s{RES_B + 2}"]
 
     @staticmethod
     def _transposing(w: str, r: int, buf: int, stage: int, row: int, copy: int, copies: int) -> list[str]:

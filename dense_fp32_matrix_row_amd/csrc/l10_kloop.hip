@@ -21,11 +21,14 @@
 // LDS buffer 0 before the loop; every stage the loop loads is then whole.
 // The loop's first stages are requested by a prelude statement before the
 // C++ loads of stage 0, so both memory latencies overlap.
-// The loop reads A and B through buffer resources whose record counts end
-// at the last element the tile may use, so the loads it issues past the
-// last stage (one or two stages of prefetch) read zeros or elements of the
-// same matrix, never beyond it; they land in the idle LDS buffer unused.
-// Byte offsets must stay below 2^31 (kloop_fits).  Tiles at the bottom and
+// The loop reads A and B through buffer resources whose base is the next
+// stage to load and whose record count ends at the last element the tile
+// may use; each stage moves the base on and shrinks the count (down to 0),
+// and the loads carry no scalar offset, so the hardware's range check on
+// the per-thread offset bounds every load: the stages loaded past the last
+// one (one or two of prefetch) read zeros without touching memory and land
+// in the idle LDS buffer unused.  Byte offsets must stay below 2^31
+// (kloop_fits).  Tiles at the bottom and
 // right edges cover fewer rows / columns; their record counts stop at the
 // last row / column of the matrix and their epilogue stores only inside it.
 //
@@ -100,10 +103,12 @@ __device__ __forceinline__ intx4 buffer_resource(const float* base, uint32_t byt
 // buffer by an immediate).  Unused inputs would still occupy registers.
 // Two statements per tile: the prelude (stages 1 .. PREFETCH requested into
 // the staging registers, its outputs) and the loop (the staging registers
-// read-write, the accumulators pinned to v0 .. v63).
-#define SGEMM_KLOOP_LOAD_INPUTS                                                            \
-  [rsA] "s"(rsA), [rsB] "s"(rsB), [oA0] "v"(oA[0]), [oA1] "v"(oA[1]), [oB0] "v"(oB[0]),    \
-      [stepA] "s"(stepA), [stepB] "s"(stepB)
+// read-write, the accumulators pinned to v0 .. v63).  Both advance the
+// buffer resources of A and B, pinned to s[60:63] and s[64:67] (the loop
+// text names their words).
+#define SGEMM_KLOOP_LOAD_INPUTS                                                  \
+  [oA0] "v"(oA[0]), [oA1] "v"(oA[1]), [oB0] "v"(oB[0]), [stepA] "s"(stepA), \
+      [stepB] "s"(stepB)
 #define SGEMM_KLOOP_TWO_B , [oB1] "v"(oB[1])
 #define SGEMM_KLOOP_ONE_B
 #define SGEMM_KLOOP_DEEP \
@@ -111,13 +116,13 @@ __device__ __forceinline__ intx4 buffer_resource(const float* base, uint32_t byt
 #define SGEMM_KLOOP_DEEP_STORES , [wA1] "v"(wA + T::A_STAGE), [wB1] "v"(wB + T::B_STAGE)
 #define SGEMM_KLOOP_PRELUDE(NAME, LOADS)                                                  \
   asm volatile(SGEMM_KLOOP_PRE_##NAME                                                     \
-               : SGEMM_KLOOP_STAGING_OUT_##NAME, [sA] "+s"(sA), [sB] "+s"(sB)             \
+               : SGEMM_KLOOP_STAGING_OUT_##NAME, "+{s[60:63]}"(rsA), "+{s[64:67]}"(rsB)   \
                : SGEMM_KLOOP_LOAD_INPUTS LOADS                                            \
                : "memory", "scc")
 #define SGEMM_KLOOP_LOOP(NAME, LOADS, STORES)                                             \
   asm volatile(SGEMM_KLOOP_ASM_##NAME                                                     \
                : "+{v[0:15]}"(a0), "+{v[16:31]}"(a1), "+{v[32:47]}"(a2), "+{v[48:63]}"(a3), \
-                 [sA] "+s"(sA), [sB] "+s"(sB), [pairs] "+s"(pairs),                       \
+                 "+{s[60:63]}"(rsA), "+{s[64:67]}"(rsB), [pairs] "+s"(pairs),             \
                  SGEMM_KLOOP_STAGING_IO_##NAME                                            \
                : SGEMM_KLOOP_LOAD_INPUTS LOADS STORES, [wA] "v"(wA), [wB] "v"(wB),       \
                  [rA] "v"(rA), [rB] "v"(rB), [odd] "s"(odd)                               \
@@ -189,8 +194,6 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   const float* const b_base = p.B + col0 * b_cs + k_lo * b_ks;
   const uint32_t a_bytes = static_cast<uint32_t>(((rows - 1) * a_rs + (K - 1) * a_ks + 1) * 4);
   const uint32_t b_bytes = static_cast<uint32_t>(((K - 1) * b_ks + (cols - 1) * b_cs + 1) * 4);
-  const intx4 rsA = buffer_resource(a_base, a_bytes);
-  const intx4 rsB = buffer_resource(b_base, b_bytes);
   uint32_t oA[4] = {0, 0, 0, 0}, oB[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int h = 0; h < T::A_LOADS; ++h) {
@@ -233,7 +236,13 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   // same element maps (zeros beyond k0 and beyond the tile's rows /
   // columns); the two latencies overlap
   const int k0 = K % T::BK ? K % T::BK : T::BK;
-  uint32_t sA = static_cast<uint32_t>(k0 * a_ks * 4), sB = static_cast<uint32_t>(k0 * b_ks * 4);
+  // the loop's resources start at stage 1 (k0 k on), their record counts
+  // reduced by as much (0 when nothing of the tile is left)
+  const int64_t a_skip = k0 * a_ks * 4, b_skip = k0 * b_ks * 4;
+  intx4 rsA = buffer_resource(a_base + k0 * a_ks,
+                              a_bytes > a_skip ? static_cast<uint32_t>(a_bytes - a_skip) : 0u);
+  intx4 rsB = buffer_resource(b_base + k0 * b_ks,
+                              b_bytes > b_skip ? static_cast<uint32_t>(b_bytes - b_skip) : 0u);
   floatx4 stg[T::PREFETCH * (T::A_LOADS + T::B_LOADS)];
   if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_PRELUDE(256x128_NN, SGEMM_KLOOP_ONE_B);
   else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_PRELUDE(256x128_NT, SGEMM_KLOOP_ONE_B);
