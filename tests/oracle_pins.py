@@ -22,6 +22,13 @@ What pins what:
   ld_views           padded buffers (NaN padding) give the dense result
   pages_row_major    the row-major buffer example of the lecture notes
   pages_sub_block    the pointer-offset + ld sub-block example
+
+The normalised-error checker has pins of its own (CHECKER_PINS), each taking
+the checker function: hand-made results whose error ratio is an exact power
+of two, in the literal mode (the acceptance metric's denominator
+sum|a*b| + |beta*c|) and the strict mode (|alpha| * sum|a*b| + |beta*c|)
+with positive and negative alpha, and zero-denominator and non-finite
+cases.
 """
 
 from __future__ import annotations
@@ -224,6 +231,71 @@ def pin_pages_sub_block(run):
     view = parent_cm[off:].copy()
     res = run(view, np.eye(h, dtype=np.float32), None, 1.0, 0.0, M=w, N=h, K=h, lda=ld)
     assert np.array_equal(res.ref, sub.T.astype(np.float64))
+
+
+def _res(ref, sumabs):
+    from oracle import oracle
+    return oracle.OracleResult(ref=np.array(ref, np.float64), sumabs=np.array(sumabs, np.float64),
+                               threads=1)
+
+
+def checker_literal(err_fn):
+    """Literal mode, alpha = 1: |out - ref| / sum|a*b|."""
+    res = _res([[1.0, 0.0]], [[2.0, 0.0]])
+    out = np.array([[1.0 + 2.0 ** -20, 0.0]], np.float32)
+    assert err_fn(out, res, None, 1.0, 0.0) == 2.0 ** -21
+
+
+def checker_zero_denominator(err_fn):
+    """A zero denominator demands an exact zero (either sign)."""
+    res = _res([[1.0, 0.0]], [[2.0, 0.0]])
+    assert err_fn(np.array([[1.0, -0.0]], np.float32), res, None, 1.0, 0.0) == 0.0
+    assert err_fn(np.array([[1.0, 1e-30]], np.float32), res, None, 1.0, 0.0) == float("inf")
+
+
+def checker_non_finite(err_fn):
+    res = _res([[1.0, 0.0]], [[2.0, 0.0]])
+    assert err_fn(np.array([[np.nan, 0.0]], np.float32), res, None, 1.0, 0.0) == float("inf")
+    assert err_fn(np.array([[np.inf, 0.0]], np.float32), res, None, 1.0, 0.0) == float("inf")
+
+
+def checker_beta_term(err_fn):
+    """|beta * c| joins the denominator only when beta != 0: ref = 13 from
+    a*b sums of magnitude 2 and beta*c = 3*4; off by 2^-16 the ratio is
+    2^-16 / (2 + 12) in literal mode."""
+    c_in = np.array([[4.0]], np.float32)
+    res = _res([[13.0]], [[2.0]])
+    out = np.array([[13.0 + 2.0 ** -16]], np.float32)
+    assert err_fn(out, res, c_in, 1.0, 3.0) == 2.0 ** -16 / 14.0
+    # beta = 0: C plays no part even if it is NaN
+    res0 = _res([[1.0]], [[2.0]])
+    nan_c = np.array([[np.nan]], np.float32)
+    assert err_fn(np.array([[1.0 + 2.0 ** -20]], np.float32), res0, nan_c, 1.0, 0.0) == 2.0 ** -21
+
+
+def checker_strict_negative_alpha(err_fn):
+    """Strict mode scales the product part by |alpha|.  alpha = -2, beta = 3,
+    sum|a*b| = 2, c = 4: den = 2 * 2 + 3 * 4 = 16 (not -4 + 12 = 8 as with
+    alpha's sign kept); alpha = -2, beta = 0: den = 4 (with the sign kept it
+    would be -4 and every error ratio negative, a vacuous pass)."""
+    c_in = np.array([[4.0]], np.float32)
+    res = _res([[8.0]], [[2.0]])
+    out = np.array([[8.0 + 2.0 ** -16]], np.float32)
+    assert err_fn(out, res, c_in, -2.0, 3.0, strict=True) == 2.0 ** -20
+    assert err_fn(out, res, c_in, -2.0, 3.0, strict=False) == 2.0 ** -16 / 14.0
+    res0 = _res([[-2.0]], [[2.0]])
+    out0 = np.array([[-2.0 + 2.0 ** -10]], np.float32)
+    assert err_fn(out0, res0, None, -2.0, 0.0, strict=True) == 2.0 ** -12
+    assert err_fn(out0, res0, None, -2.0, 0.0, strict=False) == 2.0 ** -11
+    # alpha = 0.5: strict is twice the literal ratio
+    res1 = _res([[0.5]], [[2.0]])
+    out1 = np.array([[0.5 + 2.0 ** -20]], np.float32)
+    assert err_fn(out1, res1, None, 0.5, 0.0, strict=True) == 2.0 ** -20
+    assert err_fn(out1, res1, None, 0.5, 0.0, strict=False) == 2.0 ** -21
+
+
+CHECKER_PINS = [checker_literal, checker_zero_denominator, checker_non_finite, checker_beta_term,
+                checker_strict_negative_alpha]
 
 
 ALL_PINS = [

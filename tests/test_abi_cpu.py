@@ -180,6 +180,29 @@ def test_tile32_geometry_matches_the_six_level_example():
     assert sgemm.hip_sgemm_launch_shape(3, 4096, 4096, 4096)["tile_n"] == coarse["tile"] * coarse["coarse"]
 
 
+def test_regtile8_cells_match_the_six_level_example():
+    """SGEMM 六级优化, K4 section: the thread that computed C[103][69] in K3
+    computes the eight cells C[96..103][69] of that column in K4.  Level 4
+    is that kernel on 64 x 64 tiles: wavefront w of its 512 threads owns
+    rows 8w .. 8w + 7 of the tile and lane l its column l (l4_regtile1d.hip),
+    so the thread owning C[103][69] owns exactly the page's cells."""
+    from tests.oracle_pins import golden
+    g = golden()["regtile8_thread"]
+    shape = sgemm.hip_sgemm_launch_shape(4, 4096, 4096, 4096)
+    tm, tn, threads = shape["tile_m"], shape["tile_n"], shape["threads"]
+    per_thread = tm * tn // threads
+    assert per_thread == g["rows"][1] - g["rows"][0] + 1 == 8
+
+    def cells(tile_row, tile_col, tid):
+        w, lane = divmod(tid, tn)
+        return [(tile_row * tm + per_thread * w + i, tile_col * tn + lane) for i in range(per_thread)]
+
+    owners = [(tr, tc, tid) for tr in range(2) for tc in range(2) for tid in range(threads)
+              if (103, 69) in cells(tr, tc, tid)]
+    assert len(owners) == 1
+    assert cells(*owners[0]) == [(r, g["col"]) for r in range(g["rows"][0], g["rows"][1] + 1)]
+
+
 def test_tile_split_arguments():
     assert sgemm.hip_sgemm_num_tiles() == 7
     names = [sgemm.hip_sgemm_tile_name(t) for t in range(4)]

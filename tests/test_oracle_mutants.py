@@ -85,3 +85,44 @@ def test_unmutated_source_passes(tmp_path):
     lib = oracle.load(_build_mutant(tmp_path, "identity", "acc[j] += p;", "acc[j] += p;"))
     for pin in oracle_pins.ALL_PINS:
         pin(lambda *a, **k: oracle.oracle_sgemm(*a, lib=lib, **k))
+
+
+# Mistakes planted in the checker (oracle.py's normalised_error, a Python
+# function): each variant is the function's source with one slip, compiled
+# into a scratch namespace; at least one checker pin must reject it.
+CHECKER_MUTANTS = {
+    "strict_alpha_sign_kept": ("abs(alpha) if strict", "alpha if strict"),
+    "strict_ignored": ("abs(alpha) if strict else 1.0", "1.0"),
+    "beta_term_dropped": ("den = den + np.abs(beta * np.asarray(C_in, dtype=np.float64))", "pass"),
+    "beta_term_always": ("if beta != 0.0:\n        den = den +", "if True:\n        den = den +"),
+    "zero_den_not_checked": ("if np.any(out[zero] != 0.0):", "if False:"),
+    "nan_not_checked": ("if not np.all(np.isfinite(out[np.isfinite(ref)])):", "if False:"),
+}
+
+
+def _checker_variant(old, new):
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(oracle.normalised_error))
+    assert src.count(old) == 1, old
+    ns = dict(oracle.__dict__)
+    exec(compile(src.replace(old, new), "<checker mutant>", "exec"), ns)
+    return ns["normalised_error"]
+
+
+@pytest.mark.parametrize("name", sorted(CHECKER_MUTANTS))
+def test_checker_pins_catch_mutant(name):
+    fn = _checker_variant(*CHECKER_MUTANTS[name])
+    caught = []
+    for pin in oracle_pins.CHECKER_PINS:
+        try:
+            pin(fn)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"checker mutant {name} passed every checker pin"
+
+
+def test_checker_unmutated_passes():
+    fn = _checker_variant("abs(alpha)", "abs(alpha)")
+    for pin in oracle_pins.CHECKER_PINS:
+        pin(fn)

@@ -32,20 +32,7 @@ def test_argument_errors():
         oracle.oracle_sgemm(z, z, z, 1.0, 0.0, M=2, N=3, K=2, ldb=2)
 
 
-def test_checker_metric():
-    """The normalised-error checker on hand-made cases."""
-    res = oracle.OracleResult(ref=np.array([[1.0, 0.0]]), sumabs=np.array([[2.0, 0.0]]), threads=1)
-    out = np.array([[1.0 + 2e-6, 0.0]], np.float32)
-    err = oracle.normalised_error(out, res, None, 1.0, 0.0)
-    assert abs(err - abs(float(np.float32(1.0 + 2e-6)) - 1.0) / 2.0) < 1e-12
-    # a zero denominator demands an exact zero
-    bad = np.array([[1.0, 1e-30]], np.float32)
-    assert oracle.normalised_error(bad, res, None, 1.0, 0.0) == float("inf")
-    # NaN where the reference is finite fails
-    nan = np.array([[np.nan, 0.0]], np.float32)
-    assert oracle.normalised_error(nan, res, None, 1.0, 0.0) == float("inf")
-    # beta*C enters the denominator only when beta != 0
-    c_in = np.array([[4.0, 1.0]], np.float32)
-    res2 = oracle.OracleResult(ref=np.array([[13.0, 3.0]]), sumabs=np.array([[2.0, 0.0]]), threads=1)
-    out2 = np.array([[13.0, 3.0]], np.float32)
-    assert oracle.normalised_error(out2, res2, c_in, 1.0, 3.0) == 0.0
+@pytest.mark.parametrize("pin", oracle_pins.CHECKER_PINS, ids=lambda f: f.__name__)
+def test_checker_metric(pin):
+    """The normalised-error checker on hand-made cases with exact ratios."""
+    pin(oracle.normalised_error)
