@@ -20,6 +20,7 @@
 // Every output element is computed by exactly one tile or thin kernel (or,
 // split, by one reduction over its slices); the regions are disjoint, so
 // the launches need no ordering beyond the stream's.
+#include "sgemm.h"
 #include "sgemm_internal.h"
 
 namespace sgemm {
@@ -141,6 +142,29 @@ Geometry geometry10(int M, int N, int K) {
     default: return tiles_geometry(d.shape, d.Mm, d.Nm, K);
   }
 }
+
+}  // namespace
+
+PlanInfo plan10(int M, int N, int K) {
+  PlanInfo info{SGEMM_PLAN_NONE, 0, 0};
+  if (M <= 0 || N <= 0) return info;
+  if (K <= 0) return {SGEMM_PLAN_SCALE, 1, 0};
+  const Decomp d = decompose(M, N, K);
+  switch (d.plan) {
+    case Plan::kFewRows: return {SGEMM_PLAN_FEW_ROWS, 1, 0};
+    case Plan::kFewCols: return {SGEMM_PLAN_FEW_COLS, 1, 0};
+    case Plan::kTiles: return {SGEMM_PLAN_TILES, 1, 0};
+    case Plan::kThinPanels: return {SGEMM_PLAN_THIN_PANELS, 1, 0};
+    case Plan::kSplitK:
+      return {SGEMM_PLAN_SPLIT_K, 2,
+              ceil_div(K, d.k_split) * int64_t(M) * int64_t(N) * int64_t(sizeof(float))};
+    case Plan::kTilesWithFringe:
+      return {SGEMM_PLAN_TILES_FRINGE, 1 + (d.Nm < N) + (d.Mm < M), 0};
+  }
+  return info;
+}
+
+namespace {
 
 hipError_t launch10(const Problem& p, hipStream_t s) {
   const Decomp d = decompose(p.M, p.N, p.K);

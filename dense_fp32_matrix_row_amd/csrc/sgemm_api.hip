@@ -223,4 +223,15 @@ int hip_sgemm_launch_shape(int level, int M, int N, int K,
   return 0;
 }
 
+int hip_sgemm_plan(int M, int N, int K, int* plan, int* launches, long long* workspace_bytes) {
+  if (M < 0) return -1;
+  if (N < 0) return -2;
+  if (K < 0) return -3;
+  const PlanInfo info = plan10(M, N, K);
+  if (plan) *plan = info.plan;
+  if (launches) *launches = info.launches;
+  if (workspace_bytes) *workspace_bytes = info.workspace_bytes;
+  return 0;
+}
+
 }  // extern "C"

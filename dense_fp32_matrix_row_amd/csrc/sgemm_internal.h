@@ -216,6 +216,16 @@ hipError_t launch_few_cols(const Problem& p, hipStream_t s);  // needs N <= kThi
 Geometry thin_panels_geometry(int M, int N, int K);
 hipError_t launch_thin_panels(const Problem& p, hipStream_t s);  // needs M <= 16 * 65535
 
+// Level 10's plan for a shape (the SGEMM_PLAN_* ids of sgemm.h), how many
+// kernels a call enqueues and the split-K workspace it takes, decided on
+// the host from M, N, K alone (alpha != 0).
+struct PlanInfo {
+  int plan;
+  int launches;
+  int64_t workspace_bytes;
+};
+PlanInfo plan10(int M, int N, int K);
+
 // The rungs (host-side descriptors).
 const LevelDesc* level0();
 const LevelDesc* level1();

@@ -31,7 +31,12 @@ EXPORTS = (
     "hip_sgemm", "hip_sgemm_level", "hip_sgemm_num_levels", "hip_sgemm_level_name",
     "hip_sgemm_status_string", "hip_sgemm_auto_level", "hip_sgemm_launch_shape",
     "hip_sgemm_tile_split", "hip_sgemm_num_tiles", "hip_sgemm_tile_name", "hip_sgemm_ex",
+    "hip_sgemm_plan",
 )
+
+# Plan ids of hip_sgemm_plan (SGEMM_PLAN_* in sgemm.h).
+PLAN_NAMES = {0: "none", 1: "scale", 2: "few_rows", 3: "few_cols", 4: "tiles",
+              5: "tiles_fringe", 6: "split_k", 7: "thin_panels"}
 
 _lib = None
 
@@ -81,6 +86,9 @@ def load(path: Optional[str] = None):
                                            ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(i32),
                                            ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(i32),
                                            ctypes.POINTER(i32)]
+    lib.hip_sgemm_plan.restype = i32
+    lib.hip_sgemm_plan.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                   ctypes.POINTER(ctypes.c_longlong)]
     del fptr
     if path == LIBRARY:
         _lib = lib
@@ -190,6 +198,18 @@ def hip_sgemm_launch_shape(level, M, N, K) -> dict:
         raise SgemmError(rc, hip_sgemm_status_string(rc))
     return {"workgroups": wg.value, "threads": thr.value, "k_steps": kst.value,
             "tile_m": tm.value, "tile_n": tn.value}
+
+
+def hip_sgemm_plan(M, N, K) -> dict:
+    """The plan hip_sgemm takes for a shape: plan id and name, kernels per
+    call, split-K workspace bytes (nothing is launched)."""
+    plan, launches, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_longlong()
+    rc = load().hip_sgemm_plan(int(M), int(N), int(K), ctypes.byref(plan), ctypes.byref(launches),
+                               ctypes.byref(ws))
+    if rc != 0:
+        raise SgemmError(rc, hip_sgemm_status_string(rc))
+    return {"plan": plan.value, "name": PLAN_NAMES[plan.value], "launches": launches.value,
+            "workspace_bytes": ws.value}
 
 
 def check(status: int) -> None:

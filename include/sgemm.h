@@ -27,8 +27,9 @@
  *   The caller owns every buffer; A, B and C are device pointers (HBM of the
  *   current HIP device).  The only memory the library takes is split K's
  *   workspace (level 10 splits K for deep problems with few output tiles;
- *   see hip_sgemm_tile_split for where it comes from); it keeps no other
- *   state and needs no handle; calls on different streams may run
+ *   hip_sgemm_plan tells beforehand whether a shape does and how many bytes
+ *   it takes; hip_sgemm_tile_split says where they come from); it keeps no
+ *   other state and needs no handle; calls on different streams may run
  *   concurrently.  C must not overlap A or B (undefined, unchecked, as in
  *   BLAS).
  *
@@ -222,6 +223,34 @@ int hip_sgemm_auto_level(int M, int N, int K,
 int hip_sgemm_launch_shape(int level, int M, int N, int K,
                            long long *workgroups, int *threads_per_group,
                            long long *k_steps, int *tile_m, int *tile_n);
+
+/*
+ * The plan hip_sgemm and hip_sgemm_ex take for a shape (with alpha != 0;
+ * alpha == 0 is the SCALE plan whatever K), decided on the host from M, N, K
+ * alone, without launching anything:
+ *   *plan             one of the SGEMM_PLAN_* ids below;
+ *   *launches         kernels one call enqueues on its stream;
+ *   *workspace_bytes  device memory the call takes for split K's partial
+ *                     sums (splits x M x N floats; 0 for every other plan):
+ *                     the only plan that allocates.  hip_sgemm and
+ *                     hip_sgemm_ex take it from the library's stream-ordered
+ *                     pool (see hip_sgemm_tile_split).
+ * [GEMM2] (size-sweep section) describes a library as many kernels chosen by
+ * problem size, split K among them; this reports which one a shape gets.
+ * Any output pointer may be NULL.  Returns 0, or -1 / -2 / -3 for a negative
+ * M / N / K.
+ */
+#define SGEMM_PLAN_NONE 0         /* M == 0 or N == 0: nothing is launched */
+#define SGEMM_PLAN_SCALE 1        /* K == 0 (or alpha == 0): C <- beta*C */
+#define SGEMM_PLAN_FEW_ROWS 2     /* M <= 16: thin kernel over rows of C */
+#define SGEMM_PLAN_FEW_COLS 3     /* N <= 16: thin kernel over columns of C */
+#define SGEMM_PLAN_TILES 4        /* one grid of matrix-core tiles */
+#define SGEMM_PLAN_TILES_FRINGE 5 /* whole tiles + thin kernels on <= 16-wide fringes */
+#define SGEMM_PLAN_SPLIT_K 6      /* tiles over K slices + an in-order reduction */
+#define SGEMM_PLAN_THIN_PANELS 7  /* small problems: 16-row panels of C */
+
+int hip_sgemm_plan(int M, int N, int K, int *plan, int *launches,
+                   long long *workspace_bytes);
 
 #ifdef __cplusplus
 }

@@ -235,3 +235,46 @@ def test_ex_argument_checks(ops, args, status):
     assert sgemm.hip_sgemm_ex(*ops, *args, stream=0) == status
     if status < -100:
         assert "op(" in sgemm.hip_sgemm_status_string(status)
+
+
+def test_plan_query_names_every_plan_and_its_workspace():
+    """hip_sgemm_plan says, before any call, which plan a shape takes, how
+    many kernels it enqueues, and the split-K workspace (the only memory a
+    call takes): S x M x N floats, S = ceil(K / slice)."""
+    P = sgemm.hip_sgemm_plan
+    assert P(0, 5, 5) == {"plan": 0, "name": "none", "launches": 0, "workspace_bytes": 0}
+    assert P(5, 5, 0)["name"] == "scale"
+    assert P(16, 4096, 4096)["name"] == "few_rows"
+    assert P(4096, 3, 4097)["name"] == "few_cols"
+    assert P(4096, 4096, 4096) == {"plan": 4, "name": "tiles", "launches": 1, "workspace_bytes": 0}
+    assert P(4097, 4097, 4097) == {"plan": 5, "name": "tiles_fringe", "launches": 3,
+                                   "workspace_bytes": 0}
+    assert P(4096, 4097, 64)["launches"] == 2 and P(4097, 4096, 64)["launches"] == 2
+    assert P(256, 256, 256)["name"] == "thin_panels"
+    # split K: 512 x 512 x 8192 (64 tiles of 64 x 64) in 8 slices of 1024
+    sk = P(512, 512, 8192)
+    assert sk["name"] == "split_k" and sk["launches"] == 2
+    assert sk["workspace_bytes"] == 8 * 512 * 512 * 4
+    # 700 x 600 x 8200: 110 tiles -> 4 slices of 2112 (a multiple of 64) -> 4 planes
+    sk = P(700, 600, 8200)
+    assert sk["name"] == "split_k" and sk["workspace_bytes"] == 4 * 700 * 600 * 4
+    for M, N, K in [(4096, 4096, 4096), (1024, 1024, 1024), (100, 100, 100), (4097, 4097, 4097)]:
+        assert P(M, N, K)["workspace_bytes"] == 0
+    for bad, status in [((-1, 1, 1), -1), ((1, -1, 1), -2), ((1, 1, -1), -3)]:
+        with pytest.raises(sgemm.SgemmError) as e:
+            P(*bad)
+        assert e.value.status == status
+
+
+def test_split_k_workspace_bound_over_shapes():
+    """Over a sweep of shapes, the split-K plan's workspace never exceeds
+    512 tiles' worth of 64 x 64 planes (at most two work items per CU over
+    256 CUs): 2^21 floats, 8 MiB."""
+    worst = 0
+    for M in range(64, 1100, 61):
+        for N in range(64, 1100, 67):
+            for K in (2048, 3000, 4096, 8192, 20000, 65536):
+                info = sgemm.hip_sgemm_plan(M, N, K)
+                if info["name"] == "split_k":
+                    worst = max(worst, info["workspace_bytes"])
+    assert 0 < worst <= 8 * 2 ** 20
