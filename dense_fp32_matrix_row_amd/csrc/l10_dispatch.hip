@@ -164,15 +164,13 @@ PlanInfo plan10(int M, int N, int K) {
   return info;
 }
 
-namespace {
-
-hipError_t launch10(const Problem& p, hipStream_t s) {
+hipError_t launch10_with(const Problem& p, hipStream_t s, Workspace w) {
   const Decomp d = decompose(p.M, p.N, p.K);
   switch (d.plan) {
     case Plan::kFewRows: return launch_few_rows(p, s);
     case Plan::kFewCols: return launch_few_cols(p, s);
     case Plan::kTiles: return launch_tiles(d.shape, p, s);
-    case Plan::kSplitK: return launch_splitk(d.shape, d.k_split, p, s);
+    case Plan::kSplitK: return launch_splitk(d.shape, d.k_split, p, s, w);
     case Plan::kThinPanels: return launch_thin_panels(p, s);
     case Plan::kTilesWithFringe: break;
   }
@@ -200,6 +198,10 @@ hipError_t launch10(const Problem& p, hipStream_t s) {
   }
   return e;
 }
+
+namespace {
+
+hipError_t launch10(const Problem& p, hipStream_t s) { return launch10_with(p, s, Workspace::kPool); }
 
 }  // namespace
 

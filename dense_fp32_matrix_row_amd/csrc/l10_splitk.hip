@@ -25,8 +25,19 @@
 // configured during a capture): the workspace is then a stream-ordered
 // allocation from the device's default pool, which the capture records as
 // a graph memory node.
+//
+// The no-allocation entry point (hip_sgemm_ex_noalloc) takes the workspace
+// from `scratch` instead: a fixed array in each device's memory, loaded
+// with the library's code object and kept until the process ends.  Host
+// code reaches it only through the address hipGetSymbolAddress gives for
+// the current device (looked up once per device); the array's name itself
+// is a host-side stand-in, not a device address.  Every element a call
+// reads back from its planes it has written first, so nothing needs
+// clearing between calls; calls that overlap on one device share the
+// array and race.
 #include <mutex>
 
+#include "sgemm.h"
 #include "sgemm_internal.h"
 
 namespace sgemm {
@@ -35,6 +46,28 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_pool_mutex;
 hipMemPool_t g_pools[kMaxDevices];
+
+constexpr int64_t kScratchFloats = SGEMM_NOALLOC_WORKSPACE_BYTES / int64_t(sizeof(float));
+static __device__ __align__(256) float scratch[kScratchFloats];
+std::mutex g_scratch_mutex;
+float* g_scratch[kMaxDevices];  // scratch's device address, per device
+
+hipError_t scratch_for_current_device(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
 
 hipError_t pool_for_current_device(hipMemPool_t* out) {
   int dev = 0;
@@ -100,9 +133,22 @@ hipError_t launch_reduce(const float* ws, int64_t splits, const Problem& p, hipS
 
 }  // namespace
 
-hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStream_t s) {
+int64_t static_workspace_bytes() { return SGEMM_NOALLOC_WORKSPACE_BYTES; }
+
+hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStream_t s,
+                         Workspace w) {
   const int64_t splits = ceil_div(p.K, k_split);
   const size_t bytes = size_t(splits) * size_t(p.M) * size_t(p.N) * sizeof(float);
+  if (w == Workspace::kStatic) {
+    // the fixed array: no allocation, no release
+    if (bytes > size_t(SGEMM_NOALLOC_WORKSPACE_BYTES)) return hipErrorInvalidValue;
+    float* ws = nullptr;
+    hipError_t e = scratch_for_current_device(&ws);
+    if (e != hipSuccess) return e;
+    e = launch_tiles_split(shape, p, k_split, ws, s);
+    if (e == hipSuccess) e = launch_reduce(ws, splits, p, s);
+    return e;
+  }
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   hipError_t e = hipStreamIsCapturing(s, &capture);
   if (e != hipSuccess) return e;

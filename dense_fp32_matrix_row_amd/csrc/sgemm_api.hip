@@ -163,6 +163,24 @@ int hip_sgemm_ex(int op_a, int op_b, int M, int N, int K, float alpha, const flo
   return status_of(level_desc(10)->launch(p, stream));
 }
 
+int hip_sgemm_ex_noalloc(int op_a, int op_b, int M, int N, int K, float alpha, const float* A,
+                         int lda, const float* B, int ldb, float beta, float* C, int ldc,
+                         hipStream_t stream) {
+  const int ta = parse_op(op_a), tb = parse_op(op_b);
+  if (ta < 0) return SGEMM_STATUS_BAD_OP_A;
+  if (tb < 0) return SGEMM_STATUS_BAD_OP_B;
+  const int bad = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc, ta, tb);
+  if (bad) return bad;
+  if (M == 0 || N == 0) return 0;
+  Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+  p.trans_a = ta != 0;
+  p.trans_b = tb != 0;
+  if (K == 0 || alpha == 0.0f) return status_of(launch_scale(p, stream));
+  if (plan10(M, N, K).workspace_bytes > static_workspace_bytes())
+    return SGEMM_STATUS_WORKSPACE_LIMIT;
+  return status_of(launch10_with(p, stream, Workspace::kStatic));
+}
+
 const char* hip_sgemm_tile_name(int tile) {
   if (tile < 0 || tile >= kNumTiles) return nullptr;
   static const char* const names[kNumTiles] = {"256x128x16_8w", "128x128x32_4w", "128x64x16_4w",
@@ -194,6 +212,8 @@ const char* hip_sgemm_status_string(int status) {
     case SGEMM_STATUS_UNKNOWN_CONFIG: return "unknown tile shape or split count";
     case SGEMM_STATUS_BAD_OP_A: return "op(A) is not 'N' or 'T'";
     case SGEMM_STATUS_BAD_OP_B: return "op(B) is not 'N' or 'T'";
+    case SGEMM_STATUS_WORKSPACE_LIMIT:
+      return "split K needs more workspace than the fixed array of hip_sgemm_ex_noalloc";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

@@ -194,9 +194,18 @@ hipError_t launch_mfma_split_nt(Shape shape, const Problem& p, int64_t k_split, 
                                 hipStream_t s);
 hipError_t launch_mfma_split_tt(Shape shape, const Problem& p, int64_t k_split, float* ws,
                                 hipStream_t s);
-// The whole split-K call: workspace from the library's stream-ordered pool,
-// the split tile kernel, the in-order reduction with the alpha/beta epilogue.
-hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStream_t s);
+// Where split K's workspace comes from: the library's stream-ordered pool
+// (every entry point but one), or the library's fixed device array
+// (hip_sgemm_ex_noalloc, for callers that cannot allocate).
+enum class Workspace { kPool, kStatic };
+// The whole split-K call: the workspace, the split tile kernel, the
+// in-order reduction with the alpha/beta epilogue.  With kStatic, S x M x N
+// floats beyond the fixed array's size fail with hipErrorInvalidValue
+// before anything is enqueued (the entry point checks it first).
+hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStream_t s,
+                         Workspace w = Workspace::kPool);
+// Bytes of the fixed array (SGEMM_NOALLOC_WORKSPACE_BYTES).
+int64_t static_workspace_bytes();
 // k_split for a requested slice count: ceil(K / splits) rounded up to BK.
 inline int64_t k_split_for(int64_t K, int64_t splits, int bk) {
   const int64_t per = (K + splits - 1) / splits;
@@ -225,6 +234,8 @@ struct PlanInfo {
   int64_t workspace_bytes;
 };
 PlanInfo plan10(int M, int N, int K);
+// Level 10's launch with split K's workspace from the given source.
+hipError_t launch10_with(const Problem& p, hipStream_t s, Workspace w);
 
 // The rungs (host-side descriptors).
 const LevelDesc* level0();

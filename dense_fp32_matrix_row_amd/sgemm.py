@@ -25,13 +25,15 @@ STATUS_UNKNOWN_LEVEL = -100
 STATUS_UNKNOWN_CONFIG = -101
 STATUS_BAD_OP_A = -102
 STATUS_BAD_OP_B = -103
+STATUS_WORKSPACE_LIMIT = -104
+NOALLOC_WORKSPACE_BYTES = 8 << 20  # SGEMM_NOALLOC_WORKSPACE_BYTES
 
 # Every exported symbol of include/sgemm.h.
 EXPORTS = (
     "hip_sgemm", "hip_sgemm_level", "hip_sgemm_num_levels", "hip_sgemm_level_name",
     "hip_sgemm_status_string", "hip_sgemm_auto_level", "hip_sgemm_launch_shape",
     "hip_sgemm_tile_split", "hip_sgemm_num_tiles", "hip_sgemm_tile_name", "hip_sgemm_ex",
-    "hip_sgemm_plan",
+    "hip_sgemm_plan", "hip_sgemm_ex_noalloc",
 )
 
 # Plan ids of hip_sgemm_plan (SGEMM_PLAN_* in sgemm.h).
@@ -67,6 +69,8 @@ def load(path: Optional[str] = None):
     lib.hip_sgemm_level.argtypes = [i32] + gemm_args
     lib.hip_sgemm_ex.restype = i32
     lib.hip_sgemm_ex.argtypes = [i32, i32] + gemm_args
+    lib.hip_sgemm_ex_noalloc.restype = i32
+    lib.hip_sgemm_ex_noalloc.argtypes = [i32, i32] + gemm_args
     lib.hip_sgemm_tile_split.restype = i32
     lib.hip_sgemm_tile_split.argtypes = [i32, i32] + gemm_args
     lib.hip_sgemm_num_tiles.restype = i32
@@ -150,6 +154,15 @@ def hip_sgemm_ex(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, strea
     return int(load().hip_sgemm_ex(_op(op_a), _op(op_b), int(M), int(N), int(K), float(alpha),
                                    _addr(A), int(lda), _addr(B), int(ldb), float(beta), _addr(C),
                                    int(ldc), _stream(stream)))
+
+
+def hip_sgemm_ex_noalloc(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         stream=None) -> int:
+    """hip_sgemm_ex with split K's workspace in the library's fixed device
+    array: no allocation; overlapping calls on one GPU race."""
+    return int(load().hip_sgemm_ex_noalloc(_op(op_a), _op(op_b), int(M), int(N), int(K),
+                                           float(alpha), _addr(A), int(lda), _addr(B), int(ldb),
+                                           float(beta), _addr(C), int(ldc), _stream(stream)))
 
 
 def hip_sgemm_tile_split(tile, splits, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

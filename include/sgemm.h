@@ -65,6 +65,8 @@
  *   -100          unknown level
  *   -101          unknown tile shape or split count (hip_sgemm_tile_split)
  *   -102, -103    op(A), op(B) not 'N' / 'T' (hip_sgemm_ex)
+ *   -104          split K would need more than the fixed workspace of
+ *                 hip_sgemm_ex_noalloc
  *   > 0           the hipError_t the launch reported
  */
 #ifndef LIBSGEMM_SGEMM_H
@@ -80,6 +82,7 @@ extern "C" {
 #define SGEMM_STATUS_UNKNOWN_CONFIG (-101)
 #define SGEMM_STATUS_BAD_OP_A (-102)
 #define SGEMM_STATUS_BAD_OP_B (-103)
+#define SGEMM_STATUS_WORKSPACE_LIMIT (-104)
 
 /*
  * Best kernel for the shape: C <- alpha*A*B + beta*C.
@@ -114,6 +117,31 @@ int hip_sgemm_ex(int op_a, int op_b, int M, int N, int K, float alpha,
                  const float *B, int ldb,
                  float beta, float *C, int ldc,
                  hipStream_t stream);
+
+/*
+ * hip_sgemm_ex without any device memory allocation, for the callers that
+ * cannot allocate: code being captured into a HIP graph, serving loops that
+ * must not call hipMalloc, harnesses that forbid allocation.  Same
+ * arguments, status codes, plans and kernels as hip_sgemm_ex, and the same
+ * results bit for bit.  The one plan that needs workspace, split K, takes
+ * its S x M x N floats of partial sums from a fixed array in device memory
+ * that the library holds on each GPU it runs on until the process ends
+ * (SGEMM_NOALLOC_WORKSPACE_BYTES; every split-K plan the library chooses
+ * fits it, and hip_sgemm_plan gives a shape's bytes); a call that would
+ * need more returns -104 with nothing enqueued.  The first call on a device
+ * looks the array's address up; no call allocates or frees.
+ * The array is shared by every call on one GPU and keeps the last call's
+ * contents (a call reads back only what it has written): calls that overlap
+ * in time on one GPU (other streams, other host threads) race on it, and
+ * their results are undefined.  Serialise them.
+ */
+#define SGEMM_NOALLOC_WORKSPACE_BYTES (8LL << 20)
+
+int hip_sgemm_ex_noalloc(int op_a, int op_b, int M, int N, int K, float alpha,
+                         const float *A, int lda,
+                         const float *B, int ldb,
+                         float beta, float *C, int ldc,
+                         hipStream_t stream);
 
 /*
  * Same operation with the rung of the optimisation ladder forced.  Every

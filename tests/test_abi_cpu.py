@@ -278,3 +278,17 @@ def test_split_k_workspace_bound_over_shapes():
                 if info["name"] == "split_k":
                     worst = max(worst, info["workspace_bytes"])
     assert 0 < worst <= 8 * 2 ** 20
+
+
+def test_noalloc_argument_checks():
+    """hip_sgemm_ex_noalloc validates like hip_sgemm_ex before touching the
+    device: bad ops, BLAS argument positions, M == 0 quick return."""
+    args = (4, 4, 8, 1.0, FAKE, 7, FAKE, 4, 0.0, FAKE, 4)
+    assert sgemm.hip_sgemm_ex_noalloc("N", "N", *args, stream=0) == -6
+    assert sgemm.hip_sgemm_ex_noalloc("Q", "N", *args, stream=0) == sgemm.STATUS_BAD_OP_A
+    assert sgemm.hip_sgemm_ex_noalloc("N", 7, *args, stream=0) == sgemm.STATUS_BAD_OP_B
+    assert sgemm.hip_sgemm_ex_noalloc("T", "N", 9, 4, 8, 1.0, FAKE, 8, FAKE, 4, 0.0, FAKE, 4,
+                                      stream=0) == -6
+    assert sgemm.hip_sgemm_ex_noalloc("N", "N", 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4,
+                                      stream=0) == 0
+    assert "fixed" in sgemm.hip_sgemm_status_string(sgemm.STATUS_WORKSPACE_LIMIT)
