@@ -1,8 +1,9 @@
 """Level 10 (shape-aware dispatch) on every plan it has: a whole-tile grid
-plus one- to sixteen-wide fringes (both tile shapes), a ragged K under whole
-M/N tiles, the two-K-slice tiles, split K for a deep K over a small grid, and
-thin problems (M <= 16 or N <= 16) on the vector-ALU kernels.  The plan each
-shape takes is pinned on the CPU by the launch-shape test of the ABI suite.
+plus one- to sixteen-wide fringes (both large loop tiles), a ragged K under
+whole M/N tiles, the 64 x 64 loop tiles with edges, split K for a deep K
+over a small grid (whole and edge tiles, ragged K), 16-row panels for small
+problems, and thin problems (M <= 16 or N <= 16).  Each case first asserts
+the plan hip_sgemm_plan names for its shape.
 Every case is compared in full with the CPU reference
 through the C ABI, with guard regions around C (nothing outside the window
 may change); integer-valued data must match bit for bit, and repeated calls
@@ -33,28 +34,33 @@ def _device():
     sgemm.load()
 
 
+# (M, N, K, plan hip_sgemm_plan names, what): the plan is asserted before
+# the call, so every case runs the plan its label says
 SHAPES = [
-    (2051, 2055, 300, "128x128 two-slice grid + 3-row / 7-column fringe"),
-    (4096 + 3, 4096 + 16, 40, "256x128 grid + 3-row / 16-column fringe"),
-    (4096, 4096, 36, "256x128 grid, K ragged (36 = 2*16 + 4)"),
-    (2048, 2048, 100, "128x128 two-slice grid, K ragged (100 = 3*32 + 4)"),
-    (2048, 4096, 80, "128x128 grid, 512 tiles"),
-    (1000, 1000, 300, "64x64 two-slice tiles, ragged edges"),
-    (1024, 1024, 4096, "split K: 128x128 tiles, 8 slices"),
-    (300, 260, 5000, "split K: 64x64 edge tiles, 16 slices, ragged K"),
-    (1, 3001, 5003, "one row (matrix-vector)"),
-    (5, 3001, 5003, "five rows"),
-    (16, 1000, 777, "sixteen rows"),
-    (1500, 1, 5003, "one column"),
-    (1500, 7, 5003, "seven columns"),
-    (300, 16, 2049, "sixteen columns"),
-    (17, 17, 4097, "smallest non-thin shape (level 9 tiles)"),
+    (2051, 2055, 300, "tiles_fringe", "128x128 loop grid + 3-row / 7-column fringe"),
+    (4096 + 3, 4096 + 16, 40, "tiles_fringe", "256x128 loop grid + 3-row / 16-column fringe"),
+    (4096, 4096, 36, "tiles", "256x128 loop grid, K ragged (36 = 2*16 + 4)"),
+    (2048, 2048, 100, "tiles", "128x128 loop grid, K ragged (100 = 6*16 + 4)"),
+    (2048, 4096, 80, "tiles", "128x128 loop grid, 512 tiles"),
+    (1000, 1000, 300, "tiles", "64x64 loop tiles, ragged edges"),
+    (1024, 1024, 4096, "tiles", "64x64 loop tiles, deep K, unsplit"),
+    (512, 512, 8192, "split_k", "split K: 64x64 loop tiles, 8 slices"),
+    (700, 600, 8200, "split_k", "split K: 64x64 edge tiles, 4 slices, ragged K"),
+    (300, 260, 5000, "thin_panels", "16-row panels, deep K"),
+    (1, 3001, 5003, "few_rows", "one row (matrix-vector)"),
+    (5, 3001, 5003, "few_rows", "five rows"),
+    (16, 1000, 777, "few_rows", "sixteen rows"),
+    (1500, 1, 5003, "few_cols", "one column"),
+    (1500, 7, 5003, "few_cols", "seven columns"),
+    (300, 16, 2049, "few_cols", "sixteen columns"),
+    (17, 17, 4097, "thin_panels", "smallest non-thin shape"),
 ]
 
 
-@pytest.mark.parametrize("M,N,K,what", SHAPES, ids=[s[3] for s in SHAPES])
-def test_dispatch_plans_match_reference(M, N, K, what):
+@pytest.mark.parametrize("M,N,K,plan,what", SHAPES, ids=[s[4] for s in SHAPES])
+def test_dispatch_plans_match_reference(M, N, K, plan, what):
     print(f"[dispatch] {M}x{N}x{K}: {what}", flush=True)
+    assert sgemm.hip_sgemm_plan(M, N, K)["name"] == plan
     A, B, C = inputs.make_abc(M, N, K, 7000 + M + N + K)
     for alpha, beta in [(0.5, 3.0), (1.0, 0.0)]:
         out, st = gh.run(gh.Case(M, N, K, alpha, beta, A, B, C), LEVEL)
@@ -79,7 +85,7 @@ def test_dispatch_padded_and_misaligned(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(2051, 2055, 300), (7, 2000, 3001), (2000, 9, 3001),
                                    (4096 + 1, 4096 + 1, 33), (1024, 1024, 4096),
-                                   (512, 512, 8192)])
+                                   (512, 512, 8192), (700, 600, 8200)])
 def test_dispatch_integer_exact(M, N, K):
     """Integer entries in [-8, 8]: every partial sum is an integer far below
     2^24, so any summation order is exact and the result must equal the
@@ -93,7 +99,7 @@ def test_dispatch_integer_exact(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(4097, 4097, 97), (1, 4097, 4097), (4097, 2, 4097),
-                                   (1024, 1024, 4096), (1000, 1000, 300)])
+                                   (1024, 1024, 4096), (1000, 1000, 300), (512, 512, 8192)])
 def test_dispatch_deterministic(M, N, K):
     print(f"[dispatch determinism] {M}x{N}x{K}", flush=True)
     A, B, C = inputs.make_abc(M, N, K, 9100 + K)

@@ -63,9 +63,11 @@ SHAPES = [
     (16, 16384, 777, "sixteen rows, two columns per lane", "all"),
     (2048, 2048, 100, "128x128 grid, K ragged", "all"),
     (4096, 4096, 36, "256x128 grid, K ragged", "all"),
-    (1000, 1000, 300, "64x64 two-slice tiles, edges", "all"),
-    (1024, 1024, 4096, "split K, 128x128", "all"),
-    (300, 260, 5000, "split K, 64x64 edges", "all"),
+    (1000, 1000, 300, "64x64 loop tiles, edges", "all"),
+    (1024, 1024, 4096, "64x64 loop tiles, deep K", "all"),
+    (512, 512, 8192, "split K, 64x64 loop tiles, 8 slices", "all"),
+    (700, 600, 8200, "split K, 64x64 edge tiles, ragged K", "all"),
+    (300, 260, 5000, "16-row panels, deep K", "all"),
     (17, 33, 65, "odd", "all"),
     (129, 65, 31, "odd", "all"),
 ]
