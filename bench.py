@@ -3,21 +3,26 @@
 
 Default: the 4096^3 workload (alpha = 0.5, beta = 3, i.i.d. uniform[-1, 1]
 inputs from seed 1003) through hip_sgemm (the library's own kernel choice),
-W untimed warm-up calls, then exactly K timed calls, each on its own freshly
+W untimed warm-up calls (continued until at least 300 ms of back-to-back
+calls, so the clocks have left their ramp from idle; the calls and
+milliseconds spent are reported), then exactly K timed calls, each on its own freshly
 filled copy of C (so every step computes C <- 0.5*A@B + 3*C from the same
 pristine inputs, and no restore copy sits inside the timed region).  Inputs
 are resident in HBM before timing starts.
 
-Prints one JSON line: TFLOPS over the timed region (2*M*N*K per step), the
-dominant kernel's roofline (its mean duration from HIP events recorded around
-each launch on the launch stream, against the 157.3 TFLOP/s FP32 matrix
-peak), and the CPU reference timed on the host on a bounded sample of the
-same problem (its first rows), whose output also checks the GPU's rows.
+Prints one JSON line: TFLOPS over the timed region (2*M*N*K per step, host
+clock), the dominant kernel's roofline (its mean duration from HIP events
+recorded around each launch on the launch stream, against the 157.3 TFLOP/s
+FP32 matrix peak; median and min reported beside it), and the CPU reference
+timed on the host on a bounded sample of the same problem (its first rows),
+whose output also checks the GPU's rows.
 
 Options: --level L forces a ladder rung (hip_sgemm_level); --workload picks
 another of the five problem sizes; --ladder PATH times every level on every
-workload and writes one JSON line per pair to PATH (the headline line is
-still printed last); --no-cpu skips the CPU leg.
+workload (median of the per-launch event times), the vendor BLAS beside them
+and the CPU reference on each whole problem (all host cores; also one thread
+for 256^3 and 1024^3), and writes one JSON line per record to PATH (the
+headline line is still printed last); --no-cpu skips the CPU legs.
 """
 
 from __future__ import annotations
@@ -39,6 +44,11 @@ METRIC = "SGEMM TFLOPS at M=N=K=4096 (fraction of FP32 peak) on one MI355X"
 # VOP3 v_fma_f32 form issues at half that rate).
 PEAK_FP32_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
+# Every timed region is preceded by at least this much back-to-back work
+# (and at least the requested warm-up calls): from idle, MI355X's clocks
+# take ~30 calls of the 4096^3 problem (~30 ms) to reach steady state, and
+# calls timed inside that ramp run up to 15 % slow.
+WARM_MS = 300.0
 
 
 def parse():
@@ -48,6 +58,10 @@ def parse():
     # up from idle; 50 warm-up calls reach the steady state.
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS,
+                    help="minimum milliseconds of back-to-back warm-up calls before each timed "
+                         "region (default %(default)s; 0 = exactly --warmup calls, as for "
+                         "hardware-counter passes that serialise every dispatch)")
     ap.add_argument("--level", type=int, default=None)
     ap.add_argument("--workload", default="sgemm_4096")
     ap.add_argument("--ladder", default=None, metavar="PATH")
@@ -118,7 +132,8 @@ class Problem:
 def warm_until(call, n: int, min_ms: float):
     """n calls, then more until at least min_ms of back-to-back calls (host
     clock, checked every 10 calls): the clocks ramp up from idle over tens
-    of milliseconds, which a few calls of a short kernel do not cover."""
+    of milliseconds, which a few calls of a short kernel do not cover.
+    Returns (calls made, milliseconds spent)."""
     import torch
     t0 = time.perf_counter()
     i = 0
@@ -127,12 +142,28 @@ def warm_until(call, n: int, min_ms: float):
         i += 1
         if i % 10 == 0:
             torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i, (time.perf_counter() - t0) * 1e3
 
 
-def run_timed(prob: Problem, level, steps: int, warmup: int, min_warm_ms: float = 0.0):
-    """Warm-up and timed calls on the current stream.  Returns (ms_per_step
-    from the host clock over the whole timed region, mean kernel ms from the
-    per-launch HIP events)."""
+class Timing:
+    """One timed region: host-clock ms per step over the whole region, and
+    the per-launch kernel times from the HIP event pairs around each launch
+    (mean, median, min), with the warm-up that preceded it."""
+
+    def __init__(self, ms_per_step, kernel_ms_each, warm_calls, warm_ms):
+        import statistics
+        self.ms_per_step = ms_per_step
+        self.kernel_ms_each = kernel_ms_each
+        self.mean = sum(kernel_ms_each) / len(kernel_ms_each)
+        self.median = statistics.median(kernel_ms_each)
+        self.min = min(kernel_ms_each)
+        self.warm_calls, self.warm_ms = warm_calls, warm_ms
+
+
+def run_timed(prob: Problem, level, steps: int, warmup: int, min_warm_ms: float = 0.0) -> Timing:
+    """Warm-up and timed calls on the current stream (the stream the
+    library launches on, so the events bracket its kernels)."""
     import torch
 
     from dense_fp32_matrix_row_amd import sgemm
@@ -148,7 +179,8 @@ def run_timed(prob: Problem, level, steps: int, warmup: int, min_warm_ms: float 
 
     prob.refill()
     torch.cuda.synchronize()
-    warm_until(lambda i: call(prob.copies[i % len(prob.copies)]), warmup, min_warm_ms)
+    warm_calls, warm_ms = warm_until(lambda i: call(prob.copies[i % len(prob.copies)]), warmup,
+                                     min_warm_ms)
     prob.refill()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -160,8 +192,8 @@ def run_timed(prob: Problem, level, steps: int, warmup: int, min_warm_ms: float 
         ends[i].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
-    return (t1 - t0) * 1e3 / steps, kernel_ms
+    each = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return Timing((t1 - t0) * 1e3 / steps, each, warm_calls, warm_ms)
 
 
 def cpu_baseline(prob: Problem, gpu_out_rows, target_s: float):
@@ -212,18 +244,18 @@ def device_info():
     return info
 
 
-def vendor_timed(prob: Problem, steps: int, warmup: int, min_warm_ms: float = 0.0):
+def vendor_timed(prob: Problem, steps: int, warmup: int, min_warm_ms: float = 0.0) -> Timing:
     """The same call through torch.addmm on FP32 tensors (rocBLAS/hipBLASLt,
     TF32 off): a context figure for the vendor library, never a dependency of
-    libsgemm.  Returns the mean kernel ms from HIP events, like run_timed."""
+    libsgemm.  Timed like run_timed (host clock not used)."""
     import torch
     torch.backends.cuda.matmul.allow_tf32 = False
     w = prob.w
     stream = torch.cuda.current_stream()
     prob.refill()
     torch.cuda.synchronize()
-    warm_until(lambda i: prob.copies[i % len(prob.copies)].addmm_(prob.dA, prob.dB, beta=w.beta,
-                                                                 alpha=w.alpha), warmup, min_warm_ms)
+    wc, wms = warm_until(lambda i: prob.copies[i % len(prob.copies)].addmm_(
+        prob.dA, prob.dB, beta=w.beta, alpha=w.alpha), warmup, min_warm_ms)
     prob.refill()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -233,17 +265,85 @@ def vendor_timed(prob: Problem, steps: int, warmup: int, min_warm_ms: float = 0.
         prob.copies[i].addmm_(prob.dA, prob.dB, beta=w.beta, alpha=w.alpha)
         b.record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / steps
+    return Timing(float("nan"), [a.elapsed_time(b) for a, b in ev], wc, wms)
 
 
 def bench_one(w, level, steps, warmup, prob=None, min_warm_ms=0.0):
     from dense_fp32_matrix_row_amd import sgemm
-    prob = prob or Problem(w, max(steps, warmup, 1))
-    ms, kms = run_timed(prob, level, steps, warmup, min_warm_ms)
+    prob = prob or Problem(w, max(steps, 1))
+    timing = run_timed(prob, level, steps, warmup, min_warm_ms)
     eff_level = level if level is not None else sgemm.hip_sgemm_auto_level(
         w.M, w.N, w.K, prob.dA, w.K, prob.dB, w.N, prob.dC0, w.N)
     name = sgemm.hip_sgemm_level_name(eff_level)
-    return prob, ms, kms, eff_level, name
+    return prob, timing, eff_level, name
+
+
+def ladder(args, steps: int, warmup: int) -> None:
+    """Every level on every workload, the vendor BLAS beside them, and the
+    CPU oracle on each whole problem: its wall clock (all host cores, and
+    one thread for the two smallest workloads) and, against its result,
+    every level's max normalised error over all of C (one more call on a
+    fresh C after the timed ones)."""
+    import torch
+
+    from dense_fp32_matrix_row_amd import inputs, sgemm
+    from oracle import oracle
+    with open(args.ladder, "w") as f:
+        def emit(rec, msg):
+            f.write(json.dumps(rec) + "\n")
+            f.flush()
+            print(f"[ladder] {msg}", flush=True)
+
+        for wl in inputs.WORKLOADS:
+            prob = Problem(wl, max(steps, 1))
+            A, B, C = prob.host
+            ref = None
+            if not args.no_cpu:
+                for threads in ([0, 1] if wl.M <= 1024 else [0]):
+                    t = time.perf_counter()
+                    res = oracle.oracle_sgemm(A, B, C, wl.alpha, wl.beta, threads=threads)
+                    dt = time.perf_counter() - t
+                    ref = ref or res
+                    emit({"workload": wl.name, "level": "oracle", "cores": res.threads,
+                          "seconds": round(dt, 4), "gflops": round(wl.flops / dt / 1e9, 3),
+                          "kind": "oracle (float64 accumulation, whole problem)"},
+                         f"{wl.name} oracle on {res.threads} cores: {dt:.3f} s")
+            for lv in range(sgemm.hip_sgemm_num_levels()):
+                # the two naive rungs take 0.1-0.2 s per call at 4096: fewer calls
+                slow = lv <= 1 and wl.M >= 2048
+                st = min(steps, 3) if slow else min(steps, 20)
+                wu = 1 if slow else min(warmup, 10)
+                # short kernels: at least warm_ms of calls before timing
+                _, tm, _, name = bench_one(wl, lv, st, wu, prob, 0.0 if slow else args.warm_ms)
+                kms = tm.median
+                tf = wl.flops / (kms * 1e-3) / 1e12
+                rec = {"workload": wl.name, "level": lv, "level_name": name, "steps": st,
+                       "warmup_calls": tm.warm_calls, "ms_per_step": round(tm.ms_per_step, 4),
+                       "kernel_ms_median": round(tm.median, 4),
+                       "kernel_ms_mean": round(tm.mean, 4), "kernel_ms_min": round(tm.min, 4),
+                       "tflops": round(tf, 3), "frac_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4),
+                       "algorithmic_gbs": round(wl.algorithmic_bytes / (kms * 1e-3) / 1e9, 1)}
+                if ref is not None:
+                    c = prob.copies[0]
+                    c.copy_(prob.dC0)
+                    sgemm.check(sgemm.hip_sgemm_level(lv, wl.M, wl.N, wl.K, wl.alpha, prob.dA, wl.K,
+                                                      prob.dB, wl.N, wl.beta, c, wl.N, None))
+                    torch.cuda.synchronize()
+                    rec["max_normalised_error"] = oracle.normalised_error(
+                        c.cpu().numpy(), ref, C, wl.alpha, wl.beta, strict=True)
+                emit(rec, f"{wl.name} L{lv} {name}: median {kms:.4f} ms, {rec['tflops']} TFLOPS, "
+                          f"error {rec.get('max_normalised_error')}")
+            vt = vendor_timed(prob, min(steps, 20), min(warmup, 10), args.warm_ms)
+            tf = wl.flops / (vt.median * 1e-3) / 1e12
+            emit({"workload": wl.name, "level": "vendor",
+                  "level_name": "torch.addmm (rocBLAS/hipBLASLt, FP32)",
+                  "kernel_ms_median": round(vt.median, 4), "kernel_ms_mean": round(vt.mean, 4),
+                  "kernel_ms_min": round(vt.min, 4), "tflops": round(tf, 3),
+                  "frac_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4),
+                  "algorithmic_gbs": round(wl.algorithmic_bytes / (vt.median * 1e-3) / 1e9, 1)},
+                 f"{wl.name} vendor: median {vt.median:.4f} ms, {tf:.3f} TFLOPS")
+            del prob, ref
+            torch.cuda.empty_cache()
 
 
 def main():
@@ -275,37 +375,10 @@ def main():
     steps, warmup = max(1, args.steps), max(0, args.warmup)
 
     if args.ladder:
-        with open(args.ladder, "w") as f:
-            for wl in inputs.WORKLOADS:
-                prob = Problem(wl, max(steps, warmup, 1))
-                for lv in range(sgemm.hip_sgemm_num_levels()):
-                    # the two naive rungs take 0.1-0.2 s per call at 4096: fewer calls
-                    slow = lv <= 1 and wl.M >= 2048
-                    st = min(steps, 3) if slow else min(steps, 20)
-                    wu = 1 if slow else min(warmup, 10)
-                    # short kernels: at least 30 ms of calls before timing
-                    _, ms, kms, _, name = bench_one(wl, lv, st, wu, prob, 0.0 if slow else 30.0)
-                    tf = wl.flops / (kms * 1e-3) / 1e12
-                    rec = {"workload": wl.name, "level": lv, "level_name": name, "steps": st,
-                           "warmup": wu, "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
-                           "tflops": round(tf, 3), "frac_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4),
-                           "algorithmic_gbs": round(wl.algorithmic_bytes / (kms * 1e-3) / 1e9, 1)}
-                    f.write(json.dumps(rec) + "\n")
-                    f.flush()
-                    print(f"[ladder] {wl.name} L{lv} {name}: {kms:.4f} ms, {rec['tflops']} TFLOPS",
-                          flush=True)
-                vms = vendor_timed(prob, min(steps, 20), min(warmup, 10), 30.0)
-                tf = wl.flops / (vms * 1e-3) / 1e12
-                f.write(json.dumps({"workload": wl.name, "level": "vendor",
-                                    "level_name": "torch.addmm (rocBLAS/hipBLASLt, FP32)",
-                                    "kernel_ms": round(vms, 4), "tflops": round(tf, 3),
-                                    "frac_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4),
-                                    "algorithmic_gbs": round(wl.algorithmic_bytes / (vms * 1e-3) / 1e9, 1)}) + "\n")
-                print(f"[ladder] {wl.name} vendor: {vms:.4f} ms, {tf:.3f} TFLOPS", flush=True)
-                del prob
-                torch.cuda.empty_cache()
+        ladder(args, steps, warmup)
 
-    prob, ms, kms, lv, name = bench_one(w, args.level, steps, warmup)
+    prob, tm, lv, name = bench_one(w, args.level, steps, warmup, min_warm_ms=args.warm_ms)
+    ms, kms = tm.ms_per_step, tm.mean
     tflops = w.flops / (ms * 1e-3) / 1e12
     achieved = w.flops / (kms * 1e-3) / 1e12
     # levels 9 and 10 run the matrix cores on every bench workload (level
@@ -325,14 +398,18 @@ def main():
         "roofline": roofline,
         "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
         "kernel_ms": round(kms, 4),
+        "kernel_ms_median": round(tm.median, 4), "kernel_ms_min": round(tm.min, 4),
+        "tflops_at_median": round(w.flops / (tm.median * 1e-3) / 1e12, 3),
+        "warmup_calls": tm.warm_calls, "warmup_ms": round(tm.warm_ms, 1),
         "algorithmic_gbs": round(w.algorithmic_bytes / (kms * 1e-3) / 1e9, 1),
         "device": device_info(),
     }
     if args.vendor:
-        vms = vendor_timed(prob, steps, warmup)
+        vt = vendor_timed(prob, steps, warmup, args.warm_ms)
         line["vendor_blas"] = {"library": "torch.addmm (rocBLAS/hipBLASLt), FP32, TF32 off",
-                               "kernel_ms": round(vms, 4),
-                               "tflops": round(w.flops / (vms * 1e-3) / 1e12, 3),
+                               "kernel_ms_mean": round(vt.mean, 4),
+                               "kernel_ms_median": round(vt.median, 4),
+                               "tflops": round(w.flops / (vt.mean * 1e-3) / 1e12, 3),
                                "note": "context only; not part of libsgemm"}
     if not args.no_cpu:
         def rows_out(r):

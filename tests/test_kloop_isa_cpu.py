@@ -16,13 +16,11 @@ import subprocess
 
 import pytest
 
+from dense_fp32_matrix_row_amd import build as lib_build
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "dense_fp32_matrix_row_amd", "csrc")
 HIPCC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-
-# last staging register per block tile (v80 onwards: DEPTH sets of the
-# stage's A and B float4s), as gen_kloop.py lays them out
-LAST_STAGING = {256: 80 + 12 - 1, 128: 80 + 2 * 16 - 1, 64: 80 + 2 * 32 - 1}
 
 
 @pytest.fixture(scope="module")
@@ -30,41 +28,25 @@ def assembly(tmp_path_factory):
     if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
         pytest.skip("hipcc not available")
     out = tmp_path_factory.mktemp("isa") / "l10_kloop.s"
-    cmd = [HIPCC if os.path.exists(HIPCC) else "hipcc", "--offload-arch=gfx950", "-O3",
-           "-std=c++17", "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", f"-I{os.path.join(ROOT, 'include')}", "--cuda-device-only", "-S",
-           os.path.join(CSRC, "l10_kloop.hip"), "-o", str(out)]
+    cmd = [HIPCC if os.path.exists(HIPCC) else "hipcc", *lib_build.HIPCC_FLAGS, "--cuda-device-only",
+           "-S", lib_build.KLOOP_SOURCE, "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True, timeout=600)
     return out.read_text()
 
 
-def _kernels(text):
-    starts = [m.start() for m in re.finditer(r"^_ZN5sgemm\S*k_kloop\S*:", text, re.M)]
-    for i, s in enumerate(starts):
-        body = text[s:starts[i + 1] if i + 1 < len(starts) else len(text)]
-        yield body.split(":", 1)[0], [l.split(";")[0].strip() for l in body.split("\n")]
-
-
-def _registers(ins):
-    regs = [(int(a), int(b)) for a, b in re.findall(r"\bv\[(\d+):(\d+)\]", ins)]
-    return regs + [(int(r), int(r)) for r in re.findall(r"\bv(\d+)\b", ins)]
-
-
 def test_staging_registers_untouched_between_prelude_and_loop(assembly):
-    kernels = list(_kernels(assembly))
-    assert len(kernels) == 24  # 3 tiles x 4 orientations x (plain, split K)
-    for name, lines in kernels:
-        last = LAST_STAGING[int(re.search(r"KTileILi(\d+)", name).group(1))]
-        start = lines.index("s_nop 4")                    # the prelude's first line
-        end = lines.index("s_barrier", start)             # the loop statement's barrier
-        prelude_loads = 0
-        for ins in lines[start:end]:
-            if not ins or ins.startswith((".", "s_")):
-                continue
-            m = re.match(r"buffer_load_dwordx4 v\[(\d+):\d+\], \S+, \S+, \S+ offen$", ins)
-            if m and 80 <= int(m.group(1)) <= last:
-                prelude_loads += 1
-                continue
-            touched = [r for r in _registers(ins) if r[1] >= 80 and r[0] <= last]
-            assert not touched, (name, ins)
-        assert prelude_loads * 4 == last - 80 + 1, name  # every staging register loaded once
+    """The check the build runs before linking passes on the sources."""
+    assert lib_build.check_kloop_staging(assembly) == []
+
+
+def test_check_rejects_a_staging_copy(assembly):
+    """A copy of a staging register placed between the two statements, or a
+    missing prelude load, is reported (planted in the assembly text)."""
+    name, lines = next(lib_build.kloop_kernels(assembly))
+    start = assembly.index("s_nop 4", assembly.index(name + ":"))
+    planted = assembly[:start] + "s_nop 4\n\tv_mov_b32 v3, v81\n" + assembly[start + len("s_nop 4"):]
+    bad = lib_build.check_kloop_staging(planted)
+    assert bad and "staging register" in bad[0][1]
+    load = re.search(r"buffer_load_dwordx4 v\[8[0-9]:\d+\][^\n]*offen\n", assembly[start:])
+    dropped = assembly[:start + load.start()] + assembly[start + load.end():]
+    assert any("prelude loads" in why for _, why in lib_build.check_kloop_staging(dropped))
