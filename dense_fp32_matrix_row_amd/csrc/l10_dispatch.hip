@@ -46,7 +46,10 @@ double round_fill(int64_t tiles) {
 
 // The rules below were fitted to sweeps of every tile shape and slice count
 // on MI355X (dense_fp32_matrix_row_amd.autotune); the comments give the
-// measurements that decided them.
+// measurements that decided them.  The sweep's table of record is checked
+// by tests/test_autotune_cpu.py: every swept shape must still get the plan
+// and tile configuration recorded for it, and that configuration must be
+// within the sweep's tolerance of the fastest one measured.
 Decomp decompose(int M, int N, int K) {
   if (M <= kThin) return {Plan::kFewRows, Shape::kSmall, M, N, K};
   if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, M, N, K};

@@ -131,12 +131,11 @@ hipError_t launch_reduce(const float* ws, int64_t splits, const Problem& p, hipS
   return hipGetLastError();
 }
 
-}  // namespace
-
-int64_t static_workspace_bytes() { return SGEMM_NOALLOC_WORKSPACE_BYTES; }
-
-hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStream_t s,
-                         Workspace w) {
+// Workspace, then launch_split(ws) (the split tile kernel), then the
+// reduction; the workspace from the source w.
+template <class F>
+hipError_t splitk_with(F launch_split, int64_t k_split, const Problem& p, hipStream_t s,
+                       Workspace w) {
   const int64_t splits = ceil_div(p.K, k_split);
   const size_t bytes = size_t(splits) * size_t(p.M) * size_t(p.N) * sizeof(float);
   if (w == Workspace::kStatic) {
@@ -145,7 +144,7 @@ hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStre
     float* ws = nullptr;
     hipError_t e = scratch_for_current_device(&ws);
     if (e != hipSuccess) return e;
-    e = launch_tiles_split(shape, p, k_split, ws, s);
+    e = launch_split(ws);
     if (e == hipSuccess) e = launch_reduce(ws, splits, p, s);
     return e;
   }
@@ -162,10 +161,25 @@ hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStre
     e = hipMallocFromPoolAsync(&ws, bytes, pool, s);
   }
   if (e != hipSuccess) return e;
-  e = launch_tiles_split(shape, p, k_split, static_cast<float*>(ws), s);
+  e = launch_split(static_cast<float*>(ws));
   if (e == hipSuccess) e = launch_reduce(static_cast<const float*>(ws), splits, p, s);
   const hipError_t f = hipFreeAsync(ws, s);
   return e != hipSuccess ? e : f;
+}
+
+}  // namespace
+
+int64_t static_workspace_bytes() { return SGEMM_NOALLOC_WORKSPACE_BYTES; }
+
+hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStream_t s,
+                         Workspace w) {
+  return splitk_with([&](float* ws) { return launch_tiles_split(shape, p, k_split, ws, s); },
+                     k_split, p, s, w);
+}
+
+hipError_t launch_splitk_fn(SplitLaunchFn fn, int64_t k_split, const Problem& p, hipStream_t s) {
+  return splitk_with([&](float* ws) { return fn(p, k_split, ws, s); }, k_split, p, s,
+                     Workspace::kPool);
 }
 
 }  // namespace sgemm

@@ -6,6 +6,7 @@
 // is an argument error).  Everything here runs on the host before any HIP
 // call, so argument errors never enqueue work.
 #include "../../include/sgemm.h"
+#include "l9_catalogue.h"
 #include "sgemm_internal.h"
 
 namespace sgemm {
@@ -70,7 +71,16 @@ int run(const LevelDesc* lv, int M, int N, int K, float alpha, const float* A,
   return status_of(lv->launch(p, stream));
 }
 
+// hip_sgemm_tile_split's tiles: seven named shapes, then the catalogue.
 constexpr int kNumTiles = 7;
+constexpr int kNumTileIds = kNumTiles + SGEMM_CATALOGUE_SIZE;
+
+const CatalogueEntry* catalogue_entry(int i) {
+  int first = 0, second = 0;
+  const CatalogueEntry* a = catalogue_first(&first);
+  const CatalogueEntry* b = catalogue_second(&second);
+  return i < first ? &a[i] : &b[i - first];
+}
 
 Shape tile_shape(int tile) {
   static const Shape shapes[kNumTiles] = {Shape::kHuge,        Shape::kLarge,      Shape::kMid,
@@ -123,19 +133,25 @@ int hip_sgemm_level(int level, int M, int N, int K, float alpha,
 int hip_sgemm_tile_split(int tile, int splits, int M, int N, int K, float alpha,
                         const float* A, int lda, const float* B, int ldb, float beta,
                         float* C, int ldc, hipStream_t stream) {
-  if (tile < 0 || tile >= kNumTiles || splits < 1) return SGEMM_STATUS_UNKNOWN_CONFIG;
+  if (tile < 0 || tile >= kNumTileIds || splits < 1) return SGEMM_STATUS_UNKNOWN_CONFIG;
   const int bad = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc);
   if (bad) return bad;
   if (M == 0 || N == 0) return 0;
   Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
   if (K == 0 || alpha == 0.0f) return status_of(launch_scale(p, stream));
+  if (tile >= kNumTiles) {
+    const CatalogueEntry* c = catalogue_entry(tile - kNumTiles);
+    const int64_t k_split = k_split_for(K, splits, c->bk);
+    if (k_split >= K) return status_of(c->launch(p, stream));
+    return status_of(launch_splitk_fn(c->split, k_split, p, stream));
+  }
   const Shape shape = tile_shape(tile);
   const int64_t k_split = k_split_for(K, splits, shape_bk(shape));
   if (k_split >= K) return status_of(launch_tiles(shape, p, stream));
   return status_of(launch_splitk(shape, k_split, p, stream));
 }
 
-int hip_sgemm_num_tiles(void) { return kNumTiles; }
+int hip_sgemm_num_tiles(void) { return kNumTileIds; }
 
 // 'N' / 'n' / 0: as stored; 'T' / 't' / 'C' / 'c' / 1: transposed (for real
 // data the conjugate transpose is the transpose); -1 otherwise.
@@ -182,7 +198,8 @@ int hip_sgemm_ex_noalloc(int op_a, int op_b, int M, int N, int K, float alpha, c
 }
 
 const char* hip_sgemm_tile_name(int tile) {
-  if (tile < 0 || tile >= kNumTiles) return nullptr;
+  if (tile < 0 || tile >= kNumTileIds) return nullptr;
+  if (tile >= kNumTiles) return catalogue_entry(tile - kNumTiles)->name;
   static const char* const names[kNumTiles] = {"256x128x16_8w", "128x128x32_4w", "128x64x16_4w",
                                                "64x64x16_4w", "128x128x32_8w_2slices",
                                                "64x64x32_8w_2slices", "64x64x64_4w_4slices"};

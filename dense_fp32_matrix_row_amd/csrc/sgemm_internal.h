@@ -206,6 +206,24 @@ hipError_t launch_splitk(Shape shape, int64_t k_split, const Problem& p, hipStre
                          Workspace w = Workspace::kPool);
 // Bytes of the fixed array (SGEMM_NOALLOC_WORKSPACE_BYTES).
 int64_t static_workspace_bytes();
+// The same split-K call with the split tile kernel given as a function
+// (workspace from the pool): the tile catalogue's entries.
+using SplitLaunchFn = hipError_t (*)(const Problem&, int64_t k_split, float* ws, hipStream_t);
+hipError_t launch_splitk_fn(SplitLaunchFn fn, int64_t k_split, const Problem& p, hipStream_t s);
+
+// The tile catalogue (l9_catalogue.h): legal configurations of level 9's
+// tile template for tuning sweeps, row-major operands.  launch runs the
+// tile over the whole problem, split over K slices of k_split (raw sums
+// into ws, as launch_mfma_split).
+struct CatalogueEntry {
+  const char* name;
+  int bk;
+  hipError_t (*launch)(const Problem&, hipStream_t);
+  SplitLaunchFn split;
+};
+// the two halves of the catalogue (entries, with their number in *count)
+const CatalogueEntry* catalogue_first(int* count);
+const CatalogueEntry* catalogue_second(int* count);
 // k_split for a requested slice count: ceil(K / splits) rounded up to BK.
 inline int64_t k_split_for(int64_t K, int64_t splits, int bk) {
   const int64_t per = (K + splits - 1) / splits;

@@ -189,6 +189,12 @@ int hip_sgemm_level(int level, int M, int N, int K, float alpha,
  *           (twice the wavefronts): 128 x 128 (BK 32, 8), 64 x 64 (BK 32, 8);
  *           6: level 10's 64 x 64 assembly-loop tile (BK 64 split over four
  *           wavefronts; where it does not fit, tile 5 stands in);
+ *           7 ..: a catalogue of further legal configurations of level 9's
+ *           tile template (block tile, stage depth, wavefront grid, matrix
+ *           block size, K slices), row-major operands, for sweeps over the
+ *           template's parameter space ([GEMM2] autotuning section: the
+ *           best parameters differ per GPU and are searched);
+ *           hip_sgemm_tile_name gives each one's parameters;
  *   splits  >= 1: the K range is cut into about `splits` slices (each a
  *           multiple of the tile's BK; ceil(K / slice) of them run) that
  *           compute separately, and a second kernel adds the slices' float32
@@ -215,7 +221,8 @@ int hip_sgemm_tile_split(int tile, int splits, int M, int N, int K, float alpha,
                          hipStream_t stream);
 
 /* Number of tile shapes hip_sgemm_tile_split accepts, and their names
- * ("256x128x16_8w", ...; NULL if unknown; static, owned by the library). */
+ * ("256x128x16_8w", ..., "cat_64x64x32_1x1w_m16", ...: block tile x stage
+ * depth first; NULL if unknown; static, owned by the library). */
 int hip_sgemm_num_tiles(void);
 const char *hip_sgemm_tile_name(int tile);
 

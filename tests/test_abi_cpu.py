@@ -204,15 +204,20 @@ def test_regtile8_cells_match_the_six_level_example():
 
 
 def test_tile_split_arguments():
-    assert sgemm.hip_sgemm_num_tiles() == 7
+    assert sgemm.hip_sgemm_num_tiles() == 17
     names = [sgemm.hip_sgemm_tile_name(t) for t in range(4)]
     assert names[0].startswith("256x128") and names[3].startswith("64x64")
-    names = [sgemm.hip_sgemm_tile_name(t) for t in range(7)]
+    names = [sgemm.hip_sgemm_tile_name(t) for t in range(17)]
     assert names[4].startswith("128x128") and names[5].startswith("64x64") and "2slices" in names[5]
     assert names[6].startswith("64x64x64") and "4slices" in names[6]
-    assert sgemm.hip_sgemm_tile_name(7) is None and sgemm.hip_sgemm_tile_name(-1) is None
+    # the catalogue: every name states BM x BN x BK, all distinct
+    assert all(n.startswith("cat_") for n in names[7:]) and len(set(names)) == 17
+    for n in names:
+        bm, bn, bk = (int(v) for v in n.removeprefix("cat_").split("_")[0].split("x"))
+        assert bm % 64 == 0 and bn % 64 == 0 and bk in (16, 32, 64)
+    assert sgemm.hip_sgemm_tile_name(17) is None and sgemm.hip_sgemm_tile_name(-1) is None
     args = (4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4)
-    for tile, splits in [(-1, 1), (7, 1), (0, 0), (1, -3)]:
+    for tile, splits in [(-1, 1), (17, 1), (0, 0), (1, -3), (9, 0)]:
         assert sgemm.hip_sgemm_tile_split(tile, splits, *args, stream=0) == sgemm.STATUS_UNKNOWN_CONFIG
     assert "split" in sgemm.hip_sgemm_status_string(sgemm.STATUS_UNKNOWN_CONFIG)
     # argument errors as hip_sgemm once the configuration is valid

@@ -1,5 +1,6 @@
-"""Split K (hip_sgemm_tile_split) through the C ABI: every tile shape with
-several slice counts on whole and ragged shapes against the CPU reference,
+"""Split K (hip_sgemm_tile_split) through the C ABI: every tile shape (the
+seven named ones and the tile catalogue) with several slice counts on
+whole, ragged-K and edge shapes against the CPU reference,
 integer-valued data bit for bit, repeated calls bit-identical, beta = 0
 never reading C, and nothing outside the C window written."""
 
@@ -15,7 +16,7 @@ from tests import gpu_harness as gh
 pytestmark = pytest.mark.gpu
 
 BOUND = 1e-5
-TILES = range(7)
+TILES = range(17)   # hip_sgemm_num_tiles(): 7 named tiles + a catalogue of 10
 
 
 @pytest.fixture(scope="session", autouse=True)
@@ -32,7 +33,8 @@ def run_split(case: gh.Case, tile: int, splits: int):
     return gh.run(case, lambda *args: sgemm.hip_sgemm_tile_split(tile, splits, *args))
 
 
-SHAPES = [(256, 256, 1024), (300, 260, 1000), (129, 65, 777), (1024, 1024, 1024)]
+# whole tiles for every tile shape; whole M / N with a ragged K; edge tiles
+SHAPES = [(256, 256, 1024), (512, 256, 1000), (300, 260, 1000), (129, 65, 777), (1024, 1024, 1024)]
 
 
 @pytest.mark.parametrize("tile", TILES)
