@@ -1,35 +1,40 @@
 // l78_pipeline.hip -- levels 7 and 8: the level-6 kernel on a double-buffered
-// LDS pipeline (level 7), then with wave tiling and an XCD-aware block order
-// (level 8).
+// LDS pipeline (level 7), then with wave tiling (level 8).
 //
 // Level 7 follows [CP04] double_buffer_gemm ("双缓冲流水线"): two LDS
 // buffers alternate per K step; the global loads of step k+1 are issued into
 // registers before the FMAs of step k, and stored into the other buffer
 // after them, so the HBM/L2 latency overlaps the arithmetic and one barrier
 // per step suffices: a buffer is rewritten only after the barrier that ends
-// every wavefront's reads of it.  BK = 8 and the k loop unrolled by 4 keep
-// the kernel at 118 VGPRs, four wavefronts per SIMD like level 6 (BK = 16
-// needed 140, three per SIMD, and ran 3.5 % slower at 4096^3).  On MI355X the
-// double buffer gains little over level 6: four resident blocks per CU
-// already overlap one block's loads with the others' FMAs, which is what the
-// double buffer buys a single block.  A is staged transposed with rows padded
-// to 132 words.
+// every wavefront's reads of it.  BK = 8 with the two buffers unrolled so
+// every LDS address is a base plus an immediate.  At 4096^3 four resident
+// blocks per CU already overlap one block's loads with the others' FMAs, so
+// the double buffer gains 2 % over level 6 there (88.5 against 86.5
+// TFLOP/s); at 2048^3, one block per CU, 22 % (45.5 against 37.4).  A is
+// staged transposed with rows padded to 132 words.
 //
 // Level 8 follows [GEMM2]'s warp-tiling section ("三级分块：block → warp →
 // thread") on wave64: the 128 x 128 block tile is split 2 x 2 into 64 x 64
 // wave tiles and each lane of a wave owns a 2 x 2 grid of 4 x 4 sub-tiles
 // (rows wm*64 + i*32 + lr*4 + 0..3, cols wn*64 + j*32 + lc*4 + 0..3 with
-// lr = lane/8, lc = lane%8).  Its four 128-bit LDS reads per k then cover 8
-// distinct 16-byte groups (128 contiguous bytes) per wavefront, with the other
-// lanes broadcast, and its C stores are 128-byte rows.  Blocks are re-ordered
-// twice ([GEMM2] "thread swizzling" section; on MI355X the point is the eight
-// separate L2s): the hardware hands consecutive block ids round-robin to the
-// 8 XCDs, so each XCD first receives a contiguous range of logical tile ids,
-// and logical ids walk C in groups of 8 tile-rows so that concurrently
-// resident tiles share A row panels and B column panels inside one L2.
+// lr = lane%8, lc = lane/8): a wave's reads per k are 64 A and 64 B values
+// of LDS (level 7's wave reads 32 A and all 128 B), each 128-bit read
+// covering 8 distinct 16-byte groups (128 contiguous bytes) with the other
+// lanes broadcast.  [GEMM2]'s thread-swizzling section then re-orders the
+// blocks for L2 reuse and reports no gain where the L2 already hits 80 %;
+// on MI355X, whose 8 XCDs each have their own L2, an XCD-contiguous order
+// (each XCD a contiguous range of tiles, with or without groups of 4-16
+// tile rows) measured 3-4 % slower than the plain order for this rung at
+// 4096^3 (88.0 against 91.6 TFLOP/s; equal at 2048^3), so level 8 keeps the
+// plain order; the matrix-core rungs, whose K steps are far shorter in
+// time, use the XCD-contiguous grouped order (l9_tile.h, l10_kloop.hip).
 //
-// Both keep one fused multiply-add chain per output in ascending k, so they
-// reproduce the bits of levels 0-6.
+// Level 7 and 8 keep their fragment reads and FMAs in program order per k
+// (see step below), so both fit 128 VGPRs, four wavefronts per SIMD like
+// level 6; both keep one fused multiply-add chain per output in ascending
+// k, so they reproduce the bits of levels 0-6.
+#include <type_traits>
+
 #include "sgemm_internal.h"
 
 namespace sgemm {
@@ -38,7 +43,6 @@ namespace {
 constexpr int kBM = 128, kBN = 128, kBK = 8, kTM = 8, kTN = 8;
 constexpr int kThreads = 256;
 constexpr int kLdaT = kBM + 4;  // transposed-A row stride in LDS (words)
-constexpr int kGroupM = 8;      // tile-rows per group in the level-8 order
 constexpr int kStageIters = (kBM * kBK / 4) / kThreads;  // 1 float4 of A and of B
 
 struct Staged {
@@ -77,53 +81,39 @@ __device__ __forceinline__ void store_stage(const Staged& r,
   }
 }
 
-// Thread -> outputs.  Level 7: thread (tr, tc) of a 16 x 16 grid owns the
-// contiguous 8 x 8 block at (tr*8, tc*8).  Level 8: the wave-tiled map above.
-// m_off(h) / n_off(h) give the tile offset of the h-th group of 4 rows / cols.
-struct MapContiguous {
+// Thread -> outputs.  Level 7 (as level 6): thread (tr, tc) of a 16 x 16
+// grid owns rows 4 tr .. 4 tr + 3 and 64 + 4 tr .., columns 4 tc .. 4 tc + 3
+// and 64 + 4 tc .. (the sixteen column-threads' 128-bit B reads then cover
+// 256 contiguous bytes, with no bank shared).  Level 8: the wave-tiled map
+// above.  m_off(h) / n_off(h) give the tile offset of the h-th group of 4
+// rows / cols.
+struct MapHalves {
   int m_base, n_base;
-  __device__ MapContiguous(int tid)
-      : m_base((tid / 16) * kTM), n_base((tid % 16) * kTN) {}
-  __device__ int m_off(int h) const { return m_base + 4 * h; }
-  __device__ int n_off(int h) const { return n_base + 4 * h; }
+  __device__ MapHalves(int tid) : m_base(4 * (tid / 16)), n_base(4 * (tid % 16)) {}
+  __device__ int m_off(int h) const { return m_base + (kBM / 2) * h; }
+  __device__ int n_off(int h) const { return n_base + (kBN / 2) * h; }
 };
 struct MapWaveTiled {
   int m_base, n_base;
   __device__ MapWaveTiled(int tid) {
     const int wave = tid / 64, lane = tid % 64;
-    m_base = (wave / 2) * 64 + (lane / 8) * 4;
-    n_base = (wave % 2) * 64 + (lane % 8) * 4;
+    m_base = (wave / 2) * 64 + (lane % 8) * 4;
+    n_base = (wave % 2) * 64 + (lane / 8) * 4;
   }
   __device__ int m_off(int h) const { return m_base + 32 * h; }
   __device__ int n_off(int h) const { return n_base + 32 * h; }
 };
 
-template <bool SWIZZLE, class Map>
-__device__ __forceinline__ void pipeline_tiles(const Problem& p,
-                                               int64_t tiles_m,
-                                               int64_t tiles_n,
+template <class Map>
+__device__ __forceinline__ void pipeline_tiles(const Problem& p, int64_t tiles_n,
                                                int64_t ntiles) {
   __shared__ __align__(16) float As[2][kBK][kLdaT];
   __shared__ __align__(16) float Bs[2][kBK][kBN];
   const int tid = threadIdx.x;
   const Map map(tid);
   const int64_t nk = ceil_div(p.K, kBK);
-  const int64_t first =
-      SWIZZLE ? xcd_contiguous(blockIdx.x, gridDim.x) : int64_t(blockIdx.x);
-  for (int64_t t = first; t < ntiles; t += gridDim.x) {
-    int64_t tm, tn;
-    if (SWIZZLE) {
-      const int64_t group = kGroupM * tiles_n;
-      const int64_t first_m = (t / group) * kGroupM;
-      const int64_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
-      const int64_t in = t % group;
-      tm = first_m + in % gm;
-      tn = in / gm;
-    } else {
-      tm = t / tiles_n;
-      tn = t % tiles_n;
-    }
-    const int64_t row0 = tm * kBM, col0 = tn * kBN;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t row0 = (t / tiles_n) * kBM, col0 = (t % tiles_n) * kBN;
 
     float acc[kTM][kTN];
 #pragma unroll
@@ -135,13 +125,15 @@ __device__ __forceinline__ void pipeline_tiles(const Problem& p,
     load_stage(st, p, row0, col0, 0, tid);
     store_stage(st, As[0], Bs[0], tid);
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      const int cur = static_cast<int>(kt & 1);
+    // One K step on LDS buffer CUR (a constant in each use below, so every
+    // LDS address is a base plus an immediate): the next step's global
+    // loads are issued first, its stores into the other buffer follow the
+    // FMAs, one barrier ends the step.
+    auto step = [&](auto cur_c, int64_t kt) {
+      constexpr int cur = decltype(cur_c)::value;
       const bool more = kt + 1 < nk;
       if (more) load_stage(st, p, row0, col0, (kt + 1) * kBK, tid);
-      // Unrolled by 4: fully unrolled, the compiler hoists every k-step's
-      // fragment reads above the loop (233 VGPRs, two wavefronts per SIMD).
-#pragma unroll 4
+#pragma unroll
       for (int k = 0; k < kBK; ++k) {
         const float4 m0 = *reinterpret_cast<const float4*>(&As[cur][k][map.m_off(0)]);
         const float4 m1 = *reinterpret_cast<const float4*>(&As[cur][k][map.m_off(1)]);
@@ -154,10 +146,25 @@ __device__ __forceinline__ void pipeline_tiles(const Problem& p,
 #pragma unroll
           for (int j = 0; j < kTN; ++j)
             acc[i][j] = fmaf(regM[i], regN[j], acc[i][j]);
+        // Each k's FMAs are issued before the next k's fragment reads and,
+        // after the last k, before the stores and the barrier: left free,
+        // the compiler hoists a step's 32 reads to its start or sinks its
+        // FMAs past the barrier, and either way the fragments hold up to
+        // 128 registers -- three wavefronts per SIMD instead of four.
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int j = 0; j < kTN; ++j) asm volatile("" : "+v"(acc[i][j])::"memory");
       }
       if (more) store_stage(st, As[cur ^ 1], Bs[cur ^ 1], tid);
       __syncthreads();
+    };
+    int64_t kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(std::integral_constant<int, 0>(), kt);
+      step(std::integral_constant<int, 1>(), kt + 1);
     }
+    if (kt < nk) step(std::integral_constant<int, 0>(), kt);
 
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
@@ -175,16 +182,16 @@ __device__ __forceinline__ void pipeline_tiles(const Problem& p,
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_level7(Problem p, int64_t tiles_m,
-                                                     int64_t tiles_n,
-                                                     int64_t ntiles) {
-  pipeline_tiles<false, MapContiguous>(p, tiles_m, tiles_n, ntiles);
+// 256 threads, at least four wavefronts per SIMD: 128 VGPRs (a few
+// per-tile values spill to scratch outside the K loop)
+__global__ __launch_bounds__(kThreads, 4) void k_level7(Problem p, int64_t tiles_n,
+                                                        int64_t ntiles) {
+  pipeline_tiles<MapHalves>(p, tiles_n, ntiles);
 }
 
-__global__ __launch_bounds__(kThreads) void k_level8(Problem p, int64_t tiles_m,
-                                                     int64_t tiles_n,
-                                                     int64_t ntiles) {
-  pipeline_tiles<true, MapWaveTiled>(p, tiles_m, tiles_n, ntiles);
+__global__ __launch_bounds__(kThreads, 4) void k_level8(Problem p, int64_t tiles_n,
+                                                        int64_t ntiles) {
+  pipeline_tiles<MapWaveTiled>(p, tiles_n, ntiles);
 }
 
 Geometry geometry78(int M, int N, int K) {
@@ -193,17 +200,15 @@ Geometry geometry78(int M, int N, int K) {
 
 hipError_t launch7(const Problem& p, hipStream_t s) {
   const Geometry g = geometry78(p.M, p.N, p.K);
-  const dim3 grid(static_cast<unsigned>(g.workgroups)), block(kThreads);
-  const int64_t tm = ceil_div(p.M, kBM), tn = ceil_div(p.N, kBN);
-  hipLaunchKernelGGL(k_level7, grid, block, 0, s, p, tm, tn, g.tiles);
+  hipLaunchKernelGGL(k_level7, dim3(static_cast<unsigned>(g.workgroups)), dim3(kThreads), 0, s,
+                     p, ceil_div(p.N, kBN), g.tiles);
   return hipGetLastError();
 }
 
 hipError_t launch8(const Problem& p, hipStream_t s) {
   const Geometry g = geometry78(p.M, p.N, p.K);
-  const dim3 grid(static_cast<unsigned>(g.workgroups)), block(kThreads);
-  const int64_t tm = ceil_div(p.M, kBM), tn = ceil_div(p.N, kBN);
-  hipLaunchKernelGGL(k_level8, grid, block, 0, s, p, tm, tn, g.tiles);
+  hipLaunchKernelGGL(k_level8, dim3(static_cast<unsigned>(g.workgroups)), dim3(kThreads), 0, s,
+                     p, ceil_div(p.N, kBN), g.tiles);
   return hipGetLastError();
 }
 
@@ -214,7 +219,7 @@ const LevelDesc* level7() {
   return &d;
 }
 const LevelDesc* level8() {
-  static const LevelDesc d = {"L8_wave_tile_xcd_swizzle", geometry78, launch8};
+  static const LevelDesc d = {"L8_wave_tile", geometry78, launch8};
   return &d;
 }
 

@@ -161,8 +161,9 @@ int hip_sgemm_ex_noalloc(int op_a, int op_b, int M, int N, int K, float alpha,
  *     [GEMM2] kernel 6)
  *   7 double-buffered LDS, one barrier per K step ([CP04]
  *     double_buffer_gemm)
- *   8 wave tiling (block -> wave -> lane) with an XCD-aware, grouped
- *     block-to-tile order ([GEMM2] warp tiling and thread swizzling sections)
+ *   8 wave tiling (block -> 64 x 64 wave tiles -> lane sub-tiles) ([GEMM2]
+ *     warp tiling section; its thread-swizzling block order measured slower
+ *     on this rung on MI355X, so tiles go in plain order)
  *   9 FP32 matrix cores (v_mfma_f32_32x32x2_f32 and v_mfma_f32_16x16x4_f32)
  *     on the level-8 pipeline
  *  10 shape-aware dispatch, the level hip_sgemm runs: level 9's tiles over
