@@ -83,7 +83,10 @@ class Tile:
         self.STEPS = self.GROUPS // kslices           # MFMA steps per stage per wavefront
         # floats per four-k group: a few words of pad where the stage store
         # transposes (a row-major A, a transposed B), so that its 32-bit
-        # writes hit 32 different banks per half-wavefront
+        # writes hit 32 different banks per half-wavefront (words 32 apart
+        # share a bank there; with the 64-deep stage's pad of 4 that also
+        # takes the kernel's lane order of 4 majors x 8 groups per
+        # half-wavefront)
         pad = 8 if bk == 16 else 4
         self.A_GROUP = 4 * bm + (0 if ta else pad)
         self.B_GROUP = 4 * bn + (pad if tb else 0)
@@ -178,15 +181,19 @@ class Tile:
 
     def stage_stores(self, st: int, buf: int) -> list[str]:
         """Staging set st into LDS buffer buf.  Element maps (copy h of
-        thread tid; per = float4s per row or k-row, a_per / b_per):
-          A row-major:  row tid/per + h THREADS/per, k 4 (tid%per) .. +3:
+        thread tid; per = float4s per row or k-row, a_per / b_per; (j, q)
+        the thread's slot, (tid/per, tid%per) except for a transposing
+        store with per 16, whose half-wavefronts take 4 majors x 8 groups):
+          A row-major:  row j + h THREADS/per, k 4 q .. +3:
                         transposed into four k-rows of a group;
-          A transposed: k-row tid/per + h THREADS/per, rows 4 (tid%per) ..:
+          A transposed: k-row j + h THREADS/per, rows 4 q ..:
                         stored whole;
-          B row-major:  k-row tid/per + h THREADS/per, columns 4 (tid%per) ..:
+          B row-major:  k-row j + h THREADS/per, columns 4 q ..:
                         stored whole;
-          B transposed: column tid/per + h THREADS/per, k 4 (tid%per) .. +3:
-                        transposed."""
+          B transposed: column j + h THREADS/per, k 4 q .. +3:
+                        transposed.
+        Only the per-thread bases differ between the slot orders; the
+        offsets here (h THREADS/per majors, c k-rows) are the same."""
         r = self.set_base(st)
         rb = r + 4 * self.A_LOADS
         out = []

@@ -129,20 +129,44 @@ __device__ __forceinline__ intx4 buffer_resource(const float* base, uint32_t byt
                : SGEMM_KLOOP_CLOBBERS_##NAME, "memory", "scc")
 // Per-thread element maps of one stage (the loop's loads and stores, and
 // the C++ first stage, use the same ones).  Element h of a thread, with
-// per = float4s per row (k-row) of the operand as stored (A_PER, B_PER):
-//   A row-major:  row tid/per + h THREADS/per, k 4 (tid%per) .. +3
-//   A transposed: k-row tid/per + h THREADS/per, rows 4 (tid%per) .. +3
-//   B row-major:  k-row tid/per + h THREADS/per, columns 4 (tid%per) .. +3
-//   B transposed: column tid/per + h THREADS/per, k 4 (tid%per) .. +3
+// per = float4s per row (k-row) of the operand as stored (A_PER, B_PER) and
+// (j, q) = stage_slot(tid):
+//   A row-major:  row j + h THREADS/per, k 4 q .. 4 q + 3
+//   A transposed: k-row j + h THREADS/per, rows 4 q .. 4 q + 3
+//   B row-major:  k-row j + h THREADS/per, columns 4 q .. 4 q + 3
+//   B transposed: column j + h THREADS/per, k 4 q .. 4 q + 3
+// A 32-bit LDS store is served per half-wavefront, and words 32 apart share
+// a bank there.  A transposing store (row-major A, transposed B) writes
+// word 4 q + c of each of four k-rows of group q; with per == 16 (the
+// 64-deep stage, groups 260 words apart, 4 mod 32) a half-wavefront takes
+// 4 majors x 8 groups, whose 32 words fall in 32 banks (2 majors x 16
+// groups would pair groups q and q + 8 on one bank).  Every other store
+// takes consecutive groups of one major per lane run (tid / per, tid % per);
+// either way a wavefront covers the same four majors, so its global loads
+// read the same bytes.
+template <int PER, bool TRANSPOSING>
+__device__ __forceinline__ void stage_slot(int tid, int& j, int& q) {
+  if constexpr (TRANSPOSING && PER == 16) {
+    j = 4 * (tid / 64) + (tid / 8) % 4;
+    q = tid % 8 + 8 * ((tid / 32) % 2);
+  } else {
+    j = tid / PER;
+    q = tid % PER;
+  }
+}
 template <class T>
 __device__ __forceinline__ void a_map(int tid, int h, int& row, int& k) {
-  const int major = tid / T::A_PER + h * (T::THREADS / T::A_PER), minor = 4 * (tid % T::A_PER);
+  int j, q;
+  stage_slot<T::A_PER, !T::TA>(tid, j, q);
+  const int major = j + h * (T::THREADS / T::A_PER), minor = 4 * q;
   row = T::TA ? minor : major;
   k = T::TA ? major : minor;
 }
 template <class T>
 __device__ __forceinline__ void b_map(int tid, int h, int& k, int& col) {
-  const int major = tid / T::B_PER + h * (T::THREADS / T::B_PER), minor = 4 * (tid % T::B_PER);
+  int j, q;
+  stage_slot<T::B_PER, T::TB>(tid, j, q);
+  const int major = j + h * (T::THREADS / T::B_PER), minor = 4 * q;
   k = T::TB ? minor : major;
   col = T::TB ? major : minor;
 }

@@ -42,20 +42,31 @@ def test_committed_loop_matches_generator():
 
 # Per-thread element maps of l10_kloop.hip (restated from the kernel):
 # element h, component c of thread tid, with per = float4s per row (k-row)
-# of the operand as stored:
-#   A row-major:  row tid/per + h THREADS/per, k 4 (tid%per) + c
-#   A transposed: k-row tid/per + h THREADS/per, row 4 (tid%per) + c
-#   B row-major:  k-row tid/per + h THREADS/per, column 4 (tid%per) + c
-#   B transposed: column tid/per + h THREADS/per, k 4 (tid%per) + c
+# of the operand as stored and (j, q) the thread's slot:
+#   A row-major:  row j + h THREADS/per, k 4 q + c
+#   A transposed: k-row j + h THREADS/per, row 4 q + c
+#   B row-major:  k-row j + h THREADS/per, column 4 q + c
+#   B transposed: column j + h THREADS/per, k 4 q + c
+# where a transposing store (row-major A, transposed B) with per == 16 puts
+# 4 majors x 8 groups in each half-wavefront and every other store
+# (j, q) = (tid / per, tid % per).
+def slot(tid, per, transposing):
+    if transposing and per == 16:
+        return 4 * (tid // 64) + (tid // 8) % 4, tid % 8 + 8 * ((tid // 32) % 2)
+    return tid // per, tid % per
+
+
 def a_elem(t, tid, h, c):
     per = t.BM // 4 if t.TA else t.BK // 4
-    major, minor = tid // per + h * (t.THREADS // per), 4 * (tid % per) + c
+    j, q = slot(tid, per, not t.TA)
+    major, minor = j + h * (t.THREADS // per), 4 * q + c
     return ("A", minor, major) if t.TA else ("A", major, minor)
 
 
 def b_elem(t, tid, h, c):
     per = t.BK // 4 if t.TB else t.BN // 4
-    major, minor = tid // per + h * (t.THREADS // per), 4 * (tid % per) + c
+    j, q = slot(tid, per, t.TB)
+    major, minor = j + h * (t.THREADS // per), 4 * q + c
     return ("B", minor, major) if t.TB else ("B", major, minor)
 
 
@@ -198,8 +209,14 @@ def test_k_slices_cover_every_step_once(name):
 
 def _bank_conflict_free_32bit(addrs):
     """The 32 words of one half-wavefront's 32-bit write lie in 32 different
-    banks (bank = word mod 64)."""
-    return len({(a // 4) % 64 for a in addrs}) == len(addrs)
+    banks.  A 32-bit store is served per half-wavefront and words 32 apart
+    share a bank there (bank = word mod 32): the level-6 kernel's
+    transposing store measured bank-conflict cycles with rows 136 words
+    apart (its two k-groups 544 words, 32 mod 64, apart) and none at 132
+    (16 apart), and this loop's 64 x 64 tile measured 1.40 conflict cycles
+    per LDS instruction with half-wavefronts of 2 rows x 16 four-k groups
+    260 words apart."""
+    return len({(a // 4) % 32 for a in addrs}) == len(addrs)
 
 
 @pytest.mark.parametrize("name", sorted(TILES))
@@ -211,8 +228,28 @@ def test_transposing_stores_hit_distinct_banks(name):
         if line.startswith("ds_write_b128"):
             continue
         for first in range(0, t.THREADS, 32):
-            addrs = [_pieces(t, tid, line)[1][0][1] for tid in range(first, first + 32)]
-            assert _bank_conflict_free_32bit(addrs), (name, line, first)
+            for piece in (0, 1):
+                addrs = [_pieces(t, tid, line)[1][piece][1] for tid in range(first, first + 32)]
+                assert _bank_conflict_free_32bit(addrs), (name, line, first, piece)
+
+
+@pytest.mark.parametrize("name", sorted(TILES))
+def test_whole_stores_and_fragment_reads_hit_distinct_banks(name):
+    """128-bit stores and reads: each group of 16 lanes (one pass of 64
+    words) covers 64 different banks (bank = word mod 64)."""
+    t = TILES[name]
+    lines = [l for l in t.stage_stores(0, 0) if l.startswith("ds_write_b128")]
+    for line in lines:
+        for first in range(0, t.THREADS, 16):
+            words = [(_pieces(t, tid, line)[1][0][1] // 4 + c) % 64
+                     for tid in range(first, first + 16) for c in range(4)]
+            assert len(set(words)) == 64, (name, line, first)
+    for s in range(t.STEPS):
+        offs = [int(re.search(r"offset:(\d+)", l).group(1)) for l in t.frag_reads(64, s, 0)]
+        for first in range(0, t.THREADS, 16):
+            for r, off in ((r_a, offs[0]), (r_b, offs[1])):
+                words = [((r(t, tid) + off) // 4 + c) % 64 for tid in range(first, first + 16) for c in range(4)]
+                assert len(set(words)) == 64, (name, s, first)
 
 
 @pytest.mark.parametrize("name", sorted(TILES))

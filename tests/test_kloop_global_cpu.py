@@ -54,18 +54,29 @@ ADDRS = [(0x7F12_FFFF_FF00, 0x7E34_FFFF_FE00), (0x7F12_FFFF_FFE0, 0x7E34_FFFF_FF
          (0x7F12_FFFF_0000, 0x7E34_FFFF_8000)]
 
 
+def slot(tid, per, transposing):
+    """(major, four-wide group) of thread tid's first float4: a half-
+    wavefront of a transposing 64-deep stage (per 16) takes 4 majors x 8
+    groups, every other stage consecutive groups of one major."""
+    if transposing and per == 16:
+        return 4 * (tid // 64) + (tid // 8) % 4, tid % 8 + 8 * ((tid // 32) % 2)
+    return tid // per, tid % per
+
+
 def a_map(t, tid, h):
     """(row, k) of the first element of float4 h of thread tid (A as
     stored: row-major, four k per float4; transposed, four rows)."""
     per = t.BM // 4 if t.TA else t.BK // 4
-    major, minor = tid // per + h * (t.THREADS // per), 4 * (tid % per)
+    j, q = slot(tid, per, not t.TA)
+    major, minor = j + h * (t.THREADS // per), 4 * q
     return (minor, major) if t.TA else (major, minor)
 
 
 def b_map(t, tid, h):
     """(k, column) of the first element of float4 h of thread tid."""
     per = t.BK // 4 if t.TB else t.BN // 4
-    major, minor = tid // per + h * (t.THREADS // per), 4 * (tid % per)
+    j, q = slot(tid, per, t.TB)
+    major, minor = j + h * (t.THREADS // per), 4 * q
     return (minor, major) if t.TB else (major, minor)
 
 
