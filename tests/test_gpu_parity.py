@@ -248,6 +248,32 @@ def test_levels_0_to_8_are_bit_identical():
         assert np.array_equal(outs[0], outs[level]), f"level {level} differs from level 0"
 
 
+@pytest.mark.parametrize("M,N,K,tile10", [(2048, 2048, 257, (128, 128)), (4096, 4096, 33, (256, 128)),
+                                          (3000, 2100, 100, None)])
+def test_matrix_core_tiles_reproduce_the_fma_chain(M, N, K, tile10):
+    """Where each output is still one chain over ascending k -- level 9's
+    tiles, and level 10's 256 x 128 and 128 x 128 loop tiles (whose ragged
+    first stage holds the lowest k) -- the matrix-core rungs give level 0's
+    bits: the FP32 MFMAs round after every product, as a chain of fmaf does.
+    Level 10's 64 x 64 tile sums four K slices and is left out (tile10 None).
+    A wrong lane map, k order or operand swap anywhere in the MFMA tiles
+    changes bits here even where it stays inside the error bound."""
+    levels = [9]
+    if tile10 is not None:
+        g = sgemm.hip_sgemm_launch_shape(10, M, N, K)
+        assert (g["tile_m"], g["tile_n"]) == tile10 and sgemm.hip_sgemm_plan(M, N, K)["name"] == "tiles"
+        levels.append(10)
+    A, B, C = inputs.make_abc(M, N, K, 4300 + K)
+    print(f"[mfma bits] {M}x{N}x{K} levels 0 and {levels}", flush=True)
+    ref, st = gh.run(gh.Case(M, N, K, 0.5, 3.0, A, B, C), 0)
+    assert st == 0
+    for level in levels:
+        out, st = gh.run(gh.Case(M, N, K, 0.5, 3.0, A, B, C), level)
+        assert st == 0
+        diff = np.flatnonzero(out != ref)
+        assert diff.size == 0, f"level {level}: {diff.size} outputs differ from level 0"
+
+
 @pytest.mark.parametrize("level", LEVELS)
 def test_deterministic(level):
     w, A, B, C, res, rows, ref = workload("sgemm_2048")
