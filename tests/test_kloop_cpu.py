@@ -291,3 +291,96 @@ def test_staging_sets_are_waited_for_before_their_stores(name):
         last_store = max(i for i, l in enumerate(step) if l.startswith("ds_write"))
         first_load = next(i for i, l in enumerate(step) if l.startswith("buffer_load"))
         assert "s_waitcnt lgkmcnt(0)" in step[last_store:first_load]
+
+
+# -- the loop's waits, modelled ------------------------------------------------
+# LDS instructions complete in the order they are issued, and so do the
+# buffer loads (the loop issues no scalar memory load, which would complete
+# out of order); s_waitcnt lgkmcnt(N) / vmcnt(N) returns once at most the
+# youngest N are outstanding.
+_VREGS = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
+
+
+def _regs(text):
+    out = set()
+    for lo, hi, one in _VREGS.findall(text):
+        out |= set(range(int(lo), int(hi) + 1)) if lo else {int(one)}
+    return out
+
+
+def check_waits(lines, in_flight_loads=(), in_flight_stores=1):
+    """Replay the waits of a straight-line run of the loop: every MFMA
+    operand has arrived from its LDS read, every stage store reads a
+    staging register whose load has arrived, no staging register is
+    reloaded while a store still reads it, and no LDS access is outstanding
+    at a barrier.  The run starts with the prelude's loads and the C++
+    part's stage-0 stores (registers the loop does not name) in flight.
+    Returns the list of violations."""
+    lds = [("w", set())] * in_flight_stores   # outstanding LDS ops: ("r", regs written) / ("w", regs read)
+    vm = list(in_flight_loads)     # outstanding buffer loads: regs written
+    bad = []
+    for i, line in enumerate(lines):
+        if line.startswith("s_waitcnt"):
+            m = re.search(r"lgkmcnt\((\d+)\)", line)
+            if m:
+                keep = int(m.group(1))
+                lds = lds[len(lds) - keep:] if keep else []
+            m = re.search(r"vmcnt\((\d+)\)", line)
+            if m:
+                keep = int(m.group(1))
+                vm = vm[len(vm) - keep:] if keep else []
+        elif line.startswith("ds_read"):
+            lds.append(("r", _regs(line.split(",")[0])))
+        elif line.startswith("ds_write"):
+            srcs = _regs(line.split(",", 1)[1])
+            if any(srcs & regs for regs in vm):
+                bad.append((i, line, "stores a register whose load is outstanding"))
+            lds.append(("w", srcs))
+        elif line.startswith("buffer_load"):
+            dst = _regs(line.split(",")[0])
+            if any(kind == "w" and dst & regs for kind, regs in lds):
+                bad.append((i, line, "reloads a register an outstanding store reads"))
+            vm.append(dst)
+        elif line.startswith("v_mfma"):
+            ops = _regs(line.split(",", 1)[1].rsplit(",", 1)[0])
+            if any(kind == "r" and ops & regs for kind, regs in lds):
+                bad.append((i, line, "reads a fragment whose LDS read is outstanding"))
+        elif line == "s_barrier":
+            if lds:
+                bad.append((i, line, "LDS accesses outstanding at the barrier"))
+    return bad
+
+
+def _steady_state(t):
+    prologue = t.program()[:t.program().index("s_cmp_eq_u32 %[pairs], 0")]
+    loads = [_regs(l.split(",")[0]) for l in t.prelude() if l.startswith("buffer_load")]
+    return prologue + t.k_step(0) + t.k_step(1) + t.k_step(0) + t.k_step(1), loads
+
+
+@pytest.mark.parametrize("name", sorted(TILES))
+def test_waits_cover_every_use(name):
+    t = TILES[name]
+    lines, loads = _steady_state(t)
+    assert check_waits(lines, loads) == []
+
+
+@pytest.mark.parametrize("name", sorted(TILES))
+def test_wait_model_catches_a_short_wait(name):
+    """Each wait is needed: loosening any lgkmcnt / vmcnt of the loop by
+    one is reported -- except an lgkmcnt held at the field's top (15),
+    which already waits for more than it needs."""
+    t = TILES[name]
+    lines, loads = _steady_state(t)
+    waits = [i for i, l in enumerate(lines) if l.startswith("s_waitcnt") and "lgkmcnt(15)" not in l]
+    for i in waits:
+        loose = re.sub(r"(lgkmcnt|vmcnt)\((\d+)\)", lambda m: f"{m.group(1)}({int(m.group(2)) + 1})", lines[i])
+        assert check_waits(lines[:i] + [loose] + lines[i + 1:], loads), (name, i, lines[i])
+
+
+@pytest.mark.parametrize("name", sorted(TILES))
+def test_wait_counts_fit_their_fields(name):
+    """gfx9 encodes lgkmcnt in 4 bits and vmcnt in 6."""
+    for line in TILES[name].program() + TILES[name].prelude():
+        for field, top in (("lgkmcnt", 15), ("vmcnt", 63)):
+            m = re.search(field + r"\((\d+)\)", line)
+            assert m is None or int(m.group(1)) <= top, line
