@@ -30,8 +30,11 @@
 // from `scratch` instead: a fixed array in each device's memory, loaded
 // with the library's code object and kept until the process ends.  Host
 // code reaches it only through the address hipGetSymbolAddress gives for
-// the current device (looked up once per device); the array's name itself
-// is a host-side stand-in, not a device address.  Every element a call
+// a device while that device is current (looked up once per device); the
+// array's name itself is a host-side stand-in, not a device address.
+//
+// Both workspaces belong to the device the caller's stream runs on, which
+// need not be the calling thread's current device.  Every element a call
 // reads back from its planes it has written first, so nothing needs
 // clearing between calls; calls that overlap on one device share the
 // array and race.
@@ -52,16 +55,31 @@ static __device__ __align__(256) float scratch[kScratchFloats];
 std::mutex g_scratch_mutex;
 float* g_scratch[kMaxDevices];  // scratch's device address, per device
 
-hipError_t scratch_for_current_device(float** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
+// The device whose queue a stream feeds (the current device for the null
+// stream).
+hipError_t stream_device(hipStream_t s, int* dev) {
+  if (s == nullptr) return hipGetDevice(dev);
+  hipDevice_t d = 0;
+  const hipError_t e = hipStreamGetDevice(s, &d);
+  if (e == hipSuccess) *dev = d;
+  return e;
+}
+
+hipError_t scratch_for_device(int dev, float** out) {
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
   if (g_scratch[dev] == nullptr) {
+    // the symbol's address is the current device's copy: make dev current
+    // for the lookup, then give the calling thread its device back
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
     void* ptr = nullptr;
     e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
     if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
     if (ptr == nullptr) return hipErrorInvalidSymbol;
     g_scratch[dev] = static_cast<float*>(ptr);
   }
@@ -69,11 +87,9 @@ hipError_t scratch_for_current_device(float** out) {
   return hipSuccess;
 }
 
-hipError_t pool_for_current_device(hipMemPool_t* out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
+hipError_t pool_for_device(int dev, hipMemPool_t* out) {
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  hipError_t e = hipSuccess;
   std::lock_guard<std::mutex> lock(g_pool_mutex);
   if (g_pools[dev] == nullptr) {
     hipMemPoolProps props = {};
@@ -142,7 +158,9 @@ hipError_t splitk_with(F launch_split, int64_t k_split, const Problem& p, hipStr
     // the fixed array: no allocation, no release
     if (bytes > size_t(SGEMM_NOALLOC_WORKSPACE_BYTES)) return hipErrorInvalidValue;
     float* ws = nullptr;
-    hipError_t e = scratch_for_current_device(&ws);
+    int dev = 0;
+    hipError_t e = stream_device(s, &dev);
+    if (e == hipSuccess) e = scratch_for_device(dev, &ws);
     if (e != hipSuccess) return e;
     e = launch_split(ws);
     if (e == hipSuccess) e = launch_reduce(ws, splits, p, s);
@@ -156,7 +174,9 @@ hipError_t splitk_with(F launch_split, int64_t k_split, const Problem& p, hipStr
     e = hipMallocAsync(&ws, bytes, s);
   } else {
     hipMemPool_t pool = nullptr;
-    e = pool_for_current_device(&pool);
+    int dev = 0;
+    e = stream_device(s, &dev);
+    if (e == hipSuccess) e = pool_for_device(dev, &pool);
     if (e != hipSuccess) return e;
     e = hipMallocFromPoolAsync(&ws, bytes, pool, s);
   }

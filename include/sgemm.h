@@ -128,8 +128,11 @@ int hip_sgemm_ex(int op_a, int op_b, int M, int N, int K, float alpha,
  * that the library holds on each GPU it runs on until the process ends
  * (SGEMM_NOALLOC_WORKSPACE_BYTES; every split-K plan the library chooses
  * fits it, and hip_sgemm_plan gives a shape's bytes); a call that would
- * need more returns -104 with nothing enqueued.  The first call on a device
- * looks the array's address up; no call allocates or frees.
+ * need more returns -104 with nothing enqueued.  "A device" is the one
+ * `stream` feeds (the current device for the null stream), whichever device
+ * is current on the calling thread.  The first call on a device looks the
+ * array's address up (making that device current for the lookup and then
+ * restoring the caller's); no call allocates or frees.
  * The array is shared by every call on one GPU and keeps the last call's
  * contents (a call reads back only what it has written): calls that overlap
  * in time on one GPU (other streams, other host threads) race on it, and
@@ -206,9 +209,10 @@ int hip_sgemm_level(int level, int M, int N, int K, float alpha,
  *           with the K loop in assembly; for tile 0 the same results bit
  *           for bit when K % 16 == 0).
  * Split K needs S x M x N floats of workspace: the library takes it from a
- * stream-ordered memory pool of its own (one per device, created on first
- * use, memory kept cached until the process ends), allocated and released on
- * `stream` around the two kernels; concurrent calls never share it.  On a
+ * stream-ordered memory pool of its own (one per device -- the device that
+ * `stream` feeds --, created on first use, memory kept cached until the
+ * process ends), allocated and released on `stream` around the two kernels;
+ * concurrent calls never share it.  On a
  * stream under graph capture it is a stream-ordered allocation from the
  * device's default pool instead (recorded as a graph memory node).  Results
  * are bit-reproducible for a given (tile, splits, shape).  Other arguments,

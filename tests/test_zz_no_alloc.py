@@ -89,6 +89,28 @@ def test_noalloc_plans_without_workspace(M, N, K):
     _check(M, N, K, False, False, 31100 + M + N + K)
 
 
+def test_workspace_follows_the_stream():
+    """Split K on a stream of its own (not the null stream): the pool and
+    the fixed array are those of the device the stream feeds, looked up
+    from the stream; same bits as on the current stream."""
+    import torch
+    side = torch.cuda.Stream()
+    shape = (700, 600, 8200)
+    A, B, C = inputs.make_abc(*shape, 31200)
+    print(f"[noalloc] {shape} on a side stream", flush=True)
+    outs = {}
+    for name, entry in (("pool", sgemm.hip_sgemm_ex), ("fixed", sgemm.hip_sgemm_ex_noalloc)):
+        def on_side(M_, N_, K_, al, pa, lda, pb, ldb, be, pc, ldc, stream, entry=entry):
+            torch.cuda.synchronize()  # the harness's copies are on the current stream
+            return entry("N", "N", M_, N_, K_, al, pa, lda, pb, ldb, be, pc, ldc, side)
+        out, st = gh.run(gh.Case(*shape, 0.75, -1.5, A, B, C), on_side)
+        assert st == 0, sgemm.hip_sgemm_status_string(st)
+        outs[name] = out
+    want = _call(sgemm.hip_sgemm_ex, False, False, A, B, C, 0.75, -1.5)
+    for out in outs.values():
+        assert np.array_equal(out.view(np.uint32), want.view(np.uint32))
+
+
 def test_noalloc_quick_returns_and_errors():
     """Argument errors and quick returns as hip_sgemm_ex (nothing launched
     for M == 0; C <- beta*C for K == 0)."""
