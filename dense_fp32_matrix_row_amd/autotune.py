@@ -34,7 +34,8 @@ import sys
 DEFAULT_SHAPES = ["256", "512", "768", "1024", "1536", "2048", "3072", "4096", "4097",
                   "1024x1024x4096", "1024x1024x8192", "2048x2048x8192", "512x512x8192",
                   "700x600x8200", "1024x4096x1024", "4096x1024x1024", "2048x4096x2048",
-                  "5000x3000x2000", "300x300x3000", "2051x2055x300"]
+                  "5000x3000x2000", "300x300x3000", "2051x2055x300", "64x4096x4096", "4096x64x4096",
+                  "128x4096x4096", "64x4096x1024", "32x4096x4096"]
 DEFAULT_SPLITS = [1, 2, 3, 4, 6, 8, 12, 16]
 # A pick counts as tuned when its time is within this fraction of the
 # fastest configuration's on the same shape (box-to-box spread of these

@@ -9,7 +9,8 @@
 //     mostly empty rows or columns, and the problem is bound by reading the
 //     other operand; l10_thin.hip gives them one 16-row MFMA block or
 //     vector-ALU FMA chains);
-//   - a deep K over 64-255 tiles of 64 x 64: split K (l10_splitk.hip);
+//   - a deep K over 64-255 tiles of 64 x 64, or K >= 2048 over a wide,
+//     shallow grid of 64-128 of them: split K (l10_splitk.hip);
 //   - otherwise one of the three assembly-loop tiles of l10_kloop.hip
 //     (256 x 128, 128 x 128, 64 x 64), the one that leaves the busiest CU
 //     the least work, with partial edge tiles, or whole tiles plus the thin
@@ -72,6 +73,26 @@ Decomp decompose(int M, int N, int K) {
       const int64_t k_split = k_split_for(K, parts, shape_bk(Shape::kSmallDeep));
       if (k_split < K) return {Plan::kSplitK, Shape::kSmallDeep, M, N, k_split};
     }
+  }
+
+  // 1b. A wide, shallow grid of 64-128 tiles of 64 x 64 (one side 48-128
+  //    rows or columns, the other thousands) with K >= 2048, which rule 1
+  //    leaves alone because K is not twice the long side: split into the
+  //    parts that make one round of work items, 4 over <= 64 tiles and 2
+  //    over <= 128 (more parts measured slower: items of at most ~1000 k
+  //    pay their per-launch start more often).  Sweeps against the plans
+  //    without it: 64 x 4096 x 4096 65.1 TFLOP/s against 39.4 on the thin
+  //    panels, 4096 x 64 x 4096 64.9 / 39.4, 64 x 4096 x 2048 42.8 / 37.4,
+  //    128 x 4096 x 4096 90.1 / 65.5 on unsplit 64 x 64 tiles, 64 x 8192 x
+  //    8192 104.7 / 69.0, 96 x 4096 x 4096 67.2 / 48.6, 48 x 8192 x 4096
+  //    65.7 / 48.3, 256 x 2048 x 2048 66.5 / 59.3.  Thinner sides stay on
+  //    the thin panels (32 x 4096 x 4096: 34.1 there, 32.1 split), and so
+  //    do shallower K (64 x 4096 x 1024: 32.5 there, at most 25.0 split).
+  const int64_t short_side = M < N ? M : N;
+  if (!deep && K >= 2048 && short_side >= 48 && tiles64 >= 64 && tiles64 <= 128) {
+    const int64_t parts = tiles64 <= 64 ? 4 : 2;
+    const int64_t k_split = k_split_for(K, parts, shape_bk(Shape::kSmallDeep));
+    if (k_split < K) return {Plan::kSplitK, Shape::kSmallDeep, M, N, k_split};
   }
 
   // 2. A grid of >= 128 tiles of 64 x 64: whichever of the three

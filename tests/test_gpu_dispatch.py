@@ -46,6 +46,9 @@ SHAPES = [
     (1024, 1024, 4096, "tiles", "64x64 loop tiles, deep K, unsplit"),
     (512, 512, 8192, "split_k", "split K: 64x64 loop tiles, 8 slices"),
     (700, 600, 8200, "split_k", "split K: 64x64 edge tiles, 4 slices, ragged K"),
+    (64, 4096, 2048, "split_k", "split K, wide shallow grid: 64 tiles, 4 slices"),
+    (100, 3000, 2100, "split_k", "split K, wide shallow grid: edge tiles, 2 slices, ragged K"),
+    (4200, 60, 2500, "split_k", "split K, tall narrow grid: edge tiles, 2 slices, ragged K"),
     (300, 260, 5000, "thin_panels", "16-row panels, deep K"),
     (1, 3001, 5003, "few_rows", "one row (matrix-vector)"),
     (5, 3001, 5003, "few_rows", "five rows"),

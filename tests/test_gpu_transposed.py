@@ -67,6 +67,8 @@ SHAPES = [
     (1024, 1024, 4096, "64x64 loop tiles, deep K", "all"),
     (512, 512, 8192, "split K, 64x64 loop tiles, 8 slices", "all"),
     (700, 600, 8200, "split K, 64x64 edge tiles, ragged K", "all"),
+    (100, 3000, 2100, "split K, wide shallow grid, 2 slices, ragged K", "all"),
+    (4200, 60, 2500, "split K, tall narrow grid, 2 slices, ragged K", "all"),
     (300, 260, 5000, "16-row panels, deep K", "all"),
     (17, 33, 65, "odd", "all"),
     (129, 65, 31, "odd", "all"),
