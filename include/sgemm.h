@@ -169,14 +169,20 @@ int hip_sgemm_ex_noalloc(int op_a, int op_b, int M, int N, int K, float alpha,
  *     on this rung on MI355X, so tiles go in plain order)
  *   9 FP32 matrix cores (v_mfma_f32_32x32x2_f32 and v_mfma_f32_16x16x4_f32)
  *     on the level-8 pipeline
- *  10 shape-aware dispatch, the level hip_sgemm runs: level 9's tiles over
- *     the largest whole-tile part of a problem whose M and N miss a tile
- *     multiple by at most 16, with vector-ALU kernels on the thin fringe;
- *     problems with M <= 16 or N <= 16 entirely on those kernels (their
- *     cross-lane sums have a fixed order, so results are reproducible);
- *     otherwise level 9's own choice.  A call may enqueue up to three
- *     kernels on the stream, over disjoint parts of C ([GEMM2] size-sweep
- *     section: a library is many kernels picked by shape)
+ *  10 shape-aware dispatch, the level hip_sgemm runs (hip_sgemm_plan names
+ *     the plan a shape gets): M <= 16 or N <= 16 on the thin kernels
+ *     (vector-ALU FMA chains for one to four rows or columns, otherwise
+ *     one 16-row matrix-core block; cross-lane sums in a fixed order);
+ *     fewer than 128 tiles of 64 x 64 on the thin matrix-core kernel over
+ *     16-row panels; a deep K over a small grid, or K >= 2048 over a wide,
+ *     shallow one, split over K into workspace planes that a second
+ *     kernel adds in order; otherwise one of three whole-tile kernels
+ *     whose K loop is hand-scheduled assembly (256 x 128, 128 x 128, and
+ *     64 x 64 over four K-slice wavefronts), with partial edge tiles, or
+ *     with whole tiles plus the thin kernels on a fringe of at most 16
+ *     rows / columns.  A call enqueues up to three kernels on the stream,
+ *     over disjoint parts of C ([GEMM2] size-sweep section: a library is
+ *     many kernels picked by shape)
  */
 int hip_sgemm_level(int level, int M, int N, int K, float alpha,
                     const float *A, int lda,
