@@ -50,8 +50,9 @@ class SgemmError(RuntimeError):
 
 
 def load(path: Optional[str] = None):
-    """Load libsgemm.so (built by dense_fp32_matrix_row_amd.build).  Raises
-    if it is missing: there is no other implementation to fall back on."""
+    """Load libsgemm.so (built by dense_fp32_matrix_row_amd.build), or the
+    build at `path`, which then serves every call of this module.  Raises if
+    it is missing: there is no other implementation to fall back on."""
     global _lib
     if _lib is not None and path is None:
         return _lib
@@ -94,8 +95,7 @@ def load(path: Optional[str] = None):
     lib.hip_sgemm_plan.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                    ctypes.POINTER(ctypes.c_longlong)]
     del fptr
-    if path == LIBRARY:
-        _lib = lib
+    _lib = lib
     return lib
 
 

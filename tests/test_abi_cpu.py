@@ -297,3 +297,18 @@ def test_noalloc_argument_checks():
     assert sgemm.hip_sgemm_ex_noalloc("N", "N", 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4,
                                       stream=0) == 0
     assert "fixed" in sgemm.hip_sgemm_status_string(sgemm.STATUS_WORKSPACE_LIMIT)
+
+
+def test_load_with_a_path_serves_every_later_call(tmp_path):
+    """sgemm.load(path) makes that build the module's library, so a caller
+    comparing two builds in one process times the one it loaded."""
+    import shutil
+    copy = tmp_path / "libsgemm_copy.so"
+    shutil.copy(sgemm.LIBRARY, copy)
+    try:
+        lib = sgemm.load(str(copy))
+        assert sgemm.load() is lib and lib._name == str(copy)
+        assert sgemm.hip_sgemm_num_levels() == 11
+    finally:
+        sgemm.load(sgemm.LIBRARY)
+    assert sgemm.load()._name == sgemm.LIBRARY
