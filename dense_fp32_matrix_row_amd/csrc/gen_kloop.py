@@ -42,7 +42,9 @@ step s reading k = 4 s + lane / 16.  Step s runs on one fragment set while
 the other set receives step s + 1 (128-bit LDS reads issued after the
 step's first MFMA); the next stage is stored from its staging set into the
 free LDS buffer during step 0 and the same set is reloaded (with the stage
-one or two further on) during step 1; the barrier sits halfway through
+one or two further on) during step 1 -- for the tiles with two staging sets,
+the stores spread over steps 0 and 1 and the reload waits for step 2; the
+barrier sits halfway through
 step 3, after which step 0 of the next stage is read from the other buffer,
 so the LDS latency after a barrier hides under the remaining eight MFMAs.
 Loop bookkeeping is scalar (buffer resources advanced in SGPRs, LDS offsets
@@ -236,10 +238,23 @@ class Tile:
         # next step's lgkmcnt(0): with one wavefront per SIMD nothing else
         # would cover that wait (measured: 1024 x 1024 x 4096 on the 64 x 64
         # tile 122 -> 125 TFLOP/s against stores after MFMAs 4..15)
-        store_at: dict[int, list[str]] = {}
+        # With two staging sets (a stage loaded two ahead), the stores spread
+        # over steps 0 and 1 and the set is reloaded in step 2: a burst of
+        # the whole stage's stores in step 0, from every wavefront of the
+        # CU at once, fills the LDS data queue and delays the fragment reads
+        # queued behind it (1024 x 1024 x 8192 on the 64 x 64 tile: 23x the
+        # vendor kernel's SQ_LDS_DATA_FIFO_FULL).  Step 1 then waits only
+        # for its fragment reads: LDS accesses complete in issue order, and
+        # the reads precede step 0's stores, so lgkmcnt(<stores in step 0>)
+        # suffices (lgkmcnt is a 4-bit field).
+        spread = self.DEPTH >= 2
+        span = 28 if spread else 12          # MFMA slots the stores occupy
+        store_at: dict[tuple[int, int], list[str]] = {}
         for i, ins in enumerate(stores):
-            slot = 1 + i if len(stores) <= 12 else 1 + i * 12 // len(stores)
-            store_at.setdefault(slot, []).append(ins)
+            slot = 1 + i if len(stores) <= 12 and not spread else 1 + i * span // len(stores)
+            store_at.setdefault(divmod(slot, 16), []).append(ins)
+        in_step0 = sum(len(v) for (st_, _), v in store_at.items() if st_ == 0)
+        reload_step = 2 if spread else 1
         out = []
         for ss in range(self.STEPS):
             fs, fn = sets[ss % 2], sets[(ss + 1) % 2]
@@ -250,15 +265,17 @@ class Tile:
                 # stage n + 1 complete (its set's loads are the older ones in
                 # flight), then stored into the free buffer
                 extra.setdefault(0, []).append(f"s_waitcnt vmcnt({per_stage * (self.DEPTH - 1)})")
-                for slot, ins in store_at.items():
+            for (st_, slot), ins in store_at.items():
+                if st_ == ss:
                     extra.setdefault(slot, []).extend(ins)
-            if ss == 1:
+            if ss == reload_step:
                 # the stores have completed (lgkmcnt(0) at this step's start),
                 # so the staging set may take stage n + 1 + DEPTH
                 for i, ins in enumerate(loads):
                     extra.setdefault(1 + i, []).append(ins)
                 extra.setdefault(len(loads) + 1, []).extend(self.ADVANCE)
-            out.append("s_waitcnt lgkmcnt(0)")
+            out.append(f"s_waitcnt lgkmcnt({min(in_step0, 15)})" if spread and ss == 1
+                       else "s_waitcnt lgkmcnt(0)")
             last = ss == self.STEPS - 1
             for b in range(16):
                 if last and b == 8:
