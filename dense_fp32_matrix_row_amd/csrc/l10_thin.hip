@@ -31,6 +31,19 @@ __device__ __forceinline__ float fget(const float4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// The vector-ALU kernels walk K in two loops: the steps whose loads all lie
+// inside the operands for the whole block (a block-uniform test) take
+// 128-bit loads with no per-lane test, issued back to back; the step at the
+// end of K, and every step of a block at the right edge, load through
+// load4's per-lane checks, behind which the compiler makes each load wait
+// for the one before (the many wavefronts per CU hide most of that).  Same
+// results; 4097 x 1 x 4097 22.8 -> 21.0 us, 4 x 4096 x 4096 with B stored
+// transposed 18.6 -> 17.0.  Edge steps without the per-lane checks
+// (addresses clamped into the operand, zeros past K) needed up to 80 % more
+// registers and lost wavefronts per CU (4097 x 1 x 4097: 37 us), and the
+// same split in the matrix-core kernel below was slower on half the shapes
+// tried (16 x 8192 x 8192: 62 -> 66-102 us), so that kernel keeps one loop.
+
 // ---------------------------------------------------------------------------
 // Few rows: M <= RP.  Block b owns columns [16b, 16b + 16).  Lane l of
 // wavefront w takes the column quad q = l % 4 (4 adjacent columns, one
@@ -40,10 +53,56 @@ __device__ __forceinline__ float fget(const float4& v, int i) {
 // those k (one 128-bit access per row of A).
 template <int RP>
 struct FewRows {
-  static constexpr int WAVES = RP <= 4 ? 16 : 8;   // register budget
+  static_assert(RP <= 4, "more rows go to the matrix-core form");
+  static constexpr int WAVES = 16;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int KSWEEP = 64 * WAVES;
 };
+
+// One lane's k quad k .. k + 3 of a sweep: its loads, then its FMAs (two
+// copies, so that the 128-bit form's loads issue back to back).  FULL: the
+// block's 16 columns and every lane's k quad are inside B and A.
+template <int RP, bool TA, bool TB, bool FULL>
+__device__ __forceinline__ void rows_step(const Problem& p, int64_t k, int64_t col, float (&acc)[RP][4]) {
+  float4 b[4], a[RP];
+  if (TB) {
+    float4 v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      v[c] = FULL ? ld_global4(p.B + (col + c) * p.ldb + k) : load4(p.B + (col + c) * p.ldb, k, p.K, col + c < p.N);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = make_float4(fget(v[0], j), fget(v[1], j), fget(v[2], j), fget(v[3], j));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = FULL ? ld_global4(p.B + (k + j) * p.ldb + col) : load4(p.B + (k + j) * p.ldb, col, p.N, k + j < p.K);
+  }
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    if (TA) {
+      const bool ok = r < p.M;  // uniform
+      const float* at = p.A + k * p.lda + r;
+      a[r] = FULL ? make_float4(ok ? at[0] : 0.0f, ok ? at[p.lda] : 0.0f, ok ? at[2 * p.lda] : 0.0f,
+                                ok ? at[3 * p.lda] : 0.0f)
+                  : make_float4(ok && k < p.K ? at[0] : 0.0f, ok && k + 1 < p.K ? at[p.lda] : 0.0f,
+                                ok && k + 2 < p.K ? at[2 * p.lda] : 0.0f, ok && k + 3 < p.K ? at[3 * p.lda] : 0.0f);
+    } else {
+      a[r] = FULL && r < p.M ? ld_global4(p.A + r * p.lda + k) : load4(p.A + r * p.lda, k, p.K, r < p.M);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float av = fget(a[r], j);
+      acc[r][0] = fmaf(av, b[j].x, acc[r][0]);
+      acc[r][1] = fmaf(av, b[j].y, acc[r][1]);
+      acc[r][2] = fmaf(av, b[j].z, acc[r][2]);
+      acc[r][3] = fmaf(av, b[j].w, acc[r][3]);
+    }
+  }
+}
 
 // TA: A stored K x M (element (r, k) at A[k * lda + r]); TB: B stored N x K
 // (element (k, n) at B[n * ldb + k]: the lane's four columns come as four
@@ -67,42 +126,13 @@ __global__ __launch_bounds__(FewRows<RP>::THREADS) void k_few_rows(Problem p,
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
 
-    for (int64_t k = 64 * wave + 4 * g; k < p.K; k += KSWEEP) {
-      float4 b[4];
-      if (TB) {
-        float4 v[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = load4(p.B + (col + c) * p.ldb, k, p.K, col + c < p.N);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b[j] = make_float4(fget(v[0], j), fget(v[1], j), fget(v[2], j), fget(v[3], j));
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b[j] = load4(p.B + (k + j) * p.ldb, col, p.N, k + j < p.K);
-      }
-#pragma unroll
-      for (int r = 0; r < RP; ++r) {
-        float4 a;
-        if (TA) {
-          const bool ok = r < p.M;
-          a = make_float4(ok && k < p.K ? p.A[k * p.lda + r] : 0.0f,
-                          ok && k + 1 < p.K ? p.A[(k + 1) * p.lda + r] : 0.0f,
-                          ok && k + 2 < p.K ? p.A[(k + 2) * p.lda + r] : 0.0f,
-                          ok && k + 3 < p.K ? p.A[(k + 3) * p.lda + r] : 0.0f);
-        } else {
-          a = load4(p.A + r * p.lda, k, p.K, r < p.M);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float av = fget(a, j);
-          acc[r][0] = fmaf(av, b[j].x, acc[r][0]);
-          acc[r][1] = fmaf(av, b[j].y, acc[r][1]);
-          acc[r][2] = fmaf(av, b[j].z, acc[r][2]);
-          acc[r][3] = fmaf(av, b[j].w, acc[r][3]);
-        }
-      }
-    }
+    const bool cols_full = c0 + 16 <= p.N;  // block-uniform
+    // whole sweeps first (128-bit loads), then the partial sweep at the end
+    // of K, and every sweep of a block at the right edge, element by element
+    const int64_t k_whole = cols_full ? p.K / KSWEEP * KSWEEP : 0;
+    const int64_t k0 = 64 * wave + 4 * g;
+    for (int64_t base = 0; base < k_whole; base += KSWEEP) rows_step<RP, TA, TB, true>(p, base + k0, col, acc);
+    for (int64_t base = k_whole; base < p.K; base += KSWEEP) rows_step<RP, TA, TB, false>(p, base + k0, col, acc);
 
     // Sum over the 16 k quads of the wavefront (lane bits 2-5), then over
     // the wavefronts in order.
@@ -146,13 +176,26 @@ constexpr int kColThreads = 64 * kRowsPerBlock;
 
 template <int WP>
 struct FewCols {
-  static constexpr int KC = WP <= 8 ? 2048 : 1024;  // LDS: 64 KB at most
+  static_assert(WP <= 4, "more columns go to the matrix-core form");
+  static constexpr int KC = 2048;
   static constexpr int QUADS = KC / 256;            // k quads per lane per chunk
 };
 
 // TB: B stored N x K (the staged strip is then contiguous along k).  A is
 // always row-major here: with A stored K x M a wavefront's row would be a
 // strided column, so the dispatcher gives such problems to the tile kernels.
+// A chunk's A loads: the lane's QUADS k quads of its wavefront's A row.
+// FULL: the chunk lies inside K (128-bit loads, no per-lane test).
+template <int WP, bool FULL>
+__device__ __forceinline__ void cols_a_loads(const Problem& p, const float* arow, bool has_row, int64_t kc,
+                                             int lane, float4 (&a)[FewCols<WP>::QUADS]) {
+#pragma unroll
+  for (int t = 0; t < FewCols<WP>::QUADS; ++t) {
+    const int64_t k = kc + 4 * lane + 256 * t;
+    a[t] = FULL ? ld_global4(arow + k) : load4(arow, k, p.K, has_row);
+  }
+}
+
 template <int WP, bool TB>
 __global__ __launch_bounds__(kColThreads) void k_few_cols(Problem p, int64_t nblocks) {
   constexpr int KC = FewCols<WP>::KC, QUADS = FewCols<WP>::QUADS;
@@ -169,8 +212,8 @@ __global__ __launch_bounds__(kColThreads) void k_few_cols(Problem p, int64_t nbl
 
     for (int64_t kc = 0; kc < p.K; kc += KC) {
       float4 a[QUADS];
-#pragma unroll
-      for (int t = 0; t < QUADS; ++t) a[t] = load4(arow, kc + 4 * lane + 256 * t, p.K, has_row);
+      if (kc + KC <= p.K) cols_a_loads<WP, true>(p, arow, has_row, kc, lane, a);  // uniform
+      else cols_a_loads<WP, false>(p, arow, has_row, kc, lane, a);
       __syncthreads();  // every wavefront is done with the previous chunk
       for (int e = tid; e < WP * KC; e += kColThreads) {
         const int c = e / KC, kk = e % KC;
@@ -390,7 +433,7 @@ Geometry thin_geometry(int64_t thin_rows, int64_t n, int K, bool few_cols) {
   return g;
 }
 
-// Smallest instantiated width (1, 2, 4, 8, 16) that covers n.
+// Smallest power of two that covers n (the kernels take 1, 2 or 4).
 int padded_width(int n) {
   int w = 1;
   while (w < n) w *= 2;
@@ -422,10 +465,7 @@ hipError_t launch_cols_t(const Problem& p, hipStream_t s) {
 Geometry few_rows_geometry(int M, int N, int K) {
   if (!thin_on_valu(M, N)) return thin_geometry(M, N, K, false);
   const int rp = padded_width(M);
-  const int threads = rp <= 4 ? FewRows<4>::THREADS : FewRows<16>::THREADS;
-  Geometry g = make_geometry(rp, N, K, rp, 16, rp <= 4 ? FewRows<4>::KSWEEP
-                                                       : FewRows<16>::KSWEEP, threads);
-  return g;
+  return make_geometry(rp, N, K, rp, 16, FewRows<4>::KSWEEP, FewRows<4>::THREADS);
 }
 
 template <bool TA, bool TB>
@@ -434,9 +474,7 @@ hipError_t launch_rows_op(const Problem& p, hipStream_t s) {
     case 1: return launch_rows_t<1, TA, TB>(p, s);
     case 2: return launch_rows_t<2, TA, TB>(p, s);
     case 4: return launch_rows_t<4, TA, TB>(p, s);
-    case 8: return launch_rows_t<8, TA, TB>(p, s);
-    case 16: return launch_rows_t<16, TA, TB>(p, s);
-    default: return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;  // more rows go to the matrix-core form
   }
 }
 
@@ -454,7 +492,7 @@ hipError_t launch_few_rows(const Problem& p, hipStream_t s) {
 Geometry few_cols_geometry(int M, int N, int K) {
   if (!thin_on_valu(N, M)) return thin_geometry(N, M, K, true);
   const int wp = padded_width(N);
-  return make_geometry(M, wp, K, kRowsPerBlock, wp, wp <= 8 ? 2048 : 1024, kColThreads);
+  return make_geometry(M, wp, K, kRowsPerBlock, wp, FewCols<4>::KC, kColThreads);
 }
 
 template <bool TB>
@@ -463,9 +501,7 @@ hipError_t launch_cols_op(const Problem& p, hipStream_t s) {
     case 1: return launch_cols_t<1, TB>(p, s);
     case 2: return launch_cols_t<2, TB>(p, s);
     case 4: return launch_cols_t<4, TB>(p, s);
-    case 8: return launch_cols_t<8, TB>(p, s);
-    case 16: return launch_cols_t<16, TB>(p, s);
-    default: return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;  // more columns go to the matrix-core form
   }
 }
 
