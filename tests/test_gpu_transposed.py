@@ -54,6 +54,11 @@ def run_ex(op_a, op_b, A, B, C, alpha, beta, pads=(0, 0, 0), offs=(0, 0, 0)):
 # B's orientation does not matter)
 SHAPES = [
     (5, 3001, 777, "few rows", "all"),
+    (1, 4097, 4097, "one row on the vector ALUs: whole sweeps, K tail, edge block", "all"),
+    (2, 1000, 2049, "two rows on the vector ALUs: whole sweeps, K tail", "all"),
+    (3, 3001, 2300, "three rows on the vector ALUs: whole sweeps, K tail, edge block", "all"),
+    (4097, 1, 4097, "one column on the vector ALUs (A^T: matrix-core thin form)", "b"),
+    (2500, 3, 2300, "three columns on the vector ALUs, whole and partial chunks", "b"),
     (16, 1000, 333, "sixteen rows", "all"),
     (1500, 7, 2003, "few columns", "all"),
     (1500, 3, 2003, "three columns (A^T: matrix-core thin form)", "b"),
@@ -107,7 +112,8 @@ def test_transposed_padded_misaligned(M, N, K):
         assert oracle.normalised_error(out, ref, None, -1.5, 0.0, strict=True) <= BOUND, (op_a, op_b)
 
 
-@pytest.mark.parametrize("M,N,K", [(4097, 4097, 33), (520, 390, 3000), (3, 2000, 999)])
+@pytest.mark.parametrize("M,N,K", [(4097, 4097, 33), (520, 390, 3000), (3, 2000, 999), (4, 3001, 2300),
+                                   (2500, 2, 2300)])
 def test_transposed_integer_exact(M, N, K):
     """Integer entries: every orientation equals the reference bit for bit."""
     print(f"[transposed integer] {M}x{N}x{K}", flush=True)
