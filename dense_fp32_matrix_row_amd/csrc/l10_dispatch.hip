@@ -38,13 +38,6 @@ struct Decomp {
 
 constexpr int kCUs = 256;
 
-// Fraction of the last round of blocks that is busy: tiles over whole
-// rounds of one block per CU.
-double round_fill(int64_t tiles) {
-  const int64_t rounds = ceil_div(tiles, kCUs);
-  return double(tiles) / double(rounds * kCUs);
-}
-
 // The rules below were fitted to sweeps of every tile shape and slice count
 // on MI355X (dense_fp32_matrix_row_amd.autotune); the comments give the
 // measurements that decided them.  The sweep's table of record is checked

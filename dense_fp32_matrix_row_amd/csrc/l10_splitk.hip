@@ -1,13 +1,14 @@
 // l10_splitk.hip -- split K for problems too small in M x N to fill the
-// GPU: level 9's tiles, each with its K range cut into slices that run as
-// separate work items, then one reduction kernel.
+// GPU: a matrix-core tile kernel (level 10's 64 x 64 assembly loop, or any
+// tile hip_sgemm_tile_split names) with each tile's K range cut into slices
+// that run as separate work items, then one reduction kernel.
 //
 // The technique is the one the pages describe behind the vendor library's
 // small-size advantage ([GEMM2], size-sweep section: at 256 the vendor calls
 // a tiled GEMM plus a reduce kernel; each block computes part of the K sum
 // for its C block, the partial sums need extra storage, a reduce kernel adds
-// them).  At 1024^3 the 128 x 128 tile grid has 64 tiles for 256 CUs; four
-// slices of K make 256 work items, eight make 512 (two per CU).
+// them).  At 512 x 512 x 8192 the 64 x 64 tile grid has 64 tiles for 256
+// CUs; eight slices of K make 512 work items (two per CU).
 //
 // Determinism: the number of slices depends only on the shape, every slice
 // stores its float32 sums into its own plane of the workspace (no atomics),

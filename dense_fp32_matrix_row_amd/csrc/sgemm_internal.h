@@ -165,9 +165,10 @@ Geometry mfma_geometry(Shape shape, int M, int N, int K);
 hipError_t launch_mfma(Shape shape, const Problem& p, hipStream_t s);
 // Level 10's whole-tile kernels with their K loop in assembly
 // (l10_kloop.hip), for the Huge (256 x 128), Large (128 x 128) and
-// SmallDeep (64 x 64) shapes, any operand orientation: M and N multiples of
-// the tile, buffer offsets below 2^31.  launch_tiles runs one where it
-// fits, else the compiled tile kernel.
+// SmallDeep (64 x 64) shapes, any operand orientation, any M and N (edge
+// tiles load and store only inside the matrix): buffer offsets below
+// 2^31.  launch_tiles runs one where it fits, else the compiled tile
+// kernel.
 bool kloop_fits(Shape shape, const Problem& p);
 hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s);
 Geometry tiles_geometry(Shape shape, int M, int N, int K);  // of launch_tiles, dense row-major
