@@ -76,15 +76,41 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and blank lines (string and
+    character literals kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(line.rstrip() for line in "".join(out).splitlines() if line.strip())
+
+
 def kernel_source_digest() -> str:
-    """Digest of the HIP sources, used to tell whether recorded hardware
-    counters still describe the kernels being timed."""
+    """Digest of the HIP sources without their comments, used to tell
+    whether recorded hardware counters still describe the kernels being
+    timed (an edit to a comment keeps it; any code change, host side
+    included, makes a new one)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_fp32_matrix_row_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h", ".inc")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
