@@ -24,8 +24,9 @@
  * Element (i, j) of A is A[i*lda + j]; of B, B[i*ldb + j]; of C, C[i*ldc + j].
  *
  * Ownership and concurrency
- *   The caller owns every buffer; A, B and C are device pointers (HBM of the
- *   current HIP device).  The only memory the library takes is split K's
+ *   The caller owns every buffer; A, B and C are device pointers in the
+ *   HBM of the device that `stream` feeds (the current device for the null
+ *   stream).  The only memory the library takes is split K's
  *   workspace (level 10 splits K for deep problems with few output tiles;
  *   hip_sgemm_plan tells beforehand whether a shape does and how many bytes
  *   it takes; hip_sgemm_tile_split says where they come from); it keeps no
