@@ -91,3 +91,42 @@ def test_split_random_data_deterministic():
     b, st2 = run_split(gh.Case(M, N, K, 1.0, 1.0, A, B, C), 1, 8)
     assert st1 == st2 == 0
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_split_k_on_two_streams_at_once():
+    """hip_sgemm's split-K plan on two streams with no synchronisation
+    between them: each call takes its workspace from the pool in its own
+    stream's order, so interleaved calls never share one.  Every result
+    equals the same call made alone, bit for bit."""
+    import torch
+    M, N, K = 512, 512, 8192
+    assert sgemm.hip_sgemm_plan(M, N, K)["name"] == "split_k"
+    print("[split-K two streams] 512x512x8192, 6 calls per stream", flush=True)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    data = []
+    for i in range(2):
+        A, B, C = inputs.make_abc(M, N, K, 6400 + i)
+        data.append(tuple(torch.from_numpy(x).cuda() for x in (A, B, C)))
+    torch.cuda.synchronize()
+
+    def call(i, out, stream):
+        dA, dB, _ = data[i]
+        st = sgemm.hip_sgemm(M, N, K, 1.5, dA, K, dB, N, -0.5, out, N, stream)
+        assert st == 0, sgemm.hip_sgemm_status_string(st)
+
+    alone = []
+    for i in range(2):
+        out = data[i][2].clone()
+        torch.cuda.synchronize()
+        call(i, out, streams[i])
+        torch.cuda.synchronize()
+        alone.append(out.cpu().numpy())
+    outs = [[data[i][2].clone() for _ in range(6)] for i in range(2)]
+    torch.cuda.synchronize()
+    for r in range(6):
+        for i in range(2):
+            call(i, outs[i][r], streams[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r in range(6):
+            assert np.array_equal(outs[i][r].cpu().numpy().view(np.uint32), alone[i].view(np.uint32)), (i, r)
