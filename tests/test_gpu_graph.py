@@ -73,3 +73,38 @@ def test_graph_replays_match_eager(M, N, K, alpha, beta):
                               alpha, beta)
     got = out[torch.as_tensor(rows, device="cuda")].cpu().numpy()
     assert oracle.normalised_error(got, ref, C[rows], alpha, beta) <= BOUND
+
+
+@pytest.mark.parametrize("M,N,K,alpha,beta", [(512, 512, 8192, 1.0, 0.0), (700, 600, 8200, 0.5, 2.0),
+                                               (2048, 2048, 512, 0.5, 3.0)])
+def test_noalloc_graph_replays_match_eager(M, N, K, alpha, beta):
+    """hip_sgemm_ex_noalloc captured into a graph (the callers it is for):
+    split K's partial sums then live in the library's fixed device array,
+    so the graph holds no memory node; every replay equals the eager call
+    (and hip_sgemm_ex) bit for bit, with eager work between replays."""
+    import torch
+    print(f"[graph no-alloc] {M}x{N}x{K} alpha={alpha} beta={beta}", flush=True)
+    A, B, C = inputs.make_abc(M, N, K, 4100 + M + N + K)
+    dA, dB, dC0 = (torch.from_numpy(x).cuda() for x in (A, B, C))
+
+    eager = dC0.clone()   # the first call also looks the array's address up, outside the capture
+    sgemm.check(sgemm.hip_sgemm_ex_noalloc("N", "N", M, N, K, alpha, dA, K, dB, N, beta, eager, N))
+    pooled = dC0.clone()
+    sgemm.check(sgemm.hip_sgemm_ex("N", "N", M, N, K, alpha, dA, K, dB, N, beta, pooled, N))
+    torch.cuda.synchronize()
+    assert torch.equal(eager.view(torch.int32), pooled.view(torch.int32))
+
+    out = dC0.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        status = sgemm.hip_sgemm_ex_noalloc("N", "N", M, N, K, alpha, dA, K, dB, N, beta, out, N)
+    assert status == 0, sgemm.hip_sgemm_status_string(status)
+
+    other = torch.ones(1 << 20, device="cuda")
+    for rep in range(REPLAYS):
+        out.copy_(dC0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), f"replay {rep}"
+        other.mul_(1.5).add_(out[0, 0])
+        torch.cuda.synchronize()
