@@ -50,9 +50,14 @@ def sources():
 KLOOP_SOURCE = os.path.join(CSRC, "l10_kloop.hip")
 FIRST_STAGING = 80
 # last staging register per block tile (DEPTH sets of a stage's A and B
-# float4s from v80, as gen_kloop.py lays them out)
+# float4s from v80, as gen_kloop.py lays them out); the 256 x 128 tile's
+# fringe variant also stages one word of the extra row and one of the
+# extra column (v92, v93)
 LAST_STAGING = {256: 80 + 12 - 1, 128: 80 + 2 * 16 - 1, 64: 80 + 2 * 32 - 1}
-KLOOP_KERNELS = 24  # 3 tiles x 4 orientations x (plain, split K)
+LAST_STAGING_FRINGE = 93
+# 3 tiles x 4 orientations x (plain, split K), and the fringe variant of the
+# 256 x 128 tile in 4 orientations
+KLOOP_KERNELS = 28
 
 
 def kloop_kernels(asm: str):
@@ -76,8 +81,9 @@ def check_kloop_staging(asm: str) -> list:
     if len(kernels) != KLOOP_KERNELS:
         bad.append(("*", f"{len(kernels)} loop kernels found, expected {KLOOP_KERNELS}"))
     for name, lines in kernels:
-        m = re.search(r"KTileILi(\d+)", name)
-        last = LAST_STAGING.get(int(m.group(1))) if m else None
+        # KTile<BM, BN, BK, KS, TA, TB, FR> as mangled
+        m = re.search(r"KTileILi(\d+)ELi\d+ELi\d+ELi\d+ELb[01]ELb[01]ELb([01])E", name)
+        last = (LAST_STAGING_FRINGE if m.group(2) == "1" else LAST_STAGING.get(int(m.group(1)))) if m else None
         if last is None or "s_nop 4" not in lines:
             bad.append((name, "no prelude found"))
             continue
@@ -87,18 +93,19 @@ def check_kloop_staging(asm: str) -> list:
         except ValueError:
             bad.append((name, "no loop barrier after the prelude"))
             continue
-        prelude_loads = 0
+        prelude_words = 0  # staging registers the prelude's loads fill
         for ins in lines[start:end]:
             if not ins or ins.startswith((".", "s_")):
                 continue
-            lm = re.match(r"buffer_load_dwordx4 v\[(\d+):\d+\], \S+, \S+, \S+ offen$", ins)
-            if lm and FIRST_STAGING <= int(lm.group(1)) <= last:
-                prelude_loads += 1
+            lm = re.match(r"buffer_load_dword(x4)? v\[?(\d+)(:\d+\])?, \S+, \S+, \S+ offen$", ins)
+            if lm and FIRST_STAGING <= int(lm.group(2)) <= last:
+                prelude_words += 4 if lm.group(1) else 1
                 continue
             if [r for r in _registers(ins) if r[1] >= FIRST_STAGING and r[0] <= last]:
                 bad.append((name, f"touches a staging register before the loop: {ins}"))
-        if prelude_loads * 4 != last - FIRST_STAGING + 1:
-            bad.append((name, f"{prelude_loads} prelude loads for staging v{FIRST_STAGING}..v{last}"))
+        if prelude_words != last - FIRST_STAGING + 1:
+            bad.append((name, f"prelude loads fill {prelude_words} staging registers of "
+                              f"v{FIRST_STAGING}..v{last}"))
     return bad
 
 

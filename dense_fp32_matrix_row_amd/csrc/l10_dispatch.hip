@@ -14,8 +14,10 @@
 //   - otherwise one of the three assembly-loop tiles of l10_kloop.hip
 //     (256 x 128, 128 x 128, 64 x 64), the one that leaves the busiest CU
 //     the least work, with partial edge tiles, or whole tiles plus the thin
-//     kernels on a fringe of <= 16 rows / columns (at 4097^3: the 512 whole
-//     tiles of 4096^3 and two one-element strips);
+//     kernels on a fringe of <= 16 rows / columns; a fringe of one row and /
+//     or one column beside 256 x 128 tiles (4097^3: the 512 whole tiles of
+//     4096^3 and two one-element strips) is summed by the tiles' own blocks
+//     from the operands they hold in LDS, in the same launch;
 //   - small problems (fewer than 128 tiles of 64 x 64): the thin
 //     matrix-core kernel over 16-row panels of C.
 // Every output element is computed by exactly one tile or thin kernel (or,
@@ -149,6 +151,26 @@ Decomp decompose(int M, int N, int K) {
   return {Plan::kThinPanels, Shape::kSmallSliced, M, N, K};
 }
 
+// A fringe of at most one row and one column beside 256 x 128 tiles runs in
+// the tiles' launch (l10_kloop.hip's fringe variant) where its offsets fit;
+// the plan query assumes packed operands (lda = K, ldb = N as op(A), op(B)
+// are stored row-major, M and K when transposed), the launch checks the
+// caller's and falls back to the three launches.
+bool one_launch_fringe(const Decomp& d, const Problem& p) {
+  return d.plan == Plan::kTilesWithFringe && d.shape == Shape::kHuge && tiles_fringe_fits(p, d.Mm, d.Nm);
+}
+
+bool one_launch_fringe(const Decomp& d, int M, int N, int K) {
+  Problem p{};
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.lda = K;
+  p.ldb = N;
+  p.ldc = N;
+  return one_launch_fringe(d, p);
+}
+
 Geometry geometry10(int M, int N, int K) {
   const Decomp d = decompose(M, N, K);
   switch (d.plan) {
@@ -176,7 +198,7 @@ PlanInfo plan10(int M, int N, int K) {
       return {SGEMM_PLAN_SPLIT_K, 2,
               ceil_div(K, d.k_split) * int64_t(M) * int64_t(N) * int64_t(sizeof(float))};
     case Plan::kTilesWithFringe:
-      return {SGEMM_PLAN_TILES_FRINGE, 1 + (d.Nm < N) + (d.Mm < M), 0};
+      return {SGEMM_PLAN_TILES_FRINGE, one_launch_fringe(d, M, N, K) ? 1 : 1 + (d.Nm < N) + (d.Mm < M), 0};
   }
   return info;
 }
@@ -191,6 +213,7 @@ hipError_t launch10_with(const Problem& p, hipStream_t s, Workspace w) {
     case Plan::kThinPanels: return launch_thin_panels(p, s);
     case Plan::kTilesWithFringe: break;
   }
+  if (one_launch_fringe(d, p)) return launch_tiles_fringe(p, d.Mm, d.Nm, s);
   Problem grid = p;
   grid.M = d.Mm;
   grid.N = d.Nm;

@@ -60,17 +60,22 @@ constexpr int round256(int n) { return (n + 255) / 256 * 256; }
 // tile runs 64 tiles per XCD at once; 4 x 16 of them (A 1024 rows, B 2048
 // columns) measured the fewest fabric fetches at 4096^3: 605 MB per call
 // against 741 MB for 8 x 8 and 739 MB for 2 x 32, at the same time.
-template <int BM_, int BN_, int BK_, int KS_, bool TA_, bool TB_>
+// FR: the 256 x 128 tile's fringe variant (one more row of C below the
+// grid and / or one more column to its right, computed beside the tiles).
+template <int BM_, int BN_, int BK_, int KS_, bool TA_, bool TB_, bool FR_ = false>
 struct KTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, KS = KS_, GROUP_M = BM == 256 ? 4 : 8;
-  static constexpr bool TA = TA_, TB = TB_;
+  static constexpr bool TA = TA_, TB = TB_, FR = FR_;
   static constexpr int WAVES_M = BM / 64, WAVES_N = BN / 64, WAVE_TILES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * WAVE_TILES * KS;
   static constexpr int GROUPS = BK / 4, STEPS = GROUPS / KS;  // MFMA steps per stage / per slice
   static constexpr int PAD = BK == 16 ? 8 : 4;  // words between four-k groups, transposing stores
   static constexpr int A_GROUP = 4 * BM + (TA ? 0 : PAD);  // floats per four-k group
   static constexpr int B_GROUP = 4 * BN + (TB ? PAD : 0);
-  static constexpr int A_STAGE = round256(GROUPS * A_GROUP * 4);  // bytes per stage
+  // bytes per stage; the fringe variant keeps 16 + 16 words after the
+  // groups (the extra row's k, then the extra column's k)
+  static constexpr int FPAD = GROUPS * A_GROUP * 4;
+  static constexpr int A_STAGE = round256(FPAD + (FR ? 128 : 0));
   static constexpr int B_STAGE = round256(GROUPS * B_GROUP * 4);
   static constexpr int STAGES_LDS = 2 * A_STAGE + 2 * B_STAGE;
   // K slices: each wavefront finishes 4 / KS block rows of its wave tile
@@ -84,6 +89,7 @@ struct KTile {
   static_assert(A_LOADS >= 1 && A_LOADS <= 4 && B_LOADS >= 1 && B_LOADS <= 4, "loads per stage");
   static_assert(THREADS % A_PER == 0 && THREADS % B_PER == 0, "whole rows per load round");
   static_assert(4 % KS == 0 && STEPS >= 2, "K slices");
+  static_assert(!FR || (BM == 256 && BN == 128 && BK == 16 && KS == 1), "fringe: the 256 x 128 tile");
 };
 
 // Raw buffer resource (stride 0): loads at byte offsets >= bytes return 0.
@@ -114,6 +120,8 @@ __device__ __forceinline__ intx4 buffer_resource(const float* base, uint32_t byt
 #define SGEMM_KLOOP_DEEP \
   , [oB1] "v"(oB[1]), [oA2] "v"(oA[2]), [oA3] "v"(oA[3]), [oB2] "v"(oB[2]), [oB3] "v"(oB[3])
 #define SGEMM_KLOOP_DEEP_STORES , [wA1] "v"(wA + T::A_STAGE), [wB1] "v"(wB + T::B_STAGE)
+#define SGEMM_KLOOP_FRINGE_LOADS , [foa] "v"(foa), [fob] "v"(fob)
+#define SGEMM_KLOOP_FRINGE_WORDS , [fst] "v"(fst), [frB] "v"(frB), [fcA] "v"(fcA), [fpk] "v"(fpk)
 #define SGEMM_KLOOP_PRELUDE(NAME, LOADS)                                                  \
   asm volatile(SGEMM_KLOOP_PRE_##NAME                                                     \
                : SGEMM_KLOOP_STAGING_OUT_##NAME, "+{s[60:63]}"(rsA), "+{s[64:67]}"(rsB)   \
@@ -176,6 +184,19 @@ __device__ __forceinline__ void b_map(int tid, int h, int& k, int& col) {
 // stores its raw sums (no alpha, beta or C) into plane `part` of ws, an
 // M x N row-major array per part; the reduction kernel adds the planes in
 // part order.
+// T::FR (the fringe variant): the tiles_m x tiles_n whole tiles cover all of
+// C but row M - 1 when M = 256 tiles_m + 1, and column N - 1 when
+// N = 128 tiles_n + 1.  Block (i, j) holds, over its K loop, op(A)'s rows
+// of tile row i and op(B)'s columns of tile column j, all of K; so it also
+// sums row M - 1 of op(A) against its share of those columns (columns
+// i cpt .. i cpt + cpt - 1 of the tile, cpt = ceil(128 / tiles_m) <= 32)
+// and its share of those rows (j rpt .., rpt = ceil(256 / tiles_n) <= 32)
+// against column N - 1 of op(B), and the last block the corner: every
+// output of the fringe is summed in one block, k = tid / 32 of each stage
+// per thread (the corner: k = tid % 16), and those sixteen partial sums
+// are added in k order.  Row M - 1's and column N - 1's elements reach LDS
+// with the stage they belong to; the block's record counts then reach
+// that row / column.
 template <class T, bool SPLIT>
 __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m, int64_t tiles_n,
                                                       int64_t k_split, float* __restrict__ ws) {
@@ -200,6 +221,10 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   const int rows = static_cast<int>(p.M - row0 < BM ? p.M - row0 : BM);
   const int cols = static_cast<int>(p.N - col0 < T::BN ? p.N - col0 : T::BN);
   const bool whole = rows == BM && cols == T::BN;
+  // fringe variant: the grid has row M - 1 / column N - 1 beside it (the
+  // same for every block)
+  const bool f_row = T::FR && p.M == tiles_m * BM + 1;
+  const bool f_col = T::FR && p.N == tiles_n * T::BN + 1;
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int slice = wave / T::WAVE_TILES, wv = wave % T::WAVE_TILES;
@@ -216,8 +241,12 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   const int64_t b_ks = TB ? 1 : ldb, b_cs = TB ? ldb : 1;
   const float* const a_base = p.A + row0 * a_rs + k_lo * a_ks;
   const float* const b_base = p.B + col0 * b_cs + k_lo * b_ks;
-  const uint32_t a_bytes = static_cast<uint32_t>(((rows - 1) * a_rs + (K - 1) * a_ks + 1) * 4);
-  const uint32_t b_bytes = static_cast<uint32_t>(((K - 1) * b_ks + (cols - 1) * b_cs + 1) * 4);
+  // (fringe variant: rows / columns of the extra row / column, relative
+  // to the tile, at which the record counts end where it exists)
+  const int64_t a_last = f_row ? p.M - 1 - row0 : rows - 1;
+  const int64_t b_last = f_col ? p.N - 1 - col0 : cols - 1;
+  const uint32_t a_bytes = static_cast<uint32_t>((a_last * a_rs + (K - 1) * a_ks + 1) * 4);
+  const uint32_t b_bytes = static_cast<uint32_t>(((K - 1) * b_ks + b_last * b_cs + 1) * 4);
   uint32_t oA[4] = {0, 0, 0, 0}, oB[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int h = 0; h < T::A_LOADS; ++h) {
@@ -254,6 +283,29 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
                       static_cast<uint32_t>((g0 * T::B_GROUP + kg * T::BN + wn * 64 + 4 * lrow) * 4);
   const uint32_t stepA = static_cast<uint32_t>(T::BK * a_ks * 4);
   const uint32_t stepB = static_cast<uint32_t>(T::BK * b_ks * 4);
+  // fringe variant, per thread: the k of a stage it stages (tid % 16): the
+  // byte offsets of element (a_last, k) of the tile's A and (k, b_last) of
+  // its B; the k it multiplies (tid / 32) and the column n / row m of the
+  // block's share it takes (tid % 32; beyond the share, a column / row of
+  // the tile whose sums are not stored); its LDS bases: the staged words
+  // of that k (extra row's at k, extra column's at 16 + k), B's word (k, n),
+  // A's word (m, k), and the staged words of k = tid % 16.
+  const int64_t f_cpt = ceil_div(T::BN, tiles_m), f_rpt = ceil_div(BM, tiles_n);
+  const int64_t f_n0 = (row0 / BM) * f_cpt, f_m0 = (col0 / T::BN) * f_rpt;
+  uint32_t foa = 0, fob = 0, fst = 0, frB = 0, fcA = 0, fpk = 0;
+  float fa, fb, frow = 0.0f, fcol = 0.0f, fcor = 0.0f;
+  if constexpr (T::FR) {
+    const int ks = tid % 16, kf = tid / 32, c = tid % 32;
+    foa = static_cast<uint32_t>((a_last * a_rs + ks * a_ks) * 4);
+    fob = static_cast<uint32_t>((ks * b_ks + b_last * b_cs) * 4);
+    const int n = c < f_cpt && f_n0 + c < T::BN ? static_cast<int>(f_n0) + c : c;
+    const int m = c < f_rpt && f_m0 + c < BM ? static_cast<int>(f_m0) + c : c;
+    fst = base + static_cast<uint32_t>(4 * ks);
+    fpk = base + static_cast<uint32_t>(4 * kf);
+    frB = base + 2 * T::A_STAGE +
+          static_cast<uint32_t>(((kf / 4) * T::B_GROUP + (kf % 4) * T::BN + n) * 4);
+    fcA = base + static_cast<uint32_t>(((kf / 4) * T::A_GROUP + (kf % 4) * BM + m) * 4);
+  }
 
   // stages 1 .. PREFETCH requested first (their loads stay in flight in the
   // staging registers), then stage 0: k < k0, into buffer 0 through the
@@ -268,7 +320,11 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   intx4 rsB = buffer_resource(b_base + k0 * b_ks,
                               b_bytes > b_skip ? static_cast<uint32_t>(b_bytes - b_skip) : 0u);
   floatx4 stg[T::PREFETCH * (T::A_LOADS + T::B_LOADS)];
-  if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_PRELUDE(256x128_NN, SGEMM_KLOOP_ONE_B);
+  if constexpr (T::FR && !TA && !TB) SGEMM_KLOOP_PRELUDE(256x128_NN_F, SGEMM_KLOOP_FRINGE_LOADS);
+  else if constexpr (T::FR && !TA) SGEMM_KLOOP_PRELUDE(256x128_NT_F, SGEMM_KLOOP_FRINGE_LOADS);
+  else if constexpr (T::FR && !TB) SGEMM_KLOOP_PRELUDE(256x128_TN_F, SGEMM_KLOOP_FRINGE_LOADS);
+  else if constexpr (T::FR) SGEMM_KLOOP_PRELUDE(256x128_TT_F, SGEMM_KLOOP_FRINGE_LOADS);
+  else if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_PRELUDE(256x128_NN, SGEMM_KLOOP_ONE_B);
   else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_PRELUDE(256x128_NT, SGEMM_KLOOP_ONE_B);
   else if constexpr (BM == 256 && !TB) SGEMM_KLOOP_PRELUDE(256x128_TN, SGEMM_KLOOP_ONE_B);
   else if constexpr (BM == 256) SGEMM_KLOOP_PRELUDE(256x128_TT, SGEMM_KLOOP_ONE_B);
@@ -293,6 +349,14 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   const __amdgpu_buffer_rsrc_t rb0 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(b_base), 0, static_cast<int>(b_bytes), 0x00020000);
   float av[T::A_LOADS][4], bv[T::B_LOADS][4];
+  // fringe variant: stage 0's words of the extra row and column (zeros
+  // beyond k0, and beyond the record counts where the block has none)
+  float fa0 = 0.0f, fb0 = 0.0f;
+  if constexpr (T::FR) {
+    const bool in = tid % 16 < k0;
+    fa0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra0, in ? foa : kOutside, 0, 0));
+    fb0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb0, in ? fob : kOutside, 0, 0));
+  }
   if (k0 % 4 == 0 && whole) {
 #pragma unroll
     for (int h = 0; h < T::A_LOADS; ++h) {
@@ -374,11 +438,25 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
           make_float4(bv[h][0], bv[h][1], bv[h][2], bv[h][3]);
     }
   }
+  if constexpr (T::FR) {
+    // every thread of a k stores the same value
+    float* const pad = lds_a + T::FPAD / 4;
+    pad[tid % 16] = fa0;
+    pad[16 + tid % 16] = fb0;
+  }
   const int stages = (K + T::BK - 1) / T::BK;
   uint32_t pairs = static_cast<uint32_t>(stages / 2);
   const uint32_t odd = static_cast<uint32_t>(stages % 2);
   floatx16 a0 = {}, a1 = {}, a2 = {}, a3 = {};
-  if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_LOOP(256x128_NN, SGEMM_KLOOP_ONE_B, );
+  if constexpr (T::FR && !TA && !TB)
+    SGEMM_KLOOP_LOOP(256x128_NN_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FRINGE_WORDS);
+  else if constexpr (T::FR && !TA)
+    SGEMM_KLOOP_LOOP(256x128_NT_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FRINGE_WORDS);
+  else if constexpr (T::FR && !TB)
+    SGEMM_KLOOP_LOOP(256x128_TN_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FRINGE_WORDS);
+  else if constexpr (T::FR)
+    SGEMM_KLOOP_LOOP(256x128_TT_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FRINGE_WORDS);
+  else if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_LOOP(256x128_NN, SGEMM_KLOOP_ONE_B, );
   else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_LOOP(256x128_NT, SGEMM_KLOOP_ONE_B, );
   else if constexpr (BM == 256 && !TB) SGEMM_KLOOP_LOOP(256x128_TN, SGEMM_KLOOP_ONE_B, );
   else if constexpr (BM == 256) SGEMM_KLOOP_LOOP(256x128_TT, SGEMM_KLOOP_ONE_B, );
@@ -391,6 +469,40 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   else if constexpr (!TB) SGEMM_KLOOP_LOOP(64x64_TN, SGEMM_KLOOP_DEEP, SGEMM_KLOOP_DEEP_STORES);
   else SGEMM_KLOOP_LOOP(64x64_TT, SGEMM_KLOOP_DEEP, SGEMM_KLOOP_DEEP_STORES);
   floatx16 acc[4] = {a0, a1, a2, a3};
+
+  // fringe variant: the partial sums meet in LDS (free once every
+  // wavefront has left the loop) and each output adds its sixteen in k
+  // order: the block's share of row M - 1 (threads 0 .. 31), of column
+  // N - 1 (threads 32 .. 63), and in the last block the corner (thread 64)
+  if constexpr (T::FR) {
+    if (f_row || f_col) {
+      float* const red = reinterpret_cast<float*>(smem);
+      __syncthreads();
+      red[tid] = frow;
+      red[T::THREADS + tid] = fcol;
+      if (tid < 16) red[2 * T::THREADS + tid] = fcor;
+      __syncthreads();
+      if (f_row && tid < 32 && tid < f_cpt && f_n0 + tid < T::BN) {
+        float sum = red[tid];
+        for (int k = 1; k < 16; ++k) sum += red[32 * k + tid];
+        float* const c = p.C + int64_t(p.M - 1) * p.ldc + col0 + f_n0 + tid;
+        *c = epilogue(sum, p.alpha, p.beta, c);
+      }
+      const int r = tid - 32;
+      if (f_col && r >= 0 && r < 32 && r < f_rpt && f_m0 + r < BM) {
+        float sum = red[T::THREADS + r];
+        for (int k = 1; k < 16; ++k) sum += red[T::THREADS + 32 * k + r];
+        float* const c = p.C + (row0 + f_m0 + r) * p.ldc + (p.N - 1);
+        *c = epilogue(sum, p.alpha, p.beta, c);
+      }
+      if (f_row && f_col && tid == 64 && t == tiles_m * tiles_n - 1) {
+        float sum = red[2 * T::THREADS];
+        for (int k = 1; k < 16; ++k) sum += red[2 * T::THREADS + k];
+        float* const c = p.C + int64_t(p.M - 1) * p.ldc + (p.N - 1);
+        *c = epilogue(sum, p.alpha, p.beta, c);
+      }
+    }
+  }
 
   // K slices: slice s finishes block rows i with i / (4 / KS) == s.  Every
   // wavefront writes the block rows the others finish into LDS (lane-
@@ -502,6 +614,22 @@ bool fits(const Problem& p) {
   return a_end * 4 < lim && b_end * 4 < lim;
 }
 
+// The fringe variant over a grid of Mm x Nm (whole tiles) inside p, with
+// p.M - Mm and p.N - Nm each 0 or 1: at least 4 tile rows and 8 tile
+// columns (each block's share of the fringe at most 32 columns / rows),
+// and every block's offsets down to row M - 1 / across to column N - 1
+// (largest from the first tile) below 2^31 bytes.
+template <class T>
+bool fits_fringe(const Problem& p, int Mm, int Nm) {
+  if (p.trans_a != T::TA || p.trans_b != T::TB) return false;
+  if (Mm < 4 * T::BM || Nm < 8 * T::BN || Mm % T::BM || Nm % T::BN || p.K < 1) return false;
+  if (p.M - Mm < 0 || p.M - Mm > 1 || p.N - Nm < 0 || p.N - Nm > 1) return false;
+  const int64_t lim = int64_t(1) << 31, past = p.K + (T::PREFETCH + 1) * T::BK;
+  const int64_t a_end = T::TA ? past * p.lda + p.M : (p.M - 1) * p.lda + past;
+  const int64_t b_end = T::TB ? (p.N - 1) * p.ldb + past : past * p.ldb + p.N;
+  return a_end * 4 < lim && b_end * 4 < lim;
+}
+
 template <class T, bool SPLIT>
 hipError_t launch_t(const Problem& p, int64_t k_split, float* ws, hipStream_t s) {
   const int64_t tm = ceil_div(p.M, T::BM), tn = ceil_div(p.N, T::BN);
@@ -519,6 +647,14 @@ auto with_orientation(const Problem& p, F f) {
   if (p.trans_a) return f(KTile<BM, BN, BK, KS, true, false>());
   if (p.trans_b) return f(KTile<BM, BN, BK, KS, false, true>());
   return f(KTile<BM, BN, BK, KS, false, false>());
+}
+
+template <class F>
+auto with_fringe_tile(const Problem& p, F f) {
+  if (p.trans_a && p.trans_b) return f(KTile<256, 128, 16, 1, true, true, true>());
+  if (p.trans_a) return f(KTile<256, 128, 16, 1, true, false, true>());
+  if (p.trans_b) return f(KTile<256, 128, 16, 1, false, true, true>());
+  return f(KTile<256, 128, 16, 1, false, false, true>());
 }
 
 template <class F>
@@ -561,6 +697,21 @@ Geometry tiles_geometry(Shape shape, int M, int N, int K) {
 hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s) {
   if (!kloop_fits(shape, p)) return launch_mfma(compiled(shape), p, s);
   return with_tile(shape, p, [&](auto t) { return launch_t<decltype(t), false>(p, p.K, nullptr, s); });
+}
+
+bool tiles_fringe_fits(const Problem& p, int Mm, int Nm) {
+  return with_fringe_tile(p, [&](auto t) { return fits_fringe<decltype(t)>(p, Mm, Nm); });
+}
+
+hipError_t launch_tiles_fringe(const Problem& p, int Mm, int Nm, hipStream_t s) {
+  if (!tiles_fringe_fits(p, Mm, Nm)) return hipErrorInvalidValue;
+  return with_fringe_tile(p, [&](auto t) {
+    typedef decltype(t) T;
+    const int64_t tm = Mm / T::BM, tn = Nm / T::BN;
+    hipLaunchKernelGGL((k_kloop<T, false>), dim3(static_cast<unsigned>(tm * tn)), dim3(T::THREADS), 0, s,
+                       p, tm, tn, int64_t(p.K), nullptr);
+    return hipGetLastError();
+  });
 }
 
 Geometry tiles_split_geometry(Shape shape, int M, int N, int K, int64_t k_split) {

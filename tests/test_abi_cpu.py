@@ -252,9 +252,15 @@ def test_plan_query_names_every_plan_and_its_workspace():
     assert P(16, 4096, 4096)["name"] == "few_rows"
     assert P(4096, 3, 4097)["name"] == "few_cols"
     assert P(4096, 4096, 4096) == {"plan": 4, "name": "tiles", "launches": 1, "workspace_bytes": 0}
-    assert P(4097, 4097, 4097) == {"plan": 5, "name": "tiles_fringe", "launches": 3,
+    # a fringe of one row and / or one column beside 256 x 128 tiles runs in
+    # the tiles' own launch; wider fringes, and fringes beside the 128 x 128
+    # tile, add a thin-kernel launch per side
+    assert P(4097, 4097, 4097) == {"plan": 5, "name": "tiles_fringe", "launches": 1,
                                    "workspace_bytes": 0}
-    assert P(4096, 4097, 64)["launches"] == 2 and P(4097, 4096, 64)["launches"] == 2
+    assert P(4096, 4097, 64)["launches"] == 1 and P(4097, 4096, 64)["launches"] == 1
+    assert P(4098, 4097, 64)["launches"] == 3 and P(4097, 4098, 64)["launches"] == 3
+    assert P(4096, 4098, 64)["launches"] == 2
+    assert P(2049, 2049, 2048)["launches"] == 3  # 128 x 128 tiles
     assert P(256, 256, 256)["name"] == "thin_panels"
     # split K: 512 x 512 x 8192 (64 tiles of 64 x 64) in 8 slices of 1024
     sk = P(512, 512, 8192)

@@ -1,5 +1,7 @@
 """Level 10 (shape-aware dispatch) on every plan it has: a whole-tile grid
-plus one- to sixteen-wide fringes (both large loop tiles), a ragged K under
+plus one- to sixteen-wide fringes (both large loop tiles; a one-row and /
+or one-column fringe beside 256 x 128 tiles in the tiles' own launch), a
+ragged K under
 whole M/N tiles, the 64 x 64 loop tiles with edges, split K for a deep K
 over a small grid (whole and edge tiles, ragged K), 16-row panels for small
 problems, and thin problems (M <= 16 or N <= 16).  Each case first asserts
@@ -39,6 +41,11 @@ def _device():
 SHAPES = [
     (2051, 2055, 300, "tiles_fringe", "128x128 loop grid + 3-row / 7-column fringe"),
     (4096 + 3, 4096 + 16, 40, "tiles_fringe", "256x128 loop grid + 3-row / 16-column fringe"),
+    (4096, 4096 + 2, 64, "tiles_fringe", "256x128 loop grid + 2-column fringe"),
+    (4097, 4097, 300, "tiles_fringe", "256x128 grid, one row and one column in the tiles' launch"),
+    (4097, 4096, 17, "tiles_fringe", "256x128 grid, one row in the tiles' launch, K ragged"),
+    (4096, 4097, 1, "tiles_fringe", "256x128 grid, one column in the tiles' launch, K = 1"),
+    (8193, 4097, 8, "tiles_fringe", "1024 tiles of 256x128, one row and one column, K below a stage"),
     (4096, 4096, 36, "tiles", "256x128 loop grid, K ragged (36 = 2*16 + 4)"),
     (2048, 2048, 100, "tiles", "128x128 loop grid, K ragged (100 = 6*16 + 4)"),
     (2048, 4096, 80, "tiles", "128x128 loop grid, 512 tiles"),
@@ -87,8 +94,8 @@ def test_dispatch_padded_and_misaligned(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2051, 2055, 300), (7, 2000, 3001), (2000, 9, 3001),
-                                   (4096 + 1, 4096 + 1, 33), (1024, 1024, 4096),
-                                   (512, 512, 8192), (700, 600, 8200)])
+                                   (4096 + 1, 4096 + 1, 33), (4097, 4096, 40), (4096, 4097, 5),
+                                   (1024, 1024, 4096), (512, 512, 8192), (700, 600, 8200)])
 def test_dispatch_integer_exact(M, N, K):
     """Integer entries in [-8, 8]: every partial sum is an integer far below
     2^24, so any summation order is exact and the result must equal the

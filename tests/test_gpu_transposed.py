@@ -64,6 +64,9 @@ SHAPES = [
     (1500, 3, 2003, "three columns (A^T: matrix-core thin form)", "b"),
     (2051, 2055, 300, "128x128 grid + fringe", "all"),
     (4096 + 3, 4096 + 16, 40, "256x128 grid + fringe", "all"),
+    (4097, 4097, 70, "256x128 grid, one row and one column in the tiles' launch", "all"),
+    (4097, 4096, 17, "256x128 grid, one row in the tiles' launch", "all"),
+    (4096, 4097, 5, "256x128 grid, one column in the tiles' launch, K below a stage", "all"),
     (8192, 8, 1000, "eight columns, two per lane", "all"),
     (16, 16384, 777, "sixteen rows, two columns per lane", "all"),
     (2048, 2048, 100, "128x128 grid, K ragged", "all"),
@@ -98,7 +101,8 @@ def test_transposed_operands(M, N, K, plan, same):
             assert np.array_equal(outs[group[0]].view(np.uint32), outs[key].view(np.uint32)), (group[0], key)
 
 
-@pytest.mark.parametrize("M,N,K", [(131, 257, 515), (7, 1029, 301), (1029, 9, 301), (2051, 2053, 64)])
+@pytest.mark.parametrize("M,N,K", [(131, 257, 515), (7, 1029, 301), (1029, 9, 301), (2051, 2053, 64),
+                                   (4097, 4097, 40)])
 def test_transposed_padded_misaligned(M, N, K):
     """Row padding that breaks 16-byte alignment of rows and bases that are
     only 4-byte aligned, beta = 0 with NaN in C (C must not be read)."""

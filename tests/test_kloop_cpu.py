@@ -10,6 +10,12 @@ allocation and inside its operand's region, every stage store must land
 where the k-major layout puts its element, and the word each MFMA operand
 read finds must be the one stored there for that (row, k) or (k, column) --
 the loop's layout is consistent with the operand map the epilogue assumes.
+For the 256 x 128 tile's fringe variant the same replay follows the staged
+words of the extra row and column and every FMA of the fringe sums: each
+multiplies the extra row's k with B's (k, column), or A's (row, k) with the
+extra column's k, for the block's share of columns and rows, and the sums
+of a share cover every k of a stage exactly once; the blocks' shares cover
+the extra row's and column's outputs exactly once.
 """
 
 from __future__ import annotations
@@ -89,6 +95,49 @@ def w_b(t, tid):
     return 4 * b_word(t, k, n)
 
 
+# The fringe variant's per-block shares and per-thread LDS bases (restated
+# from l10_kloop.hip).  Block (i, j) of a tiles_m x tiles_n grid takes
+# columns i cpt .. of its tile for the extra row, cpt = ceil(128 / tiles_m),
+# and rows j rpt .. for the extra column, rpt = ceil(256 / tiles_n); thread
+# tid multiplies k = tid / 32 of each stage for share position tid % 32
+# (positions beyond the share, or beyond the tile, take column / row
+# tid % 32, whose sums are not stored); its staged words are those of
+# k = tid / 32 (%[fpk]) and, for the corner, of k = tid % 16 (%[fst]).
+def f_share(t, tiles_m, tiles_n, i, j):
+    cpt, rpt = -(-t.BN // tiles_m), -(-t.BM // tiles_n)
+    return cpt, rpt, i * cpt, j * rpt
+
+
+def f_cols(t, grid, tid):
+    """(column n, row m) of the tile that thread tid's fringe sums take."""
+    cpt, rpt, n0, m0 = f_share(t, *grid)
+    c = tid % 32
+    n = n0 + c if c < cpt and n0 + c < t.BN else c
+    m = m0 + c if c < rpt and m0 + c < t.BM else c
+    return n, m
+
+
+def f_st(t, grid, tid):
+    return 4 * (tid % 16)
+
+
+def f_pk(t, grid, tid):
+    return 4 * (tid // 32)
+
+
+def f_rb(t, grid, tid):
+    k, (n, _) = tid // 32, f_cols(t, grid, tid)
+    return 2 * t.A_STAGE + ((k // 4) * t.B_GROUP + (k % 4) * t.BN + n) * 4
+
+
+def f_ca(t, grid, tid):
+    k, (_, m) = tid // 32, f_cols(t, grid, tid)
+    return ((k // 4) * t.A_GROUP + (k % 4) * t.BM + m) * 4
+
+
+F_BASES = {"fst": f_st, "frB": f_rb, "fcA": f_ca, "fpk": f_pk}
+
+
 def _wave(t, tid):
     """(K slice, wm, wn, lrow, kg) of a thread."""
     wave, lane = divmod(tid, 64)
@@ -109,10 +158,15 @@ def r_b(t, tid):
 STORE_2ST64 = re.compile(r"ds_write2st64_b32 %\[w([AB])\], v(\d+), v(\d+) offset0:(\d+) offset1:(\d+)$")
 STORE_2 = re.compile(r"ds_write2_b32 %\[w([AB])(1?)\], v(\d+), v(\d+) offset0:(\d+) offset1:(\d+)$")
 STORE_128 = re.compile(r"ds_write_b128 %\[w([AB])\], v\[(\d+):(\d+)\] offset:(\d+)$")
+STORE_F = re.compile(r"ds_write_b32 %\[fst\], v(\d+) offset:(\d+)$")
 
 
 def _pieces(t, tid, line):
-    """(operand, [(register, byte address)]) of one store instruction."""
+    """(operand, [(register, byte address)]) of one store instruction
+    (operand "F": the fringe variant's staged words, in the A buffer)."""
+    m = STORE_F.match(line)
+    if m:
+        return "F", [(int(m.group(1)), f_st(t, None, tid) + int(m.group(2)))]
     m = STORE_2ST64.match(line)
     if m:
         op, r0, r1, o0, o1 = m.group(1), *(int(x) for x in m.groups()[1:])
@@ -135,7 +189,9 @@ def _pieces(t, tid, line):
 
 def _stage_stores(t, st, buf):
     """{byte address: ('A', row, k) or ('B', k, col)} written by one stage's
-    stores from staging set st into buffer buf."""
+    stores from staging set st into buffer buf; for the fringe variant also
+    ('R', k) (the extra row's element of k) and ('C', k) (the extra
+    column's), which every thread of that k stores."""
     written = {}
     a_end = 2 * t.A_STAGE
     base = t.set_base(st)
@@ -148,14 +204,23 @@ def _stage_stores(t, st, buf):
         for h in range(t.B_LOADS):
             for c in range(4):
                 regs[base + 4 * t.A_LOADS + 4 * h + c] = b_elem(t, tid, h, c)
+        if t.FRINGE:
+            regs[G.FA] = ("R", tid % 16)
+            regs[G.FB] = ("C", tid % 16)
         for line in lines:
             op, pieces = _pieces(t, tid, line)
-            lo, hi = (buf * t.A_STAGE, (buf + 1) * t.A_STAGE) if op == "A" else \
-                     (a_end + buf * t.B_STAGE, a_end + (buf + 1) * t.B_STAGE)
+            if op == "F":
+                lo, hi = buf * t.A_STAGE + t.FPAD, buf * t.A_STAGE + t.FPAD + G.FPAD_BYTES
+            else:
+                lo, hi = (buf * t.A_STAGE, (buf + 1) * t.A_STAGE) if op == "A" else \
+                         (a_end + buf * t.B_STAGE, a_end + (buf + 1) * t.B_STAGE)
             for reg, addr in pieces:
                 assert lo <= addr and addr + 4 <= hi, (t.name, tid, line)
-                assert addr not in written, ("store overlap", t.name, tid, line)
-                assert regs[reg][0] == op, (t.name, line)
+                if op == "F":  # the same word from every thread of its k
+                    assert written.get(addr, regs[reg]) == regs[reg], ("store overlap", t.name, tid, line)
+                else:
+                    assert addr not in written, ("store overlap", t.name, tid, line)
+                    assert regs[reg][0] == op, (t.name, line)
                 written[addr] = regs[reg]
     return written
 
@@ -169,8 +234,13 @@ def test_stage_stores_follow_the_layout(name, buf):
     t = TILES[name]
     for st in range(t.DEPTH):
         written = _stage_stores(t, st, buf)
-        assert len(written) == t.BM * t.BK + t.BK * t.BN
+        assert len(written) == t.BM * t.BK + t.BK * t.BN + (2 * t.BK if t.FRINGE else 0)
         for addr, e in written.items():
+            if e[0] in "RC":
+                # the extra row's k at word k of the fringe words, the
+                # extra column's at 16 + k
+                assert addr == buf * t.A_STAGE + t.FPAD + 4 * (e[1] + (16 if e[0] == "C" else 0)), (name, e)
+                continue
             word = a_word(t, e[1], e[2]) if e[0] == "A" else b_word(t, e[1], e[2])
             shift = buf * (t.A_STAGE if e[0] == "A" else t.B_STAGE)
             assert addr == 4 * word + shift, (name, e)
@@ -196,6 +266,75 @@ def test_fragment_reads_find_their_operands(name, buf):
                 # block e of the lane: A row 4 lrow + e, B column 4 lrow + e
                 assert written[a_addr] == ("A", wm * 64 + 4 * lrow + e, k), (s, tid, e)
                 assert written[b_addr] == ("B", k, wn * 64 + 4 * lrow + e), (s, tid, e)
+
+
+F_READ1 = re.compile(r"ds_read_b32 v(\d+), %\[(\w+)\] offset:(\d+)$")
+F_FMAC = re.compile(r"v_fmac_f32 %\[(\w+)\], v(\d+), v(\d+)$")
+# (tiles_m, tiles_n, i, j): grids of the smallest size the variant takes,
+# 4097^3's, and ones whose last shares end inside or beyond the tile
+F_GRIDS = [(4, 8, 0, 0), (4, 8, 3, 7), (16, 32, 0, 0), (16, 32, 15, 31), (16, 32, 5, 17),
+           (5, 9, 4, 8), (32, 32, 31, 30), (7, 11, 6, 10)]
+
+
+def _fringe_products(t, grid, tid, cur, written):
+    """{sum: [(element, element), ...]} the fringe FMAs of one K step on
+    buffer cur compute for thread tid of the block at grid = (tiles_m,
+    tiles_n, i, j), in issue order, replaying the step's fringe reads
+    (registers <- the elements `written` holds at their addresses)."""
+    regs, prods = {}, {}
+    for line in t.k_step(cur):
+        assert not line.startswith("ds_read") or "%[r" in line or F_READ1.match(line), line
+        m = F_READ1.match(line)
+        if m and m.group(2) in F_BASES:
+            regs[int(m.group(1))] = written[F_BASES[m.group(2)](t, grid, tid) + int(m.group(3))]
+            continue
+        m = F_FMAC.match(line)
+        if m:
+            prods.setdefault(m.group(1), []).append((regs[int(m.group(2))], regs[int(m.group(3))]))
+    return prods
+
+
+@pytest.mark.parametrize("name", sorted(n for n in TILES if TILES[n].FRINGE))
+@pytest.mark.parametrize("cur", [0, 1])
+@pytest.mark.parametrize("grid", F_GRIDS, ids=[str(g) for g in F_GRIDS])
+def test_fringe_sums_multiply_matching_k(name, cur, grid):
+    """Per K step, thread tid adds to its row sum the extra row's k times
+    B's (k, n) and to its column sum A's (m, k) times the extra column's k,
+    k = tid / 32 and (n, m) its share position's column and row, and to its
+    corner sum the extra row's and column's k = tid % 16; so the sixteen
+    sums of a share position, and the corner's sixteen, hold every k of the
+    stage exactly once."""
+    t = TILES[name]
+    written = _stage_stores(t, 0, cur)
+    for tid in range(t.THREADS):
+        prods = _fringe_products(t, grid, tid, cur, written)
+        k, ks = tid // 32, tid % 16
+        n, m = f_cols(t, grid, tid)
+        assert prods == {"frow": [(("R", k), ("B", k, n))], "fcol": [(("C", k), ("A", m, k))],
+                         "fcor": [(("R", ks), ("C", ks))]}, (tid, grid)
+
+
+def test_fringe_shares_cover_each_output_once():
+    """Over the blocks of a tile column the extra row's shares are
+    disjoint and cover the tile's 128 columns; over a tile row the extra
+    column's cover its 256 rows (every grid the variant takes: at least 4
+    tile rows and 8 tile columns, so that a share is at most 32 wide); and
+    the stored positions are those below the share's width."""
+    t = next(x for x in G.TILES if x.FRINGE)
+    for tiles_m in range(4, 300):
+        cols = []
+        for i in range(tiles_m):
+            cpt, _, n0, _ = f_share(t, tiles_m, 8, i, 0)
+            assert cpt <= 32
+            cols += [n0 + c for c in range(32) if c < cpt and n0 + c < t.BN]
+        assert sorted(cols) == list(range(t.BN)), tiles_m
+    for tiles_n in range(8, 600):
+        rows = []
+        for j in range(tiles_n):
+            _, rpt, _, m0 = f_share(t, 4, tiles_n, 0, j)
+            assert rpt <= 32
+            rows += [m0 + c for c in range(32) if c < rpt and m0 + c < t.BM]
+        assert sorted(rows) == list(range(t.BM)), tiles_n
 
 
 @pytest.mark.parametrize("name", sorted(TILES))
@@ -225,7 +364,7 @@ def test_transposing_stores_hit_distinct_banks(name):
     banks (the padded groups' purpose)."""
     t = TILES[name]
     for line in t.stage_stores(0, 0):
-        if line.startswith("ds_write_b128"):
+        if line.startswith(("ds_write_b128", "ds_write_b32 %[fst]")):
             continue
         for first in range(0, t.THREADS, 32):
             for piece in (0, 1):
@@ -310,7 +449,8 @@ def _regs(text):
 
 def check_waits(lines, in_flight_loads=(), in_flight_stores=1):
     """Replay the waits of a straight-line run of the loop: every MFMA
-    operand has arrived from its LDS read, every stage store reads a
+    operand (and fringe FMA operand) has arrived from its LDS read, every
+    stage store reads a
     staging register whose load has arrived, no staging register is
     reloaded while a store still reads it, and no LDS access is outstanding
     at a barrier.  The run starts with the prelude's loads and the C++
@@ -345,6 +485,10 @@ def check_waits(lines, in_flight_loads=(), in_flight_stores=1):
             ops = _regs(line.split(",", 1)[1].rsplit(",", 1)[0])
             if any(kind == "r" and ops & regs for kind, regs in lds):
                 bad.append((i, line, "reads a fragment whose LDS read is outstanding"))
+        elif line.startswith("v_fmac"):
+            ops = _regs(line.split(",", 1)[1])
+            if any(kind == "r" and ops & regs for kind, regs in lds):
+                bad.append((i, line, "multiplies a word whose LDS read is outstanding"))
         elif line == "s_barrier":
             if lds:
                 bad.append((i, line, "LDS accesses outstanding at the barrier"))

@@ -20,7 +20,11 @@ restated from l10_kloop.hip, over whole, ragged-K, tiny-K, edge, padded
 and split-K problems.  It also checks that every stage the MFMAs consume
 holds the elements the k-major layout expects: loaded from their own
 addresses for rows and columns inside the tile, and that the loop issues
-exactly the stages it needs plus its prefetch.
+exactly the stages it needs plus its prefetch.  The 256 x 128 tile's fringe
+variant also loads, per stage, one element of the row below the tile and
+one of the column right of it (record counts one row / column longer where
+the block has that fringe): those loads are replayed the same way, over
+grids with and without the extra row and column.
 """
 
 from __future__ import annotations
@@ -84,13 +88,20 @@ class Problem:
     """One work item's view of a problem, restated from k_kloop: the tile
     at (row0, col0), K part [k_lo, k_lo + kp)."""
 
-    def __init__(self, t, M, N, K, lda, ldb, row0, col0, k_lo=0, kp=None, addrs=ADDRS[0]):
+    def __init__(self, t, M, N, K, lda, ldb, row0, col0, k_lo=0, kp=None, addrs=ADDRS[0], grid=None):
         self.t, self.M, self.N, self.K, self.lda, self.ldb = t, M, N, K, lda, ldb
         self.addr_a, self.addr_b = addrs
         self.row0, self.col0, self.k_lo = row0, col0, k_lo
         self.kp = K - k_lo if kp is None else kp
         self.rows = min(M - row0, t.BM)
         self.cols = min(N - col0, t.BN)
+        # fringe variant over a grid of Mm x Nm whole tiles: row M - 1 /
+        # column N - 1 beside it, which every block reads
+        Mm, Nm = grid if grid else (M, N)
+        self.f_row = t.FRINGE and M == Mm + 1
+        self.f_col = t.FRINGE and N == Nm + 1
+        self.a_last = M - 1 - row0 if self.f_row else self.rows - 1
+        self.b_last = N - 1 - col0 if self.f_col else self.cols - 1
         # strides of A (m, k) and B (k, n) as stored, in elements
         self.a_rs, self.a_ks = (1, lda) if t.TA else (lda, 1)
         self.b_ks, self.b_cs = (1, ldb) if t.TB else (ldb, 1)
@@ -107,8 +118,8 @@ class Problem:
         t = self.t
         a_base = self.addr_a + 4 * (self.row0 * self.a_rs + self.k_lo * self.a_ks)
         b_base = self.addr_b + 4 * (self.col0 * self.b_cs + self.k_lo * self.b_ks)
-        a_bytes = 4 * ((self.rows - 1) * self.a_rs + (self.kp - 1) * self.a_ks + 1)
-        b_bytes = 4 * ((self.kp - 1) * self.b_ks + (self.cols - 1) * self.b_cs + 1)
+        a_bytes = 4 * (self.a_last * self.a_rs + (self.kp - 1) * self.a_ks + 1)
+        b_bytes = 4 * ((self.kp - 1) * self.b_ks + self.b_last * self.b_cs + 1)
         a_skip, b_skip = 4 * self.k0 * self.a_ks, 4 * self.k0 * self.b_ks
         sg = {}
         for reg, base, nrec in ((G.RES_A, a_base + a_skip, max(a_bytes - a_skip, 0)),
@@ -131,10 +142,16 @@ class Problem:
         for h in range(t.B_LOADS):
             k, c = b_map(t, tid, h)
             out[("B", h)] = 4 * (k * self.b_ks + c * self.b_cs)
+        if t.FRINGE:
+            # element (a_last, k) of the tile's A and (k, b_last) of its B,
+            # k = tid % 16: row M - 1 / column N - 1 where they exist
+            out[("FA", 0)] = 4 * (self.a_last * self.a_rs + (tid % 16) * self.a_ks)
+            out[("FB", 0)] = 4 * ((tid % 16) * self.b_ks + self.b_last * self.b_cs)
         return out
 
 
 LOAD = re.compile(r"buffer_load_dwordx4 v\[(\d+):(\d+)\], %\[o([AB])(\d)\], s\[(\d+):(\d+)\], (\S+) offen$")
+LOAD_F = re.compile(r"buffer_load_dword v(\d+), %\[fo([ab])\], s\[(\d+):(\d+)\], (\S+) offen$")
 SALU3 = re.compile(r"(s_add_u32|s_addc_u32|s_sub_u32|s_cselect_b32|s_min_u32) (\S+), (\S+), (\S+)$")
 SCMP = re.compile(r"(s_cmp_eq_u32|s_cmp_lg_u32) (\S+), (\S+)$")
 
@@ -172,6 +189,13 @@ def execute(t, sg, ops):
                 assert hi == lo + 3 and lo % 4 == 0, ins
                 base = sg[lo] | ((sg[lo + 1] & 0xFFFF) << 32)
                 events.append((m.group(3), int(m.group(4)), base, sg[lo + 2], val(m.group(7))))
+                continue
+            m = LOAD_F.match(ins)
+            if m:
+                lo, hi = int(m.group(3)), int(m.group(4))
+                assert hi == lo + 3 and lo % 4 == 0, ins
+                base = sg[lo] | ((sg[lo + 1] & 0xFFFF) << 32)
+                events.append(("F" + m.group(2).upper(), 0, base, sg[lo + 2], val(m.group(5))))
                 continue
             m = SALU3.match(ins)
             if m:
@@ -213,16 +237,16 @@ def replay(p: Problem):
     sg, ops = p.initial_state()
     offs = p.offsets()
     events = execute(t, sg, ops)
-    per_stage = t.A_LOADS + t.B_LOADS
+    per_stage = t.A_LOADS + t.B_LOADS + (2 if t.FRINGE else 0)
     # stages 1 .. stages - 1 are requested once each, and DEPTH + 1 past the
     # last (every step requests the stage DEPTH + 1 ahead of it)
     assert len(events) == per_stage * (p.stages + t.DEPTH), (len(events), p.stages)
-    comp = 4 * np.arange(4)
     for i, (op, h, base, nrec, soff) in enumerate(events):
         stage = 1 + i // per_stage
+        comp = 4 * np.arange(1 if op in ("FA", "FB") else 4)
         off = offs[(op, h)][:, None] + comp[None, :]          # (threads, 4) bytes
         addr = base + soff + off
-        lo, hi = (p.addr_a, p.a_end) if op == "A" else (p.addr_b, p.b_end)
+        lo, hi = (p.addr_a, p.a_end) if op in ("A", "FA") else (p.addr_b, p.b_end)
         inside = (addr >= lo) & (addr + 4 <= hi)
         for performed in (off + 4 <= nrec, soff + off + 4 <= nrec):
             bad = performed & ~inside
@@ -232,6 +256,22 @@ def replay(p: Problem):
         # consumed stage: in-tile elements must come from their own address
         tid = np.arange(t.THREADS)
         kbase = p.k_lo + p.k0 + (stage - 1) * t.BK
+        if op in ("FA", "FB"):
+            # where the grid has the fringe, the element of k = tid % 16 of
+            # row M - 1 / column N - 1, for every k of the stage below K
+            kk = (tid % 16)[:, None]
+            if op == "FA":
+                want = p.addr_a + 4 * ((p.M - 1) * p.a_rs + (kbase + kk) * p.a_ks)
+                has = p.f_row
+            else:
+                want = p.addr_b + 4 * ((kbase + kk) * p.b_ks + (p.N - 1) * p.b_cs)
+                has = p.f_col
+            if has:
+                assert (kbase + kk < p.k_lo + p.kp).all()
+                for performed in (off + 4 <= nrec, soff + off + 4 <= nrec):
+                    assert performed.all(), (t.name, op, stage, "fringe element not loaded")
+                assert (addr == want).all(), (t.name, op, stage, "wrong fringe element")
+            continue
         if op == "A":
             r, k = a_map(t, tid, h)
             rr = r[:, None] + (comp[None, :] // 4 if t.TA else 0)
@@ -275,9 +315,35 @@ def _problems(t):
     return out
 
 
+def _fringe_problems(t):
+    """(Mm, Nm, M, N, K, lda, ldb) cases for the fringe variant: whole tiles
+    over the first Mm x Nm of C (at least 4 x 8 of them), and one more row
+    and / or column."""
+    BM, BN, BK = t.BM, t.BN, t.BK
+    out = []
+    for Mm, Nm, K in [(4 * BM, 8 * BN, 4 * BK), (5 * BM, 8 * BN, 3 * BK + 5), (4 * BM, 9 * BN, 1),
+                      (4 * BM, 8 * BN, BK), (4 * BM, 8 * BN, BK + 1), (4 * BM, 8 * BN, 5 * BK + 15)]:
+        for dm, dn in ((1, 1), (1, 0), (0, 1)):
+            M, N = Mm + dm, Nm + dn
+            ld_a = M if t.TA else K
+            ld_b = K if t.TB else N
+            out.append((Mm, Nm, M, N, K, ld_a, ld_b))
+            out.append((Mm, Nm, M, N, K, ld_a + 7, ld_b + 5))
+    return out
+
+
 @pytest.mark.parametrize("name", sorted(TILES))
 def test_global_loads_stay_inside_their_operands(name):
     t = TILES[name]
+    if t.FRINGE:
+        # the grid's tiles only (the kernel's grid): its corners and an
+        # inner one, every block reading row M - 1 / column N - 1
+        for Mm, Nm, M, N, K, lda, ldb in _fringe_problems(t):
+            lm, ln = Mm - t.BM, Nm - t.BN
+            for row0, col0 in [(0, 0), (0, ln), (lm, 0), (lm, ln), (t.BM, 2 * t.BN)]:
+                for addrs in ADDRS:
+                    replay(Problem(t, M, N, K, lda, ldb, row0, col0, 0, K, addrs, grid=(Mm, Nm)))
+        return
     for M, N, K, lda, ldb, ks in _problems(t):
         parts = [(0, K)] if ks is None else [(lo, min(ks, K - lo)) for lo in range(0, K, ks)]
         for row0 in range(0, M, t.BM):
