@@ -180,10 +180,13 @@ int hip_sgemm_ex_noalloc(int op_a, int op_b, int M, int N, int K, float alpha,
  *     kernel adds in order; otherwise one of three whole-tile kernels
  *     whose K loop is hand-scheduled assembly (256 x 128, 128 x 128, and
  *     64 x 64 over four K-slice wavefronts), with partial edge tiles, or
- *     with whole tiles plus the thin kernels on a fringe of at most 16
- *     rows / columns.  A call enqueues up to three kernels on the stream,
- *     over disjoint parts of C ([GEMM2] size-sweep section: a library is
- *     many kernels picked by shape)
+ *     with whole tiles plus a fringe of at most 16 rows / columns: one row
+ *     and / or one column beside a grid of at least 4 x 8 tiles of
+ *     256 x 128 is summed by the tiles' own blocks in the same launch
+ *     (each fringe output by one block, sixteen partial sums added in k
+ *     order), a wider fringe by the thin kernels.  A call enqueues up to
+ *     three kernels on the stream, over disjoint parts of C ([GEMM2]
+ *     size-sweep section: a library is many kernels picked by shape)
  */
 int hip_sgemm_level(int level, int M, int N, int K, float alpha,
                     const float *A, int lda,
@@ -276,7 +279,13 @@ int hip_sgemm_launch_shape(int level, int M, int N, int K,
  * alpha == 0 is the SCALE plan whatever K), decided on the host from M, N, K
  * alone, without launching anything:
  *   *plan             one of the SGEMM_PLAN_* ids below;
- *   *launches         kernels one call enqueues on its stream;
+ *   *launches         kernels one call enqueues on its stream (for
+ *                     SGEMM_PLAN_TILES_FRINGE as hip_sgemm takes the shape
+ *                     with packed operands, lda = K and ldb = N for
+ *                     row-major storage: leading dimensions large enough to
+ *                     put an offset at or past 2^31 bytes move a one-row /
+ *                     one-column fringe to the thin kernels, one launch
+ *                     per side);
  *   *workspace_bytes  device memory the call takes for split K's partial
  *                     sums (splits x M x N floats; 0 for every other plan):
  *                     the only plan that allocates.  hip_sgemm and
@@ -292,7 +301,7 @@ int hip_sgemm_launch_shape(int level, int M, int N, int K,
 #define SGEMM_PLAN_FEW_ROWS 2     /* M <= 16: thin kernel over rows of C */
 #define SGEMM_PLAN_FEW_COLS 3     /* N <= 16: thin kernel over columns of C */
 #define SGEMM_PLAN_TILES 4        /* one grid of matrix-core tiles */
-#define SGEMM_PLAN_TILES_FRINGE 5 /* whole tiles + thin kernels on <= 16-wide fringes */
+#define SGEMM_PLAN_TILES_FRINGE 5 /* whole tiles + a <= 16-wide fringe (see level 10) */
 #define SGEMM_PLAN_SPLIT_K 6      /* tiles over K slices + an in-order reduction */
 #define SGEMM_PLAN_THIN_PANELS 7  /* small problems: 16-row panels of C */
 
