@@ -141,3 +141,31 @@ def test_transposed_a_beyond_2_31_elements():
     # beta = 0 with NaN in C: C must not be read
     _check(call, A_rows, B_h, None, buf, rows, N, alpha, beta, "A^T")
     del At, B, buf
+
+
+@pytest.mark.parametrize("lda,launches", [(131000, 1), (131080, 3)])
+def test_fringe_beside_the_tiles_near_2_31_bytes(lda, launches):
+    """4097 x 4097 x 64 with A's rows lda apart: every block of the
+    one-launch plan reads row M - 1 of A, 4096 lda floats past its first
+    row.  At lda = 131000 that is just below 2^31 bytes and the one launch
+    runs; at 131080 it is past, and the call falls back to the grid plus the
+    thin kernels (three launches).  Either way row M - 1 and column N - 1
+    must match the reference."""
+    import torch
+    M = N = 4097
+    K, alpha, beta = 64, 0.5, 3.0
+    assert (4096 * lda + K + 32) * 4 < 2 ** 31 if launches == 1 else 4096 * lda * 4 >= 2 ** 31
+    print(f"[large] fringe beside the tiles, lda {lda} ({M * lda:.3g} elements)", flush=True)
+    A = _uniform(M, lda, 41)
+    B = _uniform(K, N, 42)
+    C0 = _padded_c(M, N, 43)
+    buf = C0.clone()
+    rows = _sample_rows(M)
+    A_rows = A[rows, :K].cpu().numpy()
+    B_h = B.cpu().numpy()
+    C0_rows = C0[rows, :N].cpu().numpy()
+
+    def call():
+        return sgemm.hip_sgemm(M, N, K, alpha, A, lda, B, N, beta, buf, N + PAD)
+    _check(call, A_rows, B_h, C0_rows, buf, rows, N, alpha, beta, f"lda {lda}")
+    del A, B, C0, buf
