@@ -50,14 +50,13 @@ def sources():
 KLOOP_SOURCE = os.path.join(CSRC, "l10_kloop.hip")
 FIRST_STAGING = 80
 # last staging register per block tile (DEPTH sets of a stage's A and B
-# float4s from v80, as gen_kloop.py lays them out); the 256 x 128 tile's
-# fringe variant also stages one word of the extra row and one of the
-# extra column (v92, v93)
+# float4s from v80, as gen_kloop.py lays them out); a fringe variant also
+# stages one word of the extra row and one of the extra column per set,
+# right after them
 LAST_STAGING = {256: 80 + 12 - 1, 128: 80 + 2 * 16 - 1, 64: 80 + 2 * 32 - 1}
-LAST_STAGING_FRINGE = 93
-# 3 tiles x 4 orientations x (plain, split K), and the fringe variant of the
-# 256 x 128 tile in 4 orientations
-KLOOP_KERNELS = 28
+FRINGE_SETS = {256: 1, 128: 2, 64: 2}
+# 3 tiles x 4 orientations x (plain, split K, fringe variant)
+KLOOP_KERNELS = 36
 
 
 def kloop_kernels(asm: str):
@@ -83,7 +82,10 @@ def check_kloop_staging(asm: str) -> list:
     for name, lines in kernels:
         # KTile<BM, BN, BK, KS, TA, TB, FR> as mangled
         m = re.search(r"KTileILi(\d+)ELi\d+ELi\d+ELi\d+ELb[01]ELb[01]ELb([01])E", name)
-        last = (LAST_STAGING_FRINGE if m.group(2) == "1" else LAST_STAGING.get(int(m.group(1)))) if m else None
+        bm = int(m.group(1)) if m else None
+        last = LAST_STAGING.get(bm) if m else None
+        if m and last is not None and m.group(2) == "1":
+            last += 2 * FRINGE_SETS[bm]
         if last is None or "s_nop 4" not in lines:
             bad.append((name, "no prelude found"))
             continue

@@ -20,16 +20,16 @@ transposed A and a row-major B are stored whole):
             block runs per CU: two stages of global prefetch in two
             register sets.
 
-The 256 x 128 tile also has a variant for a grid with one more row of C
-below it and / or one more column to its right (M = 256 a + 1, N = 128 b + 1):
-every block holds, over its K loop, all of A for its 256 rows and all of B
-for its 128 columns, so it can also sum the extra row of A against up to 32
-of its columns and up to 32 of its rows against the extra column of B (a
-share of them per block, so that each block adds only a few vector-ALU FMAs
-per stage: 8 and 8 at 4097^3), and the one corner element.  The 16 values
-of the extra row and column per stage travel like the stage itself (loaded
-with it, stored after it into 32 words after the A stage), so that nothing
-of A or B is read a second time.
+Each tile also has a fringe variant, for a grid with one more row of C
+below it and / or one more column to its right (M = BM a + 1, N = BN b + 1):
+every block holds, over its K loop, all of A for its BM rows and all of B
+for its BN columns, so it can also sum the extra row of A against a share
+of its columns and a share of its rows against the extra column of B (at
+most THREADS / BK of each per block, so that each block adds only a few
+vector-ALU FMAs per stage: 8 and 8 at 4097^3 on 256 x 128), and the one
+corner element.  The BK values of the extra row and column per stage travel
+like the stage itself (loaded with it, stored after it into 2 BK words
+after the A stage), so that nothing of A or B is read a second time.
 
 Stage 0 is the first K % 16 k (a whole stage when K % 16 == 0), zero-padded,
 and is put into LDS buffer 0 by the kernel's C++ part; every stage the
@@ -47,10 +47,11 @@ Register map (the kernels pin these with asm operand constraints/clobbers):
   v[72:79]  fragment set O, the same for the alternate step
   v[80:..]  global-load staging: per set, the A float4s then the B float4s
             of one stage (12 words for 256 x 128, 16 for 128 x 128)
-  fringe variant: v92 / v93 stage the extra row's / column's value of the
-            thread's k (tid % 16) like the stage; v[94:99] hold the LDS
-            words the fringe FMAs read; its three sums (row, column, corner)
-            are compiler-placed operands
+  fringe variant: after the staging sets, one register pair per set
+            stages the extra row's and column's value of the thread's k
+            (tid % BK) like the stage (v92 / v93 for 256 x 128); the next
+            six hold the LDS words the fringe FMAs read; its three sums
+            (row, column, corner) are compiler-placed operands
 
 One K step (16 deep) per wavefront: four MFMA steps s = 0..3 of 16 MFMAs,
 step s reading k = 4 s + lane / 16.  Step s runs on one fragment set while
@@ -75,9 +76,6 @@ import os
 
 FE, FO = 64, 72                # fragment sets
 STAGING = 80                   # first staging register
-FA, FB = 92, 93                # fringe variant: staged values of the extra row / column
-FT = 94                        # fringe variant: v[FT : FT + 6], LDS words for its FMAs
-FPAD_BYTES = 128               # fringe variant: 16 + 16 words after each A stage
 RES_A, RES_B = 60, 64          # buffer resources of A and B: s[60:63], s[64:67]
 
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "l10_kloop.inc")
@@ -98,7 +96,6 @@ class Tile:
         self.BM, self.BN, self.BK = bm, bn, bk
         self.WAVES_M, self.WAVES_N, self.KSLICES, self.DEPTH = waves_m, waves_n, kslices, depth
         self.TA, self.TB, self.FRINGE = ta, tb, fringe
-        assert not fringe or (bm, bn, bk, kslices, depth) == (256, 128, 16, 1, 1)
         self.THREADS = 64 * waves_m * waves_n * kslices
         self.GROUPS = bk // 4                         # four-k groups (MFMA steps) per stage
         self.STEPS = self.GROUPS // kslices           # MFMA steps per stage per wavefront
@@ -112,17 +109,26 @@ class Tile:
         self.A_GROUP = 4 * bm + (0 if ta else pad)
         self.B_GROUP = 4 * bn + (pad if tb else 0)
         # bytes per stage, a whole number of 256; the fringe variant's words
-        # (extra row's k then extra column's k) at FPAD after the groups
+        # (BK of the extra row, then BK of the extra column) at FPAD after
+        # the groups
         self.FPAD = self.GROUPS * self.A_GROUP * 4
-        self.A_STAGE = _round256(self.FPAD + (FPAD_BYTES if fringe else 0))
+        self.A_STAGE = _round256(self.FPAD + (8 * bk if fringe else 0))
         self.B_STAGE = _round256(self.GROUPS * self.B_GROUP * 4)
         self.A_LOADS = bm * bk // 4 // self.THREADS   # A float4s per thread per stage
         self.B_LOADS = bk * bn // 4 // self.THREADS   # B float4s per thread per stage
         self.SET = 4 * (self.A_LOADS + self.B_LOADS)  # staging words per set
+        # buffer loads per stage (the fringe variant: one word of the extra
+        # row and one of the extra column per thread)
+        self.LOADS = self.A_LOADS + self.B_LOADS + (2 if fringe else 0)
+        # fringe variant: positions of its share per k (thread tid takes k =
+        # tid / FP, position tid % FP), registers after the staging sets
+        self.FP = self.THREADS // bk
+        self.F_STAGE = STAGING + depth * self.SET
+        self.FT = self.F_STAGE + 2 * depth
         self.LDS = 2 * self.A_STAGE + 2 * self.B_STAGE
         assert bm == 64 * waves_m and bn == 64 * waves_n and self.STEPS >= 2
         assert self.A_LOADS * self.THREADS * 4 == bm * bk and self.B_LOADS * self.THREADS * 4 == bk * bn
-        assert STAGING + depth * self.SET <= (FA if fringe else 256)
+        assert self.last_vgpr() < 256 and self.THREADS % bk == 0
 
     @property
     def name(self) -> str:
@@ -130,11 +136,16 @@ class Tile:
             ("_F" if self.FRINGE else "")
 
     def last_vgpr(self) -> int:
-        return FT + 5 if self.FRINGE else STAGING + self.DEPTH * self.SET - 1
+        return self.FT + 5 if self.FRINGE else STAGING + self.DEPTH * self.SET - 1
 
     def last_staging(self) -> int:
         """Last register a load of the prelude leaves in flight."""
-        return FB if self.FRINGE else STAGING + self.DEPTH * self.SET - 1
+        return self.FT - 1 if self.FRINGE else STAGING + self.DEPTH * self.SET - 1
+
+    def fa(self, st: int) -> int:
+        """Fringe variant: staging register of the extra row's word (set st);
+        the extra column's is the next."""
+        return self.F_STAGE + 2 * st
 
     # -- per-thread element maps (restated by the kernel and the tests) ------
     def a_per(self) -> int:
@@ -170,10 +181,10 @@ class Tile:
         out += [f"buffer_load_dwordx4 v[{rb + 4*h}:{rb + 4*h + 3}], %[oB{h}], s[{RES_B}:{RES_B + 3}], 0 offen"
                 for h in range(self.B_LOADS)]
         if self.FRINGE:
-            # the extra row's element (BM, k) and the extra column's (k, BN)
-            # of the same stage, k = tid % 16, through the same resources
-            out += [f"buffer_load_dword v{FA}, %[foa], s[{RES_A}:{RES_A + 3}], 0 offen",
-                    f"buffer_load_dword v{FB}, %[fob], s[{RES_B}:{RES_B + 3}], 0 offen"]
+            # the extra row's element of k and the extra column's, same
+            # stage, k = tid % BK, through the same resources
+            out += [f"buffer_load_dword v{self.fa(st)}, %[foa], s[{RES_A}:{RES_A + 3}], 0 offen",
+                    f"buffer_load_dword v{self.fa(st) + 1}, %[fob], s[{RES_B}:{RES_B + 3}], 0 offen"]
         return out
 
     # The next stage of each operand: the resource's base moves one stage on
@@ -250,40 +261,39 @@ class Tile:
                 out.append(f"ds_write_b128 %[wB], v[{rb + 4*h}:{rb + 4*h + 3}] "
                            f"offset:{buf * self.B_STAGE + h * (dk // 4) * self.B_GROUP * 4}")
         if self.FRINGE:
-            # word k of the extra row, word 16 + k of the extra column
-            # (%[fst] = 4 (tid % 16); the 32 threads of each k store the
-            # same value)
+            # word k of the extra row, word BK + k of the extra column
+            # (%[fst] = 4 (tid % BK); the THREADS / BK threads of each k store
+            # the same value)
             pad = buf * self.A_STAGE + self.FPAD
-            out += [f"ds_write_b32 %[fst], v{FA} offset:{pad}", f"ds_write_b32 %[fst], v{FB} offset:{pad + 64}"]
+            out += [f"ds_write_b32 %[fst], v{self.fa(st)} offset:{pad}",
+                    f"ds_write_b32 %[fst], v{self.fa(st) + 1} offset:{pad + 4 * self.BK}"]
         return out
 
-    def fringe_work(self, ss: int, cur: int) -> dict[int, list[str]]:
-        """The fringe variant's reads and FMAs in MFMA step ss of a stage on
-        LDS buffer cur, by the MFMA slot they follow: the reads in step 0,
-        the FMAs in step 1 (which starts with lgkmcnt(0)), long before step
-        3's barrier releases the buffer.  Per thread, with k = tid / 32 of
-        the stage:
+    def fringe_reads(self, cur: int) -> list[str]:
+        """The fringe variant's LDS reads of one stage on buffer cur.  Per
+        thread, with k = tid / FP of the stage:
           row sum (%[frow]): B's word (k, n) of one of the block's columns
             (%[frB]) times the extra row's word k (%[fpk]);
           column sum (%[fcol]): A's word (m, k) of one of the block's rows
-            (%[fcA]) times the extra column's word k (%[fpk], 64 bytes on);
+            (%[fcA]) times the extra column's word k (%[fpk], 4 BK bytes on);
           corner (%[fcor]): the extra row's and column's words of
-            k = tid % 16 (%[fst]).
+            k = tid % BK (%[fst]).
         The kernel sets which column and row (n, m) a thread takes."""
         a0 = cur * self.A_STAGE
         pad = a0 + self.FPAD
-        t = [f"v{FT + i}" for i in range(6)]
-        if ss == 0:
-            return {6: [f"ds_read_b32 {t[0]}, %[frB] offset:{cur * self.B_STAGE}",
-                        f"ds_read_b32 {t[1]}, %[fpk] offset:{pad}",
-                        f"ds_read_b32 {t[2]}, %[fcA] offset:{a0}",
-                        f"ds_read_b32 {t[3]}, %[fpk] offset:{pad + 64}",
-                        f"ds_read_b32 {t[4]}, %[fst] offset:{pad}",
-                        f"ds_read_b32 {t[5]}, %[fst] offset:{pad + 64}"]}
-        if ss == 1:
-            return {2: [f"v_fmac_f32 %[frow], {t[1]}, {t[0]}", f"v_fmac_f32 %[fcol], {t[3]}, {t[2]}",
-                        f"v_fmac_f32 %[fcor], {t[4]}, {t[5]}"]}
-        return {}
+        col = 4 * self.BK
+        t = [f"v{self.FT + i}" for i in range(6)]
+        return [f"ds_read_b32 {t[0]}, %[frB] offset:{cur * self.B_STAGE}",
+                f"ds_read_b32 {t[1]}, %[fpk] offset:{pad}",
+                f"ds_read_b32 {t[2]}, %[fcA] offset:{a0}",
+                f"ds_read_b32 {t[3]}, %[fpk] offset:{pad + col}",
+                f"ds_read_b32 {t[4]}, %[fst] offset:{pad}",
+                f"ds_read_b32 {t[5]}, %[fst] offset:{pad + col}"]
+
+    def fringe_fmas(self) -> list[str]:
+        t = [f"v{self.FT + i}" for i in range(6)]
+        return [f"v_fmac_f32 %[frow], {t[1]}, {t[0]}", f"v_fmac_f32 %[fcol], {t[3]}, {t[2]}",
+                f"v_fmac_f32 %[fcor], {t[4]}, {t[5]}"]
 
     # -- the loop ------------------------------------------------------------
     def k_step(self, cur: int) -> list[str]:
@@ -294,7 +304,7 @@ class Tile:
         it)."""
         nxt = 1 - cur
         st = nxt % self.DEPTH
-        per_stage = self.A_LOADS + self.B_LOADS
+        per_stage = self.LOADS
         sets = (FE, FO)
         stores = self.stage_stores(st, nxt)
         loads = self.loads(st)
@@ -341,8 +351,26 @@ class Tile:
                     extra.setdefault(1 + i, []).append(ins)
                 extra.setdefault(len(loads) + 1, []).extend(self.ADVANCE)
             if self.FRINGE:
-                for slot, ins in self.fringe_work(ss, cur).items():
-                    extra.setdefault(slot, []).extend(ins)
+                # the fringe's reads of this stage and, a step later, its
+                # FMAs.  With one staging set: reads after MFMA 6 of the first
+                # step, FMAs after MFMA 2 of the second (the other wavefronts
+                # of the SIMD keep the matrix pipe busy).  With two: reads
+                # two per slot after the second step's stores (slots 13-15),
+                # FMAs one per slot after the third step's loads (12-14), so
+                # that a wavefront alone on its SIMD issues few of them
+                # between two MFMAs; either way they complete at the next
+                # step's lgkmcnt(0), before the last step's barrier.
+                reads, fmas = self.fringe_reads(cur), self.fringe_fmas()
+                if not spread and ss == 0:
+                    extra.setdefault(6, []).extend(reads)
+                if not spread and ss == 1:
+                    extra.setdefault(2, []).extend(fmas)
+                if spread and ss == 1:
+                    for i, ins in enumerate(reads):
+                        extra.setdefault(13 + i // 2, []).append(ins)
+                if spread and ss == 2:
+                    for i, ins in enumerate(fmas):
+                        extra.setdefault(12 + i, []).append(ins)
             out.append(f"s_waitcnt lgkmcnt({min(in_step0, 15)})" if spread and ss == 1
                        else "s_waitcnt lgkmcnt(0)")
             last = ss == self.STEPS - 1
@@ -393,7 +421,7 @@ class Tile:
 # (BM, BN, BK, WAVES_M, WAVES_N, KSLICES, DEPTH)
 SHAPES = [(256, 128, 16, 4, 2, 1, 1), (128, 128, 16, 2, 2, 1, 2), (64, 64, 64, 1, 1, 4, 2)]
 TILES = [Tile(*shape, ta, tb) for shape in SHAPES for ta in (False, True) for tb in (False, True)]
-TILES += [Tile(*SHAPES[0], ta, tb, fringe=True) for ta in (False, True) for tb in (False, True)]
+TILES += [Tile(*shape, ta, tb, fringe=True) for shape in SHAPES for ta in (False, True) for tb in (False, True)]
 
 
 def render() -> str:
@@ -413,9 +441,11 @@ def render() -> str:
         io = ", ".join(f'"+{{v[{STAGING + 4*q}:{STAGING + 4*q + 3}]}}"(stg[{q}])' for q in quads)
         clobbered = list(range(FE, STAGING))
         if t.FRINGE:
-            out += f', "=&{{v{FA}}}"(fa), "=&{{v{FB}}}"(fb)'
-            io += f', "+{{v{FA}}}"(fa), "+{{v{FB}}}"(fb), [frow] "+v"(frow), [fcol] "+v"(fcol), [fcor] "+v"(fcor)'
-            clobbered += list(range(FT, FT + 6))
+            for st in range(t.DEPTH):
+                out += f', "=&{{v{t.fa(st)}}}"(fa[{st}]), "=&{{v{t.fa(st) + 1}}}"(fb[{st}])'
+                io += f', "+{{v{t.fa(st)}}}"(fa[{st}]), "+{{v{t.fa(st) + 1}}}"(fb[{st}])'
+            io += ', [frow] "+v"(frow), [fcol] "+v"(fcol), [fcor] "+v"(fcor)'
+            clobbered += list(range(t.FT, t.FT + 6))
         lines.append(f"#define SGEMM_KLOOP_STAGING_OUT_{t.name} {out}")
         lines.append(f"#define SGEMM_KLOOP_STAGING_IO_{t.name} {io}")
         regs = ", ".join(f'"v{r}"' for r in clobbered)

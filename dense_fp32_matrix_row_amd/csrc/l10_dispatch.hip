@@ -13,11 +13,12 @@
 //     shallow grid of 64-128 of them: split K (l10_splitk.hip);
 //   - otherwise one of the three assembly-loop tiles of l10_kloop.hip
 //     (256 x 128, 128 x 128, 64 x 64), the one that leaves the busiest CU
-//     the least work, with partial edge tiles, or whole tiles plus the thin
-//     kernels on a fringe of <= 16 rows / columns; a fringe of one row and /
-//     or one column beside 256 x 128 tiles (4097^3: the 512 whole tiles of
-//     4096^3 and two one-element strips) is summed by the tiles' own blocks
-//     from the operands they hold in LDS, in the same launch;
+//     the least work, with partial edge tiles, or with whole tiles and a
+//     fringe: one row and / or one column (4097^3: the 512 whole tiles of
+//     4096^3 and two one-element strips; 1025^3: 256 tiles of 64 x 64) is
+//     summed by the tiles' own blocks from the operands they hold in LDS,
+//     in the same launch; up to 16 beside the two large tiles by the thin
+//     kernels;
 //   - small problems (fewer than 128 tiles of 64 x 64): the thin
 //     matrix-core kernel over 16-row panels of C.
 // Every output element is computed by exactly one tile or thin kernel (or,
@@ -46,6 +47,19 @@ constexpr int kCUs = 256;
 // by tests/test_autotune_cpu.py: every swept shape must still get the plan
 // and tile configuration recorded for it, and that configuration must be
 // within the sweep's tolerance of the fastest one measured.
+// A packed problem of this shape (lda = K, ldb = N, row-major), for the
+// decisions made from M, N and K alone.
+Problem packed(int M, int N, int K) {
+  Problem p{};
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.lda = K;
+  p.ldb = N;
+  p.ldc = N;
+  return p;
+}
+
 Decomp decompose(int M, int N, int K) {
   if (M <= kThin) return {Plan::kFewRows, Shape::kSmall, M, N, K};
   if (N <= kThin) return {Plan::kFewCols, Shape::kSmall, M, N, K};
@@ -95,11 +109,13 @@ Decomp decompose(int M, int N, int K) {
   //    ceil(tiles / CUs) x tile area / efficiency, the efficiency measured
   //    for that tile at that many tiles per CU (256 x 128: 0.955 from two
   //    per CU, 0.85 with one; 128 x 128: 0.935 / 0.895; 64 x 64, 64-deep
-  //    stages over four K-slice wavefronts: 0.89).  The 256 x 128 and
-  //    128 x 128 tiles count whole tiles only when M and N miss a multiple
-  //    by at most 16 (the rest goes to the thin kernels: 4097^3 on 512 tiles
-  //    of 256 x 128 and two one-element strips, 143-144 against 114 for the
-  //    vendor BLAS), and partial edge tiles otherwise.  Picks on the
+  //    stages over four K-slice wavefronts: 0.89).  A tile counts whole
+  //    tiles only where M and N miss a multiple by one (the tiles' own
+  //    blocks sum that row and column, where the grid has enough tiles for
+  //    their shares: 4097^3 on 512 tiles of 256 x 128 and two one-element
+  //    strips, 148 against 121 for the vendor BLAS), or, for the 256 x 128
+  //    and 128 x 128 tiles, by at most 16 (the rest goes to the thin
+  //    kernels), and partial edge tiles otherwise.  Picks on the
   //    sweeps: 256 x 128 at 4096^3 (150-152), 4000^3 (145 against 137 for
   //    64 x 64), 5000 x 3000 x 2000 (133.5); 128 x 128 at 2048^3 (140-141
   //    against 132.6), 1792^3 (109 against 100), 2048 x 4096, 1024 x 4096 x
@@ -122,8 +138,20 @@ Decomp decompose(int M, int N, int K) {
     double best_cost = 0.0;
     for (const Candidate& c : candidates) {
       const int mr = M % c.bm, nr = N % c.bn;
-      const bool fringe = c.shape != Shape::kSmallDeep && mr <= kThin && nr <= kThin &&
-                          M - mr > 0 && N - nr > 0;
+      // one row and / or column that the tiles' blocks sum (enough tiles
+      // for their shares), or up to 16 beside the large tiles for the thin
+      // kernels.  The 64 x 64 tile's alternative is a grid with partial
+      // edge tiles: its fringe variant only where that leaves the busiest
+      // CU fewer tiles (1025^3: 256 tiles against 289, 40.5 -> 28.0 us; at
+      // the same count, 1537^3: 576 against 625, the edges measured 79 us
+      // against 88)
+      bool fused = mr <= 1 && nr <= 1 && (mr || nr) &&
+                   tiles_fringe_fits(c.shape, packed(M, N, K), M - mr, N - nr);
+      if (fused && c.shape == Shape::kSmallDeep)
+        fused = ceil_div(int64_t(M / c.bm) * (N / c.bn), kCUs) <
+                ceil_div(ceil_div(M, c.bm) * ceil_div(N, c.bn), kCUs);
+      const bool fringe = fused || (c.shape != Shape::kSmallDeep && mr <= kThin && nr <= kThin &&
+                                    M - mr > 0 && N - nr > 0);
       const int Mm = fringe ? M - mr : M, Nm = fringe ? N - nr : N;
       const int64_t per_cu = ceil_div(ceil_div(Mm, c.bm) * ceil_div(Nm, c.bn), kCUs);
       const double cost = double(per_cu) * c.bm * c.bn / (per_cu > 1 ? c.eff_more : c.eff_one);
@@ -151,25 +179,16 @@ Decomp decompose(int M, int N, int K) {
   return {Plan::kThinPanels, Shape::kSmallSliced, M, N, K};
 }
 
-// A fringe of at most one row and one column beside 256 x 128 tiles runs in
-// the tiles' launch (l10_kloop.hip's fringe variant) where its offsets fit;
-// the plan query assumes packed operands (lda = K, ldb = N as op(A), op(B)
-// are stored row-major, M and K when transposed), the launch checks the
-// caller's and falls back to the three launches.
+// A fringe of at most one row and one column runs in the tiles' launch
+// (l10_kloop.hip's fringe variant) where its offsets fit; the plan query
+// assumes packed operands (lda = K, ldb = N for row-major storage), the
+// launch checks the caller's and falls back to the grid plus the thin
+// kernels.
 bool one_launch_fringe(const Decomp& d, const Problem& p) {
-  return d.plan == Plan::kTilesWithFringe && d.shape == Shape::kHuge && tiles_fringe_fits(p, d.Mm, d.Nm);
+  return d.plan == Plan::kTilesWithFringe && tiles_fringe_fits(d.shape, p, d.Mm, d.Nm);
 }
 
-bool one_launch_fringe(const Decomp& d, int M, int N, int K) {
-  Problem p{};
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.lda = K;
-  p.ldb = N;
-  p.ldc = N;
-  return one_launch_fringe(d, p);
-}
+bool one_launch_fringe(const Decomp& d, int M, int N, int K) { return one_launch_fringe(d, packed(M, N, K)); }
 
 Geometry geometry10(int M, int N, int K) {
   const Decomp d = decompose(M, N, K);
@@ -213,7 +232,7 @@ hipError_t launch10_with(const Problem& p, hipStream_t s, Workspace w) {
     case Plan::kThinPanels: return launch_thin_panels(p, s);
     case Plan::kTilesWithFringe: break;
   }
-  if (one_launch_fringe(d, p)) return launch_tiles_fringe(p, d.Mm, d.Nm, s);
+  if (one_launch_fringe(d, p)) return launch_tiles_fringe(d.shape, p, d.Mm, d.Nm, s);
   Problem grid = p;
   grid.M = d.Mm;
   grid.N = d.Nm;

@@ -60,8 +60,8 @@ constexpr int round256(int n) { return (n + 255) / 256 * 256; }
 // tile runs 64 tiles per XCD at once; 4 x 16 of them (A 1024 rows, B 2048
 // columns) measured the fewest fabric fetches at 4096^3: 605 MB per call
 // against 741 MB for 8 x 8 and 739 MB for 2 x 32, at the same time.
-// FR: the 256 x 128 tile's fringe variant (one more row of C below the
-// grid and / or one more column to its right, computed beside the tiles).
+// FR: the fringe variant (one more row of C below the grid and / or one
+// more column to its right, summed by the tiles' own blocks).
 template <int BM_, int BN_, int BK_, int KS_, bool TA_, bool TB_, bool FR_ = false>
 struct KTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, KS = KS_, GROUP_M = BM == 256 ? 4 : 8;
@@ -72,10 +72,13 @@ struct KTile {
   static constexpr int PAD = BK == 16 ? 8 : 4;  // words between four-k groups, transposing stores
   static constexpr int A_GROUP = 4 * BM + (TA ? 0 : PAD);  // floats per four-k group
   static constexpr int B_GROUP = 4 * BN + (TB ? PAD : 0);
-  // bytes per stage; the fringe variant keeps 16 + 16 words after the
+  // bytes per stage; the fringe variant keeps BK + BK words after the
   // groups (the extra row's k, then the extra column's k)
   static constexpr int FPAD = GROUPS * A_GROUP * 4;
-  static constexpr int A_STAGE = round256(FPAD + (FR ? 128 : 0));
+  static constexpr int A_STAGE = round256(FPAD + (FR ? 8 * BK : 0));
+  // fringe variant: positions of a block's share per k (thread tid takes
+  // k = tid / FP of each stage, position tid % FP)
+  static constexpr int FP = THREADS / BK;
   static constexpr int B_STAGE = round256(GROUPS * B_GROUP * 4);
   static constexpr int STAGES_LDS = 2 * A_STAGE + 2 * B_STAGE;
   // K slices: each wavefront finishes 4 / KS block rows of its wave tile
@@ -89,7 +92,7 @@ struct KTile {
   static_assert(A_LOADS >= 1 && A_LOADS <= 4 && B_LOADS >= 1 && B_LOADS <= 4, "loads per stage");
   static_assert(THREADS % A_PER == 0 && THREADS % B_PER == 0, "whole rows per load round");
   static_assert(4 % KS == 0 && STEPS >= 2, "K slices");
-  static_assert(!FR || (BM == 256 && BN == 128 && BK == 16 && KS == 1), "fringe: the 256 x 128 tile");
+  static_assert(THREADS % BK == 0 && 3 * THREADS + BK <= STAGES_LDS / 4, "fringe shares and sums");
 };
 
 // Raw buffer resource (stride 0): loads at byte offsets >= bytes return 0.
@@ -185,16 +188,16 @@ __device__ __forceinline__ void b_map(int tid, int h, int& k, int& col) {
 // M x N row-major array per part; the reduction kernel adds the planes in
 // part order.
 // T::FR (the fringe variant): the tiles_m x tiles_n whole tiles cover all of
-// C but row M - 1 when M = 256 tiles_m + 1, and column N - 1 when
-// N = 128 tiles_n + 1.  Block (i, j) holds, over its K loop, op(A)'s rows
+// C but row M - 1 when M = BM tiles_m + 1, and column N - 1 when
+// N = BN tiles_n + 1.  Block (i, j) holds, over its K loop, op(A)'s rows
 // of tile row i and op(B)'s columns of tile column j, all of K; so it also
 // sums row M - 1 of op(A) against its share of those columns (columns
-// i cpt .. i cpt + cpt - 1 of the tile, cpt = ceil(128 / tiles_m) <= 32)
-// and its share of those rows (j rpt .., rpt = ceil(256 / tiles_n) <= 32)
+// i cpt .. i cpt + cpt - 1 of the tile, cpt = ceil(BN / tiles_m) <= FP)
+// and its share of those rows (j rpt .., rpt = ceil(BM / tiles_n) <= FP)
 // against column N - 1 of op(B), and the last block the corner: every
-// output of the fringe is summed in one block, k = tid / 32 of each stage
-// per thread (the corner: k = tid % 16), and those sixteen partial sums
-// are added in k order.  Row M - 1's and column N - 1's elements reach LDS
+// output of the fringe is summed in one block, k = tid / FP of each stage
+// per thread (the corner: k = tid % BK), and those BK partial sums are
+// added in k order.  Row M - 1's and column N - 1's elements reach LDS
 // with the stage they belong to; the block's record counts then reach
 // that row / column.
 template <class T, bool SPLIT>
@@ -283,19 +286,19 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
                       static_cast<uint32_t>((g0 * T::B_GROUP + kg * T::BN + wn * 64 + 4 * lrow) * 4);
   const uint32_t stepA = static_cast<uint32_t>(T::BK * a_ks * 4);
   const uint32_t stepB = static_cast<uint32_t>(T::BK * b_ks * 4);
-  // fringe variant, per thread: the k of a stage it stages (tid % 16): the
+  // fringe variant, per thread: the k of a stage it stages (tid % BK): the
   // byte offsets of element (a_last, k) of the tile's A and (k, b_last) of
-  // its B; the k it multiplies (tid / 32) and the column n / row m of the
-  // block's share it takes (tid % 32; beyond the share, a column / row of
+  // its B; the k it multiplies (tid / FP) and the column n / row m of the
+  // block's share it takes (tid % FP; beyond the share, a column / row of
   // the tile whose sums are not stored); its LDS bases: the staged words
-  // of that k (extra row's at k, extra column's at 16 + k), B's word (k, n),
-  // A's word (m, k), and the staged words of k = tid % 16.
+  // of that k (extra row's at k, extra column's at BK + k), B's word (k, n),
+  // A's word (m, k), and the staged words of k = tid % BK.
   const int64_t f_cpt = ceil_div(T::BN, tiles_m), f_rpt = ceil_div(BM, tiles_n);
   const int64_t f_n0 = (row0 / BM) * f_cpt, f_m0 = (col0 / T::BN) * f_rpt;
   uint32_t foa = 0, fob = 0, fst = 0, frB = 0, fcA = 0, fpk = 0;
-  float fa, fb, frow = 0.0f, fcol = 0.0f, fcor = 0.0f;
+  float fa[T::PREFETCH], fb[T::PREFETCH], frow = 0.0f, fcol = 0.0f, fcor = 0.0f;
   if constexpr (T::FR) {
-    const int ks = tid % 16, kf = tid / 32, c = tid % 32;
+    const int ks = tid % T::BK, kf = tid / T::FP, c = tid % T::FP;
     foa = static_cast<uint32_t>((a_last * a_rs + ks * a_ks) * 4);
     fob = static_cast<uint32_t>((ks * b_ks + b_last * b_cs) * 4);
     const int n = c < f_cpt && f_n0 + c < T::BN ? static_cast<int>(f_n0) + c : c;
@@ -320,10 +323,20 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   intx4 rsB = buffer_resource(b_base + k0 * b_ks,
                               b_bytes > b_skip ? static_cast<uint32_t>(b_bytes - b_skip) : 0u);
   floatx4 stg[T::PREFETCH * (T::A_LOADS + T::B_LOADS)];
-  if constexpr (T::FR && !TA && !TB) SGEMM_KLOOP_PRELUDE(256x128_NN_F, SGEMM_KLOOP_FRINGE_LOADS);
-  else if constexpr (T::FR && !TA) SGEMM_KLOOP_PRELUDE(256x128_NT_F, SGEMM_KLOOP_FRINGE_LOADS);
-  else if constexpr (T::FR && !TB) SGEMM_KLOOP_PRELUDE(256x128_TN_F, SGEMM_KLOOP_FRINGE_LOADS);
-  else if constexpr (T::FR) SGEMM_KLOOP_PRELUDE(256x128_TT_F, SGEMM_KLOOP_FRINGE_LOADS);
+#define SGEMM_KLOOP_F2 SGEMM_KLOOP_TWO_B SGEMM_KLOOP_FRINGE_LOADS
+#define SGEMM_KLOOP_F4 SGEMM_KLOOP_DEEP SGEMM_KLOOP_FRINGE_LOADS
+  if constexpr (T::FR && BM == 256 && !TA && !TB) SGEMM_KLOOP_PRELUDE(256x128_NN_F, SGEMM_KLOOP_FRINGE_LOADS);
+  else if constexpr (T::FR && BM == 256 && !TA) SGEMM_KLOOP_PRELUDE(256x128_NT_F, SGEMM_KLOOP_FRINGE_LOADS);
+  else if constexpr (T::FR && BM == 256 && !TB) SGEMM_KLOOP_PRELUDE(256x128_TN_F, SGEMM_KLOOP_FRINGE_LOADS);
+  else if constexpr (T::FR && BM == 256) SGEMM_KLOOP_PRELUDE(256x128_TT_F, SGEMM_KLOOP_FRINGE_LOADS);
+  else if constexpr (T::FR && BM == 128 && !TA && !TB) SGEMM_KLOOP_PRELUDE(128x128_NN_F, SGEMM_KLOOP_F2);
+  else if constexpr (T::FR && BM == 128 && !TA) SGEMM_KLOOP_PRELUDE(128x128_NT_F, SGEMM_KLOOP_F2);
+  else if constexpr (T::FR && BM == 128 && !TB) SGEMM_KLOOP_PRELUDE(128x128_TN_F, SGEMM_KLOOP_F2);
+  else if constexpr (T::FR && BM == 128) SGEMM_KLOOP_PRELUDE(128x128_TT_F, SGEMM_KLOOP_F2);
+  else if constexpr (T::FR && !TA && !TB) SGEMM_KLOOP_PRELUDE(64x64_NN_F, SGEMM_KLOOP_F4);
+  else if constexpr (T::FR && !TA) SGEMM_KLOOP_PRELUDE(64x64_NT_F, SGEMM_KLOOP_F4);
+  else if constexpr (T::FR && !TB) SGEMM_KLOOP_PRELUDE(64x64_TN_F, SGEMM_KLOOP_F4);
+  else if constexpr (T::FR) SGEMM_KLOOP_PRELUDE(64x64_TT_F, SGEMM_KLOOP_F4);
   else if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_PRELUDE(256x128_NN, SGEMM_KLOOP_ONE_B);
   else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_PRELUDE(256x128_NT, SGEMM_KLOOP_ONE_B);
   else if constexpr (BM == 256 && !TB) SGEMM_KLOOP_PRELUDE(256x128_TN, SGEMM_KLOOP_ONE_B);
@@ -353,7 +366,7 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   // beyond k0, and beyond the record counts where the block has none)
   float fa0 = 0.0f, fb0 = 0.0f;
   if constexpr (T::FR) {
-    const bool in = tid % 16 < k0;
+    const bool in = tid % T::BK < k0;
     fa0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra0, in ? foa : kOutside, 0, 0));
     fb0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb0, in ? fob : kOutside, 0, 0));
   }
@@ -441,21 +454,27 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   if constexpr (T::FR) {
     // every thread of a k stores the same value
     float* const pad = lds_a + T::FPAD / 4;
-    pad[tid % 16] = fa0;
-    pad[16 + tid % 16] = fb0;
+    pad[tid % T::BK] = fa0;
+    pad[T::BK + tid % T::BK] = fb0;
   }
   const int stages = (K + T::BK - 1) / T::BK;
   uint32_t pairs = static_cast<uint32_t>(stages / 2);
   const uint32_t odd = static_cast<uint32_t>(stages % 2);
   floatx16 a0 = {}, a1 = {}, a2 = {}, a3 = {};
-  if constexpr (T::FR && !TA && !TB)
-    SGEMM_KLOOP_LOOP(256x128_NN_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FRINGE_WORDS);
-  else if constexpr (T::FR && !TA)
-    SGEMM_KLOOP_LOOP(256x128_NT_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FRINGE_WORDS);
-  else if constexpr (T::FR && !TB)
-    SGEMM_KLOOP_LOOP(256x128_TN_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FRINGE_WORDS);
-  else if constexpr (T::FR)
-    SGEMM_KLOOP_LOOP(256x128_TT_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FRINGE_WORDS);
+#define SGEMM_KLOOP_FW SGEMM_KLOOP_FRINGE_WORDS
+#define SGEMM_KLOOP_FW4 SGEMM_KLOOP_DEEP_STORES SGEMM_KLOOP_FRINGE_WORDS
+  if constexpr (T::FR && BM == 256 && !TA && !TB) SGEMM_KLOOP_LOOP(256x128_NN_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FW);
+  else if constexpr (T::FR && BM == 256 && !TA) SGEMM_KLOOP_LOOP(256x128_NT_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FW);
+  else if constexpr (T::FR && BM == 256 && !TB) SGEMM_KLOOP_LOOP(256x128_TN_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FW);
+  else if constexpr (T::FR && BM == 256) SGEMM_KLOOP_LOOP(256x128_TT_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FW);
+  else if constexpr (T::FR && BM == 128 && !TA && !TB) SGEMM_KLOOP_LOOP(128x128_NN_F, SGEMM_KLOOP_F2, SGEMM_KLOOP_FW);
+  else if constexpr (T::FR && BM == 128 && !TA) SGEMM_KLOOP_LOOP(128x128_NT_F, SGEMM_KLOOP_F2, SGEMM_KLOOP_FW);
+  else if constexpr (T::FR && BM == 128 && !TB) SGEMM_KLOOP_LOOP(128x128_TN_F, SGEMM_KLOOP_F2, SGEMM_KLOOP_FW);
+  else if constexpr (T::FR && BM == 128) SGEMM_KLOOP_LOOP(128x128_TT_F, SGEMM_KLOOP_F2, SGEMM_KLOOP_FW);
+  else if constexpr (T::FR && !TA && !TB) SGEMM_KLOOP_LOOP(64x64_NN_F, SGEMM_KLOOP_F4, SGEMM_KLOOP_FW4);
+  else if constexpr (T::FR && !TA) SGEMM_KLOOP_LOOP(64x64_NT_F, SGEMM_KLOOP_F4, SGEMM_KLOOP_FW4);
+  else if constexpr (T::FR && !TB) SGEMM_KLOOP_LOOP(64x64_TN_F, SGEMM_KLOOP_F4, SGEMM_KLOOP_FW4);
+  else if constexpr (T::FR) SGEMM_KLOOP_LOOP(64x64_TT_F, SGEMM_KLOOP_F4, SGEMM_KLOOP_FW4);
   else if constexpr (BM == 256 && !TA && !TB) SGEMM_KLOOP_LOOP(256x128_NN, SGEMM_KLOOP_ONE_B, );
   else if constexpr (BM == 256 && !TA) SGEMM_KLOOP_LOOP(256x128_NT, SGEMM_KLOOP_ONE_B, );
   else if constexpr (BM == 256 && !TB) SGEMM_KLOOP_LOOP(256x128_TN, SGEMM_KLOOP_ONE_B, );
@@ -471,35 +490,50 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   floatx16 acc[4] = {a0, a1, a2, a3};
 
   // fringe variant: the partial sums meet in LDS (free once every
-  // wavefront has left the loop) and each output adds its sixteen in k
-  // order: the block's share of row M - 1 (threads 0 .. 31), of column
-  // N - 1 (threads 32 .. 63), and in the last block the corner (thread 64)
+  // wavefront has left the loop), one per k of a stage for each output.
+  // Each output adds its BK in a fixed order: in groups of G consecutive k
+  // (G = BK up to 16, else 8), then the groups in order -- the block's
+  // share of row M - 1 at share positions 0 .. FP - 1, of column N - 1 at
+  // FP .. 2 FP - 1, and in the last block the corner at 2 FP.
   if constexpr (T::FR) {
     if (f_row || f_col) {
+      constexpr int FP = T::FP, G = T::BK <= 16 ? T::BK : 8, NG = T::BK / G;
+      static_assert(T::BK % G == 0 && (2 * FP + 1) * NG <= T::THREADS, "fringe sums");
       float* const red = reinterpret_cast<float*>(smem);
+      float* const part = red + 2 * T::THREADS + T::BK;  // NG group sums per output
       __syncthreads();
       red[tid] = frow;
       red[T::THREADS + tid] = fcol;
-      if (tid < 16) red[2 * T::THREADS + tid] = fcor;
+      if (tid < T::BK) red[2 * T::THREADS + tid] = fcor;
       __syncthreads();
-      if (f_row && tid < 32 && tid < f_cpt && f_n0 + tid < T::BN) {
-        float sum = red[tid];
-        for (int k = 1; k < 16; ++k) sum += red[32 * k + tid];
+      // thread (o, g): output o (row share positions, column share
+      // positions, corner), group g of its k
+      const int o = tid / NG, g = tid % NG;
+      if (o <= 2 * FP) {
+        const float* const src = o < FP ? red + o : o < 2 * FP ? red + T::THREADS + (o - FP) : red + 2 * T::THREADS;
+        const int stride = o < 2 * FP ? FP : 1;
+        float sum = src[stride * (g * G)];
+        for (int k = 1; k < G; ++k) sum += src[stride * (g * G + k)];
+        part[o * NG + g] = sum;
+      }
+      if constexpr (NG > 1) __syncthreads();
+      auto total = [&](int out) {
+        float sum = part[out * NG];
+        for (int q = 1; q < NG; ++q) sum += part[out * NG + q];
+        return sum;
+      };
+      if (f_row && tid < FP && tid < f_cpt && f_n0 + tid < T::BN) {
         float* const c = p.C + int64_t(p.M - 1) * p.ldc + col0 + f_n0 + tid;
-        *c = epilogue(sum, p.alpha, p.beta, c);
+        *c = epilogue(total(tid), p.alpha, p.beta, c);
       }
-      const int r = tid - 32;
-      if (f_col && r >= 0 && r < 32 && r < f_rpt && f_m0 + r < BM) {
-        float sum = red[T::THREADS + r];
-        for (int k = 1; k < 16; ++k) sum += red[T::THREADS + 32 * k + r];
+      const int r = tid - FP;
+      if (f_col && r >= 0 && r < FP && r < f_rpt && f_m0 + r < BM) {
         float* const c = p.C + (row0 + f_m0 + r) * p.ldc + (p.N - 1);
-        *c = epilogue(sum, p.alpha, p.beta, c);
+        *c = epilogue(total(tid), p.alpha, p.beta, c);
       }
-      if (f_row && f_col && tid == 64 && t == tiles_m * tiles_n - 1) {
-        float sum = red[2 * T::THREADS];
-        for (int k = 1; k < 16; ++k) sum += red[2 * T::THREADS + k];
+      if (f_row && f_col && tid == 2 * FP && t == tiles_m * tiles_n - 1) {
         float* const c = p.C + int64_t(p.M - 1) * p.ldc + (p.N - 1);
-        *c = epilogue(sum, p.alpha, p.beta, c);
+        *c = epilogue(total(tid), p.alpha, p.beta, c);
       }
     }
   }
@@ -615,14 +649,16 @@ bool fits(const Problem& p) {
 }
 
 // The fringe variant over a grid of Mm x Nm (whole tiles) inside p, with
-// p.M - Mm and p.N - Nm each 0 or 1: at least 4 tile rows and 8 tile
-// columns (each block's share of the fringe at most 32 columns / rows),
-// and every block's offsets down to row M - 1 / across to column N - 1
-// (largest from the first tile) below 2^31 bytes.
+// p.M - Mm and p.N - Nm each 0 or 1: enough tile rows and columns that
+// each block's share of the fringe is at most FP columns / rows (256 x 128:
+// 4 x 8 tiles, 128 x 128: 8 x 8, 64 x 64: 16 x 16), and every block's
+// offsets down to row M - 1 / across to column N - 1 (largest from the
+// first tile) below 2^31 bytes.
 template <class T>
 bool fits_fringe(const Problem& p, int Mm, int Nm) {
   if (p.trans_a != T::TA || p.trans_b != T::TB) return false;
-  if (Mm < 4 * T::BM || Nm < 8 * T::BN || Mm % T::BM || Nm % T::BN || p.K < 1) return false;
+  if (Mm < T::BM || Nm < T::BN || Mm % T::BM || Nm % T::BN || p.K < 1) return false;
+  if (ceil_div(T::BN, Mm / T::BM) > T::FP || ceil_div(T::BM, Nm / T::BN) > T::FP) return false;
   if (p.M - Mm < 0 || p.M - Mm > 1 || p.N - Nm < 0 || p.N - Nm > 1) return false;
   const int64_t lim = int64_t(1) << 31, past = p.K + (T::PREFETCH + 1) * T::BK;
   const int64_t a_end = T::TA ? past * p.lda + p.M : (p.M - 1) * p.lda + past;
@@ -649,12 +685,22 @@ auto with_orientation(const Problem& p, F f) {
   return f(KTile<BM, BN, BK, KS, false, false>());
 }
 
+template <int BM, int BN, int BK, int KS, class F>
+auto with_fringe_orientation(const Problem& p, F f) {
+  if (p.trans_a && p.trans_b) return f(KTile<BM, BN, BK, KS, true, true, true>());
+  if (p.trans_a) return f(KTile<BM, BN, BK, KS, true, false, true>());
+  if (p.trans_b) return f(KTile<BM, BN, BK, KS, false, true, true>());
+  return f(KTile<BM, BN, BK, KS, false, false, true>());
+}
+
+// The fringe variant of each loop tile (has_loop(shape) must hold).
 template <class F>
-auto with_fringe_tile(const Problem& p, F f) {
-  if (p.trans_a && p.trans_b) return f(KTile<256, 128, 16, 1, true, true, true>());
-  if (p.trans_a) return f(KTile<256, 128, 16, 1, true, false, true>());
-  if (p.trans_b) return f(KTile<256, 128, 16, 1, false, true, true>());
-  return f(KTile<256, 128, 16, 1, false, false, true>());
+auto with_fringe_tile(Shape shape, const Problem& p, F f) {
+  switch (shape) {
+    case Shape::kHuge: return with_fringe_orientation<256, 128, 16, 1>(p, f);
+    case Shape::kLarge: return with_fringe_orientation<128, 128, 16, 1>(p, f);
+    default: return with_fringe_orientation<64, 64, 64, 4>(p, f);
+  }
 }
 
 template <class F>
@@ -699,13 +745,14 @@ hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s) {
   return with_tile(shape, p, [&](auto t) { return launch_t<decltype(t), false>(p, p.K, nullptr, s); });
 }
 
-bool tiles_fringe_fits(const Problem& p, int Mm, int Nm) {
-  return with_fringe_tile(p, [&](auto t) { return fits_fringe<decltype(t)>(p, Mm, Nm); });
+bool tiles_fringe_fits(Shape shape, const Problem& p, int Mm, int Nm) {
+  return has_loop(shape) &&
+         with_fringe_tile(shape, p, [&](auto t) { return fits_fringe<decltype(t)>(p, Mm, Nm); });
 }
 
-hipError_t launch_tiles_fringe(const Problem& p, int Mm, int Nm, hipStream_t s) {
-  if (!tiles_fringe_fits(p, Mm, Nm)) return hipErrorInvalidValue;
-  return with_fringe_tile(p, [&](auto t) {
+hipError_t launch_tiles_fringe(Shape shape, const Problem& p, int Mm, int Nm, hipStream_t s) {
+  if (!tiles_fringe_fits(shape, p, Mm, Nm)) return hipErrorInvalidValue;
+  return with_fringe_tile(shape, p, [&](auto t) {
     typedef decltype(t) T;
     const int64_t tm = Mm / T::BM, tn = Nm / T::BN;
     hipLaunchKernelGGL((k_kloop<T, false>), dim3(static_cast<unsigned>(tm * tn)), dim3(T::THREADS), 0, s,

@@ -172,15 +172,16 @@ hipError_t launch_mfma(Shape shape, const Problem& p, hipStream_t s);
 bool kloop_fits(Shape shape, const Problem& p);
 hipError_t launch_tiles(Shape shape, const Problem& p, hipStream_t s);
 Geometry tiles_geometry(Shape shape, int M, int N, int K);  // of launch_tiles, dense row-major
-// The Huge tile's fringe variant, one launch: whole tiles over the first
-// Mm x Nm of C (multiples of 256 and 128) and, summed by the same blocks,
-// row M - 1 when p.M == Mm + 1 and column N - 1 when p.N == Nm + 1.  Fits
-// when the grid has at least 4 x 8 tiles and the buffer offsets (down to
-// row M - 1 and across to column N - 1) stay below 2^31;
+// A loop tile's fringe variant, one launch: whole tiles over the first
+// Mm x Nm of C (multiples of the tile) and, summed by the same blocks, row
+// M - 1 when p.M == Mm + 1 and column N - 1 when p.N == Nm + 1.  Fits when
+// the grid has enough tiles for each block's share of the fringe (256 x
+// 128: 4 x 8 tiles, 128 x 128: 8 x 8, 64 x 64: 16 x 16) and the buffer
+// offsets (down to row M - 1 and across to column N - 1) stay below 2^31;
 // launch_tiles_fringe returns hipErrorInvalidValue, enqueueing nothing,
 // where it does not.
-bool tiles_fringe_fits(const Problem& p, int Mm, int Nm);
-hipError_t launch_tiles_fringe(const Problem& p, int Mm, int Nm, hipStream_t s);
+bool tiles_fringe_fits(Shape shape, const Problem& p, int Mm, int Nm);
+hipError_t launch_tiles_fringe(Shape shape, const Problem& p, int Mm, int Nm, hipStream_t s);
 // The same kernels over K slices (see launch_mfma_split): work item (tile,
 // slice) stores raw sums into plane `slice` of ws.
 hipError_t launch_tiles_split(Shape shape, const Problem& p, int64_t k_split, float* ws,

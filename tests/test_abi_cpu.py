@@ -252,15 +252,27 @@ def test_plan_query_names_every_plan_and_its_workspace():
     assert P(16, 4096, 4096)["name"] == "few_rows"
     assert P(4096, 3, 4097)["name"] == "few_cols"
     assert P(4096, 4096, 4096) == {"plan": 4, "name": "tiles", "launches": 1, "workspace_bytes": 0}
-    # a fringe of one row and / or one column beside 256 x 128 tiles runs in
-    # the tiles' own launch; wider fringes, and fringes beside the 128 x 128
-    # tile, add a thin-kernel launch per side
+    # a fringe of one row and / or one column runs in the tiles' own launch
+    # (every loop tile, on a grid with enough tiles for the blocks' shares);
+    # wider fringes beside the 256 x 128 and 128 x 128 tiles add a
+    # thin-kernel launch per side
     assert P(4097, 4097, 4097) == {"plan": 5, "name": "tiles_fringe", "launches": 1,
                                    "workspace_bytes": 0}
     assert P(4096, 4097, 64)["launches"] == 1 and P(4097, 4096, 64)["launches"] == 1
     assert P(4098, 4097, 64)["launches"] == 3 and P(4097, 4098, 64)["launches"] == 3
     assert P(4096, 4098, 64)["launches"] == 2
-    assert P(2049, 2049, 2048)["launches"] == 3  # 128 x 128 tiles
+    for M, N, K, tile in [(2049, 2049, 2048, 128), (2049, 2048, 2048, 128), (1025, 1025, 1025, 64),
+                          (1024, 1025, 1024, 64), (3073, 3073, 3073, 64)]:
+        assert P(M, N, K) == {"plan": 5, "name": "tiles_fringe", "launches": 1, "workspace_bytes": 0}
+        g = sgemm.hip_sgemm_launch_shape(10, M, N, K)
+        assert (g["tile_m"], g["workgroups"]) == (tile, (M // tile) * (N // tile)), (M, N, K, g)
+    assert P(2051, 2055, 300)["launches"] == 3  # 3 rows and 7 columns: thin kernels
+    assert P(769, 769, 769)["name"] == "tiles"  # 12 x 12 tiles of 64 x 64: too few for the shares
+    # 64 x 64 tiles take the fringe only where it leaves a CU fewer tiles
+    # than the edge tiles would: 1537^3 has 576 whole tiles or 625 with
+    # edges, three per CU either way
+    assert P(1537, 1537, 1537)["name"] == "tiles"
+    assert sgemm.hip_sgemm_launch_shape(10, 1537, 1537, 1537)["workgroups"] == 625
     assert P(256, 256, 256)["name"] == "thin_panels"
     # split K: 512 x 512 x 8192 (64 tiles of 64 x 64) in 8 slices of 1024
     sk = P(512, 512, 8192)

@@ -1,6 +1,6 @@
 """Level 10 (shape-aware dispatch) on every plan it has: a whole-tile grid
 plus one- to sixteen-wide fringes (both large loop tiles; a one-row and /
-or one-column fringe beside 256 x 128 tiles in the tiles' own launch), a
+or one-column fringe, beside any loop tile, in the tiles' own launch), a
 ragged K under
 whole M/N tiles, the 64 x 64 loop tiles with edges, split K for a deep K
 over a small grid (whole and edge tiles, ragged K), 16-row panels for small
@@ -46,6 +46,12 @@ SHAPES = [
     (4097, 4096, 17, "tiles_fringe", "256x128 grid, one row in the tiles' launch, K ragged"),
     (4096, 4097, 1, "tiles_fringe", "256x128 grid, one column in the tiles' launch, K = 1"),
     (8193, 4097, 8, "tiles_fringe", "1024 tiles of 256x128, one row and one column, K below a stage"),
+    (2049, 2049, 300, "tiles_fringe", "128x128 grid, one row and one column in the tiles' launch"),
+    (2049, 2048, 17, "tiles_fringe", "128x128 grid, one row in the tiles' launch, K ragged"),
+    (1025, 1025, 1025, "tiles_fringe", "64x64 grid, one row and one column in the tiles' launch"),
+    (1024, 1025, 200, "tiles_fringe", "64x64 grid, one column in the tiles' launch, K ragged"),
+    (1025, 1024, 64, "tiles_fringe", "64x64 grid, one row in the tiles' launch, K of one stage"),
+    (3073, 3073, 5, "tiles_fringe", "2304 tiles of 64x64, one row and one column, K below a stage"),
     (4096, 4096, 36, "tiles", "256x128 loop grid, K ragged (36 = 2*16 + 4)"),
     (2048, 2048, 100, "tiles", "128x128 loop grid, K ragged (100 = 6*16 + 4)"),
     (2048, 4096, 80, "tiles", "128x128 loop grid, 512 tiles"),
@@ -95,6 +101,7 @@ def test_dispatch_padded_and_misaligned(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(2051, 2055, 300), (7, 2000, 3001), (2000, 9, 3001),
                                    (4096 + 1, 4096 + 1, 33), (4097, 4096, 40), (4096, 4097, 5),
+                                   (2049, 2049, 100), (1025, 1025, 333),
                                    (1024, 1024, 4096), (512, 512, 8192), (700, 600, 8200)])
 def test_dispatch_integer_exact(M, N, K):
     """Integer entries in [-8, 8]: every partial sum is an integer far below
@@ -108,7 +115,8 @@ def test_dispatch_integer_exact(M, N, K):
     assert np.array_equal(out.astype(np.float64), ref.ref)
 
 
-@pytest.mark.parametrize("M,N,K", [(4097, 4097, 97), (1, 4097, 4097), (4097, 2, 4097),
+@pytest.mark.parametrize("M,N,K", [(4097, 4097, 97), (2049, 2049, 97), (1025, 1025, 1025),
+                                   (1, 4097, 4097), (4097, 2, 4097),
                                    (1024, 1024, 4096), (1000, 1000, 300), (512, 512, 8192)])
 def test_dispatch_deterministic(M, N, K):
     print(f"[dispatch determinism] {M}x{N}x{K}", flush=True)

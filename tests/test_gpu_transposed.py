@@ -67,6 +67,8 @@ SHAPES = [
     (4097, 4097, 70, "256x128 grid, one row and one column in the tiles' launch", "all"),
     (4097, 4096, 17, "256x128 grid, one row in the tiles' launch", "all"),
     (4096, 4097, 5, "256x128 grid, one column in the tiles' launch, K below a stage", "all"),
+    (2049, 2049, 70, "128x128 grid, one row and one column in the tiles' launch", "all"),
+    (1025, 1025, 130, "64x64 grid, one row and one column in the tiles' launch", "all"),
     (8192, 8, 1000, "eight columns, two per lane", "all"),
     (16, 16384, 777, "sixteen rows, two columns per lane", "all"),
     (2048, 2048, 100, "128x128 grid, K ragged", "all"),
@@ -102,7 +104,7 @@ def test_transposed_operands(M, N, K, plan, same):
 
 
 @pytest.mark.parametrize("M,N,K", [(131, 257, 515), (7, 1029, 301), (1029, 9, 301), (2051, 2053, 64),
-                                   (4097, 4097, 40)])
+                                   (4097, 4097, 40), (2049, 2049, 40), (1025, 1025, 77)])
 def test_transposed_padded_misaligned(M, N, K):
     """Row padding that breaks 16-byte alignment of rows and bases that are
     only 4-byte aligned, beta = 0 with NaN in C (C must not be read)."""
@@ -116,8 +118,8 @@ def test_transposed_padded_misaligned(M, N, K):
         assert oracle.normalised_error(out, ref, None, -1.5, 0.0, strict=True) <= BOUND, (op_a, op_b)
 
 
-@pytest.mark.parametrize("M,N,K", [(4097, 4097, 33), (520, 390, 3000), (3, 2000, 999), (4, 3001, 2300),
-                                   (2500, 2, 2300)])
+@pytest.mark.parametrize("M,N,K", [(4097, 4097, 33), (2049, 2049, 33), (1025, 1025, 200), (520, 390, 3000),
+                                   (3, 2000, 999), (4, 3001, 2300), (2500, 2, 2300)])
 def test_transposed_integer_exact(M, N, K):
     """Integer entries: every orientation equals the reference bit for bit."""
     print(f"[transposed integer] {M}x{N}x{K}", flush=True)

@@ -97,12 +97,13 @@ def w_b(t, tid):
 
 # The fringe variant's per-block shares and per-thread LDS bases (restated
 # from l10_kloop.hip).  Block (i, j) of a tiles_m x tiles_n grid takes
-# columns i cpt .. of its tile for the extra row, cpt = ceil(128 / tiles_m),
-# and rows j rpt .. for the extra column, rpt = ceil(256 / tiles_n); thread
-# tid multiplies k = tid / 32 of each stage for share position tid % 32
-# (positions beyond the share, or beyond the tile, take column / row
-# tid % 32, whose sums are not stored); its staged words are those of
-# k = tid / 32 (%[fpk]) and, for the corner, of k = tid % 16 (%[fst]).
+# columns i cpt .. of its tile for the extra row, cpt = ceil(BN / tiles_m),
+# and rows j rpt .. for the extra column, rpt = ceil(BM / tiles_n); thread
+# tid multiplies k = tid / FP of each stage (FP = THREADS / BK) for share
+# position tid % FP (positions beyond the share, or beyond the tile, take
+# column / row tid % FP, whose sums are not stored); its staged words are
+# those of k = tid / FP (%[fpk]) and, for the corner, of k = tid % BK
+# (%[fst]).
 def f_share(t, tiles_m, tiles_n, i, j):
     cpt, rpt = -(-t.BN // tiles_m), -(-t.BM // tiles_n)
     return cpt, rpt, i * cpt, j * rpt
@@ -111,28 +112,33 @@ def f_share(t, tiles_m, tiles_n, i, j):
 def f_cols(t, grid, tid):
     """(column n, row m) of the tile that thread tid's fringe sums take."""
     cpt, rpt, n0, m0 = f_share(t, *grid)
-    c = tid % 32
+    c = tid % t.FP
     n = n0 + c if c < cpt and n0 + c < t.BN else c
     m = m0 + c if c < rpt and m0 + c < t.BM else c
     return n, m
 
 
 def f_st(t, grid, tid):
-    return 4 * (tid % 16)
+    return 4 * (tid % t.BK)
 
 
 def f_pk(t, grid, tid):
-    return 4 * (tid // 32)
+    return 4 * (tid // t.FP)
 
 
 def f_rb(t, grid, tid):
-    k, (n, _) = tid // 32, f_cols(t, grid, tid)
+    k, (n, _) = tid // t.FP, f_cols(t, grid, tid)
     return 2 * t.A_STAGE + ((k // 4) * t.B_GROUP + (k % 4) * t.BN + n) * 4
 
 
 def f_ca(t, grid, tid):
-    k, (_, m) = tid // 32, f_cols(t, grid, tid)
+    k, (_, m) = tid // t.FP, f_cols(t, grid, tid)
     return ((k // 4) * t.A_GROUP + (k % 4) * t.BM + m) * 4
+
+
+def f_min_grid(t):
+    """Fewest tile rows and columns the variant takes (shares <= FP)."""
+    return -(-t.BN // t.FP), -(-t.BM // t.FP)
 
 
 F_BASES = {"fst": f_st, "frB": f_rb, "fcA": f_ca, "fpk": f_pk}
@@ -205,12 +211,12 @@ def _stage_stores(t, st, buf):
             for c in range(4):
                 regs[base + 4 * t.A_LOADS + 4 * h + c] = b_elem(t, tid, h, c)
         if t.FRINGE:
-            regs[G.FA] = ("R", tid % 16)
-            regs[G.FB] = ("C", tid % 16)
+            regs[t.fa(st)] = ("R", tid % t.BK)
+            regs[t.fa(st) + 1] = ("C", tid % t.BK)
         for line in lines:
             op, pieces = _pieces(t, tid, line)
             if op == "F":
-                lo, hi = buf * t.A_STAGE + t.FPAD, buf * t.A_STAGE + t.FPAD + G.FPAD_BYTES
+                lo, hi = buf * t.A_STAGE + t.FPAD, buf * t.A_STAGE + t.FPAD + 8 * t.BK
             else:
                 lo, hi = (buf * t.A_STAGE, (buf + 1) * t.A_STAGE) if op == "A" else \
                          (a_end + buf * t.B_STAGE, a_end + (buf + 1) * t.B_STAGE)
@@ -238,8 +244,8 @@ def test_stage_stores_follow_the_layout(name, buf):
         for addr, e in written.items():
             if e[0] in "RC":
                 # the extra row's k at word k of the fringe words, the
-                # extra column's at 16 + k
-                assert addr == buf * t.A_STAGE + t.FPAD + 4 * (e[1] + (16 if e[0] == "C" else 0)), (name, e)
+                # extra column's at BK + k
+                assert addr == buf * t.A_STAGE + t.FPAD + 4 * (e[1] + (t.BK if e[0] == "C" else 0)), (name, e)
                 continue
             word = a_word(t, e[1], e[2]) if e[0] == "A" else b_word(t, e[1], e[2])
             shift = buf * (t.A_STAGE if e[0] == "A" else t.B_STAGE)
@@ -270,10 +276,17 @@ def test_fragment_reads_find_their_operands(name, buf):
 
 F_READ1 = re.compile(r"ds_read_b32 v(\d+), %\[(\w+)\] offset:(\d+)$")
 F_FMAC = re.compile(r"v_fmac_f32 %\[(\w+)\], v(\d+), v(\d+)$")
-# (tiles_m, tiles_n, i, j): grids of the smallest size the variant takes,
-# 4097^3's, and ones whose last shares end inside or beyond the tile
-F_GRIDS = [(4, 8, 0, 0), (4, 8, 3, 7), (16, 32, 0, 0), (16, 32, 15, 31), (16, 32, 5, 17),
-           (5, 9, 4, 8), (32, 32, 31, 30), (7, 11, 6, 10)]
+def f_grids(t):
+    """(tiles_m, tiles_n, i, j): grids of the smallest size the variant
+    takes, larger ones (4097^3's for 256 x 128), and ones whose last shares
+    end inside or beyond the tile."""
+    mm, mn = f_min_grid(t)
+    return [(mm, mn, 0, 0), (mm, mn, mm - 1, mn - 1), (2 * mm, 2 * mn, 0, 0), (2 * mm, 2 * mn, 2 * mm - 1, 2 * mn - 1),
+            (2 * mm, 2 * mn, mm - 1, mn + 1), (mm + 1, mn + 1, mm, mn), (32, 32, 31, 30), (mm + 3, mn + 3, mm + 2, mn + 2)]
+
+
+FRINGE_CASES = [(n, cur, g) for n in sorted(n for n in TILES if TILES[n].FRINGE) for cur in (0, 1)
+                for g in f_grids(TILES[n])]
 
 
 def _fringe_products(t, grid, tid, cur, written):
@@ -294,46 +307,46 @@ def _fringe_products(t, grid, tid, cur, written):
     return prods
 
 
-@pytest.mark.parametrize("name", sorted(n for n in TILES if TILES[n].FRINGE))
-@pytest.mark.parametrize("cur", [0, 1])
-@pytest.mark.parametrize("grid", F_GRIDS, ids=[str(g) for g in F_GRIDS])
+@pytest.mark.parametrize("name,cur,grid", FRINGE_CASES, ids=[f"{n}-{c}-{g}" for n, c, g in FRINGE_CASES])
 def test_fringe_sums_multiply_matching_k(name, cur, grid):
     """Per K step, thread tid adds to its row sum the extra row's k times
     B's (k, n) and to its column sum A's (m, k) times the extra column's k,
-    k = tid / 32 and (n, m) its share position's column and row, and to its
-    corner sum the extra row's and column's k = tid % 16; so the sixteen
-    sums of a share position, and the corner's sixteen, hold every k of the
-    stage exactly once."""
+    k = tid / FP and (n, m) its share position's column and row, and to its
+    corner sum the extra row's and column's k = tid % BK; so the BK sums of
+    a share position, and the corner's BK, hold every k of the stage exactly
+    once."""
     t = TILES[name]
     written = _stage_stores(t, 0, cur)
     for tid in range(t.THREADS):
         prods = _fringe_products(t, grid, tid, cur, written)
-        k, ks = tid // 32, tid % 16
+        k, ks = tid // t.FP, tid % t.BK
         n, m = f_cols(t, grid, tid)
         assert prods == {"frow": [(("R", k), ("B", k, n))], "fcol": [(("C", k), ("A", m, k))],
                          "fcor": [(("R", ks), ("C", ks))]}, (tid, grid)
 
 
-def test_fringe_shares_cover_each_output_once():
+@pytest.mark.parametrize("shape", sorted({(t.BM, t.BN) for t in G.TILES}))
+def test_fringe_shares_cover_each_output_once(shape):
     """Over the blocks of a tile column the extra row's shares are
-    disjoint and cover the tile's 128 columns; over a tile row the extra
-    column's cover its 256 rows (every grid the variant takes: at least 4
-    tile rows and 8 tile columns, so that a share is at most 32 wide); and
-    the stored positions are those below the share's width."""
-    t = next(x for x in G.TILES if x.FRINGE)
-    for tiles_m in range(4, 300):
+    disjoint and cover the tile's BN columns; over a tile row the extra
+    column's cover its BM rows (every grid the variant takes: enough tile
+    rows and columns that a share is at most FP wide); and the stored
+    positions are those below the share's width."""
+    t = next(x for x in G.TILES if x.FRINGE and (x.BM, x.BN) == shape)
+    mm, mn = f_min_grid(t)
+    for tiles_m in range(mm, 300):
         cols = []
         for i in range(tiles_m):
-            cpt, _, n0, _ = f_share(t, tiles_m, 8, i, 0)
-            assert cpt <= 32
-            cols += [n0 + c for c in range(32) if c < cpt and n0 + c < t.BN]
+            cpt, _, n0, _ = f_share(t, tiles_m, mn, i, 0)
+            assert cpt <= t.FP
+            cols += [n0 + c for c in range(t.FP) if c < cpt and n0 + c < t.BN]
         assert sorted(cols) == list(range(t.BN)), tiles_m
-    for tiles_n in range(8, 600):
+    for tiles_n in range(mn, 600):
         rows = []
         for j in range(tiles_n):
-            _, rpt, _, m0 = f_share(t, 4, tiles_n, 0, j)
-            assert rpt <= 32
-            rows += [m0 + c for c in range(32) if c < rpt and m0 + c < t.BM]
+            _, rpt, _, m0 = f_share(t, mm, tiles_n, 0, j)
+            assert rpt <= t.FP
+            rows += [m0 + c for c in range(t.FP) if c < rpt and m0 + c < t.BM]
         assert sorted(rows) == list(range(t.BM)), tiles_n
 
 
@@ -421,7 +434,7 @@ def test_staging_sets_are_waited_for_before_their_stores(name):
     flight, and each set is reloaded only after an lgkmcnt(0) that follows
     its stores (the stores have read the registers)."""
     t = TILES[name]
-    per_stage = t.A_LOADS + t.B_LOADS
+    per_stage = t.LOADS
     for cur in (0, 1):
         step = t.k_step(cur)
         first_store = next(i for i, l in enumerate(step) if l.startswith("ds_write"))

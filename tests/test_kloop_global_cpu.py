@@ -144,9 +144,9 @@ class Problem:
             out[("B", h)] = 4 * (k * self.b_ks + c * self.b_cs)
         if t.FRINGE:
             # element (a_last, k) of the tile's A and (k, b_last) of its B,
-            # k = tid % 16: row M - 1 / column N - 1 where they exist
-            out[("FA", 0)] = 4 * (self.a_last * self.a_rs + (tid % 16) * self.a_ks)
-            out[("FB", 0)] = 4 * ((tid % 16) * self.b_ks + self.b_last * self.b_cs)
+            # k = tid % BK: row M - 1 / column N - 1 where they exist
+            out[("FA", 0)] = 4 * (self.a_last * self.a_rs + (tid % t.BK) * self.a_ks)
+            out[("FB", 0)] = 4 * ((tid % t.BK) * self.b_ks + self.b_last * self.b_cs)
         return out
 
 
@@ -257,9 +257,9 @@ def replay(p: Problem):
         tid = np.arange(t.THREADS)
         kbase = p.k_lo + p.k0 + (stage - 1) * t.BK
         if op in ("FA", "FB"):
-            # where the grid has the fringe, the element of k = tid % 16 of
+            # where the grid has the fringe, the element of k = tid % BK of
             # row M - 1 / column N - 1, for every k of the stage below K
-            kk = (tid % 16)[:, None]
+            kk = (tid % t.BK)[:, None]
             if op == "FA":
                 want = p.addr_a + 4 * ((p.M - 1) * p.a_rs + (kbase + kk) * p.a_ks)
                 has = p.f_row
@@ -317,12 +317,14 @@ def _problems(t):
 
 def _fringe_problems(t):
     """(Mm, Nm, M, N, K, lda, ldb) cases for the fringe variant: whole tiles
-    over the first Mm x Nm of C (at least 4 x 8 of them), and one more row
-    and / or column."""
+    over the first Mm x Nm of C (at least as many as the variant takes:
+    shares of at most THREADS / BK), and one more row and / or column."""
     BM, BN, BK = t.BM, t.BN, t.BK
+    fp = t.THREADS // BK
+    mt, nt = -(-BN // fp), -(-BM // fp)
     out = []
-    for Mm, Nm, K in [(4 * BM, 8 * BN, 4 * BK), (5 * BM, 8 * BN, 3 * BK + 5), (4 * BM, 9 * BN, 1),
-                      (4 * BM, 8 * BN, BK), (4 * BM, 8 * BN, BK + 1), (4 * BM, 8 * BN, 5 * BK + 15)]:
+    for Mm, Nm, K in [(mt * BM, nt * BN, 4 * BK), ((mt + 1) * BM, nt * BN, 3 * BK + 5), (mt * BM, (nt + 1) * BN, 1),
+                      (mt * BM, nt * BN, BK), (mt * BM, nt * BN, BK + 1), (mt * BM, nt * BN, 5 * BK + 15)]:
         for dm, dn in ((1, 1), (1, 0), (0, 1)):
             M, N = Mm + dm, Nm + dn
             ld_a = M if t.TA else K
