@@ -180,11 +180,12 @@ int hip_sgemm_ex_noalloc(int op_a, int op_b, int M, int N, int K, float alpha,
  *     kernel adds in order; otherwise one of three whole-tile kernels
  *     whose K loop is hand-scheduled assembly (256 x 128, 128 x 128, and
  *     64 x 64 over four K-slice wavefronts), with partial edge tiles, or
- *     with whole tiles plus a fringe of at most 16 rows / columns: one row
- *     and / or one column beside a grid of at least 4 x 8 tiles of
- *     256 x 128 is summed by the tiles' own blocks in the same launch
- *     (each fringe output by one block, sixteen partial sums added in k
- *     order), a wider fringe by the thin kernels.  A call enqueues up to
+ *     with whole tiles plus a fringe: one row and / or one column is
+ *     summed by the tiles' own blocks in the same launch (each fringe
+ *     output by one block, its per-k partial sums added in k order; grids
+ *     of at least 4 x 8 tiles of 256 x 128, 8 x 8 of 128 x 128, 16 x 16
+ *     of 64 x 64), up to 16 beside the two large tiles by the thin
+ *     kernels.  A call enqueues up to
  *     three kernels on the stream, over disjoint parts of C ([GEMM2]
  *     size-sweep section: a library is many kernels picked by shape)
  */
