@@ -24,7 +24,10 @@ REPLAYS = 3
 # (M, N, K, alpha, beta)
 SHAPES = [
     (2048, 2048, 512, 0.5, 3.0),    # assembly-loop tiles
-    (4097, 4097, 64, 1.0, 1.0),     # tiles plus the one-row and one-column fringe
+    (4097, 4097, 64, 1.0, 1.0),     # 256x128 tiles whose blocks also sum one row and one column
+    (2049, 2049, 64, 0.5, 3.0),     # the same beside 128x128 tiles
+    (1025, 1025, 300, 1.0, 0.0),    # the same beside 64x64 tiles
+    (4096 + 3, 4096 + 16, 64, 1.0, 1.0),  # tiles plus thin kernels on a 3-row / 16-column fringe
     (512, 512, 8192, 1.0, 0.0),     # split K
     (1, 4097, 1000, 1.0, 1.0),      # few rows, vector ALUs
     (3000, 3, 700, 2.0, -1.0),      # few columns, vector ALUs

@@ -82,8 +82,8 @@ def test_noalloc_split_every_orientation(ta, tb):
     _check(700, 600, 8200, ta, tb, 31010 + 2 * ta + tb)
 
 
-@pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (4097, 4097, 64), (300, 260, 500),
-                                   (12, 3000, 2000), (3000, 7, 2000)])
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (4097, 4097, 64), (2049, 2049, 64), (1025, 1025, 300),
+                                   (300, 260, 500), (12, 3000, 2000), (3000, 7, 2000)])
 def test_noalloc_plans_without_workspace(M, N, K):
     assert sgemm.hip_sgemm_plan(M, N, K)["workspace_bytes"] == 0
     _check(M, N, K, False, False, 31100 + M + N + K)
