@@ -262,10 +262,11 @@ def test_plan_query_names_every_plan_and_its_workspace():
     assert P(4098, 4097, 64)["launches"] == 3 and P(4097, 4098, 64)["launches"] == 3
     assert P(4096, 4098, 64)["launches"] == 2
     for M, N, K, tile in [(2049, 2049, 2048, 128), (2049, 2048, 2048, 128), (1025, 1025, 1025, 64),
-                          (1024, 1025, 1024, 64), (3073, 3073, 3073, 64)]:
+                          (1024, 1025, 1024, 64), (3073, 3073, 3073, 64), (1025, 4097, 37, 128),
+                          (2561, 6145, 37, 256), (1025, 3073, 65, 64), (3073, 1024, 65, 64)]:
         assert P(M, N, K) == {"plan": 5, "name": "tiles_fringe", "launches": 1, "workspace_bytes": 0}
         g = sgemm.hip_sgemm_launch_shape(10, M, N, K)
-        assert (g["tile_m"], g["workgroups"]) == (tile, (M // tile) * (N // tile)), (M, N, K, g)
+        assert (g["tile_m"], g["workgroups"]) == (tile, (M // tile) * (N // g["tile_n"])), (M, N, K, g)
     assert P(2051, 2055, 300)["launches"] == 3  # 3 rows and 7 columns: thin kernels
     assert P(769, 769, 769)["name"] == "tiles"  # 12 x 12 tiles of 64 x 64: too few for the shares
     # 64 x 64 tiles take the fringe only where it leaves a CU fewer tiles

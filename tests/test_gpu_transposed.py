@@ -69,6 +69,10 @@ SHAPES = [
     (4096, 4097, 5, "256x128 grid, one column in the tiles' launch, K below a stage", "all"),
     (2049, 2049, 70, "128x128 grid, one row and one column in the tiles' launch", "all"),
     (1025, 1025, 130, "64x64 grid, one row and one column in the tiles' launch", "all"),
+    (1025, 4097, 37, "128x128 grid of 8 tile rows (shares of 16 columns), fringe in the tiles' launch", "all"),
+    (2561, 6145, 37, "256x128 grid, uneven shares (13 columns, 6 rows), fringe in the tiles' launch", "all"),
+    (1025, 3073, 65, "64x64 grid of 16 x 48 tiles (shares of 4 columns, 2 rows), fringe in the tiles' launch", "all"),
+    (3073, 1024, 65, "64x64 grid of 48 x 16 tiles, one row in the tiles' launch", "all"),
     (8192, 8, 1000, "eight columns, two per lane", "all"),
     (16, 16384, 777, "sixteen rows, two columns per lane", "all"),
     (2048, 2048, 100, "128x128 grid, K ragged", "all"),
