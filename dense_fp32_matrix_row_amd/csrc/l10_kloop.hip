@@ -125,6 +125,11 @@ __device__ __forceinline__ intx4 buffer_resource(const float* base, uint32_t byt
 #define SGEMM_KLOOP_DEEP_STORES , [wA1] "v"(wA + T::A_STAGE), [wB1] "v"(wB + T::B_STAGE)
 #define SGEMM_KLOOP_FRINGE_LOADS , [foa] "v"(foa), [fob] "v"(fob)
 #define SGEMM_KLOOP_FRINGE_WORDS , [fst] "v"(fst), [frB] "v"(frB), [fcA] "v"(fcA), [fpk] "v"(fpk)
+// the fringe variants' operands: the tile's own, then the fringe's
+#define SGEMM_KLOOP_F2 SGEMM_KLOOP_TWO_B SGEMM_KLOOP_FRINGE_LOADS
+#define SGEMM_KLOOP_F4 SGEMM_KLOOP_DEEP SGEMM_KLOOP_FRINGE_LOADS
+#define SGEMM_KLOOP_FW SGEMM_KLOOP_FRINGE_WORDS
+#define SGEMM_KLOOP_FW4 SGEMM_KLOOP_DEEP_STORES SGEMM_KLOOP_FRINGE_WORDS
 #define SGEMM_KLOOP_PRELUDE(NAME, LOADS)                                                  \
   asm volatile(SGEMM_KLOOP_PRE_##NAME                                                     \
                : SGEMM_KLOOP_STAGING_OUT_##NAME, "+{s[60:63]}"(rsA), "+{s[64:67]}"(rsB)   \
@@ -323,8 +328,6 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   intx4 rsB = buffer_resource(b_base + k0 * b_ks,
                               b_bytes > b_skip ? static_cast<uint32_t>(b_bytes - b_skip) : 0u);
   floatx4 stg[T::PREFETCH * (T::A_LOADS + T::B_LOADS)];
-#define SGEMM_KLOOP_F2 SGEMM_KLOOP_TWO_B SGEMM_KLOOP_FRINGE_LOADS
-#define SGEMM_KLOOP_F4 SGEMM_KLOOP_DEEP SGEMM_KLOOP_FRINGE_LOADS
   if constexpr (T::FR && BM == 256 && !TA && !TB) SGEMM_KLOOP_PRELUDE(256x128_NN_F, SGEMM_KLOOP_FRINGE_LOADS);
   else if constexpr (T::FR && BM == 256 && !TA) SGEMM_KLOOP_PRELUDE(256x128_NT_F, SGEMM_KLOOP_FRINGE_LOADS);
   else if constexpr (T::FR && BM == 256 && !TB) SGEMM_KLOOP_PRELUDE(256x128_TN_F, SGEMM_KLOOP_FRINGE_LOADS);
@@ -461,8 +464,6 @@ __global__ __launch_bounds__(T::THREADS) void k_kloop(Problem p, int64_t tiles_m
   uint32_t pairs = static_cast<uint32_t>(stages / 2);
   const uint32_t odd = static_cast<uint32_t>(stages % 2);
   floatx16 a0 = {}, a1 = {}, a2 = {}, a3 = {};
-#define SGEMM_KLOOP_FW SGEMM_KLOOP_FRINGE_WORDS
-#define SGEMM_KLOOP_FW4 SGEMM_KLOOP_DEEP_STORES SGEMM_KLOOP_FRINGE_WORDS
   if constexpr (T::FR && BM == 256 && !TA && !TB) SGEMM_KLOOP_LOOP(256x128_NN_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FW);
   else if constexpr (T::FR && BM == 256 && !TA) SGEMM_KLOOP_LOOP(256x128_NT_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FW);
   else if constexpr (T::FR && BM == 256 && !TB) SGEMM_KLOOP_LOOP(256x128_TN_F, SGEMM_KLOOP_FRINGE_LOADS, SGEMM_KLOOP_FW);
