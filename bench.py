@@ -335,6 +335,24 @@ def vendor_timed(prob: Problem, steps: int, warmup: int, min_warm_ms: float = 0.
     return Timing(float("nan"), [a.elapsed_time(b) for a, b in ev], wc, wms)
 
 
+def vendor_region(prob: Problem, steps: int) -> float:
+    """The vendor call timed like the headline's region: `steps`
+    back-to-back calls between two HIP events (run after vendor_timed, so
+    the clocks are up).  Returns ms per call."""
+    import torch
+    w = prob.w
+    stream = torch.cuda.current_stream()
+    prob.refill()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        prob.copies[i].addmm_(prob.dA, prob.dB, beta=w.beta, alpha=w.alpha)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def bench_one(w, level, steps, warmup, prob=None, min_warm_ms=0.0):
     from dense_fp32_matrix_row_amd import sgemm
     prob = prob or Problem(w, max(steps, 1))
@@ -479,11 +497,15 @@ def main():
     }
     if args.vendor:
         vt = vendor_timed(prob, steps, warmup, args.warm_ms)
+        v_ms = vendor_region(prob, steps)
         line["vendor_blas"] = {"library": "torch.addmm (rocBLAS/hipBLASLt), FP32, TF32 off",
-                               "kernel_ms_mean": round(vt.mean, 4),
-                               "kernel_ms_median": round(vt.median, 4),
-                               "tflops": round(w.flops / (vt.mean * 1e-3) / 1e12, 3),
-                               "note": "context only; not part of libsgemm"}
+                               "kernel_ms": round(v_ms, 4),
+                               "tflops": round(w.flops / (v_ms * 1e-3) / 1e12, 3),
+                               "per_call_pass": {"kernel_ms_mean": round(vt.mean, 4),
+                                                 "kernel_ms_median": round(vt.median, 4)},
+                               "note": "context only; not part of libsgemm; kernel_ms between two "
+                                       "HIP events around the back-to-back calls, as for kernel_ms "
+                                       "above"}
     if not args.no_cpu:
         def rows_out(r):
             # one more call on a fresh C, outside any timed region
