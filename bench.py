@@ -16,8 +16,10 @@ the two HIP events on the launch stream that bracket the timed region's K
 back-to-back calls, against the 157.3 TFLOP/s FP32 matrix peak), and the
 CPU reference timed on the host on a bounded sample of the same problem
 (its first rows), whose output also checks the GPU's rows.  The timed
-region holds no per-call events: an event pair around every call costs
-about 1 % at 4096^3 (measured), slowing the calls it brackets.  The
+region holds no per-call events: an event pair around every call leaves
+an idle gap between consecutive kernels (back to back there is none) and
+costs the timed region about 1 % at 4096^3 (measured); the kernels
+themselves run as long either way.  The
 per-call median, mean and min come from a second pass of K calls after the
 timed region, one event pair around each call, and are reported beside the
 line's figures.
