@@ -5,8 +5,10 @@ multiple of 64, 128 or 256, or one to seventeen off it --, grids one row
 and / or column past a multiple, deep K over small grids), all four
 operand orientations, padded leading dimensions, bases offset
 by one to three elements, and alpha / beta including beta = 0 over a C full
-of NaN.  The guarded harness also checks that nothing outside C's window
-changes.  The draws are fixed by the seed, so a failure names its case.
+of NaN; and, for every forced rung of the ladder (levels 0-9), medium
+shapes with partial block tiles, ragged K, padded strides and offsets.  The
+guarded harness also checks that nothing outside C's window changes.  The
+draws are fixed by the seed, so a failure names its case.
 """
 
 from __future__ import annotations
@@ -103,3 +105,38 @@ def test_random_problem_matches_reference(case):
     ref = oracle.oracle_sgemm(A, B, C, alpha, beta)
     err = oracle.normalised_error(out, ref, C, alpha, beta, strict=True)
     assert err <= BOUND, (case, M, N, K, ta, tb, err)
+
+
+RUNG_CASES = 8
+
+
+def _rung_cases(level):
+    """Medium shapes for a forced rung: partial block tiles of every size
+    the rungs use (up to 256 x 128), ragged K, padded strides, offsets."""
+    rng = np.random.default_rng(20261203 + level)
+    out = []
+    for _ in range(RUNG_CASES):
+        M, N = (int(v) for v in rng.integers(100, 700, 2))
+        K = int(rng.integers(1, 600))
+        alpha = float(rng.choice([1.0, -1.5, 0.5]))
+        beta = float(rng.choice([0.0, 1.0, -2.0]))
+        pads = tuple(int(v) for v in rng.integers(0, 6, 3))
+        offs = tuple(int(v) for v in rng.integers(0, 4, 3))
+        out.append((M, N, K, alpha, beta, pads, offs))
+    return out
+
+
+@pytest.mark.parametrize("level", range(10))
+def test_random_problems_every_rung(level):
+    print(f"[random rung] level {level}", flush=True)
+    for i, (M, N, K, alpha, beta, pads, offs) in enumerate(_rung_cases(level)):
+        A, B, C = inputs.make_abc(M, N, K, 41000 + 10 * level + i)
+        if beta == 0.0:
+            C = np.full_like(C, np.nan)  # must not be read
+        c = gh.Case(M, N, K, alpha, beta, A, B, C, lda=K + pads[0], ldb=N + pads[1], ldc=N + pads[2],
+                    a_off=offs[0], b_off=offs[1], c_off=offs[2])
+        out, st = gh.run(c, level)
+        assert st == 0, sgemm.hip_sgemm_status_string(st)
+        ref = oracle.oracle_sgemm(A, B, C, alpha, beta)
+        err = oracle.normalised_error(out, ref, C, alpha, beta, strict=True)
+        assert err <= BOUND, (level, i, M, N, K, pads, offs, err)
