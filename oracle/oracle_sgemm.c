@@ -99,9 +99,11 @@ int oracle_default_threads(void)
 /*
  * oracle_sgemm_f64: ref and sumabs are caller-allocated dense M x N float64
  * buffers (row stride N).  nthreads <= 0 means oracle_default_threads().
- * Returns the number of threads used, or a negative value for invalid
- * arguments (-1 M, -2 N, -3 K, -6 lda, -8 ldb, -11 ldc, -5/-7/-10 null
- * pointers needed for the call, -13 output pointers).
+ * Returns the number of threads that ran (fewer than asked if a thread
+ * could not be started: its rows then run on the calling thread), or a
+ * negative value for invalid arguments (-1 M, -2 N, -3 K, -6 lda, -8 ldb,
+ * -11 ldc, -5/-7/-10 null pointers needed for the call, -13 output
+ * pointers) or -14 when the bookkeeping could not be allocated.
  */
 int oracle_sgemm_f64(int64_t M, int64_t N, int64_t K, float alpha,
                      const float *A, int64_t lda, const float *B, int64_t ldb,
@@ -159,5 +161,5 @@ int oracle_sgemm_f64(int64_t M, int64_t N, int64_t K, float alpha,
     for (int t = 1; t <= started; ++t) pthread_join(tids[t], NULL);
     free(jobs);
     free(tids);
-    return nthreads;
+    return started + 1;  /* the threads created, and this one */
 }
